@@ -1,0 +1,254 @@
+"""Float64 CPU oracle for the frame-wise Gated DeltaNet (GDN) frame scan.
+
+TEST INFRASTRUCTURE. This module is the correctness reference for the HIP
+library in ``frame_wise_gated_amd``. Only the test suite, the smoke check in
+``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` may import or
+call it. The product path never routes through it, and it imports nothing from
+the product package (the two share no code).
+
+It is the plain definition written out, one frame at a time, in float64, with
+the pages' notation. Sources (web pages, cited by title and section):
+
+* [P1] blog.hotdry.top, "SANA-WM: 2.6B 参数分布式 Diffusion Transformer 实现消费级
+  GPU 分钟级 720p 视频生成" -- section "混合线性注意力" (the three equations for
+  S_t, M_t, U_t and the paragraph on the 1/sqrt(D*S) key scaling) and section
+  "显存分片: Context-Parallel 的工程实现" (the composite identity
+  S_end = S_start * C_p + H_p).
+* [P2] xiejiayun.github.io, "好文共赏 | SANA-WM" -- section 2.1 "Frame-wise GDN"
+  (token-level GDN equation, frame-wise equation, trace inequality).
+* [P3] hyper.ai paper page 2605.15178 -- "方法" (method) section: the
+  chunk-causal variant restarts its reverse temporal scan at every chunk
+  boundary.
+
+Array conventions (per batch b and head h, frames t = 0..T-1, tokens s):
+q, k, v are [B, H, T, S, D]; beta is [B, H, T, S]; gamma is [B, H, T];
+states are [B, H, T, D, D] with entry (i, j) = (value dim, key dim).
+The pages write K_t, V_t as D x S matrices whose columns are tokens, so the
+page's K_t is ``k[t].T`` here.
+
+Readings where the pages are silent (each also listed in the design notes):
+* the readout of token s in frame t uses the state after frame t: o = S_t q;
+* q is used as given (no ReLU, no scaling);
+* the reverse scan of the chunk-causal variant is R_t = R_{t+1} M_t + U_t,
+  started from zero after the last frame of each chunk, and the
+  bidirectional readout is o = (S_t + R_t) q;
+* chunks of the reverse scan are [0, L), [L, 2L), ...; the last may be short.
+
+Every function here is pinned by tests under ``tests/`` (closed forms, brute
+force, exact rational arithmetic, invariants); none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "default_key_scale",
+    "prepare_keys",
+    "frame_terms",
+    "transition",
+    "scan_fwd",
+    "scan_reverse_chunked",
+    "scan_bidir_chunked",
+    "compose",
+    "combine",
+    "readout",
+]
+
+
+def default_key_scale(D: int, S: int) -> float:
+    """c = 1/sqrt(D*S): [P1] "混合线性注意力" key-scaling paragraph; [P2] 2.1."""
+    return 1.0 / math.sqrt(float(D) * float(S))
+
+
+def prepare_keys(k, key_scale: float | None = None):
+    """K_hat = ReLU(k) * c, elementwise, in float64.
+
+    [P1] "混合线性注意力": keys are scaled by 1/sqrt(D*S); [P2] 2.1 states the
+    trace bound that this scaling buys. ``key_scale`` <= 0 or None selects the
+    default c for the array's own D (last axis) and S (second-to-last axis).
+    """
+    k = np.asarray(k, dtype=np.float64)
+    if key_scale is None or key_scale <= 0:
+        key_scale = default_key_scale(k.shape[-1], k.shape[-2])
+    return np.maximum(k, 0.0) * float(key_scale)
+
+
+def frame_terms(k_hat_t, v_t, beta_t):
+    """A_t = K_t beta_t K_t^T and U_t = V_t beta_t K_t^T for one frame.
+
+    [P1] "混合线性注意力", the M_t and U_t equations; beta_t is the diagonal
+    matrix of per-token gates. Inputs are [S, D] (tokens as rows), so the
+    page's D x S matrices are the transposes.
+    """
+    Kp = np.asarray(k_hat_t, dtype=np.float64).T  # D x S, columns are tokens
+    Vp = np.asarray(v_t, dtype=np.float64).T
+    b = np.asarray(beta_t, dtype=np.float64)
+    KB = Kp * b[None, :]  # K_t beta_t
+    A = KB @ Kp.T
+    U = Vp @ (b[:, None] * Kp.T)
+    return A, U
+
+
+def transition(A_t, gamma_t):
+    """M_t = gamma_t (I - A_t): [P1] "混合线性注意力", the M_t equation."""
+    D = A_t.shape[0]
+    return float(gamma_t) * (np.eye(D) - A_t)
+
+
+def readout(state, q_t):
+    """o_{t,s} = state q_{t,s} for every token: rows of the result are tokens."""
+    return np.asarray(q_t, dtype=np.float64) @ state.T
+
+
+def _keys(k, key_scale, keys_prepared):
+    if keys_prepared:
+        return np.asarray(k, dtype=np.float64)
+    return prepare_keys(k, key_scale)
+
+
+def _head_fwd(q, kh, v, beta, gamma, s0, t0, t1):
+    """Forward frame loop over frames [t0, t1) of one head from state s0."""
+    D = kh.shape[-1]
+    S_state = np.zeros((D, D)) if s0 is None else np.array(s0, dtype=np.float64)
+    states = []
+    outs = []
+    for t in range(t0, t1):
+        A, U = frame_terms(kh[t], v[t], beta[t])
+        M = transition(A, gamma[t])
+        S_state = S_state @ M + U  # [P1] the S_t equation
+        states.append(S_state.copy())
+        if q is not None:
+            outs.append(readout(S_state, q[t]))
+    return S_state, states, outs
+
+
+def scan_fwd(q, k, v, beta, gamma, s0=None, key_scale=None, keys_prepared=False,
+             with_output=True):
+    """Causal frame scan S_t = S_{t-1} M_t + U_t with per-token readout.
+
+    Inputs as in the module docstring; ``s0`` is [B, H, D, D] or None (zero).
+    Returns a dict with ``states`` [B,H,T,D,D], ``s_final`` [B,H,D,D] and
+    ``o`` [B,H,T,S,D] (absent when ``with_output`` is False or q is None).
+    """
+    k = np.asarray(k)
+    B, H, T, S, D = k.shape
+    states = np.zeros((B, H, T, D, D))
+    s_final = np.zeros((B, H, D, D))
+    o = np.zeros((B, H, T, S, D)) if (with_output and q is not None) else None
+    for b in range(B):
+        for h in range(H):
+            kh = _keys(k[b, h], key_scale, keys_prepared)
+            qh = None if o is None else q[b, h]
+            sinit = None if s0 is None else s0[b, h]
+            fin, st, outs = _head_fwd(qh, kh, v[b, h], beta[b, h], gamma[b, h],
+                                      sinit, 0, T)
+            s_final[b, h] = fin
+            if T:
+                states[b, h] = np.stack(st)
+            if o is not None and T:
+                o[b, h] = np.stack(outs)
+    out = {"states": states, "s_final": s_final}
+    if o is not None:
+        out["o"] = o
+    return out
+
+
+def chunk_bounds(T: int, chunk_len: int):
+    """Uniform chunks [0, L), [L, 2L), ... of the chunk-causal reverse scan."""
+    return [(a, min(a + chunk_len, T)) for a in range(0, T, chunk_len)]
+
+
+def scan_reverse_chunked(k, v, beta, gamma, chunk_len, key_scale=None,
+                         keys_prepared=False):
+    """Reverse temporal scan restarted at every chunk boundary ([P3], method).
+
+    Inside chunk [a, b): R_{b-1} = U_{b-1} (zero state after the chunk's last
+    frame) and R_t = R_{t+1} M_t + U_t for t = b-2 down to a, with each frame's
+    own M_t, U_t. Returns ``states_rev`` [B,H,T,D,D].
+    """
+    k = np.asarray(k)
+    B, H, T, S, D = k.shape
+    rev = np.zeros((B, H, T, D, D))
+    for b in range(B):
+        for h in range(H):
+            kh = _keys(k[b, h], key_scale, keys_prepared)
+            for (a, e) in chunk_bounds(T, chunk_len):
+                R = np.zeros((D, D))
+                for t in range(e - 1, a - 1, -1):
+                    A, U = frame_terms(kh[t], v[b, h, t], beta[b, h, t])
+                    R = R @ transition(A, gamma[b, h, t]) + U
+                    rev[b, h, t] = R
+    return rev
+
+
+def scan_bidir_chunked(q, k, v, beta, gamma, chunk_len, s0=None, key_scale=None,
+                       keys_prepared=False):
+    """Chunk-causal bidirectional scan: causal forward states plus the reverse
+    chunk scan, read out together as o = (S_t + R_t) q.
+
+    ``chunk_len`` >= T gives the full-sequence bidirectional variant.
+    """
+    fwd = scan_fwd(q, k, v, beta, gamma, s0=s0, key_scale=key_scale,
+                   keys_prepared=keys_prepared, with_output=False)
+    rev = scan_reverse_chunked(k, v, beta, gamma, chunk_len, key_scale=key_scale,
+                               keys_prepared=keys_prepared)
+    B, H, T, S, D = np.asarray(k).shape
+    o = np.zeros((B, H, T, S, D))
+    for b in range(B):
+        for h in range(H):
+            for t in range(T):
+                o[b, h, t] = readout(fwd["states"][b, h, t] + rev[b, h, t], q[b, h, t])
+    return {"states_fwd": fwd["states"], "states_rev": rev,
+            "s_final": fwd["s_final"], "o": o}
+
+
+def compose(k, v, beta, gamma, offsets, key_scale=None, keys_prepared=False):
+    """Per-chunk affine composites (C_p, H_p) with S_end = S_start C_p + H_p.
+
+    [P1] "显存分片: Context-Parallel 的工程实现": C_p is the ordered product of
+    the chunk's transitions and H_p the chunk's scan from a zero state.
+    ``offsets`` holds P+1 ascending frame indices, offsets[0] = 0 and
+    offsets[P] = T. Returns C, Hc as [B, H, P, D, D].
+    """
+    k = np.asarray(k)
+    B, H, T, S, D = k.shape
+    P = len(offsets) - 1
+    C = np.zeros((B, H, P, D, D))
+    Hc = np.zeros((B, H, P, D, D))
+    for b in range(B):
+        for h in range(H):
+            kh = _keys(k[b, h], key_scale, keys_prepared)
+            for p in range(P):
+                Cp = np.eye(D)
+                Hp = np.zeros((D, D))
+                for t in range(offsets[p], offsets[p + 1]):
+                    A, U = frame_terms(kh[t], v[b, h, t], beta[b, h, t])
+                    M = transition(A, gamma[b, h, t])
+                    Cp = Cp @ M
+                    Hp = Hp @ M + U
+                C[b, h, p] = Cp
+                Hc[b, h, p] = Hp
+    return C, Hc
+
+
+def combine(C, Hc, s0=None):
+    """Exact chunk start states from the composites, left to right.
+
+    s_start[0] = S0 and s_start[p+1] = s_start[p] C_p + H_p ([P1], the
+    composite identity applied chunk after chunk). Returns s_start
+    [B, H, P, D, D] and the state after the last chunk [B, H, D, D].
+    """
+    B, H, P, D, _ = C.shape
+    s_start = np.zeros((B, H, P, D, D))
+    s_end = np.zeros((B, H, D, D))
+    for b in range(B):
+        for h in range(H):
+            X = np.zeros((D, D)) if s0 is None else np.array(s0[b, h], dtype=np.float64)
+            for p in range(P):
+                s_start[b, h, p] = X
+                X = X @ C[b, h, p] + Hc[b, h, p]
+            s_end[b, h] = X
+    return s_start, s_end

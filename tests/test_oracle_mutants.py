@@ -1,0 +1,146 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch every one of them. A mutant that no pin rejects would mean the oracle is
+not pinned against that class of error."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import gdn_oracle as orc
+
+import oracle_pins as pins
+
+
+def _head_fwd_variant(kind):
+    def f(q, kh, v, beta, gamma, s0, t0, t1):
+        D = kh.shape[-1]
+        S_state = np.zeros((D, D)) if s0 is None else np.array(s0, dtype=np.float64)
+        states, outs = [], []
+        for t in range(t0, t1):
+            A, U = orc.frame_terms(kh[t], v[t], beta[t])
+            M = orc.transition(A, gamma[t])
+            prev = S_state
+            if kind == "left_multiply":
+                S_state = M @ S_state + U
+            elif kind == "gamma_on_U":
+                S_state = gamma[t] * (S_state @ (np.eye(D) - A) + U)
+            elif kind == "no_delta":
+                S_state = gamma[t] * S_state + U
+            else:
+                S_state = S_state @ M + U
+            states.append(S_state.copy())
+            if q is not None:
+                src = prev if kind == "readout_prev_state" else S_state
+                outs.append(orc.readout(src, q[t]))
+        return S_state, states, outs
+    return f
+
+
+def _frame_terms_variant(kind):
+    good = orc.frame_terms
+
+    def f(k_hat_t, v_t, beta_t):
+        A, U = good(k_hat_t, v_t, beta_t)
+        Kp = np.asarray(k_hat_t, dtype=np.float64).T
+        Vp = np.asarray(v_t, dtype=np.float64).T
+        if kind == "U_transposed":
+            return A, U.T
+        if kind == "U_no_beta":
+            return A, Vp @ Kp.T
+        if kind == "A_no_beta":
+            return Kp @ Kp.T, U
+        if kind == "beta_squared":
+            b = np.asarray(beta_t, dtype=np.float64)
+            return (Kp * b * b) @ Kp.T, U
+        raise AssertionError(kind)
+    return f
+
+
+def _compose_reversed(k, v, beta, gamma, offsets, key_scale=None, keys_prepared=False):
+    k = np.asarray(k)
+    B, H, T, S, D = k.shape
+    P = len(offsets) - 1
+    C = np.zeros((B, H, P, D, D))
+    Hc = np.zeros((B, H, P, D, D))
+    for b in range(B):
+        for h in range(H):
+            kh = orc._keys(k[b, h], key_scale, keys_prepared)
+            for p in range(P):
+                Cp, Hp = np.eye(D), np.zeros((D, D))
+                for t in range(offsets[p], offsets[p + 1]):
+                    A, U = orc.frame_terms(kh[t], v[b, h, t], beta[b, h, t])
+                    M = orc.transition(A, gamma[b, h, t])
+                    Cp = M @ Cp
+                    Hp = Hp @ M + U
+                C[b, h, p], Hc[b, h, p] = Cp, Hp
+    return C, Hc
+
+
+def _combine_swapped(C, Hc, s0=None):
+    B, H, P, D, _ = C.shape
+    s_start = np.zeros((B, H, P, D, D))
+    s_end = np.zeros((B, H, D, D))
+    for b in range(B):
+        for h in range(H):
+            X = np.zeros((D, D)) if s0 is None else np.array(s0[b, h], dtype=np.float64)
+            for p in range(P):
+                s_start[b, h, p] = X
+                X = C[b, h, p] @ X + Hc[b, h, p]
+            s_end[b, h] = X
+    return s_start, s_end
+
+
+def _reverse_off_by_one(k, v, beta, gamma, chunk_len, key_scale=None, keys_prepared=False):
+    k = np.asarray(k)
+    B, H, T, S, D = k.shape
+    rev = np.zeros((B, H, T, D, D))
+    for b in range(B):
+        for h in range(H):
+            kh = orc._keys(k[b, h], key_scale, keys_prepared)
+            for (a, e) in orc.chunk_bounds(T, chunk_len):
+                R = np.zeros((D, D))
+                for t in range(e - 1, a - 1, -1):
+                    tt = min(t + 1, e - 1)  # gates of the wrong frame
+                    A, _ = orc.frame_terms(kh[tt], v[b, h, tt], beta[b, h, tt])
+                    _, U = orc.frame_terms(kh[t], v[b, h, t], beta[b, h, t])
+                    R = R @ orc.transition(A, gamma[b, h, tt]) + U
+                    rev[b, h, t] = R
+    return rev
+
+
+MUTANTS = {
+    "U_transposed": ("frame_terms", _frame_terms_variant("U_transposed")),
+    "U_no_beta": ("frame_terms", _frame_terms_variant("U_no_beta")),
+    "A_no_beta": ("frame_terms", _frame_terms_variant("A_no_beta")),
+    "beta_squared": ("frame_terms", _frame_terms_variant("beta_squared")),
+    "M_plus_A": ("transition", lambda A, g: float(g) * (np.eye(A.shape[0]) + A)),
+    "M_no_gamma": ("transition", lambda A, g: np.eye(A.shape[0]) - A),
+    "left_multiply": ("_head_fwd", _head_fwd_variant("left_multiply")),
+    "gamma_on_U": ("_head_fwd", _head_fwd_variant("gamma_on_U")),
+    "no_delta": ("_head_fwd", _head_fwd_variant("no_delta")),
+    "readout_prev_state": ("_head_fwd", _head_fwd_variant("readout_prev_state")),
+    "readout_transposed": ("readout", lambda st, q: np.asarray(q, dtype=np.float64) @ st),
+    "scale_1_over_sqrt_S": ("default_key_scale", lambda D, S: 1.0 / math.sqrt(S)),
+    "scale_1_over_D": ("default_key_scale", lambda D, S: 1.0 / D / math.sqrt(S)),
+    "no_relu": ("prepare_keys", lambda k, key_scale=None: np.asarray(k, dtype=np.float64)
+                * (key_scale if key_scale and key_scale > 0
+                   else 1.0 / math.sqrt(np.shape(k)[-1] * np.shape(k)[-2]))),
+    "reverse_not_reset": ("chunk_bounds", lambda T, L: [(0, T)]),
+    "reverse_wrong_gates": ("scan_reverse_chunked", _reverse_off_by_one),
+    "compose_reversed_product": ("compose", _compose_reversed),
+    "combine_left_multiply": ("combine", _combine_swapped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(orc, attr, fn)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin rejects the mutant {name}"
