@@ -1,0 +1,388 @@
+// C ABI of libgdn: argument checks, workspace layout and launch sequencing.
+// Every check runs on the host before anything is enqueued.
+#include <stdint.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "gdn.h"
+#include "gdn_common.h"
+
+namespace {
+
+using gdn::Shape;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p % 16) == 0; }
+
+gdn_status check_desc(const gdn_desc* d, Shape* sh) {
+  if (d == nullptr) return GDN_EINVAL;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->S < 1 || d->D < 1) return GDN_EINVAL;
+  if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) return GDN_EINVAL;
+  if ((d->flags & ~GDN_KEYS_PREPARED) != 0) return GDN_EINVAL;
+  if (!(std::isfinite(d->key_scale))) return GDN_EINVAL;
+  if (d->D != 16 && d->D != 32 && d->D != 64 && d->D != 128) return GDN_EUNSUPPORTED;
+  // element counts must stay far from 64-bit overflow
+  const double elems = (double)d->B * d->H * d->T * d->S * d->D;
+  if (elems > 4.0e18) return GDN_EINVAL;
+  sh->B = d->B;
+  sh->H = d->H;
+  sh->T = d->T;
+  sh->S = d->S;
+  sh->D = d->D;
+  sh->io = d->io_dtype;
+  sh->prepared = (d->flags & GDN_KEYS_PREPARED) ? 1 : 0;
+  if (sh->prepared) {
+    sh->c = 1.0f;
+  } else if (d->key_scale > 0.f) {
+    sh->c = d->key_scale;
+  } else {
+    sh->c = (float)(1.0 / std::sqrt((double)d->D * (double)d->S));
+  }
+  return GDN_OK;
+}
+
+struct Layout {
+  size_t terms = 0, partial = 0, states = 0, rev = 0, compC = 0, compH = 0, start = 0;
+  size_t total = 0;
+  int n_split = 1;
+};
+
+Layout layout(const Shape& sh, int P) {
+  Layout L;
+  const size_t DD = (size_t)sh.D * sh.D * sizeof(float);
+  const size_t FH = (size_t)sh.FH();
+  const size_t BH = (size_t)sh.BH();
+  L.n_split = gdn::terms_split(sh);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  L.terms = take(FH * 2 * DD);
+  L.partial = take(L.n_split > 1 ? FH * L.n_split * 2 * DD : 0);
+  L.states = take(FH * DD);
+  L.rev = take(FH * DD);
+  const size_t Pn = (size_t)(P > 1 ? P : 1);
+  L.compC = take(BH * Pn * DD);
+  L.compH = take(BH * Pn * DD);
+  L.start = take(BH * Pn * DD);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+#define GDN_HIP(x)                                 \
+  do {                                             \
+    if ((x) != hipSuccess) return GDN_EHIP;        \
+  } while (0)
+
+// Phase 1 into the workspace terms buffer [FH][2D][D].
+gdn_status run_terms(const Shape& sh, const Layout& L, const void* k, const void* v,
+                     const float* beta, void* ws, hipStream_t st) {
+  const int64_t DD = (int64_t)sh.D * sh.D;
+  float* terms = at<float>(ws, L.terms);
+  gdn::TermsOut direct{terms, terms + DD, 2 * DD, 0};
+  if (L.n_split == 1) {
+    GDN_HIP(gdn::launch_terms(sh, k, v, beta, 1, direct, st));
+  } else {
+    float* part = at<float>(ws, L.partial);
+    gdn::TermsOut po{part, part + DD, (int64_t)L.n_split * 2 * DD, 2 * DD};
+    GDN_HIP(gdn::launch_terms(sh, k, v, beta, L.n_split, po, st));
+    GDN_HIP(gdn::launch_reduce_partials(sh, part, L.n_split, direct, st));
+  }
+  return GDN_OK;
+}
+
+void uniform_offsets(int* offs, int T, int P) {
+  for (int p = 0; p <= P; ++p) offs[p] = (int)(((int64_t)p * T) / P);
+}
+
+// Forward scan (sequential or composite) from the terms buffer.
+gdn_status run_forward(const Shape& sh, const Layout& L, const float* gamma, const float* s0,
+                       float* states, float* s_final, int P, void* ws, hipStream_t st) {
+  const int64_t DD = (int64_t)sh.D * sh.D;
+  const float* terms = at<float>(ws, L.terms);
+  if (P <= 1) {
+    gdn::ScanParams p;
+    memset(&p, 0, sizeof(p));
+    p.terms = terms;
+    p.gamma = gamma;
+    p.T = sh.T;
+    p.nchunk = 1;
+    p.mode = gdn::SCAN_FORWARD;
+    p.init = s0;
+    p.init_bh_stride = DD;
+    p.init_c_stride = 0;
+    p.states = states;
+    p.finA = s_final;
+    p.fin_bh_stride = DD;
+    p.fin_last_only = 1;
+    p.offsets[0] = 0;
+    p.offsets[1] = sh.T;
+    GDN_HIP(gdn::launch_scan(sh, p, st));
+    return GDN_OK;
+  }
+  float* C = at<float>(ws, L.compC);
+  float* H = at<float>(ws, L.compH);
+  float* start = at<float>(ws, L.start);
+  {
+    gdn::ScanParams p;
+    memset(&p, 0, sizeof(p));
+    p.terms = terms;
+    p.gamma = gamma;
+    p.T = sh.T;
+    p.nchunk = P;
+    p.mode = gdn::SCAN_COMPOSE;
+    p.finA = C;
+    p.finB = H;
+    p.fin_bh_stride = (int64_t)P * DD;
+    p.fin_c_stride = DD;
+    uniform_offsets(p.offsets, sh.T, P);
+    GDN_HIP(gdn::launch_scan(sh, p, st));
+  }
+  {
+    gdn::CombineParams cp{C, H, s0, start, P};
+    GDN_HIP(gdn::launch_combine(sh, cp, st));
+  }
+  {
+    gdn::ScanParams p;
+    memset(&p, 0, sizeof(p));
+    p.terms = terms;
+    p.gamma = gamma;
+    p.T = sh.T;
+    p.nchunk = P;
+    p.mode = gdn::SCAN_FORWARD;
+    p.init = start;
+    p.init_bh_stride = (int64_t)P * DD;
+    p.init_c_stride = DD;
+    p.states = states;
+    p.finA = s_final;
+    p.fin_bh_stride = DD;
+    p.fin_last_only = 1;
+    uniform_offsets(p.offsets, sh.T, P);
+    GDN_HIP(gdn::launch_scan(sh, p, st));
+  }
+  return GDN_OK;
+}
+
+// No frames: the final state is the initial state.
+gdn_status run_empty(const Shape& sh, const float* s0, float* s_final, hipStream_t st) {
+  if (s_final == nullptr) return GDN_OK;
+  const int64_t n = sh.BH() * sh.D * sh.D;
+  if (s0)
+    GDN_HIP(gdn::launch_copy_f32(s0, s_final, n, st));
+  else
+    GDN_HIP(gdn::launch_zero_f32(s_final, n, st));
+  return GDN_OK;
+}
+
+gdn_status check_ws(const Layout& L, const void* ws, size_t ws_bytes) {
+  if (ws_bytes < L.total) return GDN_EWORKSPACE;
+  if (L.total > 0 && ws == nullptr) return GDN_EINVAL;
+  if (((uintptr_t)ws % kAlign) != 0) return GDN_EINVAL;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_str(int32_t s) {
+  switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_EINVAL: return "GDN_EINVAL: invalid argument";
+    case GDN_EUNSUPPORTED: return "GDN_EUNSUPPORTED: unsupported configuration";
+    case GDN_EWORKSPACE: return "GDN_EWORKSPACE: workspace too small";
+    case GDN_EHIP: return "GDN_EHIP: HIP launch failed";
+    default: return "GDN: unknown status";
+  }
+}
+
+gdn_status gdn_workspace_bytes(const gdn_desc* desc, int32_t n_time_chunks, size_t* bytes) {
+  Shape sh;
+  gdn_status s = check_desc(desc, &sh);
+  if (s != GDN_OK) return s;
+  if (bytes == nullptr || n_time_chunks < 1 || n_time_chunks > GDN_MAX_TIME_CHUNKS)
+    return GDN_EINVAL;
+  *bytes = layout(sh, n_time_chunks).total;
+  return GDN_OK;
+}
+
+gdn_status gdn_prepare(const gdn_desc* desc, const void* k, void* k_hat, void* stream) {
+  Shape sh;
+  gdn_status s = check_desc(desc, &sh);
+  if (s != GDN_OK) return s;
+  if (sh.prepared) return GDN_EINVAL;
+  if (sh.FH() == 0) return GDN_OK;
+  if (k == nullptr || k_hat == nullptr || !aligned16(k) || !aligned16(k_hat)) return GDN_EINVAL;
+  GDN_HIP(gdn::launch_prepare(sh, k, k_hat, (hipStream_t)stream));
+  return GDN_OK;
+}
+
+gdn_status gdn_frame_terms(const gdn_desc* desc, const void* k, const void* v, const float* beta,
+                           float* A, float* U, void* ws, size_t ws_bytes, void* stream) {
+  Shape sh;
+  gdn_status s = check_desc(desc, &sh);
+  if (s != GDN_OK) return s;
+  if (sh.FH() == 0 || (A == nullptr && U == nullptr)) return GDN_OK;
+  if (!k || !v || !beta) return GDN_EINVAL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(A) || !aligned16(U)) return GDN_EINVAL;
+  Layout L = layout(sh, 1);
+  if ((s = check_ws(L, ws, ws_bytes)) != GDN_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t DD = (int64_t)sh.D * sh.D;
+  gdn::TermsOut direct{A, U, DD, 0};
+  if (L.n_split == 1) {
+    GDN_HIP(gdn::launch_terms(sh, k, v, beta, 1, direct, st));
+  } else {
+    float* part = at<float>(ws, L.partial);
+    gdn::TermsOut po{part, part + DD, (int64_t)L.n_split * 2 * DD, 2 * DD};
+    GDN_HIP(gdn::launch_terms(sh, k, v, beta, L.n_split, po, st));
+    GDN_HIP(gdn::launch_reduce_partials(sh, part, L.n_split, direct, st));
+  }
+  return GDN_OK;
+}
+
+gdn_status gdn_scan_fwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                        const float* beta, const float* gamma, const float* s0, float* states,
+                        float* s_final, void* o, int32_t n_time_chunks, void* ws, size_t ws_bytes,
+                        void* stream) {
+  Shape sh;
+  gdn_status s = check_desc(desc, &sh);
+  if (s != GDN_OK) return s;
+  if (n_time_chunks < 1 || n_time_chunks > GDN_MAX_TIME_CHUNKS) return GDN_EINVAL;
+  if (sh.T > 0 && n_time_chunks > sh.T) return GDN_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(s0) || !aligned16(states) ||
+      !aligned16(s_final) || !aligned16(o))
+    return GDN_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  if (sh.BH() == 0) return GDN_OK;
+  if (sh.T == 0) return run_empty(sh, s0, s_final, st);
+  if (states == nullptr && s_final == nullptr && o == nullptr) return GDN_OK;
+  if (!k || !v || !beta || !gamma || (o && !q)) return GDN_EINVAL;
+  Layout L = layout(sh, n_time_chunks);
+  if ((s = check_ws(L, ws, ws_bytes)) != GDN_OK) return s;
+  float* st_buf = states ? states : (o ? at<float>(ws, L.states) : nullptr);
+  if ((s = run_terms(sh, L, k, v, beta, ws, st)) != GDN_OK) return s;
+  if ((s = run_forward(sh, L, gamma, s0, st_buf, s_final, n_time_chunks, ws, st)) != GDN_OK) return s;
+  if (o) GDN_HIP(gdn::launch_readout(sh, q, st_buf, nullptr, o, st));
+  return GDN_OK;
+}
+
+gdn_status gdn_scan_bidir_chunked(const gdn_desc* desc, const void* q, const void* k,
+                                  const void* v, const float* beta, const float* gamma,
+                                  const float* s0, int32_t chunk_len, float* states_fwd,
+                                  float* states_rev, float* s_final, void* o,
+                                  int32_t n_time_chunks, void* ws, size_t ws_bytes, void* stream) {
+  Shape sh;
+  gdn_status s = check_desc(desc, &sh);
+  if (s != GDN_OK) return s;
+  if (chunk_len < 1) return GDN_EINVAL;
+  if (n_time_chunks < 1 || n_time_chunks > GDN_MAX_TIME_CHUNKS) return GDN_EINVAL;
+  if (sh.T > 0 && n_time_chunks > sh.T) return GDN_EINVAL;
+  const int64_t n_rev = sh.T > 0 ? ((int64_t)sh.T + chunk_len - 1) / chunk_len : 0;
+  if (n_rev > gdn::kMaxChunks) return GDN_EUNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(s0) ||
+      !aligned16(states_fwd) || !aligned16(states_rev) || !aligned16(s_final) || !aligned16(o))
+    return GDN_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  if (sh.BH() == 0) return GDN_OK;
+  if (sh.T == 0) return run_empty(sh, s0, s_final, st);
+  if (!states_fwd && !states_rev && !s_final && !o) return GDN_OK;
+  if (!k || !v || !beta || !gamma || (o && !q)) return GDN_EINVAL;
+  Layout L = layout(sh, n_time_chunks);
+  if ((s = check_ws(L, ws, ws_bytes)) != GDN_OK) return s;
+  float* fwd_buf = states_fwd ? states_fwd : (o ? at<float>(ws, L.states) : nullptr);
+  float* rev_buf = states_rev ? states_rev : (o ? at<float>(ws, L.rev) : nullptr);
+  if ((s = run_terms(sh, L, k, v, beta, ws, st)) != GDN_OK) return s;
+  if (fwd_buf || s_final) {
+    if ((s = run_forward(sh, L, gamma, s0, fwd_buf, s_final, n_time_chunks, ws, st)) != GDN_OK)
+      return s;
+  }
+  if (rev_buf) {
+    gdn::ScanParams p;
+    memset(&p, 0, sizeof(p));
+    p.terms = at<float>(ws, L.terms);
+    p.gamma = gamma;
+    p.T = sh.T;
+    p.nchunk = (int)n_rev;
+    p.mode = gdn::SCAN_REVERSE;
+    p.states = rev_buf;
+    for (int c = 0; c <= (int)n_rev; ++c) {
+      int64_t off = (int64_t)c * chunk_len;
+      p.offsets[c] = (int)(off < sh.T ? off : sh.T);
+    }
+    GDN_HIP(gdn::launch_scan(sh, p, st));
+  }
+  if (o) GDN_HIP(gdn::launch_readout(sh, q, fwd_buf, rev_buf, o, st));
+  return GDN_OK;
+}
+
+gdn_status gdn_compose(const gdn_desc* desc, const void* k, const void* v, const float* beta,
+                       const float* gamma, const int32_t* chunk_offsets, int32_t P, float* C,
+                       float* Hc, const float* s0, float* s_start, void* ws, size_t ws_bytes,
+                       void* stream) {
+  Shape sh;
+  gdn_status s = check_desc(desc, &sh);
+  if (s != GDN_OK) return s;
+  if (P < 1 || P > GDN_MAX_TIME_CHUNKS || chunk_offsets == nullptr) return GDN_EINVAL;
+  if (chunk_offsets[0] != 0 || chunk_offsets[P] != sh.T) return GDN_EINVAL;
+  for (int p = 0; p < P; ++p)
+    if (chunk_offsets[p + 1] < chunk_offsets[p]) return GDN_EINVAL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(C) || !aligned16(Hc) || !aligned16(s0) ||
+      !aligned16(s_start))
+    return GDN_EINVAL;
+  if (sh.BH() == 0 || (!C && !Hc && !s_start)) return GDN_OK;
+  if (sh.T > 0 && (!k || !v || !beta || !gamma)) return GDN_EINVAL;
+  Layout L = layout(sh, P);
+  if ((s = check_ws(L, ws, ws_bytes)) != GDN_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t DD = (int64_t)sh.D * sh.D;
+  float* Cb = C ? C : at<float>(ws, L.compC);
+  float* Hb = Hc ? Hc : at<float>(ws, L.compH);
+  if (sh.T > 0) {
+    if ((s = run_terms(sh, L, k, v, beta, ws, st)) != GDN_OK) return s;
+  }
+  gdn::ScanParams p;
+  memset(&p, 0, sizeof(p));
+  p.terms = at<float>(ws, L.terms);
+  p.gamma = gamma;
+  p.T = sh.T;
+  p.nchunk = P;
+  p.mode = gdn::SCAN_COMPOSE;
+  p.finA = Cb;
+  p.finB = Hb;
+  p.fin_bh_stride = (int64_t)P * DD;
+  p.fin_c_stride = DD;
+  for (int c = 0; c <= P; ++c) p.offsets[c] = chunk_offsets[c];
+  GDN_HIP(gdn::launch_scan(sh, p, st));
+  if (s_start) {
+    gdn::CombineParams cp{Cb, Hb, s0, s_start, P};
+    GDN_HIP(gdn::launch_combine(sh, cp, st));
+  }
+  return GDN_OK;
+}
+
+gdn_status gdn_readout(const gdn_desc* desc, const void* q, const float* states,
+                       const float* states_add, void* o, void* stream) {
+  Shape sh;
+  gdn_status s = check_desc(desc, &sh);
+  if (s != GDN_OK) return s;
+  if (sh.FH() == 0) return GDN_OK;
+  if (!q || !states || !o) return GDN_EINVAL;
+  if (!aligned16(q) || !aligned16(states) || !aligned16(states_add) || !aligned16(o))
+    return GDN_EINVAL;
+  GDN_HIP(gdn::launch_readout(sh, q, states, states_add, o, (hipStream_t)stream));
+  return GDN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Shared device helpers and launch interfaces of libgdn (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kMaxChunks = 256;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Two floats -> packed bf16 pair (lo = a, hi = b), round to nearest even
+// (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t r;
+  r.x = (__bf16)a;
+  r.y = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// ReLU on two packed bf16 values: a half whose sign bit is set becomes +0.
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t w) {
+  uint32_t neg = (w >> 15) & 0x00010001u;
+  return w & ~(neg * 0xFFFFu);
+}
+
+// Geometry shared by the host dispatcher and the kernels.
+struct Shape {
+  int B, H, T, S, D;
+  int io;          // 0 = fp32, 1 = bf16
+  float c;         // key scale applied to ReLU(k) (1 for prepared keys)
+  int prepared;    // keys already hold K_hat: no ReLU
+  int64_t BH() const { return (int64_t)B * H; }
+  int64_t FH() const { return (int64_t)B * H * T; }
+};
+
+// Frame-term outputs: for frame-head f and split p, A rows go to
+// outA + f*fstride + p*sstride and U rows to outU + f*fstride + p*sstride.
+struct TermsOut {
+  float* outA;
+  float* outU;
+  int64_t fstride;
+  int64_t sstride;
+};
+
+enum ScanMode : int {
+  SCAN_FORWARD = 0,  // rows = D, frames ascending, U added
+  SCAN_COMPOSE = 1,  // rows = 2D: C rows (identity start, no U) then H rows (zero start, U)
+  SCAN_REVERSE = 2,  // rows = D, frames descending, U added, zero start
+};
+
+struct ScanParams {
+  const float* terms;   // [FH][2D][D]: A rows then U rows of every frame
+  const float* gamma;   // [FH]
+  int T;
+  int nchunk;           // chunks per head
+  int mode;             // ScanMode
+  const float* init;    // nullable start states: base + bh*init_bh_stride + c*init_c_stride
+  int64_t init_bh_stride;
+  int64_t init_c_stride;
+  float* states;        // nullable [FH][D][D] per-frame states
+  float* finA;          // nullable final rows < D: base + bh*fin_bh_stride + c*fin_c_stride
+  float* finB;          // nullable final rows >= D (compose H rows)
+  int64_t fin_bh_stride;
+  int64_t fin_c_stride;
+  int fin_last_only;    // write finals only for the last chunk of each head
+  int offsets[kMaxChunks + 1];
+};
+
+struct CombineParams {
+  const float* C;       // [BH][P][D][D]
+  const float* Hc;      // [BH][P][D][D]
+  const float* s0;      // nullable [BH][D][D]
+  float* s_start;       // [BH][P][D][D]
+  int P;
+};
+
+// Launchers (defined in the k_*.hip files). Each returns hipGetLastError().
+hipError_t launch_prepare(const Shape& sh, const void* k, void* k_hat, hipStream_t st);
+bool terms_use_mfma(const Shape& sh);
+int terms_split(const Shape& sh);
+hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const float* beta,
+                        int n_split, TermsOut out, hipStream_t st);
+hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_split,
+                                  TermsOut out, hipStream_t st);
+hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st);
+hipError_t launch_combine(const Shape& sh, const CombineParams& p, hipStream_t st);
+hipError_t launch_readout(const Shape& sh, const void* q, const float* st_a, const float* st_b,
+                          void* o, hipStream_t st);
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st);
+hipError_t launch_zero_f32(float* dst, int64_t n, hipStream_t st);
+
+}  // namespace gdn

@@ -1,0 +1,343 @@
+// Phase 1: per-frame terms A_t = K_t beta_t K_t^T and U_t = V_t beta_t K_t^T.
+//
+// Source: blog.hotdry.top SANA-WM post, section "混合线性注意力" (the M_t and U_t
+// equations); keys K_hat = ReLU(k) / sqrt(D*S) from the same section.
+//
+// With tokens as rows (k, v are [S, D] per frame), both products contract over
+// the S tokens of a frame:
+//   [A; U] (2D x D) = [R^T; V^T] (2D x S) * (beta . R) (S x D),  R = ReLU(k)
+// followed by the scales c^2 (A rows) and c (U rows) in fp32. Every frame-head
+// is independent, so the grid is frame-parallel.
+//
+// MFMA path (bf16, D = 128): one workgroup per frame-head (or per token range
+// of it), 4 wave64s, v_mfma_f32_32x32x16_bf16 with fp32 accumulation. Tokens
+// are the contraction index but are the strided dimension in memory, so each
+// 64-token tile is transposed on its way to LDS: a thread loads 8 tokens x 8
+// features with eight coalesced 16-byte loads, transposes the 8x8 bf16 block
+// in registers and writes eight 16-byte rows "feature-major" into LDS, where
+// an MFMA operand fragment (8 consecutive tokens of one feature) is a single
+// 16-byte read. ReLU(k) is exact in bf16; beta . ReLU(k) is rounded to bf16
+// once (round to nearest even) to form the second operand.
+#include <algorithm>
+
+#include "gdn_common.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kTS = 64;          // tokens per LDS tile
+constexpr int kChunks = kTS / 8; // 16-byte chunks (8 tokens) per LDS row
+
+// XOR swizzle of the 16-byte chunk inside a 128-byte LDS row. Row-consecutive
+// reads (8 lanes, same chunk) and the transposed writes (8 lanes, rows 8 apart)
+// both land in 8 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return chunk ^ ((row + (row >> 3)) & 7);
+}
+
+__global__ void __launch_bounds__(256, 2)
+terms_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                     const float* __restrict__ beta, int S, int n_split, float c, int prepared,
+                     TermsOut out) {
+  constexpr int D = 128;
+  // rows 0..127: ReLU(k)^T, rows 128..255: v^T, rows 256..383: (beta . ReLU(k))^T
+  __shared__ uint4 lds[(2 * D + D) * kChunks];
+
+  const int64_t fh = blockIdx.x / n_split;
+  const int split = blockIdx.x % n_split;
+  const int tiles = (S + kTS - 1) / kTS;
+  const int t_begin = (int)(((int64_t)split * tiles) / n_split);
+  const int t_end = (int)(((int64_t)(split + 1) * tiles) / n_split);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const bool isK = tid < 128;           // waves 0,1 stage keys; waves 2,3 stage values
+  const int lt = tid & 127;
+  const int g = lt >> 4;                // token group: tokens 8g..8g+7 of the tile
+  const int db = lt & 15;               // feature block: features 8db..8db+7
+  const uint16_t* src = (isK ? k : v) + fh * (int64_t)S * D + 8 * db;
+  const float* bsrc = beta + fh * (int64_t)S;
+
+  uint4 x[8];
+  float bt[8];
+
+  auto load_tile = [&](int tile) {
+    const int s0 = tile * kTS + 8 * g;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int s = s0 + e;
+      x[e] = (s < S) ? *(const uint4*)(src + (int64_t)s * D) : make_uint4(0, 0, 0, 0);
+    }
+    if (isK) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bt[e] = (s0 + e < S) ? bsrc[s0 + e] : 0.f;
+    }
+  };
+
+  auto stage_tile = [&]() {
+    uint32_t xw[8][4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      xw[e][0] = x[e].x;
+      xw[e][1] = x[e].y;
+      xw[e][2] = x[e].z;
+      xw[e][3] = x[e].w;
+      if (isK && !prepared) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) xw[e][p] = relu_bf16x2(xw[e][p]);
+      }
+    }
+    const int rbase = isK ? 0 : D;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const int hw = f >> 1;
+      const int shf = (f & 1) * 16;
+      uint32_t lo[4], hi[4], y[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        lo[p] = (xw[2 * p][hw] >> shf) & 0xFFFFu;
+        hi[p] = (xw[2 * p + 1][hw] >> shf) & 0xFFFFu;
+        y[p] = lo[p] | (hi[p] << 16);
+      }
+      const int row = rbase + 8 * db + f;
+      lds[row * kChunks + swz(row, g)] = make_uint4(y[0], y[1], y[2], y[3]);
+      if (isK) {
+        uint32_t w[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          w[p] = pack_bf16x2(bf16_to_f32(lo[p]) * bt[2 * p], bf16_to_f32(hi[p]) * bt[2 * p + 1]);
+        const int wrow = 2 * D + 8 * db + f;
+        lds[wrow * kChunks + swz(wrow, g)] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  };
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[mt][nt][j] = 0.f;
+
+  if (t_begin < t_end) load_tile(t_begin);
+  for (int tile = t_begin; tile < t_end; ++tile) {
+    __syncthreads();  // every wave is done reading the previous tile
+    stage_tile();
+    if (tile + 1 < t_end) load_tile(tile + 1);  // in flight during the MFMAs below
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kTS / 16; ++kk) {
+      const int ch = 2 * kk + (lane >> 5);
+      bf16x8_t a[2], b[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int row = 64 * wave + 32 * mt + (lane & 31);
+        a[mt] = __builtin_bit_cast(bf16x8_t, lds[row * kChunks + swz(row, ch)]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int row = 2 * D + 32 * nt + (lane & 31);
+        b[nt] = __builtin_bit_cast(bf16x8_t, lds[row * kChunks + swz(row, ch)]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+    }
+  }
+
+  // Epilogue: 32x32 accumulator layout, lane holds column (lane & 31) and rows
+  // 8*(j/4) + 4*(lane/32) + (j%4) of each tile.
+  const bool rowsA = wave < 2;
+  const float scale = rowsA ? c * c : c;
+  float* dst = (rowsA ? out.outA : out.outU);
+  if (dst == nullptr) return;
+  dst += fh * out.fstride + (int64_t)split * out.sstride;
+  const int mbase = 64 * (wave & 1);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int m = mbase + 32 * mt + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+        const int n = 32 * nt + (lane & 31);
+        dst[m * D + n] = acc[mt][nt][j] * scale;
+      }
+}
+
+// fp32 vector path: any io type, D in {16, 32, 64, 128}. One workgroup per
+// frame-head (or token range); tokens staged through LDS 16 at a time.
+template <typename TIn>
+__device__ __forceinline__ float ld(const TIn* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+template <typename TIn, int D>
+__global__ void __launch_bounds__(256)
+terms_generic(const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ beta,
+              int S, int n_split, float c, int prepared, TermsOut out) {
+  constexpr int TSG = 16;
+  constexpr int OPT = 2 * D * D / 256;
+  __shared__ float Ls[TSG][2 * D];
+  __shared__ float Ws[TSG][D];
+
+  const int64_t fh = blockIdx.x / n_split;
+  const int split = blockIdx.x % n_split;
+  const int s_begin = (int)(((int64_t)split * S) / n_split);
+  const int s_end = (int)(((int64_t)(split + 1) * S) / n_split);
+  const TIn* kf = k + fh * (int64_t)S * D;
+  const TIn* vf = v + fh * (int64_t)S * D;
+  const float* bf = beta + fh * (int64_t)S;
+  const int tid = threadIdx.x;
+
+  float acc[OPT];
+#pragma unroll
+  for (int r = 0; r < OPT; ++r) acc[r] = 0.f;
+
+  for (int s0 = s_begin; s0 < s_end; s0 += TSG) {
+    __syncthreads();
+    for (int idx = tid; idx < TSG * 2 * D; idx += 256) {
+      const int s = idx / (2 * D);
+      const int m = idx % (2 * D);
+      const int tok = s0 + s;
+      float val = 0.f;
+      if (tok < s_end) {
+        if (m < D) {
+          float kv = ld<TIn>(kf, (int64_t)tok * D + m);
+          val = prepared ? kv : (kv > 0.f ? kv : 0.f) * c;
+        } else {
+          val = ld<TIn>(vf, (int64_t)tok * D + (m - D));
+        }
+      }
+      Ls[s][m] = val;
+    }
+    for (int idx = tid; idx < TSG * D; idx += 256) {
+      const int s = idx / D;
+      const int n = idx % D;
+      const int tok = s0 + s;
+      float val = 0.f;
+      if (tok < s_end) {
+        float kv = ld<TIn>(kf, (int64_t)tok * D + n);
+        val = bf[tok] * (prepared ? kv : (kv > 0.f ? kv : 0.f) * c);
+      }
+      Ws[s][n] = val;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int s = 0; s < TSG; ++s) {
+#pragma unroll
+      for (int r = 0; r < OPT; ++r) {
+        const int o = tid + 256 * r;
+        acc[r] = fmaf(Ls[s][o / D], Ws[s][o % D], acc[r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < OPT; ++r) {
+    const int o = tid + 256 * r;
+    const int m = o / D;
+    const int n = o % D;
+    float* dst = m < D ? out.outA : out.outU;
+    if (dst == nullptr) continue;
+    dst[fh * out.fstride + (int64_t)split * out.sstride + (m % D) * D + n] = acc[r];
+  }
+}
+
+// Sum of the token-range partials in a fixed order (deterministic).
+__global__ void __launch_bounds__(256)
+reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, int64_t FH,
+                       TermsOut out) {
+  const int64_t per = (int64_t)2 * D * D / 4;  // float4 per frame-head
+  const int64_t n = FH * per;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) {
+    const int64_t f = i / per;
+    const int64_t e = (i % per) * 4;
+    const float4* src = (const float4*)(partial + (f * n_split) * 2 * D * D + e);
+    float4 s = src[0];
+    for (int p = 1; p < n_split; ++p) {
+      float4 t = src[(int64_t)p * 2 * D * D / 4];
+      s.x += t.x;
+      s.y += t.y;
+      s.z += t.z;
+      s.w += t.w;
+    }
+    const int64_t row = e / D;
+    const int64_t col = e % D;
+    float* dst = row < D ? out.outA : out.outU;
+    if (dst == nullptr) continue;
+    *(float4*)(dst + f * out.fstride + (row % D) * D + col) = s;
+  }
+}
+
+template <typename TIn>
+hipError_t launch_generic(const Shape& sh, const void* k, const void* v, const float* beta,
+                          int n_split, TermsOut out, hipStream_t st) {
+  dim3 grid((unsigned)(sh.FH() * n_split));
+  const TIn* kk = (const TIn*)k;
+  const TIn* vv = (const TIn*)v;
+  switch (sh.D) {
+    case 16:
+      terms_generic<TIn, 16><<<grid, 256, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, sh.prepared, out);
+      break;
+    case 32:
+      terms_generic<TIn, 32><<<grid, 256, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, sh.prepared, out);
+      break;
+    case 64:
+      terms_generic<TIn, 64><<<grid, 256, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, sh.prepared, out);
+      break;
+    case 128:
+      terms_generic<TIn, 128><<<grid, 256, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, sh.prepared, out);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool terms_use_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
+
+int terms_split(const Shape& sh) {
+  const int64_t fh = sh.FH();
+  if (fh <= 0) return 1;
+  const int64_t want = (512 + fh - 1) / fh;  // about two workgroups per CU on 256 CUs
+  int64_t cap = sh.S / 512;                   // keep at least 512 tokens per split
+  cap = std::min<int64_t>(std::max<int64_t>(cap, 1), 4);
+  return (int)std::max<int64_t>(1, std::min(want, cap));
+}
+
+hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const float* beta,
+                        int n_split, TermsOut out, hipStream_t st) {
+  if (sh.FH() == 0) return hipSuccess;
+  if (terms_use_mfma(sh)) {
+    dim3 grid((unsigned)(sh.FH() * n_split));
+    terms_mfma_bf16_d128<<<grid, 256, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, beta, sh.S,
+                                               n_split, sh.c, sh.prepared, out);
+    return hipGetLastError();
+  }
+  if (sh.io == 1) return launch_generic<uint16_t>(sh, k, v, beta, n_split, out, st);
+  return launch_generic<float>(sh, k, v, beta, n_split, out, st);
+}
+
+hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_split, TermsOut out,
+                                  hipStream_t st) {
+  const int64_t n = sh.FH() * 2 * sh.D * sh.D / 4;
+  if (n == 0) return hipSuccess;
+  int64_t g = std::min<int64_t>((n + 255) / 256, 8192);
+  reduce_partials_kernel<<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

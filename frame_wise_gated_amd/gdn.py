@@ -1,0 +1,258 @@
+"""ctypes binding of libgdn (the HIP/gfx950 frame-wise GDN library).
+
+Argument marshalling only: shapes and dtypes are read off the tensors, device
+pointers and the current HIP stream are passed to the C entry points of the
+same names (declared in include/gdn.h), and PyTorch provides the device
+memory for outputs and the workspace. Every step of the computation runs in
+the library's kernels; there is no fallback when the library is missing.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "gdn.h")
+
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = range(5)
+GDN_F32, GDN_BF16 = 0, 1
+GDN_KEYS_RAW, GDN_KEYS_PREPARED = 0, 1
+GDN_MAX_TIME_CHUNKS = 256
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {gdn_status_str(status)} (status {status})")
+
+
+class gdn_desc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("T", ctypes.c_int32),
+        ("S", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32),
+        ("key_scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_st = ctypes.c_int32
+
+
+def exported_names_in_header() -> list[str]:
+    with open(HEADER_PATH) as f:
+        return re.findall(r"GDN_API\s+[\w\s\*]+?\b(gdn_\w+)\s*\(", f.read())
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgdn.so (built in-tree by frame_wise_gated_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m frame_wise_gated_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    L.gdn_status_str.restype = ctypes.c_char_p
+    L.gdn_status_str.argtypes = [ctypes.c_int32]
+    L.gdn_workspace_bytes.restype = _st
+    L.gdn_workspace_bytes.argtypes = [P(gdn_desc), ctypes.c_int32, P(ctypes.c_size_t)]
+    L.gdn_prepare.restype = _st
+    L.gdn_prepare.argtypes = [P(gdn_desc), _vp, _vp, _vp]
+    L.gdn_frame_terms.restype = _st
+    L.gdn_frame_terms.argtypes = [P(gdn_desc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.gdn_scan_fwd.restype = _st
+    L.gdn_scan_fwd.argtypes = [P(gdn_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
+    L.gdn_scan_bidir_chunked.restype = _st
+    L.gdn_scan_bidir_chunked.argtypes = [P(gdn_desc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                         _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
+    L.gdn_compose.restype = _st
+    L.gdn_compose.argtypes = [P(gdn_desc), _vp, _vp, _vp, _vp, P(ctypes.c_int32), ctypes.c_int32,
+                              _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.gdn_readout.restype = _st
+    L.gdn_readout.argtypes = [P(gdn_desc), _vp, _vp, _vp, _vp, _vp]
+    _lib = L
+    return L
+
+
+def gdn_status_str(status: int) -> str:
+    return lib().gdn_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != GDN_OK:
+        raise GdnError(status, where)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def make_desc(B, H, T, S, D, io_dtype, key_scale=0.0, keys_prepared=False) -> gdn_desc:
+    return gdn_desc(B, H, T, S, D, io_dtype, float(key_scale),
+                    GDN_KEYS_PREPARED if keys_prepared else GDN_KEYS_RAW)
+
+
+def _desc_from(k: torch.Tensor, key_scale, keys_prepared) -> gdn_desc:
+    if k.dim() != 5:
+        raise ValueError("k must be [B, H, T, S, D]")
+    if k.dtype == torch.float32:
+        io = GDN_F32
+    elif k.dtype == torch.bfloat16:
+        io = GDN_BF16
+    else:
+        raise ValueError(f"unsupported io dtype {k.dtype}")
+    B, H, T, S, D = k.shape
+    return make_desc(B, H, T, S, D, io, key_scale, keys_prepared)
+
+
+def _need(t: torch.Tensor | None, name: str, shape, dtype) -> None:
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)}, got "
+                         f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
+
+
+def _out(given, want: bool, shape, dtype, device):
+    if given is not None:
+        return given
+    return torch.empty(shape, dtype=dtype, device=device) if want else None
+
+
+def gdn_workspace_bytes(desc: gdn_desc, n_time_chunks: int = 1) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_workspace_bytes(ctypes.byref(desc), int(n_time_chunks), ctypes.byref(n)),
+           "gdn_workspace_bytes")
+    return int(n.value)
+
+
+def workspace(desc: gdn_desc, n_time_chunks: int = 1, device="cuda") -> torch.Tensor:
+    """A workspace tensor of the size the library asks for."""
+    return torch.empty(max(gdn_workspace_bytes(desc, n_time_chunks), 1), dtype=torch.uint8, device=device)
+
+
+def _ws(ws, desc, n_time_chunks, device):
+    if ws is None:
+        ws = workspace(desc, n_time_chunks, device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def gdn_prepare(k, k_hat=None, key_scale=0.0, stream=None):
+    d = _desc_from(k, key_scale, False)
+    k_hat = _out(k_hat, True, k.shape, k.dtype, k.device)
+    _need(k, "k", k.shape, k.dtype)
+    _need(k_hat, "k_hat", k.shape, k.dtype)
+    _check(lib().gdn_prepare(ctypes.byref(d), _ptr(k), _ptr(k_hat), _stream(stream)), "gdn_prepare")
+    return k_hat
+
+
+def gdn_frame_terms(k, v, beta, A=None, U=None, key_scale=0.0, keys_prepared=False, ws=None,
+                    stream=None):
+    d = _desc_from(k, key_scale, keys_prepared)
+    B, H, T, S, D = k.shape
+    for t, n in ((k, "k"), (v, "v")):
+        _need(t, n, k.shape, k.dtype)
+    _need(beta, "beta", (B, H, T, S), torch.float32)
+    A = _out(A, True, (B, H, T, D, D), torch.float32, k.device)
+    U = _out(U, True, (B, H, T, D, D), torch.float32, k.device)
+    ws, nb = _ws(ws, d, 1, k.device)
+    _check(lib().gdn_frame_terms(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(beta), _ptr(A), _ptr(U),
+                                 _ptr(ws), nb, _stream(stream)), "gdn_frame_terms")
+    return A, U
+
+
+def gdn_scan_fwd(q, k, v, beta, gamma, s0=None, n_time_chunks=1, key_scale=0.0,
+                 keys_prepared=False, want_states=True, want_s_final=True, want_o=True,
+                 states=None, s_final=None, o=None, ws=None, stream=None):
+    d = _desc_from(k, key_scale, keys_prepared)
+    B, H, T, S, D = k.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _need(t, n, k.shape, k.dtype)
+    _need(beta, "beta", (B, H, T, S), torch.float32)
+    _need(gamma, "gamma", (B, H, T), torch.float32)
+    _need(s0, "s0", (B, H, D, D), torch.float32)
+    states = _out(states, want_states, (B, H, T, D, D), torch.float32, k.device)
+    s_final = _out(s_final, want_s_final, (B, H, D, D), torch.float32, k.device)
+    o = _out(o, want_o, k.shape, k.dtype, k.device)
+    _need(states, "states", (B, H, T, D, D), torch.float32)
+    _need(s_final, "s_final", (B, H, D, D), torch.float32)
+    ws, nb = _ws(ws, d, n_time_chunks, k.device)
+    _check(lib().gdn_scan_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gamma),
+                              _ptr(s0), _ptr(states), _ptr(s_final), _ptr(o), int(n_time_chunks),
+                              _ptr(ws), nb, _stream(stream)), "gdn_scan_fwd")
+    return {"states": states, "s_final": s_final, "o": o}
+
+
+def gdn_scan_bidir_chunked(q, k, v, beta, gamma, chunk_len, s0=None, n_time_chunks=1,
+                           key_scale=0.0, keys_prepared=False, want_states=True, want_s_final=True,
+                           want_o=True, states_fwd=None, states_rev=None, s_final=None, o=None,
+                           ws=None, stream=None):
+    d = _desc_from(k, key_scale, keys_prepared)
+    B, H, T, S, D = k.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _need(t, n, k.shape, k.dtype)
+    _need(beta, "beta", (B, H, T, S), torch.float32)
+    _need(gamma, "gamma", (B, H, T), torch.float32)
+    _need(s0, "s0", (B, H, D, D), torch.float32)
+    states_fwd = _out(states_fwd, want_states, (B, H, T, D, D), torch.float32, k.device)
+    states_rev = _out(states_rev, want_states, (B, H, T, D, D), torch.float32, k.device)
+    s_final = _out(s_final, want_s_final, (B, H, D, D), torch.float32, k.device)
+    o = _out(o, want_o, k.shape, k.dtype, k.device)
+    ws, nb = _ws(ws, d, n_time_chunks, k.device)
+    _check(lib().gdn_scan_bidir_chunked(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                        _ptr(gamma), _ptr(s0), int(chunk_len), _ptr(states_fwd),
+                                        _ptr(states_rev), _ptr(s_final), _ptr(o),
+                                        int(n_time_chunks), _ptr(ws), nb, _stream(stream)),
+           "gdn_scan_bidir_chunked")
+    return {"states_fwd": states_fwd, "states_rev": states_rev, "s_final": s_final, "o": o}
+
+
+def gdn_compose(k, v, beta, gamma, chunk_offsets, s0=None, key_scale=0.0, keys_prepared=False,
+                want_C=True, want_H=True, want_s_start=True, C=None, Hc=None, s_start=None,
+                ws=None, stream=None):
+    d = _desc_from(k, key_scale, keys_prepared)
+    B, H, T, S, D = k.shape
+    P = len(chunk_offsets) - 1
+    offs = (ctypes.c_int32 * (P + 1))(*[int(x) for x in chunk_offsets])
+    _need(beta, "beta", (B, H, T, S), torch.float32)
+    _need(gamma, "gamma", (B, H, T), torch.float32)
+    _need(s0, "s0", (B, H, D, D), torch.float32)
+    C = _out(C, want_C, (B, H, P, D, D), torch.float32, k.device)
+    Hc = _out(Hc, want_H, (B, H, P, D, D), torch.float32, k.device)
+    s_start = _out(s_start, want_s_start, (B, H, P, D, D), torch.float32, k.device)
+    ws, nb = _ws(ws, d, max(P, 1), k.device)
+    _check(lib().gdn_compose(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(beta), _ptr(gamma), offs, P,
+                             _ptr(C), _ptr(Hc), _ptr(s0), _ptr(s_start), _ptr(ws), nb,
+                             _stream(stream)), "gdn_compose")
+    return {"C": C, "Hc": Hc, "s_start": s_start}
+
+
+def gdn_readout(q, states, states_add=None, o=None, stream=None):
+    d = _desc_from(q, 0.0, False)
+    B, H, T, S, D = q.shape
+    _need(q, "q", q.shape, q.dtype)
+    _need(states, "states", (B, H, T, D, D), torch.float32)
+    _need(states_add, "states_add", (B, H, T, D, D), torch.float32)
+    o = _out(o, True, q.shape, q.dtype, q.device)
+    _need(o, "o", q.shape, q.dtype)
+    _check(lib().gdn_readout(ctypes.byref(d), _ptr(q), _ptr(states), _ptr(states_add), _ptr(o),
+                             _stream(stream)), "gdn_readout")
+    return o

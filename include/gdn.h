@@ -1,0 +1,158 @@
+/*
+ * gdn.h -- C ABI of libgdn, the frame-wise Gated DeltaNet (GDN) frame scan for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (blog.hotdry.top SANA-WM post, section "混合线性注意力", the
+ * three equations; xiejiayun.github.io "好文共赏 | SANA-WM", section 2.1):
+ *
+ *   K_hat = ReLU(k) * c,            c = 1/sqrt(D*S) unless given
+ *   A_t   = K_t beta_t K_t^T         (D x D; K_t has the frame's S tokens as columns)
+ *   U_t   = V_t beta_t K_t^T         (D x D; rows = value dim, cols = key dim)
+ *   M_t   = gamma_t (I - A_t)
+ *   S_t   = S_{t-1} M_t + U_t,       S_{-1} = s0 (zero when s0 is NULL)
+ *   o_{t,s} = S_t q_{t,s}            (readout with the state after frame t)
+ *
+ * Memory layouts (row-major, last index fastest; all device memory unless
+ * marked "host"):
+ *   q, k, v, o, k_hat : [B, H, T, S, D]  element type io_dtype (fp32 or bf16)
+ *   beta              : [B, H, T, S]     fp32, per-token gate
+ *   gamma             : [B, H, T]        fp32, per-frame decay gate
+ *   s0, s_final       : [B, H, D, D]     fp32, entry (i, j) = (value dim, key dim)
+ *   states, states_*  : [B, H, T, D, D]  fp32, the state after each frame
+ *   A, U              : [B, H, T, D, D]  fp32
+ *   C, Hc, s_start    : [B, H, P, D, D]  fp32
+ *
+ * Conventions for every entry point:
+ *   - Ownership: the caller owns every buffer, the workspace included. The
+ *     library allocates and frees no device memory and keeps no global state;
+ *     calls are re-entrant.
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream). Work is
+ *     only enqueued on it; no call synchronises.
+ *   - Errors: arguments are checked on the host before anything is enqueued.
+ *     On any status other than GDN_OK nothing has been enqueued, except for
+ *     GDN_EHIP (a launch failed; earlier launches of the same call may have
+ *     been enqueued). Device faults surface at the caller's next
+ *     synchronisation, as usual in HIP.
+ *   - Outputs are overwritten, never accumulated into. A NULL optional output
+ *     is not computed. Output buffers must not alias inputs.
+ *   - Determinism: the same call on the same device gives bitwise-identical
+ *     results (no atomics, fixed reduction orders).
+ *   - Supported shapes: B, H, T >= 0, S >= 1. D = 128 with bf16 runs the MFMA
+ *     path; D in {16, 32, 64} (bf16 or fp32) and D = 128 with fp32 run the
+ *     fp32 vector path. Other D give GDN_EUNSUPPORTED.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define GDN_API __attribute__((visibility("default")))
+#else
+#define GDN_API
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_EINVAL = 1,        /* NULL required pointer, bad size, bad dtype, bad chunking */
+  GDN_EUNSUPPORTED = 2,  /* valid request this build does not implement (e.g. D) */
+  GDN_EWORKSPACE = 3,    /* ws_bytes smaller than gdn_workspace_bytes() asks for */
+  GDN_EHIP = 4           /* a HIP launch failed */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* flags */
+#define GDN_KEYS_RAW 0u       /* kernels apply ReLU and the key scale to k */
+#define GDN_KEYS_PREPARED 1u  /* k already holds K_hat; no ReLU, no scale */
+
+#define GDN_MAX_TIME_CHUNKS 256
+
+typedef struct {
+  int32_t B, H, T, S, D;  /* batch, heads, frames, tokens per frame, head dim (Dk = Dv) */
+  int32_t io_dtype;       /* gdn_dtype of q, k, v, o, k_hat */
+  float key_scale;        /* <= 0 selects 1/sqrt(D*S) */
+  uint32_t flags;         /* GDN_KEYS_RAW or GDN_KEYS_PREPARED */
+} gdn_desc;
+
+/* Human-readable name of a status code (static string; never NULL). */
+GDN_API const char* gdn_status_str(int32_t status);
+
+/* Workspace size in bytes that every entry point below needs for `desc` and
+ * `n_time_chunks` (1 = sequential scan). Host-only; enqueues nothing.
+ * Returns GDN_EINVAL / GDN_EUNSUPPORTED for a bad descriptor (then *bytes is
+ * left unchanged). */
+GDN_API gdn_status gdn_workspace_bytes(const gdn_desc* desc, int32_t n_time_chunks, size_t* bytes);
+
+/* K_hat = ReLU(k) * c, elementwise, written in io_dtype (bf16: round to
+ * nearest even of the fp32 product). Key scaling: blog.hotdry.top SANA-WM post,
+ * section "混合线性注意力", paragraph on the 1/sqrt(D*S) factor. Requires
+ * flags = GDN_KEYS_RAW. k and k_hat: [B,H,T,S,D]; may not overlap. */
+GDN_API gdn_status gdn_prepare(const gdn_desc* desc, const void* k, void* k_hat, void* stream);
+
+/* Phase 1 alone: A_t = K_t beta_t K_t^T and U_t = V_t beta_t K_t^T for every
+ * frame of every head (same section, the M_t and U_t equations). A and U are
+ * [B,H,T,D,D] fp32; either may be NULL. */
+GDN_API gdn_status gdn_frame_terms(const gdn_desc* desc, const void* k, const void* v, const float* beta,
+                           float* A, float* U, void* ws, size_t ws_bytes, void* stream);
+
+/* Causal frame scan S_t = S_{t-1} M_t + U_t with readout o = S_t q (same
+ * section). n_time_chunks = 1 scans frames one after another; P > 1 splits
+ * the frames into P chunks at offsets floor(p*T/P), forms each chunk's affine
+ * composite (C_p, H_p) in parallel, combines them into exact chunk start states
+ * and replays the chunks in parallel (blog.hotdry.top SANA-WM post, section
+ * "显存分片: Context-Parallel 的工程实现", S_end = S_start C_p + H_p). Requires
+ * 1 <= P <= max(T, 1) and P <= GDN_MAX_TIME_CHUNKS.
+ * q may be NULL when o is NULL. s0 NULL = zero initial state. states,
+ * s_final, o may each be NULL. */
+GDN_API gdn_status gdn_scan_fwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                        const float* beta, const float* gamma, const float* s0, float* states,
+                        float* s_final, void* o, int32_t n_time_chunks, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Chunk-causal bidirectional scan (hyper.ai page 2605.15178, method section:
+ * the reverse temporal scan restarts at every chunk boundary). Forward states
+ * as gdn_scan_fwd; reverse states R_t = R_{t+1} M_t + U_t inside each chunk
+ * [a, a+L) (chunks start at frame 0, the last one may be short), starting from
+ * zero after the chunk's last frame; readout o = (S_t + R_t) q.
+ * chunk_len >= T gives the full-sequence bidirectional scan. chunk_len >= 1.
+ * states_fwd, states_rev, s_final, o may each be NULL. */
+GDN_API gdn_status gdn_scan_bidir_chunked(const gdn_desc* desc, const void* q, const void* k,
+                                  const void* v, const float* beta, const float* gamma,
+                                  const float* s0, int32_t chunk_len, float* states_fwd,
+                                  float* states_rev, float* s_final, void* o,
+                                  int32_t n_time_chunks, void* ws, size_t ws_bytes, void* stream);
+
+/* Affine composites of explicit time chunks (blog.hotdry.top SANA-WM post,
+ * section "显存分片: Context-Parallel 的工程实现"): for chunk p = [a_p, a_{p+1}),
+ * C_p = M_{a_p} ... M_{a_{p+1}-1} (ordered product) and H_p = the chunk scanned
+ * from a zero state, so that S_end = S_start C_p + H_p. chunk_offsets is a
+ * HOST array of P+1 ascending ints with [0] = 0 and [P] = T (empty chunks
+ * allowed: C = I, H = 0). 1 <= P <= GDN_MAX_TIME_CHUNKS. When s_start is not
+ * NULL it receives the exact chunk start states s_start[0] = s0 (or zero),
+ * s_start[p+1] = s_start[p] C_p + H_p. C and Hc may each be NULL. */
+GDN_API gdn_status gdn_compose(const gdn_desc* desc, const void* k, const void* v, const float* beta,
+                       const float* gamma, const int32_t* chunk_offsets, int32_t P, float* C,
+                       float* Hc, const float* s0, float* s_start, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Phase 3 alone: o_{t,s} = (states_t + states_add_t) q_{t,s} for every token
+ * of every frame (states_add may be NULL). The readout with the state after
+ * frame t is this library's reading of the frame-wise rule (the pages give the
+ * token-level Gated DeltaNet of xiejiayun.github.io "好文共赏 | SANA-WM",
+ * section 2.1, whose output uses the updated state). bf16 io: the summed state
+ * is rounded to bf16 once and products accumulate in fp32. q, o: [B,H,T,S,D];
+ * states, states_add: [B,H,T,D,D] fp32. */
+GDN_API gdn_status gdn_readout(const gdn_desc* desc, const void* q, const float* states,
+                               const float* states_add, void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

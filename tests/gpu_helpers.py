@@ -1,0 +1,61 @@
+"""Shared helpers of the GPU parity tests: device upload of seeded inputs and
+relative Frobenius errors. Expected values always come from the float64 oracle."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from frame_wise_gated_amd import inputs as gi
+
+DEV = "cuda:0"
+TOL_F32 = 1e-5   # relative Frobenius error bound for fp32 workloads
+TOL_BF16 = 2e-2  # relative Frobenius error bound for bf16 workloads
+
+
+def say(*a):
+    """Name the case before each GPU step (flushed, so it survives a crash)."""
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def tol(w: gi.Workload) -> float:
+    return TOL_F32 if w.io == "f32" else TOL_BF16
+
+
+def bits_to_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def upload(x: dict, w: gi.Workload) -> dict:
+    """Device tensors of a batch_inputs() result."""
+    out = {}
+    for n in ("q", "k", "v"):
+        if w.io == "bf16":
+            out[n] = bits_to_dev(x[n + "_bits"])
+        else:
+            out[n] = torch.from_numpy(np.ascontiguousarray(x[n])).to(DEV)
+    out["beta"] = torch.from_numpy(np.ascontiguousarray(x["beta"])).to(DEV)
+    out["gamma"] = torch.from_numpy(np.ascontiguousarray(x["gamma"])).to(DEV)
+    return out
+
+
+def head_arrays(x: dict, b: int, h: int) -> dict:
+    """One (b, h) slice as float64 arrays with [1, 1, ...] leading dims (oracle input)."""
+    return {n: np.asarray(x[n][b, h], dtype=np.float64)[None, None] for n in ("q", "k", "v", "beta", "gamma")}
+
+
+def rel_fro(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(got - ref)
+    if den == 0.0:
+        return float(num)
+    return float(num / den)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)

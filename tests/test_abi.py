@@ -1,0 +1,121 @@
+"""Host-side ABI checks of libgdn (CPU only: no kernel is launched).
+
+The library must load, export every entry point include/gdn.h declares, and
+reject bad arguments with its status codes before anything is enqueued (the
+calls below all fail validation, so none reaches a launch).
+"""
+
+import ctypes
+import subprocess
+
+import pytest
+
+from frame_wise_gated_amd import gdn
+
+
+@pytest.fixture(scope="module")
+def L():
+    return gdn.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = gdn.exported_names_in_header()
+    assert set(names) == {"gdn_status_str", "gdn_workspace_bytes", "gdn_prepare", "gdn_frame_terms",
+                          "gdn_scan_fwd", "gdn_scan_bidir_chunked", "gdn_compose", "gdn_readout"}
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        getattr(L, n)
+    # nothing but the ABI is exported from the library's own code
+    assert {n for n in exported if n.startswith("gdn")} == set(names)
+
+
+def test_status_strings():
+    assert gdn.gdn_status_str(0) == "GDN_OK"
+    for s in range(1, 5):
+        assert gdn.gdn_status_str(s).startswith("GDN_E")
+    assert "unknown" in gdn.gdn_status_str(99)
+
+
+def _ws(d, P=1):
+    return gdn.gdn_workspace_bytes(d, P)
+
+
+def test_workspace_sizes():
+    d = gdn.make_desc(1, 16, 121, 3600, 128, gdn.GDN_BF16)
+    w1 = _ws(d, 1)
+    w8 = _ws(d, 8)
+    assert w8 > w1 > 0
+    DD = 128 * 128 * 4
+    fh = 16 * 121
+    assert w1 >= fh * DD * 4  # terms (A and U) + forward and reverse state scratch
+    assert w8 - w1 >= 3 * 16 * 7 * DD  # composites C, H and chunk starts for 7 more chunks
+    # monotone in every dimension
+    for field in ("B", "H", "T", "S"):
+        d2 = gdn.make_desc(1, 16, 121, 3600, 128, gdn.GDN_BF16)
+        setattr(d2, field, getattr(d2, field) * 2)
+        assert _ws(d2, 1) >= w1, field
+    # an empty problem needs almost nothing
+    assert _ws(gdn.make_desc(1, 1, 0, 12, 16, gdn.GDN_F32)) < 4096
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (dict(D=48), gdn.GDN_EUNSUPPORTED),
+    (dict(D=256), gdn.GDN_EUNSUPPORTED),
+    (dict(S=0), gdn.GDN_EINVAL),
+    (dict(T=-1), gdn.GDN_EINVAL),
+    (dict(io_dtype=7), gdn.GDN_EINVAL),
+    (dict(flags=2), gdn.GDN_EINVAL),
+    (dict(key_scale=float("nan")), gdn.GDN_EINVAL),
+])
+def test_bad_descriptor(mutate, status):
+    d = gdn.make_desc(1, 2, 3, 12, 16, gdn.GDN_F32)
+    for kk, vv in mutate.items():
+        setattr(d, kk, vv)
+    n = ctypes.c_size_t(12345)
+    assert gdn.lib().gdn_workspace_bytes(ctypes.byref(d), 1, ctypes.byref(n)) == status
+    assert n.value == 12345  # left unchanged on error
+
+
+def test_null_and_chunk_arguments(L):
+    d = gdn.make_desc(1, 1, 4, 12, 16, gdn.GDN_F32)
+    n = ctypes.c_size_t(0)
+    assert L.gdn_workspace_bytes(None, 1, ctypes.byref(n)) == gdn.GDN_EINVAL
+    assert L.gdn_workspace_bytes(ctypes.byref(d), 0, ctypes.byref(n)) == gdn.GDN_EINVAL
+    assert L.gdn_workspace_bytes(ctypes.byref(d), 257, ctypes.byref(n)) == gdn.GDN_EINVAL
+    fake = 0x100000  # never dereferenced: every call below fails validation first
+    # n_time_chunks > T
+    assert L.gdn_scan_fwd(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake, None, None, 5,
+                          fake, 1 << 30, None) == gdn.GDN_EINVAL
+    # missing gamma
+    assert L.gdn_scan_fwd(ctypes.byref(d), fake, fake, fake, fake, None, None, fake, None, None, 1,
+                          fake, 1 << 30, None) == gdn.GDN_EINVAL
+    # o requested without q
+    assert L.gdn_scan_fwd(ctypes.byref(d), None, fake, fake, fake, fake, None, None, None, fake, 1,
+                          fake, 1 << 30, None) == gdn.GDN_EINVAL
+    # workspace too small
+    assert L.gdn_scan_fwd(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake, None, None, 1,
+                          fake, 16, None) == gdn.GDN_EWORKSPACE
+    # misaligned pointer
+    assert L.gdn_scan_fwd(ctypes.byref(d), fake, fake + 2, fake, fake, fake, None, fake, None, None,
+                          1, fake, 1 << 30, None) == gdn.GDN_EINVAL
+    # bidirectional: chunk_len < 1
+    assert L.gdn_scan_bidir_chunked(ctypes.byref(d), fake, fake, fake, fake, fake, None, 0, fake,
+                                    None, None, None, 1, fake, 1 << 30, None) == gdn.GDN_EINVAL
+    # compose: offsets must start at 0, end at T and not decrease
+    for offs in ([1, 4], [0, 3], [0, 3, 2, 4]):
+        arr = (ctypes.c_int32 * len(offs))(*offs)
+        assert L.gdn_compose(ctypes.byref(d), fake, fake, fake, fake, arr, len(offs) - 1, fake,
+                             None, None, None, fake, 1 << 30, None) == gdn.GDN_EINVAL
+    # prepare refuses already-prepared keys
+    dp = gdn.make_desc(1, 1, 4, 12, 16, gdn.GDN_F32, keys_prepared=True)
+    assert L.gdn_prepare(ctypes.byref(dp), fake, fake, None) == gdn.GDN_EINVAL
+    # nothing requested: a no-op that succeeds without touching the device
+    assert L.gdn_scan_fwd(ctypes.byref(d), None, fake, fake, fake, fake, None, None, None, None, 1,
+                          None, 0, None) == gdn.GDN_OK
+    # B*H = 0: nothing to do
+    d0 = gdn.make_desc(0, 4, 4, 12, 16, gdn.GDN_F32)
+    assert L.gdn_scan_fwd(ctypes.byref(d0), None, None, None, None, None, None, None, None, None, 1,
+                          None, 0, None) == gdn.GDN_OK

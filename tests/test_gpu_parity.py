@@ -1,0 +1,309 @@
+"""Parity of the HIP library against the float64 oracle, element by element on
+the same seeded inputs (run on an MI355X: ``pytest -m gpu``).
+
+Bars: relative Frobenius error <= 1e-5 for fp32 workloads and <= 2e-2 for
+bf16 workloads, on states and outputs separately, per head. Small cases cover
+several tiles plus ragged tails; the five named workloads run at full size in
+the launch configuration the benchmark times, checked on sampled heads.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from frame_wise_gated_amd import gdn
+from frame_wise_gated_amd import inputs as gi
+from oracle import gdn_oracle as orc
+
+from gpu_helpers import DEV, head_arrays, host, rel_fro, say, tol, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.lib()  # loud failure if the library is missing
+    yield
+    torch.cuda.synchronize()
+
+
+def _gen(w, seed=0):
+    x = gi.batch_inputs(w, seed)
+    return x, upload(x, w)
+
+
+def _s0(w, seed=1, scale=0.5):
+    rng = np.random.default_rng([99, seed])
+    return (scale * rng.standard_normal((w.B, w.H, w.D, w.D))).astype(np.float32)
+
+
+# ------------------------------------------------------------------ prepare
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_prepare(io):
+    w = gi.workload(2).with_shape(T=2, S=300, io=io)
+    x, d = _gen(w)
+    say("prepare", io)
+    kh = host(gdn.gdn_prepare(d["k"]))
+    torch.cuda.synchronize()
+    ref = orc.prepare_keys(x["k"])
+    assert (kh[ref == 0.0] == 0.0).all()
+    rel = np.abs(kh - ref) / np.maximum(np.abs(ref), 1e-300)
+    bound = 2.0 ** -8 if io == "bf16" else 2.0 ** -23
+    assert rel[ref != 0].max() <= bound * (1 + 1e-6)
+    kh2 = host(gdn.gdn_prepare(d["k"], key_scale=0.25))
+    assert np.abs(kh2 - np.maximum(x["k"], 0) * 0.25).max() <= bound * np.abs(x["k"]).max()
+
+
+# ------------------------------------------------------------- frame terms
+TERMS_CASES = {
+    "bf16_D128_ragged_S1000": gi.workload(2).with_shape(H=2, T=3, S=1000),
+    "bf16_D128_split4_S3600": gi.workload(2).with_shape(T=2),
+    "bf16_D128_S5": gi.workload(2).with_shape(T=2, S=5),
+    "bf16_D128_S1": gi.workload(2).with_shape(T=1, S=1),
+    "f32_D16": gi.workload(1),
+    "f32_D64_S50": gi.workload(1).with_shape(D=64, S=50, T=3),
+    "f32_D128_S300": gi.workload(1).with_shape(D=128, S=300, T=2),
+    "bf16_D32_S77": gi.workload(2).with_shape(D=32, S=77, T=2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TERMS_CASES))
+def test_frame_terms(name):
+    w = TERMS_CASES[name]
+    x, d = _gen(w)
+    say("frame_terms", name)
+    A, U = gdn.gdn_frame_terms(d["k"], d["v"], d["beta"])
+    A, U = host(A), host(U)
+    for b in range(w.B):
+        for h in range(w.H):
+            kh = orc.prepare_keys(x["k"][b, h].astype(np.float64))
+            for t in range(w.T):
+                Ar, Ur = orc.frame_terms(kh[t], x["v"][b, h, t], x["beta"][b, h, t])
+                assert rel_fro(A[b, h, t], Ar) <= tol(w), (b, h, t, rel_fro(A[b, h, t], Ar))
+                assert rel_fro(U[b, h, t], Ur) <= tol(w), (b, h, t, rel_fro(U[b, h, t], Ur))
+
+
+def test_frame_terms_prepared_keys():
+    w = gi.workload(2).with_shape(T=2, S=700)
+    x = gi.batch_inputs(w, 0)
+    kh = orc.prepare_keys(x["k"].astype(np.float64))
+    bits = gi.f32_to_bf16_bits(kh.astype(np.float32))
+    kh_vals = gi.bf16_bits_to_f32(bits).astype(np.float64)
+    from gpu_helpers import bits_to_dev
+    d = upload(x, w)
+    say("frame_terms prepared")
+    A, U = gdn.gdn_frame_terms(bits_to_dev(bits), d["v"], d["beta"], keys_prepared=True)
+    A, U = host(A), host(U)
+    for t in range(w.T):
+        Ar, Ur = orc.frame_terms(kh_vals[0, 0, t], x["v"][0, 0, t], x["beta"][0, 0, t])
+        assert rel_fro(A[0, 0, t], Ar) <= tol(w)
+        assert rel_fro(U[0, 0, t], Ur) <= tol(w)
+
+
+# ------------------------------------------------------------ forward scan
+SCAN_CASES = {
+    "tiny_f32_seq": (gi.workload(1), 1, False),
+    "tiny_f32_seq_s0": (gi.workload(1), 1, True),
+    "tiny_f32_cp2_s0": (gi.workload(1), 2, True),
+    "tiny_f32_cp8": (gi.workload(1), 8, False),
+    "tiny_f32_B2H3": (gi.workload(1).with_shape(B=2, H=3), 3, True),
+    "bf16_D128_seq": (gi.workload(2).with_shape(H=2, T=6, S=700), 1, False),
+    "bf16_D128_cp3_s0": (gi.workload(2).with_shape(H=2, T=6, S=700), 3, True),
+    "bf16_D64_seq": (gi.workload(2).with_shape(D=64, T=4, S=130), 1, True),
+    "f32_D128_cp2": (gi.workload(1).with_shape(D=128, T=4, S=200), 2, True),
+}
+
+
+def _check_fwd(w, x, res, s0, heads, P=1, what=""):
+    for (b, h) in heads:
+        a = head_arrays(x, b, h)
+        ref = orc.scan_fwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"],
+                           s0=None if s0 is None else s0[b, h][None, None].astype(np.float64))
+        e_st = rel_fro(host(res["states"][b, h]), ref["states"][0, 0])
+        e_o = rel_fro(host(res["o"][b, h]), ref["o"][0, 0])
+        e_f = rel_fro(host(res["s_final"][b, h]), ref["s_final"][0, 0])
+        say(what, f"head ({b},{h}) P={P}: states {e_st:.2e} o {e_o:.2e} s_final {e_f:.2e}")
+        assert e_st <= tol(w) and e_o <= tol(w) and e_f <= tol(w)
+
+
+@pytest.mark.parametrize("name", sorted(SCAN_CASES))
+def test_scan_fwd(name):
+    w, P, with_s0 = SCAN_CASES[name]
+    x, d = _gen(w)
+    s0 = _s0(w) if with_s0 else None
+    s0d = None if s0 is None else torch.from_numpy(s0).to(DEV)
+    say("scan_fwd", name)
+    res = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], s0=s0d, n_time_chunks=P)
+    torch.cuda.synchronize()
+    _check_fwd(w, x, res, s0, [(b, h) for b in range(w.B) for h in range(w.H)], P, name)
+
+
+def test_scan_fwd_optional_outputs():
+    """NULL outputs are skipped; what is requested matches the full call bitwise."""
+    w = gi.workload(2).with_shape(T=5, S=300)
+    x, d = _gen(w)
+    say("scan_fwd optional outputs")
+    full = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], n_time_chunks=2)
+    only_o = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], n_time_chunks=2,
+                              want_states=False, want_s_final=False)
+    only_fin = gdn.gdn_scan_fwd(None, d["k"], d["v"], d["beta"], d["gamma"], n_time_chunks=2,
+                                want_states=False, want_o=False)
+    assert only_o["states"] is None and only_o["s_final"] is None
+    assert torch.equal(only_o["o"], full["o"])
+    assert torch.equal(only_fin["s_final"], full["s_final"])
+
+
+# ------------------------------------------------------ bidirectional scan
+BIDIR_CASES = {
+    "tiny_f32_L3": (gi.workload(1), 3, 1),
+    "tiny_f32_L1": (gi.workload(1), 1, 1),
+    "tiny_f32_L8_full": (gi.workload(1), 8, 2),
+    "tiny_f32_L100": (gi.workload(1), 100, 1),
+    "bf16_D128_L2_cp2": (gi.workload(5).with_shape(H=2, T=5, S=600), 2, 2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BIDIR_CASES))
+def test_scan_bidir(name):
+    w, L, P = BIDIR_CASES[name]
+    x, d = _gen(w)
+    s0 = _s0(w)
+    say("scan_bidir", name)
+    res = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], L,
+                                     s0=torch.from_numpy(s0).to(DEV), n_time_chunks=P)
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        for h in range(w.H):
+            a = head_arrays(x, b, h)
+            ref = orc.scan_bidir_chunked(a["q"], a["k"], a["v"], a["beta"], a["gamma"], L,
+                                         s0=s0[b, h][None, None].astype(np.float64))
+            errs = {
+                "fwd": rel_fro(host(res["states_fwd"][b, h]), ref["states_fwd"][0, 0]),
+                "rev": rel_fro(host(res["states_rev"][b, h]), ref["states_rev"][0, 0]),
+                "o": rel_fro(host(res["o"][b, h]), ref["o"][0, 0]),
+                "fin": rel_fro(host(res["s_final"][b, h]), ref["s_final"][0, 0]),
+            }
+            say(name, (b, h), errs)
+            assert max(errs.values()) <= tol(w)
+
+
+# --------------------------------------------------------------- compose
+@pytest.mark.parametrize("name,w,offs", [
+    ("tiny_f32_empty_chunk", gi.workload(1), [0, 3, 3, 8]),
+    ("tiny_f32_one_chunk", gi.workload(1), [0, 8]),
+    ("bf16_D128", gi.workload(4).with_shape(H=2, T=7, S=500), [0, 2, 5, 7]),
+])
+def test_compose(name, w, offs):
+    x, d = _gen(w)
+    s0 = _s0(w)
+    say("compose", name)
+    res = gdn.gdn_compose(d["k"], d["v"], d["beta"], d["gamma"], offs, s0=torch.from_numpy(s0).to(DEV))
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        for h in range(w.H):
+            a = head_arrays(x, b, h)
+            C, Hc = orc.compose(a["k"], a["v"], a["beta"], a["gamma"], offs)
+            st, _ = orc.combine(C, Hc, s0=s0[b, h][None, None].astype(np.float64))
+            for p in range(len(offs) - 1):
+                assert rel_fro(host(res["C"][b, h, p]), C[0, 0, p]) <= tol(w)
+                if offs[p + 1] > offs[p]:
+                    assert rel_fro(host(res["Hc"][b, h, p]), Hc[0, 0, p]) <= tol(w)
+                else:
+                    assert np.abs(host(res["Hc"][b, h, p])).max() == 0.0
+                assert rel_fro(host(res["s_start"][b, h, p]), st[0, 0, p]) <= tol(w)
+
+
+# ------------------------------------------------------------- edge cases
+def test_no_frames_passes_state_through():
+    w = gi.workload(1).with_shape(T=0, H=2)
+    s0 = _s0(w)
+    z = torch.zeros((1, 2, 0, 12, 16), device=DEV)
+    say("T = 0")
+    res = gdn.gdn_scan_fwd(z, z, z, torch.zeros((1, 2, 0, 12), device=DEV),
+                           torch.zeros((1, 2, 0), device=DEV), s0=torch.from_numpy(s0).to(DEV))
+    assert np.array_equal(host(res["s_final"]), s0.astype(np.float64))
+    res0 = gdn.gdn_scan_fwd(z, z, z, torch.zeros((1, 2, 0, 12), device=DEV),
+                            torch.zeros((1, 2, 0), device=DEV))
+    assert host(res0["s_final"]).max() == 0.0 and host(res0["s_final"]).min() == 0.0
+
+
+def test_single_frame_is_U():
+    """T = 1 from zero: S_0 = U_0 and o = U_0 q, the same numbers gdn_frame_terms returns."""
+    w = gi.workload(2).with_shape(T=1, S=900)
+    x, d = _gen(w)
+    say("T = 1")
+    res = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"])
+    _, U = gdn.gdn_frame_terms(d["k"], d["v"], d["beta"])
+    assert torch.equal(res["states"][0, 0, 0], U[0, 0, 0])
+    _check_fwd(w, x, res, None, [(0, 0)])
+
+
+def test_deterministic():
+    w = gi.workload(3).with_shape(H=4, T=4)
+    x, d = _gen(w)
+    say("determinism")
+    r1 = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], 2, n_time_chunks=2)
+    r2 = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], 2, n_time_chunks=2)
+    for n in ("states_fwd", "states_rev", "s_final", "o"):
+        assert torch.equal(r1[n], r2[n]), n
+
+
+# ---------------------------------------------- full-size named workloads
+def _full(idx, heads, seed=0):
+    w = gi.workload(idx)
+    say("generate", w.name)
+    x = gi.batch_inputs(w, seed, keep_f32=False)
+    d = upload(x, w)
+    # float32 values of the sampled heads only (the oracle's inputs)
+    sl = {}
+    for (b, h) in heads:
+        sl[(b, h)] = gi.head_inputs(w, seed, b, h)
+    return w, x, d, sl
+
+
+def _oracle_head(w, s):
+    a = {n: np.asarray(s[n], dtype=np.float64)[None, None] for n in ("q", "k", "v", "beta", "gamma")}
+    if w.mode == "bidir":
+        return orc.scan_bidir_chunked(a["q"], a["k"], a["v"], a["beta"], a["gamma"], w.chunk_len)
+    return orc.scan_fwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"])
+
+
+def _run_workload(w, d):
+    if w.mode == "bidir":
+        return gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], w.chunk_len,
+                                          n_time_chunks=w.time_chunks)
+    return gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"],
+                            n_time_chunks=w.time_chunks)
+
+
+@pytest.mark.parametrize("idx,heads", [
+    (2, [(0, 0)]),
+    (3, [(0, 0), (0, 7), (0, 15)]),
+    (4, [(0, 0), (0, 9)]),
+    (5, [(0, 3), (0, 12)]),
+])
+def test_named_workload_full_size(idx, heads):
+    w, x, d, sl = _full(idx, heads)
+    say("run", w.name)
+    res = _run_workload(w, d)
+    torch.cuda.synchronize()
+    for (b, h) in heads:
+        ref = _oracle_head(w, sl[(b, h)])
+        if w.mode == "bidir":
+            pairs = [("states_fwd", "states_fwd"), ("states_rev", "states_rev"), ("o", "o"),
+                     ("s_final", "s_final")]
+        else:
+            pairs = [("states", "states"), ("o", "o"), ("s_final", "s_final")]
+        errs = {g: rel_fro(host(res[g][b, h]), ref[r][0, 0]) for g, r in pairs}
+        say(w.name, (b, h), {k: f"{v:.2e}" for k, v in errs.items()})
+        assert max(errs.values()) <= tol(w), errs
+    if idx == 4:
+        # composite route versus the sequential scan on every head (same terms)
+        say("sequential vs composite", w.name)
+        seq = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], n_time_chunks=1)
+        torch.cuda.synchronize()
+        for h in range(w.H):
+            e = rel_fro(host(res["states"][0, h]), host(seq["states"][0, h]))
+            assert e <= 1e-4, (h, e)
