@@ -94,6 +94,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phases", action="store_true", help="skip the per-phase timing loops")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -111,6 +113,15 @@ def main():
     w = gi.workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}))
+        return
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     x = gi.batch_inputs(w, args.seed, threads=min(16, os.cpu_count() or 1), keep_f32=False)
 

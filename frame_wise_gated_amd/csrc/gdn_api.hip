@@ -91,13 +91,14 @@ gdn_status run_terms(const Shape& sh, const Layout& L, const void* k, const void
   const int64_t DD = (int64_t)sh.D * sh.D;
   float* terms = at<float>(ws, L.terms);
   gdn::TermsOut direct{terms, terms + DD, 2 * DD, 0};
+  const bool split_a = gdn::scan_uses_mfma(sh);
   if (L.n_split == 1) {
-    GDN_HIP(gdn::launch_terms(sh, k, v, beta, 1, direct, st));
+    GDN_HIP(gdn::launch_terms(sh, k, v, beta, 1, direct, split_a, st));
   } else {
     float* part = at<float>(ws, L.partial);
     gdn::TermsOut po{part, part + DD, (int64_t)L.n_split * 2 * DD, 2 * DD};
-    GDN_HIP(gdn::launch_terms(sh, k, v, beta, L.n_split, po, st));
-    GDN_HIP(gdn::launch_reduce_partials(sh, part, L.n_split, direct, st));
+    GDN_HIP(gdn::launch_terms(sh, k, v, beta, L.n_split, po, false, st));
+    GDN_HIP(gdn::launch_reduce_partials(sh, part, L.n_split, direct, split_a, st));
   }
   return GDN_OK;
 }
@@ -242,12 +243,12 @@ gdn_status gdn_frame_terms(const gdn_desc* desc, const void* k, const void* v, c
   const int64_t DD = (int64_t)sh.D * sh.D;
   gdn::TermsOut direct{A, U, DD, 0};
   if (L.n_split == 1) {
-    GDN_HIP(gdn::launch_terms(sh, k, v, beta, 1, direct, st));
+    GDN_HIP(gdn::launch_terms(sh, k, v, beta, 1, direct, false, st));
   } else {
     float* part = at<float>(ws, L.partial);
     gdn::TermsOut po{part, part + DD, (int64_t)L.n_split * 2 * DD, 2 * DD};
-    GDN_HIP(gdn::launch_terms(sh, k, v, beta, L.n_split, po, st));
-    GDN_HIP(gdn::launch_reduce_partials(sh, part, L.n_split, direct, st));
+    GDN_HIP(gdn::launch_terms(sh, k, v, beta, L.n_split, po, false, st));
+    GDN_HIP(gdn::launch_reduce_partials(sh, part, L.n_split, direct, false, st));
   }
   return GDN_OK;
 }

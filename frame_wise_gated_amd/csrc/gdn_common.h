@@ -58,7 +58,8 @@ enum ScanMode : int {
 };
 
 struct ScanParams {
-  const float* terms;   // [FH][2D][D]: A rows then U rows of every frame
+  const float* terms;   // [FH][2D][D]: A then U of every frame (A as the bf16 hi/lo
+                        // transposed pair on the MFMA path, fp32 row-major otherwise)
   const float* gamma;   // [FH]
   int T;
   int nchunk;           // chunks per head
@@ -87,10 +88,13 @@ struct CombineParams {
 hipError_t launch_prepare(const Shape& sh, const void* k, void* k_hat, hipStream_t st);
 bool terms_use_mfma(const Shape& sh);
 int terms_split(const Shape& sh);
+// split_a: write A as the transposed bf16 hi/lo pair the MFMA scan reads
+// (MFMA path only); otherwise A is fp32 row-major.
 hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const float* beta,
-                        int n_split, TermsOut out, hipStream_t st);
+                        int n_split, TermsOut out, bool split_a, hipStream_t st);
 hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_split,
-                                  TermsOut out, hipStream_t st);
+                                  TermsOut out, bool split_a, hipStream_t st);
+bool scan_uses_mfma(const Shape& sh);
 hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st);
 hipError_t launch_combine(const Shape& sh, const CombineParams& p, hipStream_t st);
 hipError_t launch_readout(const Shape& sh, const void* q, const float* st_a, const float* st_b,

@@ -8,12 +8,13 @@
 //
 // MFMA path (bf16, D = 128): O_t^T = S_t Q_t^T, so the MFMA "A" operand is the
 // state (rows = value dim i, contraction = key dim j, contiguous in memory) and
-// the "B" operand is q (columns = tokens, contraction j contiguous): both
-// fragments are plain 16-byte loads, no transpose. Each wave keeps the whole
-// state as bf16 fragments in registers and streams 32-token tiles of q; the
-// 32x32 accumulator gives every lane four consecutive value dims of one token,
-// stored as one 8-byte write. The workgroup -> frame-head mapping keeps all
-// workgroups of a frame-head on one XCD, so the state is fetched from HBM once.
+// the "B" operand is q (columns = tokens, contraction j contiguous): q
+// fragments are plain 16-byte loads, no transpose. A workgroup stages the
+// state once in LDS as bf16 and its four waves stream 32-token tiles of q;
+// each output tile goes through a per-wave LDS buffer so that the 8 KB tile
+// (contiguous in HBM) is written with fully coalesced 16-byte stores. The
+// workgroup -> frame-head mapping keeps both workgroups of a frame-head on one
+// XCD, so the state comes from HBM once.
 #include "gdn_common.h"
 
 namespace gdn {
@@ -22,51 +23,58 @@ namespace {
 
 constexpr int kTokPerWave = 32;
 constexpr int kWavesPerBlock = 4;
+constexpr int kBlocksPerFrameHead = 2;
 constexpr int kXcd = 8;
 
 __device__ __forceinline__ uint4 ld_q(const uint16_t* q, int s, int S, int j) {
   return (s < S) ? *(const uint4*)(q + (int64_t)s * 128 + j) : make_uint4(0, 0, 0, 0);
 }
 
-__global__ void __launch_bounds__(256)
+// 16-byte chunk swizzle inside a 256-byte LDS row (16 chunks): eight
+// consecutive rows read at the same logical chunk hit eight distinct bank groups.
+__device__ __forceinline__ int rswz(int row, int chunk) { return chunk ^ (row & 7); }
+
+__global__ void __launch_bounds__(256, 2)
 readout_mfma_bf16_d128(const uint16_t* __restrict__ q, const float* __restrict__ sa,
                        const float* __restrict__ sb, uint16_t* __restrict__ o, int S, int64_t FH,
                        int nb) {
   constexpr int D = 128;
+  __shared__ uint4 Sl[D * 16];                              // state, bf16, row i = value dim
+  __shared__ uint4 Ol[kWavesPerBlock][kTokPerWave * 16];    // per-wave output tile staging
+
   const int xcd = blockIdx.x % kXcd;
   const int slot = blockIdx.x / kXcd;
   const int64_t fh = (int64_t)(slot / nb) * kXcd + xcd;
   const int b = slot % nb;
   if (fh >= FH) return;
 
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // State fragments: a[mt][kk] = S[32mt + l32][16kk + 8half .. +8] as bf16.
-  bf16x8_t a[4][8];
+  // Stage the (summed) state once per workgroup: fp32 -> bf16, coalesced.
   {
     const float* s1 = sa + fh * D * D;
     const float* s2 = sb ? sb + fh * D * D : nullptr;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int64_t off = (int64_t)(32 * mt + l32) * D + 16 * kk + 8 * half;
-        float4 x0 = *(const float4*)(s1 + off);
-        float4 x1 = *(const float4*)(s1 + off + 4);
-        if (s2) {
-          float4 y0 = *(const float4*)(s2 + off);
-          float4 y1 = *(const float4*)(s2 + off + 4);
-          x0.x += y0.x; x0.y += y0.y; x0.z += y0.z; x0.w += y0.w;
-          x1.x += y1.x; x1.y += y1.y; x1.z += y1.z; x1.w += y1.w;
-        }
-        uint4 pk = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
-                              pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
-        a[mt][kk] = __builtin_bit_cast(bf16x8_t, pk);
+    for (int c = tid; c < D * 16; c += 256) {
+      const int i = c >> 4;
+      const int ch = c & 15;
+      const int64_t off = (int64_t)i * D + 8 * ch;
+      float4 x0 = *(const float4*)(s1 + off);
+      float4 x1 = *(const float4*)(s1 + off + 4);
+      if (s2) {
+        float4 y0 = *(const float4*)(s2 + off);
+        float4 y1 = *(const float4*)(s2 + off + 4);
+        x0.x += y0.x; x0.y += y0.y; x0.z += y0.z; x0.w += y0.w;
+        x1.x += y1.x; x1.y += y1.y; x1.z += y1.z; x1.w += y1.w;
       }
+      Sl[i * 16 + rswz(i, ch)] = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
+                                            pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
+    }
   }
+  __syncthreads();
 
   const uint16_t* qf = q + fh * (int64_t)S * D;
   uint16_t* of = o + fh * (int64_t)S * D;
@@ -74,6 +82,7 @@ readout_mfma_bf16_d128(const uint16_t* __restrict__ q, const float* __restrict__
   const int wstride = nb * kWavesPerBlock;
   int tile = b * kWavesPerBlock + wave;
   if (tile >= ntiles) return;
+  uint4* stage = Ol[wave];
 
   uint4 qb[8];
   {
@@ -82,7 +91,6 @@ readout_mfma_bf16_d128(const uint16_t* __restrict__ q, const float* __restrict__
     for (int kk = 0; kk < 8; ++kk) qb[kk] = ld_q(qf, s, S, 16 * kk + 8 * half);
   }
   for (; tile < ntiles; tile += wstride) {
-    const int s = tile * kTokPerWave + l32;
     bf16x8_t bq[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) bq[kk] = __builtin_bit_cast(bf16x8_t, qb[kk]);
@@ -100,20 +108,35 @@ readout_mfma_bf16_d128(const uint16_t* __restrict__ q, const float* __restrict__
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][kk], bq[kk], acc[mt], 0, 0, 0);
-    if (s < S) {
-      uint16_t* orow = of + (int64_t)s * D;
+      for (int mt = 0; mt < 4; ++mt) {
+        const int row = 32 * mt + l32;
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, Sl[row * 16 + rswz(row, 2 * kk + half)]);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[kk], acc[mt], 0, 0, 0);
+      }
+    // Accumulator (i, s): lane holds token s = l32 and value dims
+    // 32mt + 8jg + 4half + (0..3). Stage as rows of tokens, then write the
+    // 32 x 256-byte tile (contiguous in HBM) with 16-byte stores.
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          const int i0 = 32 * mt + 8 * jg + 4 * half;
-          uint2 w = make_uint2(pack_bf16x2(acc[mt][4 * jg + 0], acc[mt][4 * jg + 1]),
-                               pack_bf16x2(acc[mt][4 * jg + 2], acc[mt][4 * jg + 3]));
-          *(uint2*)(orow + i0) = w;
-        }
+      for (int jg = 0; jg < 4; ++jg) {
+        const uint2 w = make_uint2(pack_bf16x2(acc[mt][4 * jg + 0], acc[mt][4 * jg + 1]),
+                                   pack_bf16x2(acc[mt][4 * jg + 2], acc[mt][4 * jg + 3]));
+        uint2* dst = (uint2*)&stage[l32 * 16 + rswz(l32, 4 * mt + jg)];
+        dst[half] = w;
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int s0 = tile * kTokPerWave;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int row = 4 * it + (lane >> 4);
+      const int ch = lane & 15;
+      const uint4 val = stage[row * 16 + rswz(row, ch)];
+      if (s0 + row < S) *(uint4*)(of + (int64_t)(s0 + row) * D + 8 * ch) = val;
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -195,8 +218,8 @@ hipError_t launch_readout(const Shape& sh, const void* q, const float* sa, const
   if (sh.FH() == 0) return hipSuccess;
   if (sh.io == 1 && sh.D == 128) {
     const int ntiles = (sh.S + kTokPerWave - 1) / kTokPerWave;
-    int nb = (ntiles + 4 * kWavesPerBlock - 1) / (4 * kWavesPerBlock);  // ~4 tiles per wave
-    if (nb < 1) nb = 1;
+    int nb = (ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (nb > kBlocksPerFrameHead) nb = kBlocksPerFrameHead;
     const int64_t groups = (sh.FH() + kXcd - 1) / kXcd;
     dim3 grid((unsigned)(groups * kXcd * nb));
     readout_mfma_bf16_d128<<<grid, 256, 0, st>>>((const uint16_t*)q, sa, sb, (uint16_t*)o, sh.S,

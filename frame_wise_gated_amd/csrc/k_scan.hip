@@ -102,14 +102,18 @@ __global__ void __launch_bounds__(256) scan_rows_kernel(ScanParams p) {
 }
 
 template <int D>
+constexpr int combine_rows() { return (256 / D) > 4 ? (256 / D) : 4; }
+
+template <int D>
 __global__ void __launch_bounds__(256) combine_rows_kernel(CombineParams p) {
+  constexpr int CR = combine_rows<D>();  // state rows per workgroup
   constexpr int RG = 256 / D;
-  constexpr int RPT = kR / RG;
-  __shared__ float Xs[2][kR][D];
-  constexpr int nrb = D / kR;
+  constexpr int RPT = CR / RG;
+  __shared__ float Xs[2][CR][D];
+  constexpr int nrb = D / CR;
   const int rb = blockIdx.x % nrb;
   const int64_t bh = blockIdx.x / nrb;
-  const int row0 = rb * kR;
+  const int row0 = rb * CR;
   const int tid = threadIdx.x;
   const int n = tid % D;
   const int ig = tid / D;
@@ -150,10 +154,185 @@ __global__ void __launch_bounds__(256) combine_rows_kernel(CombineParams p) {
   }
 }
 
+
+// MFMA scan step for bf16 workloads with D = 128: the product X A_t of the
+// fp32 row block X (R = 16*MT rows) with the fp32 A_t runs on bf16 MFMA with
+// both operands split into a hi/lo bf16 pair,
+//   X A ~= Xh Ah + Xh Al + Xl Ah,     |X - Xh - Xl| <= 2^-17 |X|,
+// which keeps about 16 significant bits per product at three times the bf16
+// MFMA cost (still well above the fp32 MFMA rate). Accumulation, the decay and
+// the U_t update are fp32. A_t arrives from phase 1 already split and
+// transposed ([n][k], k contiguous), so each B fragment is one 16-byte load;
+// the next frame's fragments are loaded while the current frame computes.
+// Wave w owns output columns [32w, 32w + 32) as two 16-column MFMA tiles.
+template <int MT>
+__global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
+  constexpr int D = 128;
+  constexpr int R = 16 * MT;
+  constexpr int LDX = D + 4;  // padded rows: 8 lanes reading 16 B at one column are conflict-free
+  constexpr int64_t DD = (int64_t)D * D;
+  __shared__ float Xs[2][R][LDX];
+
+  const int rows_total = (p.mode == SCAN_COMPOSE) ? 2 * D : D;
+  const int nrb = rows_total / R;
+  const int rb = blockIdx.x % nrb;
+  const int c = (blockIdx.x / nrb) % p.nchunk;
+  const int64_t bh = blockIdx.x / (nrb * p.nchunk);
+  const int row0 = rb * R;
+  const bool c_rows = (p.mode == SCAN_COMPOSE) && row0 < D;
+  const bool use_u = !c_rows;
+  const int srow0 = row0 % D;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int n0 = 32 * wave;
+
+  for (int idx = tid; idx < R * D; idx += 256) {
+    const int i = idx / D;
+    const int n = idx % D;
+    float x0 = 0.f;
+    if (p.mode == SCAN_COMPOSE) {
+      x0 = (c_rows && (srow0 + i) == n) ? 1.f : 0.f;
+    } else if (p.mode == SCAN_FORWARD && p.init != nullptr) {
+      x0 = p.init[bh * p.init_bh_stride + (int64_t)c * p.init_c_stride + (int64_t)(srow0 + i) * D + n];
+    }
+    Xs[0][i][n] = x0;
+  }
+  __syncthreads();
+
+  const int a = p.offsets[c];
+  const int e = p.offsets[c + 1];
+  const int nsteps = e - a;
+  auto frame_of = [&](int step) { return (p.mode == SCAN_REVERSE) ? (e - 1 - step) : (a + step); };
+
+  uint4 ah[2][4], al[2][4];
+  float u[MT][2][4];
+  float gm = 0.f;
+  auto load = [&](int t) {
+    const int64_t f = bh * p.T + t;
+    const uint16_t* hiT = (const uint16_t*)(p.terms + f * 2 * DD);
+    const uint16_t* loT = hiT + DD;
+    const float* Ut = p.terms + f * 2 * DD + DD;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int n = n0 + 16 * nt + l16;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        ah[nt][ks] = *(const uint4*)(hiT + n * D + 32 * ks + 8 * g);
+        al[nt][ks] = *(const uint4*)(loT + n * D + 32 * ks + 8 * g);
+      }
+    }
+    if (use_u) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            u[mt][nt][r] = Ut[(int64_t)(srow0 + 16 * mt + 4 * g + r) * D + n0 + 16 * nt + l16];
+    }
+    gm = p.gamma[f];
+  };
+
+  if (nsteps > 0) load(frame_of(0));
+  int cur = 0;
+  for (int step = 0; step < nsteps; ++step) {
+    const int t = frame_of(step);
+    uint4 ch[2][4], cl[2][4];
+    float cu[MT][2][4];
+    const float cg = gm;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        ch[nt][ks] = ah[nt][ks];
+        cl[nt][ks] = al[nt][ks];
+      }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cu[mt][nt][r] = use_u ? u[mt][nt][r] : 0.f;
+    if (step + 1 < nsteps) load(frame_of(step + 1));
+
+    f32x4_t acc[MT][2];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mt][nt][r] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const float* xr = &Xs[cur][16 * mt + l16][32 * ks + 8 * g];
+        const float4 x0 = *(const float4*)xr;
+        const float4 x1 = *(const float4*)(xr + 4);
+        const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          hw[q] = pack_bf16x2(xv[2 * q], xv[2 * q + 1]);
+          lw[q] = pack_bf16x2(xv[2 * q] - bf16_to_f32(hw[q] & 0xFFFFu),
+                              xv[2 * q + 1] - bf16_to_f32(hw[q] >> 16));
+        }
+        const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        const bf16x8_t xl = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const bf16x8_t bh_ = __builtin_bit_cast(bf16x8_t, ch[nt][ks]);
+          const bf16x8_t bl_ = __builtin_bit_cast(bf16x8_t, cl[nt][ks]);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bh_, acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bl_, acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bh_, acc[mt][nt], 0, 0, 0);
+        }
+      }
+    const int64_t f = bh * p.T + t;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = 16 * mt + 4 * g + r;
+          const int n = n0 + 16 * nt + l16;
+          const float xn = cg * (Xs[cur][m][n] - acc[mt][nt][r]) + cu[mt][nt][r];
+          Xs[cur ^ 1][m][n] = xn;
+          if (p.states != nullptr) p.states[f * DD + (int64_t)(srow0 + m) * D + n] = xn;
+        }
+    cur ^= 1;
+    __syncthreads();
+  }
+
+  if (p.fin_last_only && c != p.nchunk - 1) return;
+  float* fin = (p.mode == SCAN_COMPOSE && !c_rows) ? p.finB : p.finA;
+  if (fin == nullptr) return;
+  fin += bh * p.fin_bh_stride + (p.fin_last_only ? 0 : (int64_t)c * p.fin_c_stride);
+  for (int idx = tid; idx < R * D; idx += 256) {
+    const int i = idx / D;
+    const int n = idx % D;
+    fin[(int64_t)(srow0 + i) * D + n] = Xs[cur][i][n];
+  }
+}
+
 }  // namespace
+
+bool scan_uses_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
 
 hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st) {
   const int64_t rows_total = (p.mode == SCAN_COMPOSE) ? 2 * sh.D : sh.D;
+  if (scan_uses_mfma(sh)) {
+    constexpr int MT = 2;
+    const int64_t blocks = sh.BH() * p.nchunk * (rows_total / (16 * MT));
+    if (blocks == 0) return hipSuccess;
+    scan_mfma_d128<MT><<<dim3((unsigned)blocks), 256, 0, st>>>(p);
+    return hipGetLastError();
+  }
   const int64_t blocks = sh.BH() * p.nchunk * (rows_total / kR);
   if (blocks == 0) return hipSuccess;
   dim3 grid((unsigned)blocks);
@@ -168,7 +347,14 @@ hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st) {
 }
 
 hipError_t launch_combine(const Shape& sh, const CombineParams& p, hipStream_t st) {
-  const int64_t blocks = sh.BH() * (sh.D / kR);
+  int rows = 4;
+  switch (sh.D) {
+    case 16: rows = combine_rows<16>(); break;
+    case 32: rows = combine_rows<32>(); break;
+    case 64: rows = combine_rows<64>(); break;
+    default: rows = combine_rows<128>(); break;
+  }
+  const int64_t blocks = sh.BH() * (sh.D / rows);
   if (blocks == 0 || p.P == 0) return hipSuccess;
   dim3 grid((unsigned)blocks);
   switch (sh.D) {

@@ -36,6 +36,7 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return chunk ^ ((row + (row >> 3)) & 7);
 }
 
+template <bool kSplitA>
 __global__ void __launch_bounds__(256, 2)
 terms_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                      const float* __restrict__ beta, int S, int n_split, float c, int prepared,
@@ -158,6 +159,34 @@ terms_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict_
   if (dst == nullptr) return;
   dst += fh * out.fstride + (int64_t)split * out.sstride;
   const int mbase = 64 * (wave & 1);
+  if (kSplitA && rowsA) {
+    // A^T as a bf16 hi/lo pair (A = hi + lo to ~2^-17 relative), [n][m] with m
+    // contiguous: the scan reads 8 consecutive m of one column as one fragment.
+    uint16_t* hiT = (uint16_t*)dst;
+    uint16_t* loT = hiT + D * D;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int m = mbase + 32 * mt + 8 * jg + 4 * (lane >> 5);
+          const int n = 32 * nt + (lane & 31);
+          float a[4];
+          uint32_t h[2], l[2];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] = acc[mt][nt][4 * jg + e] * scale;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            h[e] = pack_bf16x2(a[2 * e], a[2 * e + 1]);
+            l[e] = pack_bf16x2(a[2 * e] - bf16_to_f32(h[e] & 0xFFFFu),
+                               a[2 * e + 1] - bf16_to_f32(h[e] >> 16));
+          }
+          *(uint2*)(hiT + n * D + m) = make_uint2(h[0], h[1]);
+          *(uint2*)(loT + n * D + m) = make_uint2(l[0], l[1]);
+        }
+    return;
+  }
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -252,18 +281,40 @@ terms_generic(const TIn* __restrict__ k, const TIn* __restrict__ v, const float*
   }
 }
 
-// Sum of the token-range partials in a fixed order (deterministic).
+// Sum of the token-range partials in a fixed order (deterministic). With
+// split_a, the A half is written as the transposed bf16 hi/lo pair (as the
+// MFMA epilogue does): each thread then sums four consecutive m of one column.
 __global__ void __launch_bounds__(256)
 reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, int64_t FH,
-                       TermsOut out) {
-  const int64_t per = (int64_t)2 * D * D / 4;  // float4 per frame-head
+                       TermsOut out, int split_a) {
+  const int64_t per = (int64_t)2 * D * D / 4;  // four-element groups per frame-head
   const int64_t n = FH * per;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (; i < n; i += stride) {
     const int64_t f = i / per;
     const int64_t e = (i % per) * 4;
-    const float4* src = (const float4*)(partial + (f * n_split) * 2 * D * D + e);
+    const float* base = partial + (f * n_split) * 2 * D * D;
+    if (split_a && e < (int64_t)D * D) {
+      // group = (column nn, rows mm..mm+3)
+      const int64_t nn = e / D;
+      const int64_t mm = e % D;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int p = 0; p < n_split; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += base[(int64_t)p * 2 * D * D + (mm + q) * D + nn];
+      if (out.outA == nullptr) continue;
+      uint16_t* hiT = (uint16_t*)(out.outA + f * out.fstride);
+      uint16_t* loT = hiT + (int64_t)D * D;
+      uint32_t h0 = pack_bf16x2(v[0], v[1]);
+      uint32_t h1 = pack_bf16x2(v[2], v[3]);
+      uint32_t l0 = pack_bf16x2(v[0] - bf16_to_f32(h0 & 0xFFFFu), v[1] - bf16_to_f32(h0 >> 16));
+      uint32_t l1 = pack_bf16x2(v[2] - bf16_to_f32(h1 & 0xFFFFu), v[3] - bf16_to_f32(h1 >> 16));
+      *(uint2*)(hiT + nn * D + mm) = make_uint2(h0, h1);
+      *(uint2*)(loT + nn * D + mm) = make_uint2(l0, l1);
+      continue;
+    }
+    const float4* src = (const float4*)(base + e);
     float4 s = src[0];
     for (int p = 1; p < n_split; ++p) {
       float4 t = src[(int64_t)p * 2 * D * D / 4];
@@ -319,12 +370,16 @@ int terms_split(const Shape& sh) {
 }
 
 hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const float* beta,
-                        int n_split, TermsOut out, hipStream_t st) {
+                        int n_split, TermsOut out, bool split_a, hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
   if (terms_use_mfma(sh)) {
     dim3 grid((unsigned)(sh.FH() * n_split));
-    terms_mfma_bf16_d128<<<grid, 256, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, beta, sh.S,
-                                               n_split, sh.c, sh.prepared, out);
+    if (split_a)
+      terms_mfma_bf16_d128<true><<<grid, 256, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, beta,
+                                                       sh.S, n_split, sh.c, sh.prepared, out);
+    else
+      terms_mfma_bf16_d128<false><<<grid, 256, 0, st>>>((const uint16_t*)k, (const uint16_t*)v,
+                                                        beta, sh.S, n_split, sh.c, sh.prepared, out);
     return hipGetLastError();
   }
   if (sh.io == 1) return launch_generic<uint16_t>(sh, k, v, beta, n_split, out, st);
@@ -332,11 +387,12 @@ hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const flo
 }
 
 hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_split, TermsOut out,
-                                  hipStream_t st) {
+                                  bool split_a, hipStream_t st) {
   const int64_t n = sh.FH() * 2 * sh.D * sh.D / 4;
   if (n == 0) return hipSuccess;
   int64_t g = std::min<int64_t>((n + 255) / 256, 8192);
-  reduce_partials_kernel<<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out);
+  reduce_partials_kernel<<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out,
+                                                      split_a ? 1 : 0);
   return hipGetLastError();
 }
 
