@@ -18,6 +18,11 @@
 // while the row block stays in LDS.
 #include "gdn_common.h"
 
+// Row block of the MFMA scan, in 16-row MFMA tiles (build-time tuning knob).
+#ifndef GDN_SCAN_MT
+#define GDN_SCAN_MT 4
+#endif
+
 namespace gdn {
 
 namespace {
@@ -32,9 +37,12 @@ __global__ void __launch_bounds__(256) scan_rows_kernel(ScanParams p) {
 
   const int rows_total = (p.mode == SCAN_COMPOSE) ? 2 * D : D;
   const int nrb = rows_total / kR;
-  const int rb = blockIdx.x % nrb;
-  const int c = (blockIdx.x / nrb) % p.nchunk;
-  const int64_t bh = blockIdx.x / (nrb * p.nchunk);
+  int64_t job;
+  int rb;
+  xcd_job(blockIdx.x, nrb, &job, &rb);
+  if (job >= p.njobs) return;
+  const int c = (int)(job % p.nchunk);
+  const int64_t bh = job / p.nchunk;
   const int row0 = rb * kR;                    // first row of this block in [0, rows_total)
   const bool c_rows = (p.mode == SCAN_COMPOSE) && row0 < D;  // composite transition rows
   const bool use_u = !c_rows;
@@ -104,6 +112,7 @@ __global__ void __launch_bounds__(256) scan_rows_kernel(ScanParams p) {
 template <int D>
 constexpr int combine_rows() { return (256 / D) > 4 ? (256 / D) : 4; }
 
+// combine: s_start[q+1] = s_start[q] C_q + H_q, for one head's CR-row block.
 template <int D>
 __global__ void __launch_bounds__(256) combine_rows_kernel(CombineParams p) {
   constexpr int CR = combine_rows<D>();  // state rows per workgroup
@@ -111,8 +120,10 @@ __global__ void __launch_bounds__(256) combine_rows_kernel(CombineParams p) {
   constexpr int RPT = CR / RG;
   __shared__ float Xs[2][CR][D];
   constexpr int nrb = D / CR;
-  const int rb = blockIdx.x % nrb;
-  const int64_t bh = blockIdx.x / nrb;
+  int64_t bh;
+  int rb;
+  xcd_job(blockIdx.x, nrb, &bh, &rb);
+  if (bh >= p.BH) return;
   const int row0 = rb * CR;
   const int tid = threadIdx.x;
   const int n = tid % D;
@@ -154,30 +165,39 @@ __global__ void __launch_bounds__(256) combine_rows_kernel(CombineParams p) {
   }
 }
 
-
 // MFMA scan step for bf16 workloads with D = 128: the product X A_t of the
 // fp32 row block X (R = 16*MT rows) with the fp32 A_t runs on bf16 MFMA with
 // both operands split into a hi/lo bf16 pair,
 //   X A ~= Xh Ah + Xh Al + Xl Ah,     |X - Xh - Xl| <= 2^-17 |X|,
 // which keeps about 16 significant bits per product at three times the bf16
-// MFMA cost (still well above the fp32 MFMA rate). Accumulation, the decay and
-// the U_t update are fp32. A_t arrives from phase 1 already split and
-// transposed ([n][k], k contiguous), so each B fragment is one 16-byte load;
-// the next frame's fragments are loaded while the current frame computes.
-// Wave w owns output columns [32w, 32w + 32) as two 16-column MFMA tiles.
+// MFMA cost (still far above the fp32 MFMA rate). Accumulation, the decay and
+// the U_t update are fp32.
+//
+// Data placement: each lane keeps the fp32 state entries it produces (rows
+// 16mt + 4g + r, columns 32w + 16nt + l16) in registers for the whole scan;
+// LDS holds only the split bf16 copy of the row block that the MFMA "A"
+// operand reads, written once per element by its owner lane. A_t arrives from
+// phase 1 already split and transposed ([n][k], k contiguous), so each B
+// fragment is one 16-byte load; the fragments of the next frame are requested
+// as soon as the current frame's MFMAs no longer need them. Wave w owns output
+// columns [32w, 32w + 32) as two 16-column MFMA tiles.
 template <int MT>
 __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
   constexpr int D = 128;
   constexpr int R = 16 * MT;
-  constexpr int LDX = D + 4;  // padded rows: 8 lanes reading 16 B at one column are conflict-free
+  constexpr int LDB = D + 8;  // bf16 row stride 272 B: 8 lanes reading 16 B at one column are conflict-free
   constexpr int64_t DD = (int64_t)D * D;
-  __shared__ float Xs[2][R][LDX];
+  __shared__ __attribute__((aligned(16))) uint16_t Xh[2][R][LDB];
+  __shared__ __attribute__((aligned(16))) uint16_t Xl[2][R][LDB];
 
   const int rows_total = (p.mode == SCAN_COMPOSE) ? 2 * D : D;
   const int nrb = rows_total / R;
-  const int rb = blockIdx.x % nrb;
-  const int c = (blockIdx.x / nrb) % p.nchunk;
-  const int64_t bh = blockIdx.x / (nrb * p.nchunk);
+  int64_t job;
+  int rb;
+  xcd_job(blockIdx.x, nrb, &job, &rb);
+  if (job >= p.njobs) return;
+  const int c = (int)(job % p.nchunk);
+  const int64_t bh = job / p.nchunk;
   const int row0 = rb * R;
   const bool c_rows = (p.mode == SCAN_COMPOSE) && row0 < D;
   const bool use_u = !c_rows;
@@ -190,74 +210,77 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
   const int g = lane >> 4;
   const int n0 = 32 * wave;
 
-  for (int idx = tid; idx < R * D; idx += 256) {
-    const int i = idx / D;
-    const int n = idx % D;
-    float x0 = 0.f;
-    if (p.mode == SCAN_COMPOSE) {
-      x0 = (c_rows && (srow0 + i) == n) ? 1.f : 0.f;
-    } else if (p.mode == SCAN_FORWARD && p.init != nullptr) {
-      x0 = p.init[bh * p.init_bh_stride + (int64_t)c * p.init_c_stride + (int64_t)(srow0 + i) * D + n];
-    }
-    Xs[0][i][n] = x0;
-  }
+  float xr[MT][2][4];
+  auto put_split = [&](int buf, int m, int n, float x) {
+    const uint32_t h = pack_bf16x2(x, 0.f) & 0xFFFFu;
+    const uint32_t l = pack_bf16x2(x - bf16_to_f32(h), 0.f) & 0xFFFFu;
+    Xh[buf][m][n] = (uint16_t)h;
+    Xl[buf][m][n] = (uint16_t)l;
+  };
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * mt + 4 * g + r;
+        const int n = n0 + 16 * nt + l16;
+        float x0 = 0.f;
+        if (p.mode == SCAN_COMPOSE) {
+          x0 = (c_rows && (srow0 + m) == n) ? 1.f : 0.f;
+        } else if (p.mode == SCAN_FORWARD && p.init != nullptr) {
+          x0 = p.init[bh * p.init_bh_stride + (int64_t)c * p.init_c_stride +
+                      (int64_t)(srow0 + m) * D + n];
+        }
+        xr[mt][nt][r] = x0;
+        put_split(0, m, n, x0);
+      }
   __syncthreads();
 
   const int a = p.offsets[c];
   const int e = p.offsets[c + 1];
   const int nsteps = e - a;
   auto frame_of = [&](int step) { return (p.mode == SCAN_REVERSE) ? (e - 1 - step) : (a + step); };
+  auto terms_of = [&](int step) { return p.terms + (bh * p.T + frame_of(step)) * 2 * DD; };
 
+  // Prefetches are unconditional (the last step re-reads its own frame) so
+  // that the outstanding-load bookkeeping stays exact across the loop.
   uint4 ah[2][4], al[2][4];
   float u[MT][2][4];
-  float gm = 0.f;
-  auto load = [&](int t) {
-    const int64_t f = bh * p.T + t;
-    const uint16_t* hiT = (const uint16_t*)(p.terms + f * 2 * DD);
+  const float umul = use_u ? 1.f : 0.f;
+  auto load_b = [&](const float* base, int ks) {
+    const uint16_t* hiT = (const uint16_t*)base;
     const uint16_t* loT = hiT + DD;
-    const float* Ut = p.terms + f * 2 * DD + DD;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int n = n0 + 16 * nt + l16;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        ah[nt][ks] = *(const uint4*)(hiT + n * D + 32 * ks + 8 * g);
-        al[nt][ks] = *(const uint4*)(loT + n * D + 32 * ks + 8 * g);
-      }
+      ah[nt][ks] = *(const uint4*)(hiT + n * D + 32 * ks + 8 * g);
+      al[nt][ks] = *(const uint4*)(loT + n * D + 32 * ks + 8 * g);
     }
-    if (use_u) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            u[mt][nt][r] = Ut[(int64_t)(srow0 + 16 * mt + 4 * g + r) * D + n0 + 16 * nt + l16];
-    }
-    gm = p.gamma[f];
   };
-
-  if (nsteps > 0) load(frame_of(0));
-  int cur = 0;
-  for (int step = 0; step < nsteps; ++step) {
-    const int t = frame_of(step);
-    uint4 ch[2][4], cl[2][4];
-    float cu[MT][2][4];
-    const float cg = gm;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        ch[nt][ks] = ah[nt][ks];
-        cl[nt][ks] = al[nt][ks];
-      }
+  auto load_u = [&](const float* base) {
+    const float* Ut = base + DD + (int64_t)srow0 * D + n0 + l16;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) cu[mt][nt][r] = use_u ? u[mt][nt][r] : 0.f;
-    if (step + 1 < nsteps) load(frame_of(step + 1));
+        for (int r = 0; r < 4; ++r) u[mt][nt][r] = Ut[(16 * mt + 4 * g + r) * D + 16 * nt];
+  };
+
+  int cur = 0;
+  if (nsteps > 0) {
+    const float* base = terms_of(0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) load_b(base, ks);
+    load_u(base);
+  }
+  float gm = nsteps > 0 ? p.gamma[bh * p.T + frame_of(0)] : 0.f;
+  for (int step = 0; step < nsteps; ++step) {
+    const int64_t f = bh * p.T + frame_of(step);
+    const int nstep = (step + 1 < nsteps) ? step + 1 : step;
+    const float* nbase = terms_of(nstep);
+    const float gm_next = p.gamma[bh * p.T + frame_of(nstep)];
 
     f32x4_t acc[MT][2];
 #pragma unroll
@@ -267,32 +290,24 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[mt][nt][r] = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const float* xr = &Xs[cur][16 * mt + l16][32 * ks + 8 * g];
-        const float4 x0 = *(const float4*)xr;
-        const float4 x1 = *(const float4*)(xr + 4);
-        const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          hw[q] = pack_bf16x2(xv[2 * q], xv[2 * q + 1]);
-          lw[q] = pack_bf16x2(xv[2 * q] - bf16_to_f32(hw[q] & 0xFFFFu),
-                              xv[2 * q + 1] - bf16_to_f32(hw[q] >> 16));
-        }
-        const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-        const bf16x8_t xl = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + l16;
+        const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, *(const uint4*)&Xh[cur][m][32 * ks + 8 * g]);
+        const bf16x8_t xl = __builtin_bit_cast(bf16x8_t, *(const uint4*)&Xl[cur][m][32 * ks + 8 * g]);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          const bf16x8_t bh_ = __builtin_bit_cast(bf16x8_t, ch[nt][ks]);
-          const bf16x8_t bl_ = __builtin_bit_cast(bf16x8_t, cl[nt][ks]);
+          const bf16x8_t bh_ = __builtin_bit_cast(bf16x8_t, ah[nt][ks]);
+          const bf16x8_t bl_ = __builtin_bit_cast(bf16x8_t, al[nt][ks]);
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bh_, acc[mt][nt], 0, 0, 0);
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bl_, acc[mt][nt], 0, 0, 0);
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bh_, acc[mt][nt], 0, 0, 0);
         }
       }
-    const int64_t f = bh * p.T + t;
+      load_b(nbase, ks);  // fragments of the next frame, k-slice ks
+    }
+
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -301,10 +316,21 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
         for (int r = 0; r < 4; ++r) {
           const int m = 16 * mt + 4 * g + r;
           const int n = n0 + 16 * nt + l16;
-          const float xn = cg * (Xs[cur][m][n] - acc[mt][nt][r]) + cu[mt][nt][r];
-          Xs[cur ^ 1][m][n] = xn;
-          if (p.states != nullptr) p.states[f * DD + (int64_t)(srow0 + m) * D + n] = xn;
+          const float xn = gm * (xr[mt][nt][r] - acc[mt][nt][r]) + umul * u[mt][nt][r];
+          xr[mt][nt][r] = xn;
+          put_split(cur ^ 1, m, n, xn);
         }
+    if (p.states != nullptr) {
+      float* st = p.states + f * DD + (int64_t)srow0 * D + n0 + l16;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) st[(16 * mt + 4 * g + r) * D + 16 * nt] = xr[mt][nt][r];
+    }
+    load_u(nbase);
+    gm = gm_next;
     cur ^= 1;
     __syncthreads();
   }
@@ -313,11 +339,13 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
   float* fin = (p.mode == SCAN_COMPOSE && !c_rows) ? p.finB : p.finA;
   if (fin == nullptr) return;
   fin += bh * p.fin_bh_stride + (p.fin_last_only ? 0 : (int64_t)c * p.fin_c_stride);
-  for (int idx = tid; idx < R * D; idx += 256) {
-    const int i = idx / D;
-    const int n = idx % D;
-    fin[(int64_t)(srow0 + i) * D + n] = Xs[cur][i][n];
-  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        fin[(int64_t)(srow0 + 16 * mt + 4 * g + r) * D + n0 + 16 * nt + l16] = xr[mt][nt][r];
 }
 
 }  // namespace
@@ -326,21 +354,21 @@ bool scan_uses_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
 
 hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st) {
   const int64_t rows_total = (p.mode == SCAN_COMPOSE) ? 2 * sh.D : sh.D;
+  ScanParams q = p;
+  q.njobs = sh.BH() * p.nchunk;
+  if (q.njobs == 0) return hipSuccess;
   if (scan_uses_mfma(sh)) {
-    constexpr int MT = 2;
-    const int64_t blocks = sh.BH() * p.nchunk * (rows_total / (16 * MT));
-    if (blocks == 0) return hipSuccess;
-    scan_mfma_d128<MT><<<dim3((unsigned)blocks), 256, 0, st>>>(p);
+    constexpr int MT = GDN_SCAN_MT;
+    const int64_t blocks = xcd_grid(q.njobs, (int)(rows_total / (16 * MT)));
+    scan_mfma_d128<MT><<<dim3((unsigned)blocks), 256, 0, st>>>(q);
     return hipGetLastError();
   }
-  const int64_t blocks = sh.BH() * p.nchunk * (rows_total / kR);
-  if (blocks == 0) return hipSuccess;
-  dim3 grid((unsigned)blocks);
+  dim3 grid((unsigned)xcd_grid(q.njobs, (int)(rows_total / kR)));
   switch (sh.D) {
-    case 16: scan_rows_kernel<16><<<grid, 256, 0, st>>>(p); break;
-    case 32: scan_rows_kernel<32><<<grid, 256, 0, st>>>(p); break;
-    case 64: scan_rows_kernel<64><<<grid, 256, 0, st>>>(p); break;
-    case 128: scan_rows_kernel<128><<<grid, 256, 0, st>>>(p); break;
+    case 16: scan_rows_kernel<16><<<grid, 256, 0, st>>>(q); break;
+    case 32: scan_rows_kernel<32><<<grid, 256, 0, st>>>(q); break;
+    case 64: scan_rows_kernel<64><<<grid, 256, 0, st>>>(q); break;
+    case 128: scan_rows_kernel<128><<<grid, 256, 0, st>>>(q); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -354,14 +382,15 @@ hipError_t launch_combine(const Shape& sh, const CombineParams& p, hipStream_t s
     case 64: rows = combine_rows<64>(); break;
     default: rows = combine_rows<128>(); break;
   }
-  const int64_t blocks = sh.BH() * (sh.D / rows);
-  if (blocks == 0 || p.P == 0) return hipSuccess;
-  dim3 grid((unsigned)blocks);
+  if (sh.BH() == 0 || p.P == 0) return hipSuccess;
+  CombineParams q = p;
+  q.BH = sh.BH();
+  dim3 grid((unsigned)xcd_grid(q.BH, sh.D / rows));
   switch (sh.D) {
-    case 16: combine_rows_kernel<16><<<grid, 256, 0, st>>>(p); break;
-    case 32: combine_rows_kernel<32><<<grid, 256, 0, st>>>(p); break;
-    case 64: combine_rows_kernel<64><<<grid, 256, 0, st>>>(p); break;
-    case 128: combine_rows_kernel<128><<<grid, 256, 0, st>>>(p); break;
+    case 16: combine_rows_kernel<16><<<grid, 256, 0, st>>>(q); break;
+    case 32: combine_rows_kernel<32><<<grid, 256, 0, st>>>(q); break;
+    case 64: combine_rows_kernel<64><<<grid, 256, 0, st>>>(q); break;
+    case 128: combine_rows_kernel<128><<<grid, 256, 0, st>>>(q); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -69,7 +69,7 @@ terms_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict_
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int s = s0 + e;
-      x[e] = (s < S) ? *(const uint4*)(src + (int64_t)s * D) : make_uint4(0, 0, 0, 0);
+      x[e] = (s < S) ? ld_stream16(src + (int64_t)s * D) : make_uint4(0, 0, 0, 0);
     }
     if (isK) {
 #pragma unroll
