@@ -37,6 +37,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// ReLU on two packed bf16 values with one packed 16-bit integer max: a bf16
+// with the sign bit set is a negative int16 (-0 included), so max(x, 0) as
+// int16 maps it to +0 and keeps every non-negative value.
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t relu_bf16x2_pk(uint32_t w) {
+  const i16x2_t x = __builtin_bit_cast(i16x2_t, w);
+  const i16x2_t z = {0, 0};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, z));
+}
+
 // ReLU on two packed bf16 values: a half whose sign bit is set becomes +0.
 __device__ __forceinline__ uint32_t relu_bf16x2(uint32_t w) {
   uint32_t neg = (w >> 15) & 0x00010001u;

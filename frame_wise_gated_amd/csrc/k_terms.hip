@@ -19,8 +19,13 @@
 // 16-byte read. ReLU(k) is exact in bf16; beta . ReLU(k) is rounded to bf16
 // once (round to nearest even) to form the second operand.
 #include <algorithm>
+#include <type_traits>
 
 #include "gdn_common.h"
+
+#ifndef GDN_TERMS_DMA
+#define GDN_TERMS_DMA 1
+#endif
 
 namespace gdn {
 
@@ -199,6 +204,257 @@ terms_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict_
       }
 }
 
+// ---------------------------------------------------------------------------
+// Deep-pipeline variant of the MFMA path. The bytes in flight per CU, not
+// the MFMA work, bound phase 1: with two register-staged workgroups per CU
+// (about 64 KB of loads outstanding) the k/v stream reaches ~5 TB/s, while
+// the same access pattern with more loads in flight reaches ~6.9 TB/s. Here
+// the loads bypass registers: global_load_lds_dwordx4 copies 16 bytes per
+// lane straight into a ring of kNst LDS stages (32 tokens of k and v each, in
+// their natural token-major layout, 16-byte chunks XOR-swizzled by token), so
+// kNst - 1 stages stay in flight while one is consumed. MFMA fragments (eight
+// consecutive tokens of one feature) are read with ds_read_b64_tr_b16, which
+// returns, for each 16-lane group, the columns of the 4 x 16 block its lanes
+// address: two reads give a lane its eight tokens. ReLU and beta . ReLU(k)
+// are formed per fragment in registers (beta rides along in the same ring).
+// 8 waves: wave w owns output columns 32(w%4)..+32 and the 128 rows of A
+// (w < 4) or of U (w >= 4), as four 32 x 32 tiles.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+#define GDN_LDS __attribute__((address_space(3)))
+#define GDN_GLB __attribute__((address_space(1)))
+
+#ifndef GDN_TERMS_NST
+#define GDN_TERMS_NST 4
+#endif
+constexpr int kTsd = 32;                        // tokens per stage
+constexpr int kNst = GDN_TERMS_NST;             // stages in the ring (power of two)
+constexpr int kKvBytes = kTsd * 256;            // one stage of k (or v): 32 rows x 256 B
+constexpr int kStageBytes = 2 * kKvBytes + 4 * kTsd;
+
+// LDS layout of a stage tensor: token block b (tokens 4b..4b+3) occupies
+// bytes [1024 b, 1024 b + 1024), chunk-major inside: 16-byte chunk c (features
+// 8c..8c+7) of token 4b+e sits at 1024 b + 64 c + 16 e. One DMA instruction
+// fills one block from four contiguous 256-byte token rows; a transposed read
+// by a 16-lane group (4 tokens x 16 features) covers 128 contiguous bytes, and
+// every fragment address is a per-lane base plus a compile-time offset.
+__device__ __forceinline__ int tr_lane_base(int lane) {
+  const int G = lane >> 4;
+  const int j = lane & 15;
+  return 2048 * (G >> 1) + 64 * (2 * (G & 1) + ((j & 3) >> 1)) + 16 * (j >> 2) + 8 * (j & 1);
+}
+
+// Global -> LDS copies, issued as inline asm: lane i's bytes land at
+// lds + 16 i (dma16) or lds + 4 i (dma4). The instruction has no result
+// register. The compiler does not track these copies (when it does, it cannot
+// tell the ring slots apart and waits for every copy in flight before any LDS
+// read), so every wait for them is explicit; its own vmcnt waits can only
+// over-wait because of them.
+// M0 is a reserved register: clobbering it in asm is only sound because no
+// other instruction of the kernels that use these helpers reads M0 (checked in
+// their ISA: the only M0 writes are the ones below).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GDN_LDS void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds, bool active) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GDN_LDS void*)lds);
+  if (active)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(g)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding): this wave's copies except
+// the n youngest have landed and its own LDS reads are complete.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | 0x70 | (((N >> 4) & 3) << 14));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads() (which would
+// also wait for every copy in flight); the empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One MFMA operand fragment: lane gets the 8 consecutive tokens
+// k0 + 8*(lane/32) + 0..7 of feature f0 + (lane % 32) (k0 % 16 == 0,
+// f0 % 32 == 0), from the stage tensor at `base`, `lb` = tr_lane_base(lane).
+__device__ __forceinline__ uint4 tr_frag(const uint8_t* base, int lb, int k0, int f0) {
+  const uint8_t* p = base + lb + 256 * k0 + 8 * f0;
+  const v4i16_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDN_LDS v4i16_t*)(p));
+  const v4i16_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDN_LDS v4i16_t*)(p + 1024));
+  const uint2 a = __builtin_bit_cast(uint2, r0);
+  const uint2 b = __builtin_bit_cast(uint2, r1);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+#if GDN_TERMS_NST <= 4
+#define GDN_TERMS_WAVES_PER_EU 4  // two 8-wave workgroups per CU: at most 128 VGPRs
+#else
+#define GDN_TERMS_WAVES_PER_EU 2  // one workgroup per CU (its ring fills the LDS)
+#endif
+template <bool kSplitA, bool kPrepared>
+__global__ void __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(GDN_TERMS_WAVES_PER_EU, GDN_TERMS_WAVES_PER_EU)))
+terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                    const float* __restrict__ beta, int S, int n_split, float c,
+                    TermsOut out) {
+  constexpr int D = 128;
+  static_assert((kNst & (kNst - 1)) == 0, "ring depth is a power of two");
+  // ring slot: k block, v block, then the stage's 32 gates; wbuf holds the
+  // second operand bf16(beta . ReLU(k)) of the stage being consumed
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kNst][kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf[kKvBytes];
+
+  const int64_t fh = blockIdx.x / n_split;
+  const int split = blockIdx.x % n_split;
+  const int stages = (S + kTsd - 1) / kTsd;
+  const int st_begin = (int)(((int64_t)split * stages) / n_split);
+  const int st_end = (int)(((int64_t)(split + 1) * stages) / n_split);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const uint16_t* kf = k + fh * (int64_t)S * D;
+  const uint16_t* vf = v + fh * (int64_t)S * D;
+  const float* bf = beta + fh * (int64_t)S;
+
+  // DMA of stage `st` into its ring slot: wave w copies tokens 4w..4w+3 of
+  // k and of v (one 1 KB instruction each) and their 4 gates. Lane L of a
+  // copy instruction fills LDS slot L of its block: chunk L/4 of token
+  // 4w + L%4. Tokens past the end are clamped to the last token (valid
+  // memory); their gate is zeroed by the transform pass.
+  const int dtok = 4 * wave + (lane & 3);            // token within the stage
+  const int dchunk = lane >> 2;
+  auto issue = [&](int st) {
+    uint8_t* slot = ring[st & (kNst - 1)];
+    const int t = min(st * kTsd + dtok, S - 1);
+    const int64_t off = (int64_t)t * D + 8 * dchunk;
+    dma16(kf + off, slot + 1024 * wave);
+    dma16(vf + off, slot + kKvBytes + 1024 * wave);
+    dma4(bf + t, slot + 2 * kKvBytes + 16 * wave, lane < 4);
+  };
+  const int lb = tr_lane_base(lane);
+
+  // Transform pass: thread i owns bytes [16 i, 16 i + 16) of the k block,
+  // i.e. chunk (i % 64) / 4 of token 4 (i / 64) + i % 4. It applies ReLU in
+  // place (the first operand of the A rows) and writes bf16(beta . ReLU(k))
+  // to wbuf (the second operand of every row).
+  const int ttok = 4 * (tid >> 6) + (tid & 3);       // == dtok
+  auto transform = [&](int st) {
+    uint8_t* Ks = ring[st & (kNst - 1)];
+    const float* gates = (const float*)(Ks + 2 * kKvBytes);
+    uint4 x = *(const uint4*)(Ks + 16 * tid);
+    const float b = (st * kTsd + ttok < S) ? gates[ttok] : 0.f;
+    if (!kPrepared) {
+      x.x = relu_bf16x2_pk(x.x);
+      x.y = relu_bf16x2_pk(x.y);
+      x.z = relu_bf16x2_pk(x.z);
+      x.w = relu_bf16x2_pk(x.w);
+      *(uint4*)(Ks + 16 * tid) = x;
+    }
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = pack_bf16x2(__uint_as_float(w[q] << 16) * b, __uint_as_float(w[q] & 0xFFFF0000u) * b);
+    *(uint4*)(wbuf + 16 * tid) = make_uint4(o[0], o[1], o[2], o[3]);
+  };
+
+  // Wave w: output column tile nt = w % 4 (columns 32nt..32nt+31) and the four
+  // 32-row tiles of A (waves 0-3, first operand ReLU(k)) or of U (waves 4-7,
+  // first operand v).
+  const int nt = wave & 3;
+  const bool rowsK = wave < 4;
+  // the v block sits kKvBytes = 1024 eight-byte feature slots after the k block
+  const int aoff = rowsK ? 0 : kKvBytes / 8;
+  f32x16_t acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[mt][q] = 0.f;
+
+  auto compute = [&](int st) {
+    const uint8_t* Ks = ring[st & (kNst - 1)];
+#pragma unroll
+    for (int kk = 0; kk < kTsd / 16; ++kk) {
+      const int k0 = 16 * kk;
+      uint4 fa[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) fa[mt] = tr_frag(Ks, lb, k0, aoff + 32 * mt);
+      const uint4 fb = tr_frag(wbuf, lb, k0, 32 * nt);
+      const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, fb);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[mt]), bw,
+                                                          acc[mt], 0, 0, 0);
+    }
+  };
+
+  // Pipeline: kNst - 1 stages in flight. Each step waits for this wave's
+  // copies of stage st (and for its own LDS accesses), meets every other wave
+  // (their copies of stage st have landed; nobody still reads the slot about
+  // to be refilled or wbuf), starts the copy of stage st + kNst - 1 (past the
+  // end it re-reads the last token: harmless), transforms stage st, meets
+  // again, and consumes stage st.
+#pragma unroll
+  for (int i = 0; i < kNst - 1; ++i) issue(st_begin + i);
+  for (int st = st_begin; st < st_end; ++st) {
+    wait_vmcnt_lgkm0<(kNst - 2) * 3>();
+    bare_barrier();
+    issue(st + kNst - 1);
+    transform(st);
+    wait_vmcnt_lgkm0<kNst * 3>();  // lgkmcnt(0): this wave's transform writes are done
+    bare_barrier();
+    compute(st);
+  }
+  wait_vmcnt_lgkm0<0>();  // no copy may still be landing in LDS when the workgroup retires
+
+  const float scale = rowsK ? c * c : c;
+  float* dst = rowsK ? out.outA : out.outU;
+  if (dst == nullptr) return;
+  dst += fh * out.fstride + (int64_t)split * out.sstride;
+  const int n = 32 * nt + (lane & 31);
+  if (kSplitA && rowsK) {
+    uint16_t* hiT = (uint16_t*)dst;
+    uint16_t* loT = hiT + D * D;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int m = 32 * mt + 8 * jg + 4 * (lane >> 5);
+        float x[4];
+        uint32_t h[2], l[2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[q] = acc[mt][4 * jg + q] * scale;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          h[q] = pack_bf16x2(x[2 * q], x[2 * q + 1]);
+          l[q] = pack_bf16x2(x[2 * q] - bf16_to_f32(h[q] & 0xFFFFu),
+                             x[2 * q + 1] - bf16_to_f32(h[q] >> 16));
+        }
+        *(uint2*)(hiT + n * D + m) = make_uint2(h[0], h[1]);
+        *(uint2*)(loT + n * D + m) = make_uint2(l[0], l[1]);
+      }
+    return;
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int m = 32 * mt + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+      dst[m * D + n] = acc[mt][q] * scale;
+    }
+}
+
 // fp32 vector path: any io type, D in {16, 32, 64, 128}. One workgroup per
 // frame-head (or token range); tokens staged through LDS 16 at a time.
 template <typename TIn>
@@ -372,6 +628,22 @@ int terms_split(const Shape& sh) {
 hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const float* beta,
                         int n_split, TermsOut out, bool split_a, hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
+#if GDN_TERMS_DMA
+  if (terms_use_mfma(sh)) {
+    dim3 grid((unsigned)(sh.FH() * n_split));
+    const uint16_t* kk = (const uint16_t*)k;
+    const uint16_t* vv = (const uint16_t*)v;
+    if (split_a && !sh.prepared)
+      terms_dma_bf16_d128<true, false><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out);
+    else if (split_a)
+      terms_dma_bf16_d128<true, true><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out);
+    else if (!sh.prepared)
+      terms_dma_bf16_d128<false, false><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out);
+    else
+      terms_dma_bf16_d128<false, true><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out);
+    return hipGetLastError();
+  }
+#endif
   if (terms_use_mfma(sh)) {
     dim3 grid((unsigned)(sh.FH() * n_split));
     if (split_a)
