@@ -224,7 +224,7 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 #define GDN_GLB __attribute__((address_space(1)))
 
 #ifndef GDN_TERMS_NST
-#define GDN_TERMS_NST 4
+#define GDN_TERMS_NST 2
 #endif
 constexpr int kTsd = 32;                        // tokens per stage
 constexpr int kNst = GDN_TERMS_NST;             // stages in the ring (power of two)
@@ -418,41 +418,98 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   }
   wait_vmcnt_lgkm0<0>();  // no copy may still be landing in LDS when the workgroup retires
 
+  // Epilogue, staged through the idle ring so that every global store
+  // instruction writes 1 KB of consecutive bytes: block by block (32 KB each:
+  // the hi or lo half of the split A, or 64 rows of an fp32 result), the
+  // owning waves drop their values into LDS, the workgroup meets, and all 512
+  // threads copy the block out with 16-byte stores. Scattered 8-byte stores
+  // straight from the MFMA accumulators cost phase 1 about a seventh of its
+  // time on MI355X.
+  static_assert(kNst * kStageBytes >= 32768, "epilogue staging needs 32 KB of ring");
+  uint8_t* const stage = &ring[0][0];
+  bare_barrier();  // every wave has finished reading the ring
   const float scale = rowsK ? c * c : c;
-  float* dst = rowsK ? out.outA : out.outU;
-  if (dst == nullptr) return;
-  dst += fh * out.fstride + (int64_t)split * out.sstride;
   const int n = 32 * nt + (lane & 31);
-  if (kSplitA && rowsK) {
-    uint16_t* hiT = (uint16_t*)dst;
-    uint16_t* loT = hiT + D * D;
+  const int64_t obase = fh * out.fstride + (int64_t)split * out.sstride;
+
+  // 32 KB staged block -> dst. bf16 blocks sit swizzled in LDS (row n is
+  // 256 bytes; its 16-byte chunk j lives at position j ^ (n % 16)); fp32
+  // blocks are plain row-major.
+  auto flush = [&](void* dst, bool swz) {
+    wait_vmcnt_lgkm0<63>();  // lgkmcnt(0): this wave's LDS writes are done
+    bare_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = 512 * i + tid;
+      const int lo = swz ? ((ci >> 4) << 8) + (((ci & 15) ^ ((ci >> 4) & 15)) << 4) : 16 * ci;
+      ((uint4*)dst)[ci] = *(const uint4*)(stage + lo);
+    }
+    wait_vmcnt_lgkm0<63>();  // this wave's LDS reads are done before the block is refilled
+    bare_barrier();
+  };
+  // Owning waves: rows 64 hh .. 64 hh + 63 of their (scaled) fp32 result.
+  auto put_rows = [&](int hh) {
+    float* Sf = (float*)stage;
+#pragma unroll
+    for (int mt2 = 0; mt2 < 2; ++mt2)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = 32 * mt2 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        Sf[m * D + n] = acc[2 * hh + mt2][q] * scale;
+      }
+  };
+  // A waves: the hi (hl = 0) or lo (hl = 1) bf16 half of A, transposed
+  // (row n holds A[0..D)[n]); hi = bf16(x), lo = bf16(x - hi). The hi pass
+  // leaves the scaled residual x - hi in the accumulators for the lo pass.
+  auto put_split = [&](int hl) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
         const int m = 32 * mt + 8 * jg + 4 * (lane >> 5);
-        float x[4];
-        uint32_t h[2], l[2];
+        uint32_t w[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) x[q] = acc[mt][4 * jg + q] * scale;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          h[q] = pack_bf16x2(x[2 * q], x[2 * q + 1]);
-          l[q] = pack_bf16x2(x[2 * q] - bf16_to_f32(h[q] & 0xFFFFu),
-                             x[2 * q + 1] - bf16_to_f32(h[q] >> 16));
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int i0 = 4 * jg + 2 * q2;
+          if (hl == 0) {
+            const float x0 = acc[mt][i0] * scale;
+            const float x1 = acc[mt][i0 + 1] * scale;
+            w[q2] = pack_bf16x2(x0, x1);
+            acc[mt][i0] = x0 - bf16_to_f32(w[q2] & 0xFFFFu);
+            acc[mt][i0 + 1] = x1 - bf16_to_f32(w[q2] >> 16);
+          } else {
+            w[q2] = pack_bf16x2(acc[mt][i0], acc[mt][i0 + 1]);
+          }
         }
-        *(uint2*)(hiT + n * D + m) = make_uint2(h[0], h[1]);
-        *(uint2*)(loT + n * D + m) = make_uint2(l[0], l[1]);
+        *(uint2*)(stage + n * 256 + (((m >> 3) ^ (n & 15)) << 4) + 2 * (m & 7)) =
+            make_uint2(w[0], w[1]);
       }
-    return;
-  }
+  };
+
+  // The output pointers are kernel arguments, so every wave takes the same
+  // branches and meets the same barriers.
+  if (out.outA != nullptr) {
+    if (kSplitA) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+      for (int hl = 0; hl < 2; ++hl) {
+        if (rowsK) put_split(hl);
+        flush((uint16_t*)(out.outA + obase) + hl * D * D, true);
+      }
+    } else {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int m = 32 * mt + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-      dst[m * D + n] = acc[mt][q] * scale;
+      for (int hh = 0; hh < 2; ++hh) {
+        if (rowsK) put_rows(hh);
+        flush(out.outA + obase + hh * 64 * D, false);
+      }
     }
+  }
+  if (out.outU != nullptr) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (!rowsK) put_rows(hh);
+      flush(out.outU + obase + hh * 64 * D, false);
+    }
+  }
 }
 
 // fp32 vector path: any io type, D in {16, 32, 64, 128}. One workgroup per
