@@ -256,7 +256,7 @@ __device__ __forceinline__ int tr_lane_base(int lane) {
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GDN_LDS void*)lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g)
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(m0), "v"(g)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, void* lds, bool active) {
@@ -309,10 +309,10 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
                     TermsOut out) {
   constexpr int D = 128;
   static_assert((kNst & (kNst - 1)) == 0, "ring depth is a power of two");
-  // ring slot: k block, v block, then the stage's 32 gates; wbuf holds the
-  // second operand bf16(beta . ReLU(k)) of the stage being consumed
+  // ring slot: k block, v block, then the stage's 32 gates; wbuf[st % 2]
+  // holds the second operand bf16(beta . ReLU(k)) of stage st
   __shared__ __attribute__((aligned(16))) uint8_t ring[kNst][kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t wbuf[kKvBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t wbuf[2][kKvBytes];
 
   const int64_t fh = blockIdx.x / n_split;
   const int split = blockIdx.x % n_split;
@@ -345,9 +345,11 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   const int lb = tr_lane_base(lane);
 
   // Transform pass: thread i owns bytes [16 i, 16 i + 16) of the k block,
-  // i.e. chunk (i % 64) / 4 of token 4 (i / 64) + i % 4. It applies ReLU in
-  // place (the first operand of the A rows) and writes bf16(beta . ReLU(k))
-  // to wbuf (the second operand of every row).
+  // i.e. chunk (i % 64) / 4 of token 4 (i / 64) + i % 4: exactly the bytes
+  // (and the gate) that lane i % 64 of its own wave copied, so it needs only
+  // its own wave's copies to have landed. It applies ReLU in place (the first
+  // operand of the A rows) and writes bf16(beta . ReLU(k)) to wbuf[st % 2]
+  // (the second operand of every row).
   const int ttok = 4 * (tid >> 6) + (tid & 3);       // == dtok
   auto transform = [&](int st) {
     uint8_t* Ks = ring[st & (kNst - 1)];
@@ -366,7 +368,7 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       o[q] = pack_bf16x2(__uint_as_float(w[q] << 16) * b, __uint_as_float(w[q] & 0xFFFF0000u) * b);
-    *(uint4*)(wbuf + 16 * tid) = make_uint4(o[0], o[1], o[2], o[3]);
+    *(uint4*)(wbuf[st & 1] + 16 * tid) = make_uint4(o[0], o[1], o[2], o[3]);
   };
 
   // Wave w: output column tile nt = w % 4 (columns 32nt..32nt+31) and the four
@@ -390,7 +392,7 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
       uint4 fa[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) fa[mt] = tr_frag(Ks, lb, k0, aoff + 32 * mt);
-      const uint4 fb = tr_frag(wbuf, lb, k0, 32 * nt);
+      const uint4 fb = tr_frag(wbuf[st & 1], lb, k0, 32 * nt);
       const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, fb);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -399,21 +401,22 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
     }
   };
 
-  // Pipeline: kNst - 1 stages in flight. Each step waits for this wave's
-  // copies of stage st (and for its own LDS accesses), meets every other wave
-  // (their copies of stage st have landed; nobody still reads the slot about
-  // to be refilled or wbuf), starts the copy of stage st + kNst - 1 (past the
-  // end it re-reads the last token: harmless), transforms stage st, meets
-  // again, and consumes stage st.
+  // Pipeline: kNst - 1 stages in flight, one barrier per stage. Each step
+  // waits for this wave's copies of stage st (and its own LDS reads of the
+  // step before), transforms its share of stage st, waits for those LDS
+  // writes, and meets every other wave: then all of stage st is transformed,
+  // and every wave has finished consuming stage st - 1, so its ring slot can
+  // be refilled with stage st + kNst - 1 (past the end the copy re-reads the
+  // last token: harmless) and wbuf[(st + 1) % 2] rewritten in the next step.
+  // Then the wave consumes stage st.
 #pragma unroll
   for (int i = 0; i < kNst - 1; ++i) issue(st_begin + i);
   for (int st = st_begin; st < st_end; ++st) {
     wait_vmcnt_lgkm0<(kNst - 2) * 3>();
+    transform(st);
+    wait_vmcnt_lgkm0<(kNst - 2) * 3>();  // lgkmcnt(0): this wave's transform writes are done
     bare_barrier();
     issue(st + kNst - 1);
-    transform(st);
-    wait_vmcnt_lgkm0<kNst * 3>();  // lgkmcnt(0): this wave's transform writes are done
-    bare_barrier();
     compute(st);
   }
   wait_vmcnt_lgkm0<0>();  // no copy may still be landing in LDS when the workgroup retires
@@ -442,7 +445,7 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
     for (int i = 0; i < 4; ++i) {
       const int ci = 512 * i + tid;
       const int lo = swz ? ((ci >> 4) << 8) + (((ci & 15) ^ ((ci >> 4) & 15)) << 4) : 16 * ci;
-      ((uint4*)dst)[ci] = *(const uint4*)(stage + lo);
+      __builtin_nontemporal_store(*(const u32x4_t*)(stage + lo), (u32x4_t*)dst + ci);
     }
     wait_vmcnt_lgkm0<63>();  // this wave's LDS reads are done before the block is refilled
     bare_barrier();
