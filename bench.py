@@ -18,10 +18,13 @@ bounded sample of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
 import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
@@ -42,6 +45,34 @@ def per_frame_head(w):
     step_bytes = 3 * S * D * io + 4 * S + 4 + S * D * io + nstate * 4 * D * D
     return dict(terms_flop=terms_flop, terms_bytes=terms_bytes, readout_flop=readout_flop,
                 readout_bytes=readout_bytes, step_flop=step_flop, step_bytes=step_bytes)
+
+
+def kernel_names(w):
+    """Names of the phase-1 and readout kernels the library launches for w."""
+    if w.io == "bf16" and w.D == 128:
+        return {"terms": ("terms_dma_bf16_d128", "k_terms.hip"),
+                "readout": ("readout_mfma_bf16_d128", "k_readout.hip")}
+    return {"terms": ("terms_generic", "k_terms.hip"), "readout": ("readout_generic", "k_readout.hip")}
+
+
+def recorded_traffic(kernel, source, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled by the
+    plain-copy calibration), or None when there is none or the kernel's
+    source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__hbm_traffic.txt")
+    src = os.path.join(ROOT, "frame_wise_gated_amd", "csrc", source)
+    if not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    fields = {}
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 2 and parts[0] in ("source_sha256", "hbm_bytes_per_launch"):
+            fields[parts[0]] = parts[1]
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != sha or "hbm_bytes_per_launch" not in fields:
+        return None
+    return int(fields["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(w, seed, budget_s):
@@ -214,16 +245,19 @@ def main():
         name = max(phases, key=lambda n: phases[n][0])
         t, nbytes, nflop = phases[name]
         achieved = nbytes / (t / 1e3) / 1e9
+        kname, ksrc = kernel_names(w)[name]
         out["roofline"] = {
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
-            "kernel": "terms_mfma_bf16_d128" if name == "terms" else "readout_mfma_bf16_d128",
+            "traffic": recorded_traffic(kname, ksrc, w.name),
+            "kernel": kname,
+            "algorithmic_bytes_per_launch": nbytes,
             "ms_per_launch": t,
             "mfma_tflops": nflop / (t / 1e3) / 1e12,
+            "mfma_frac": nflop / (t / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
         }
         del A, U
 

@@ -1,0 +1,70 @@
+"""Host-side logic of bench.py and the rocprofv3 summary tool (no GPU)."""
+
+import hashlib
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from frame_wise_gated_amd import inputs as gi  # noqa: E402
+from frame_wise_gated_amd import profsum  # noqa: E402
+
+
+def test_gpus_other_than_one_exit(monkeypatch, capsys):
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--gpus", "2"])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code == 2
+    assert "one GPU" in capsys.readouterr().err
+
+
+def test_per_frame_head_bytes_and_flops():
+    w = gi.workload(4)
+    pf = bench.per_frame_head(w)
+    S, D = 3600, 128
+    assert pf["terms_bytes"] == 2 * S * D * 2 + 4 * S + 2 * D * D * 4
+    assert pf["readout_bytes"] == 2 * S * D * 2 + 4 * D * D
+    assert pf["terms_flop"] == 4 * D * D * S
+    assert pf["step_flop"] == 4 * D * D * S + 2 * D * D * S + 2 * D ** 3
+
+
+def _traffic_file(tmp_path, kernel, workload, sha, nbytes):
+    (tmp_path / "profiles").mkdir(exist_ok=True)
+    (tmp_path / "profiles" / f"{kernel}__{workload}__hbm_traffic.txt").write_text(
+        f"header\nsource_sha256 {sha}\nhbm_bytes_per_launch {nbytes}\n")
+
+
+def test_recorded_traffic_follows_source_hash(tmp_path, monkeypatch):
+    src_dir = tmp_path / "frame_wise_gated_amd" / "csrc"
+    src_dir.mkdir(parents=True)
+    (src_dir / "k.hip").write_text("kernel v1\n")
+    sha = hashlib.sha256(b"kernel v1\n").hexdigest()
+    _traffic_file(tmp_path, "kern", "wl", sha, 1234)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.recorded_traffic("kern", "k.hip", "wl") == 1234
+    (src_dir / "k.hip").write_text("kernel v2\n")      # source changed: counters are stale
+    assert bench.recorded_traffic("kern", "k.hip", "wl") is None
+    assert bench.recorded_traffic("other", "k.hip", "wl") is None
+
+
+def test_profsum_trace_and_pmc(tmp_path):
+    (tmp_path / "run_kernel_trace.csv").write_text(
+        "Kernel_Name,Grid_Size_X,Start_Timestamp,End_Timestamp\n"
+        "gdn::terms_dma_bf16_d128<true>(x),991232,0,1000\n"
+        "gdn::terms_dma_bf16_d128<true>(x),991232,0,3000\n"
+        "gdn::terms_dma_bf16_d128<true>(x),991232,0,5000\n")
+    lines = profsum.trace(str(tmp_path), skip=1)
+    row = [l for l in lines if l.startswith("terms_dma_bf16_d128")][0].split()
+    assert row[2] == "2" and float(row[3]) == pytest.approx(4.0)
+    (tmp_path / "run_counter_collection.csv").write_text(
+        "Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n"
+        "readout_mfma_bf16_d128,64,FETCH_SIZE,100\n"
+        "readout_mfma_bf16_d128,64,FETCH_SIZE,300\n")
+    lines = profsum.pmc(str(tmp_path), scale=2.0)
+    row = [l for l in lines if l.startswith("readout_mfma_bf16_d128")][0].split()
+    assert float(row[4]) == pytest.approx(200.0)
+    assert float(row[5]) == pytest.approx(200 * 1024 * 2 / 1e6, rel=1e-3)
