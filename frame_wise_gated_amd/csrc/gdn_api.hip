@@ -85,20 +85,48 @@ T* at(void* ws, size_t off) {
     if ((x) != hipSuccess) return GDN_EHIP;        \
   } while (0)
 
-// Phase 1 into the workspace terms buffer [FH][2D][D].
-gdn_status run_terms(const Shape& sh, const Layout& L, const void* k, const void* v,
-                     const float* beta, void* ws, hipStream_t st) {
+// Device pointers of one call.
+struct Slice {
+  const char* q;
+  const char* k;
+  const char* v;
+  const float* beta;
+  const float* gamma;
+  const float* s0;
+  float* fwd;        // per-frame forward states (nullable)
+  float* rev;        // per-frame reverse states (nullable)
+  float* s_final;    // nullable
+  char* o;           // nullable
+  float* terms;      // workspace [FH][2D][D]
+  float* partial;    // workspace [FH][n_split][2D][D] (n_split > 1 only)
+  float* compC;      // workspace [BH][P][D][D]
+  float* compH;
+  float* start;
+
+};
+
+Slice work_slice(const Layout& L, void* ws) {
+  Slice w;
+  memset(&w, 0, sizeof(w));
+  w.terms = at<float>(ws, L.terms);
+  w.partial = at<float>(ws, L.partial);
+  w.compC = at<float>(ws, L.compC);
+  w.compH = at<float>(ws, L.compH);
+  w.start = at<float>(ws, L.start);
+  return w;
+}
+
+// Phase 1 into the terms buffer [FH][2D][D].
+gdn_status run_terms(const Shape& sh, int n_split, const Slice& x, hipStream_t st) {
   const int64_t DD = (int64_t)sh.D * sh.D;
-  float* terms = at<float>(ws, L.terms);
-  gdn::TermsOut direct{terms, terms + DD, 2 * DD, 0};
+  gdn::TermsOut direct{x.terms, x.terms + DD, 2 * DD, 0};
   const bool split_a = gdn::scan_uses_mfma(sh);
-  if (L.n_split == 1) {
-    GDN_HIP(gdn::launch_terms(sh, k, v, beta, 1, direct, split_a, st));
+  if (n_split == 1) {
+    GDN_HIP(gdn::launch_terms(sh, x.k, x.v, x.beta, 1, direct, split_a, st));
   } else {
-    float* part = at<float>(ws, L.partial);
-    gdn::TermsOut po{part, part + DD, (int64_t)L.n_split * 2 * DD, 2 * DD};
-    GDN_HIP(gdn::launch_terms(sh, k, v, beta, L.n_split, po, false, st));
-    GDN_HIP(gdn::launch_reduce_partials(sh, part, L.n_split, direct, split_a, st));
+    gdn::TermsOut po{x.partial, x.partial + DD, (int64_t)n_split * 2 * DD, 2 * DD};
+    GDN_HIP(gdn::launch_terms(sh, x.k, x.v, x.beta, n_split, po, false, st));
+    GDN_HIP(gdn::launch_reduce_partials(sh, x.partial, n_split, direct, split_a, st));
   }
   return GDN_OK;
 }
@@ -107,24 +135,23 @@ void uniform_offsets(int* offs, int T, int P) {
   for (int p = 0; p <= P; ++p) offs[p] = (int)(((int64_t)p * T) / P);
 }
 
-// Forward scan (sequential or composite) from the terms buffer.
-gdn_status run_forward(const Shape& sh, const Layout& L, const float* gamma, const float* s0,
-                       float* states, float* s_final, int P, void* ws, hipStream_t st) {
+// Forward scan (sequential or composite) from the terms buffer into x.fwd
+// (per-frame states, nullable) and x.s_final (nullable).
+gdn_status run_forward(const Shape& sh, int P, const Slice& x, hipStream_t st) {
   const int64_t DD = (int64_t)sh.D * sh.D;
-  const float* terms = at<float>(ws, L.terms);
   if (P <= 1) {
     gdn::ScanParams p;
     memset(&p, 0, sizeof(p));
-    p.terms = terms;
-    p.gamma = gamma;
+    p.terms = x.terms;
+    p.gamma = x.gamma;
     p.T = sh.T;
     p.nchunk = 1;
     p.mode = gdn::SCAN_FORWARD;
-    p.init = s0;
+    p.init = x.s0;
     p.init_bh_stride = DD;
     p.init_c_stride = 0;
-    p.states = states;
-    p.finA = s_final;
+    p.states = x.fwd;
+    p.finA = x.s_final;
     p.fin_bh_stride = DD;
     p.fin_last_only = 1;
     p.offsets[0] = 0;
@@ -132,47 +159,89 @@ gdn_status run_forward(const Shape& sh, const Layout& L, const float* gamma, con
     GDN_HIP(gdn::launch_scan(sh, p, st));
     return GDN_OK;
   }
-  float* C = at<float>(ws, L.compC);
-  float* H = at<float>(ws, L.compH);
-  float* start = at<float>(ws, L.start);
   {
     gdn::ScanParams p;
     memset(&p, 0, sizeof(p));
-    p.terms = terms;
-    p.gamma = gamma;
+    p.terms = x.terms;
+    p.gamma = x.gamma;
     p.T = sh.T;
     p.nchunk = P;
     p.mode = gdn::SCAN_COMPOSE;
-    p.finA = C;
-    p.finB = H;
+    p.finA = x.compC;
+    p.finB = x.compH;
     p.fin_bh_stride = (int64_t)P * DD;
     p.fin_c_stride = DD;
     uniform_offsets(p.offsets, sh.T, P);
     GDN_HIP(gdn::launch_scan(sh, p, st));
   }
   {
-    gdn::CombineParams cp{C, H, s0, start, P};
+    gdn::CombineParams cp{x.compC, x.compH, x.s0, x.start, P};
     GDN_HIP(gdn::launch_combine(sh, cp, st));
   }
   {
     gdn::ScanParams p;
     memset(&p, 0, sizeof(p));
-    p.terms = terms;
-    p.gamma = gamma;
+    p.terms = x.terms;
+    p.gamma = x.gamma;
     p.T = sh.T;
     p.nchunk = P;
     p.mode = gdn::SCAN_FORWARD;
-    p.init = start;
+    p.init = x.start;
     p.init_bh_stride = (int64_t)P * DD;
     p.init_c_stride = DD;
-    p.states = states;
-    p.finA = s_final;
+    p.states = x.fwd;
+    p.finA = x.s_final;
     p.fin_bh_stride = DD;
     p.fin_last_only = 1;
     uniform_offsets(p.offsets, sh.T, P);
     GDN_HIP(gdn::launch_scan(sh, p, st));
   }
   return GDN_OK;
+}
+
+// Reverse scan restarted at every chunk_len-frame boundary into x.rev.
+gdn_status run_reverse(const Shape& sh, int chunk_len, const Slice& x, hipStream_t st) {
+  const int64_t n_rev = ((int64_t)sh.T + chunk_len - 1) / chunk_len;
+  gdn::ScanParams p;
+  memset(&p, 0, sizeof(p));
+  p.terms = x.terms;
+  p.gamma = x.gamma;
+  p.T = sh.T;
+  p.nchunk = (int)n_rev;
+  p.mode = gdn::SCAN_REVERSE;
+  p.states = x.rev;
+  for (int c = 0; c <= (int)n_rev; ++c) {
+    int64_t off = (int64_t)c * chunk_len;
+    p.offsets[c] = (int)(off < sh.T ? off : sh.T);
+  }
+  GDN_HIP(gdn::launch_scan(sh, p, st));
+  return GDN_OK;
+}
+
+// Everything after phase 1 except the readout: forward scan (when per-frame
+// forward states or the final state are wanted) and the chunk-reset reverse
+// scan (chunk_len > 0, when reverse states are wanted).
+gdn_status run_scans(const Shape& sh, int P, int chunk_len, const Slice& x, hipStream_t st) {
+  gdn_status s;
+  if (x.fwd || x.s_final)
+    if ((s = run_forward(sh, P, x, st)) != GDN_OK) return s;
+  if (chunk_len > 0 && x.rev)
+    if ((s = run_reverse(sh, chunk_len, x, st)) != GDN_OK) return s;
+  return GDN_OK;
+}
+
+gdn_status run_readout(const Shape& sh, const Slice& x, hipStream_t st) {
+  if (x.o) GDN_HIP(gdn::launch_readout(sh, x.q, x.fwd, x.rev, x.o, st));
+  return GDN_OK;
+}
+
+// Phase 1, scans and readout of a whole call, in stream order.
+gdn_status run_path(const Shape& sh, int n_split, int P, int chunk_len, const Slice& x,
+                    hipStream_t st) {
+  gdn_status s;
+  if ((s = run_terms(sh, n_split, x, st)) != GDN_OK) return s;
+  if ((s = run_scans(sh, P, chunk_len, x, st)) != GDN_OK) return s;
+  return run_readout(sh, x, st);
 }
 
 // No frames: the final state is the initial state.
@@ -272,11 +341,17 @@ gdn_status gdn_scan_fwd(const gdn_desc* desc, const void* q, const void* k, cons
   if (!k || !v || !beta || !gamma || (o && !q)) return GDN_EINVAL;
   Layout L = layout(sh, n_time_chunks);
   if ((s = check_ws(L, ws, ws_bytes)) != GDN_OK) return s;
-  float* st_buf = states ? states : (o ? at<float>(ws, L.states) : nullptr);
-  if ((s = run_terms(sh, L, k, v, beta, ws, st)) != GDN_OK) return s;
-  if ((s = run_forward(sh, L, gamma, s0, st_buf, s_final, n_time_chunks, ws, st)) != GDN_OK) return s;
-  if (o) GDN_HIP(gdn::launch_readout(sh, q, st_buf, nullptr, o, st));
-  return GDN_OK;
+  Slice x = work_slice(L, ws);
+  x.q = (const char*)q;
+  x.k = (const char*)k;
+  x.v = (const char*)v;
+  x.beta = beta;
+  x.gamma = gamma;
+  x.s0 = s0;
+  x.fwd = states ? states : (o ? at<float>(ws, L.states) : nullptr);
+  x.s_final = s_final;
+  x.o = (char*)o;
+  return run_path(sh, L.n_split, n_time_chunks, 0, x, st);
 }
 
 gdn_status gdn_scan_bidir_chunked(const gdn_desc* desc, const void* q, const void* k,
@@ -302,30 +377,18 @@ gdn_status gdn_scan_bidir_chunked(const gdn_desc* desc, const void* q, const voi
   if (!k || !v || !beta || !gamma || (o && !q)) return GDN_EINVAL;
   Layout L = layout(sh, n_time_chunks);
   if ((s = check_ws(L, ws, ws_bytes)) != GDN_OK) return s;
-  float* fwd_buf = states_fwd ? states_fwd : (o ? at<float>(ws, L.states) : nullptr);
-  float* rev_buf = states_rev ? states_rev : (o ? at<float>(ws, L.rev) : nullptr);
-  if ((s = run_terms(sh, L, k, v, beta, ws, st)) != GDN_OK) return s;
-  if (fwd_buf || s_final) {
-    if ((s = run_forward(sh, L, gamma, s0, fwd_buf, s_final, n_time_chunks, ws, st)) != GDN_OK)
-      return s;
-  }
-  if (rev_buf) {
-    gdn::ScanParams p;
-    memset(&p, 0, sizeof(p));
-    p.terms = at<float>(ws, L.terms);
-    p.gamma = gamma;
-    p.T = sh.T;
-    p.nchunk = (int)n_rev;
-    p.mode = gdn::SCAN_REVERSE;
-    p.states = rev_buf;
-    for (int c = 0; c <= (int)n_rev; ++c) {
-      int64_t off = (int64_t)c * chunk_len;
-      p.offsets[c] = (int)(off < sh.T ? off : sh.T);
-    }
-    GDN_HIP(gdn::launch_scan(sh, p, st));
-  }
-  if (o) GDN_HIP(gdn::launch_readout(sh, q, fwd_buf, rev_buf, o, st));
-  return GDN_OK;
+  Slice x = work_slice(L, ws);
+  x.q = (const char*)q;
+  x.k = (const char*)k;
+  x.v = (const char*)v;
+  x.beta = beta;
+  x.gamma = gamma;
+  x.s0 = s0;
+  x.fwd = states_fwd ? states_fwd : (o ? at<float>(ws, L.states) : nullptr);
+  x.rev = states_rev ? states_rev : (o ? at<float>(ws, L.rev) : nullptr);
+  x.s_final = s_final;
+  x.o = (char*)o;
+  return run_path(sh, L.n_split, n_time_chunks, chunk_len, x, st);
 }
 
 gdn_status gdn_compose(const gdn_desc* desc, const void* k, const void* v, const float* beta,
@@ -351,7 +414,11 @@ gdn_status gdn_compose(const gdn_desc* desc, const void* k, const void* v, const
   float* Cb = C ? C : at<float>(ws, L.compC);
   float* Hb = Hc ? Hc : at<float>(ws, L.compH);
   if (sh.T > 0) {
-    if ((s = run_terms(sh, L, k, v, beta, ws, st)) != GDN_OK) return s;
+    Slice x = work_slice(L, ws);
+    x.k = (const char*)k;
+    x.v = (const char*)v;
+    x.beta = beta;
+    if ((s = run_terms(sh, L.n_split, x, st)) != GDN_OK) return s;
   }
   gdn::ScanParams p;
   memset(&p, 0, sizeof(p));

@@ -53,6 +53,31 @@ __device__ __forceinline__ uint32_t relu_bf16x2(uint32_t w) {
   return w & ~(neg * 0xFFFFu);
 }
 
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding): this wave's global loads
+// except the n youngest have completed and its own LDS accesses are done.
+// n = 63 leaves every global load in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | 0x70 | (((N >> 4) & 3) << 14));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(), which waits
+// for every global load in flight (vmcnt(0)) and so drains any prefetch; the
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Barrier for data exchanged through LDS only: this wave's LDS accesses
+// complete, then the workgroup meets; global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  wait_vmcnt_lgkm0<63>();
+  bare_barrier();
+}
+
 // Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each
 // XCD has its own L2. Kernels whose workgroups come in groups of `per` that
 // read the same data (e.g. the row blocks of one head's scan, which all read
@@ -68,6 +93,24 @@ __device__ __forceinline__ void xcd_job(int64_t linear, int per, int64_t* job, i
   const int64_t slot = linear / kNumXcd;
   *job = (slot / per) * kNumXcd + xcd;
   *member = (int)(slot % per);
+}
+
+// Internal layout of the phase-1 terms read by the MFMA scan (bf16 inputs,
+// D = 128), per frame-head: A hi (32 KB), A lo (32 KB), U (64 KB, fp32).
+// Both are stored as 16-byte granules in the order in which the scan's MFMA
+// lanes load them, so every 64-lane load instruction reads 1 KB of
+// consecutive bytes:
+//   A granule (n, kc): A[8kc .. 8kc+7][n] (bf16, hi or lo part), at granule
+//     index ((n/16)*4 + kc/4)*64 + (kc%4)*16 + n%16;
+//   U granule (m, nc): U[m][4nc .. 4nc+3] (fp32), at granule index
+//     ((m/16)*8 + nc/4)*64 + (nc%4)*16 + m%16.
+// Lane l of the scan's wave w, tile nt, k-slice ks reads A granule
+// (32w + 16nt + l%16, 4ks + l/16): index ((2w + nt)*4 + ks)*64 + l.
+__host__ __device__ constexpr int a_granule(int n, int kc) {
+  return ((n >> 4) * 4 + (kc >> 2)) * 64 + (kc & 3) * 16 + (n & 15);
+}
+__host__ __device__ constexpr int u_granule(int m, int nc) {
+  return ((m >> 4) * 8 + (nc >> 2)) * 64 + (nc & 3) * 16 + (m & 15);
 }
 
 // Geometry shared by the host dispatcher and the kernels.
@@ -96,8 +139,8 @@ enum ScanMode : int {
 };
 
 struct ScanParams {
-  const float* terms;   // [FH][2D][D]: A then U of every frame (A as the bf16 hi/lo
-                        // transposed pair on the MFMA path, fp32 row-major otherwise)
+  const float* terms;   // [FH][2D][D]: A then U of every frame (granule layout of
+                        // a_granule / u_granule on the MFMA path, fp32 row-major otherwise)
   const float* gamma;   // [FH]
   int T;
   int nchunk;           // chunks per head
@@ -128,8 +171,8 @@ struct CombineParams {
 hipError_t launch_prepare(const Shape& sh, const void* k, void* k_hat, hipStream_t st);
 bool terms_use_mfma(const Shape& sh);
 int terms_split(const Shape& sh);
-// split_a: write A as the transposed bf16 hi/lo pair the MFMA scan reads
-// (MFMA path only); otherwise A is fp32 row-major.
+// split_a: write A as the bf16 hi/lo pair and U in the granule layout the
+// MFMA scan reads (MFMA path only); otherwise A and U are fp32 row-major.
 hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const float* beta,
                         int n_split, TermsOut out, bool split_a, hipStream_t st);
 hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_split,

@@ -18,9 +18,13 @@
 // while the row block stays in LDS.
 #include "gdn_common.h"
 
-// Row block of the MFMA scan, in 16-row MFMA tiles (build-time tuning knob).
+// Build-time tuning knobs of the MFMA scan: row block in 16-row MFMA tiles,
+// and frames of A_t / U_t prefetched in registers.
 #ifndef GDN_SCAN_MT
 #define GDN_SCAN_MT 4
+#endif
+#ifndef GDN_SCAN_F
+#define GDN_SCAN_F 2
 #endif
 
 namespace gdn {
@@ -173,15 +177,23 @@ __global__ void __launch_bounds__(256) combine_rows_kernel(CombineParams p) {
 // MFMA cost (still far above the fp32 MFMA rate). Accumulation, the decay and
 // the U_t update are fp32.
 //
-// Data placement: each lane keeps the fp32 state entries it produces (rows
-// 16mt + 4g + r, columns 32w + 16nt + l16) in registers for the whole scan;
-// LDS holds only the split bf16 copy of the row block that the MFMA "A"
-// operand reads, written once per element by its owner lane. A_t arrives from
-// phase 1 already split and transposed ([n][k], k contiguous), so each B
-// fragment is one 16-byte load; the fragments of the next frame are requested
-// as soon as the current frame's MFMAs no longer need them. Wave w owns output
-// columns [32w, 32w + 32) as two 16-column MFMA tiles.
-template <int MT>
+// The MFMA computes (X A)^T tiles: A_t^T (from phase 1 already split, in the
+// granule layout described with a_granule) is the first operand, one 16-byte
+// load per fragment and 1 KB per wave, and the state rows are the second. A lane then owns
+// four consecutive columns n of one state row m, so its U_t entries, its
+// per-frame state store and its share of the split bf16 copy in LDS are
+// single 16- or 8-byte accesses. Each lane keeps its fp32 state entries in
+// registers for the whole scan; LDS holds only the split copy that the MFMA
+// reads (double-buffered, one barrier per frame).
+//
+// The per-frame step is short (96 MFMAs per wave for MT = 4) next to the
+// latency of a global load, so the A_t fragments and U_t entries of the next
+// kF frames live in a register ring: the loads of frame s + kF are issued as
+// soon as frame s has consumed the slot. Slot indices are compile-time (the
+// frame loop is unrolled by kF); loads past the last frame re-read it, so
+// the outstanding-load bookkeeping is identical in every step. Wave w owns
+// output columns [32w, 32w + 32) as two 16-column MFMA tiles.
+template <int MT, int kF>
 __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
   constexpr int D = 128;
   constexpr int R = 16 * MT;
@@ -200,7 +212,7 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
   const int64_t bh = job / p.nchunk;
   const int row0 = rb * R;
   const bool c_rows = (p.mode == SCAN_COMPOSE) && row0 < D;
-  const bool use_u = !c_rows;
+  const float umul = c_rows ? 0.f : 1.f;
   const int srow0 = row0 % D;
 
   const int tid = threadIdx.x;
@@ -209,130 +221,147 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
   const int l16 = lane & 15;
   const int g = lane >> 4;
   const int n0 = 32 * wave;
+  // this lane's state entries: rows m = 16 mt + l16, columns ncol(nt) .. + 3
+  auto ncol = [&](int nt) { return n0 + 16 * nt + 4 * g; };
 
-  float xr[MT][2][4];
-  auto put_split = [&](int buf, int m, int n, float x) {
-    const uint32_t h = pack_bf16x2(x, 0.f) & 0xFFFFu;
-    const uint32_t l = pack_bf16x2(x - bf16_to_f32(h), 0.f) & 0xFFFFu;
-    Xh[buf][m][n] = (uint16_t)h;
-    Xl[buf][m][n] = (uint16_t)l;
+  f32x4_t xr[MT][2];
+  auto put_split = [&](int buf, int m, int n, const f32x4_t& x) {
+    uint32_t h[2], l[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      h[q] = pack_bf16x2(x[2 * q], x[2 * q + 1]);
+      l[q] = pack_bf16x2(x[2 * q] - bf16_to_f32(h[q] & 0xFFFFu), x[2 * q + 1] - bf16_to_f32(h[q] >> 16));
+    }
+    *(uint2*)&Xh[buf][m][n] = make_uint2(h[0], h[1]);
+    *(uint2*)&Xl[buf][m][n] = make_uint2(l[0], l[1]);
   };
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < 2; ++nt) {
+      const int m = 16 * mt + l16;
+      const int n = ncol(nt);
+      f32x4_t x0 = {0.f, 0.f, 0.f, 0.f};
+      if (p.mode == SCAN_COMPOSE) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 16 * mt + 4 * g + r;
-        const int n = n0 + 16 * nt + l16;
-        float x0 = 0.f;
-        if (p.mode == SCAN_COMPOSE) {
-          x0 = (c_rows && (srow0 + m) == n) ? 1.f : 0.f;
-        } else if (p.mode == SCAN_FORWARD && p.init != nullptr) {
-          x0 = p.init[bh * p.init_bh_stride + (int64_t)c * p.init_c_stride +
-                      (int64_t)(srow0 + m) * D + n];
-        }
-        xr[mt][nt][r] = x0;
-        put_split(0, m, n, x0);
+        for (int r = 0; r < 4; ++r) x0[r] = (c_rows && srow0 + m == n + r) ? 1.f : 0.f;
+      } else if (p.mode == SCAN_FORWARD && p.init != nullptr) {
+        x0 = *(const f32x4_t*)(p.init + bh * p.init_bh_stride + (int64_t)c * p.init_c_stride +
+                              (int64_t)(srow0 + m) * D + n);
       }
+      xr[mt][nt] = x0;
+      put_split(0, m, n, x0);
+    }
   __syncthreads();
 
   const int a = p.offsets[c];
   const int e = p.offsets[c + 1];
   const int nsteps = e - a;
-  auto frame_of = [&](int step) { return (p.mode == SCAN_REVERSE) ? (e - 1 - step) : (a + step); };
+  auto frame_of = [&](int step) {
+    step = step < nsteps ? step : nsteps - 1;
+    return (p.mode == SCAN_REVERSE) ? (e - 1 - step) : (a + step);
+  };
   auto terms_of = [&](int step) { return p.terms + (bh * p.T + frame_of(step)) * 2 * DD; };
 
-  // Prefetches are unconditional (the last step re-reads its own frame) so
-  // that the outstanding-load bookkeeping stays exact across the loop.
-  uint4 ah[2][4], al[2][4];
-  float u[MT][2][4];
-  const float umul = use_u ? 1.f : 0.f;
-  auto load_b = [&](const float* base, int ks) {
-    const uint16_t* hiT = (const uint16_t*)base;
-    const uint16_t* loT = hiT + DD;
+  // register ring: A_t^T fragments (hi, lo), U_t entries and gamma_t of kF
+  // frames. gamma rides with U_t: waiting for a load issued later than the
+  // prefetches would wait for all of them (vmcnt counts in order).
+  uint4 ah[kF][2][4], al[kF][2][4];
+  f32x4_t u[kF][MT][2];
+  float gmr[kF];
+  // granule layout of the terms (a_granule / u_granule): each load below is
+  // 1 KB of consecutive bytes per wave
+  auto load_a = [&](int j, int step) {
+    const uint4* hiT = (const uint4*)terms_of(step);
+    const uint4* loT = hiT + DD / 8;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int n = n0 + 16 * nt + l16;
-      ah[nt][ks] = *(const uint4*)(hiT + n * D + 32 * ks + 8 * g);
-      al[nt][ks] = *(const uint4*)(loT + n * D + 32 * ks + 8 * g);
-    }
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int gi = ((2 * wave + nt) * 4 + ks) * 64 + lane;  // a_granule(n0 + 16nt + l16, 4ks + g)
+        ah[j][nt][ks] = hiT[gi];
+        al[j][nt][ks] = loT[gi];
+      }
   };
-  auto load_u = [&](const float* base) {
-    const float* Ut = base + DD + (int64_t)srow0 * D + n0 + l16;
+  auto load_u = [&](int j, int step) {
+    const f32x4_t* Ug = (const f32x4_t*)(terms_of(step) + DD);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) u[mt][nt][r] = Ut[(16 * mt + 4 * g + r) * D + 16 * nt];
+      for (int nt = 0; nt < 2; ++nt)  // u_granule(srow0 + 16mt + l16, ncol(nt) / 4)
+        u[j][mt][nt] = Ug[((srow0 / 16 + mt) * 8 + 2 * wave + nt) * 64 + lane];
+    gmr[j] = p.gamma[bh * p.T + frame_of(step)];
   };
+  if (nsteps > 0) {
+#pragma unroll
+    for (int j = 0; j < kF; ++j) {
+      load_a(j, j);
+      load_u(j, j);
+    }
+  }
 
   int cur = 0;
-  if (nsteps > 0) {
-    const float* base = terms_of(0);
+  for (int s0 = 0; s0 < nsteps; s0 += kF) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) load_b(base, ks);
-    load_u(base);
-  }
-  float gm = nsteps > 0 ? p.gamma[bh * p.T + frame_of(0)] : 0.f;
-  for (int step = 0; step < nsteps; ++step) {
-    const int64_t f = bh * p.T + frame_of(step);
-    const int nstep = (step + 1 < nsteps) ? step + 1 : step;
-    const float* nbase = terms_of(nstep);
-    const float gm_next = p.gamma[bh * p.T + frame_of(nstep)];
-
-    f32x4_t acc[MT][2];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[mt][nt][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = 16 * mt + l16;
-        const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, *(const uint4*)&Xh[cur][m][32 * ks + 8 * g]);
-        const bf16x8_t xl = __builtin_bit_cast(bf16x8_t, *(const uint4*)&Xl[cur][m][32 * ks + 8 * g]);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const bf16x8_t bh_ = __builtin_bit_cast(bf16x8_t, ah[nt][ks]);
-          const bf16x8_t bl_ = __builtin_bit_cast(bf16x8_t, al[nt][ks]);
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bh_, acc[mt][nt], 0, 0, 0);
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bl_, acc[mt][nt], 0, 0, 0);
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bh_, acc[mt][nt], 0, 0, 0);
-        }
-      }
-      load_b(nbase, ks);  // fragments of the next frame, k-slice ks
-    }
-
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = 16 * mt + 4 * g + r;
-          const int n = n0 + 16 * nt + l16;
-          const float xn = gm * (xr[mt][nt][r] - acc[mt][nt][r]) + umul * u[mt][nt][r];
-          xr[mt][nt][r] = xn;
-          put_split(cur ^ 1, m, n, xn);
-        }
-    if (p.states != nullptr) {
-      float* st = p.states + f * DD + (int64_t)srow0 * D + n0 + l16;
+    for (int j = 0; j < kF; ++j) {
+      const int step = s0 + j;
+      const bool active = step < nsteps;
+      const int64_t f = bh * p.T + frame_of(step);
+      const float gm = gmr[j];
+      f32x4_t acc[MT][2];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // per k-slice: the state fragments of every row tile first, then the
+      // three split products in an order that puts 2*MT independent MFMAs
+      // between two that accumulate into the same tile
 #pragma unroll
-          for (int r = 0; r < 4; ++r) st[(16 * mt + 4 * g + r) * D + 16 * nt] = xr[mt][nt][r];
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8_t xh[MT], xl[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = 16 * mt + l16;
+          xh[mt] = __builtin_bit_cast(bf16x8_t, *(const uint4*)&Xh[cur][m][32 * ks + 8 * g]);
+          xl[mt] = __builtin_bit_cast(bf16x8_t, *(const uint4*)&Xl[cur][m][32 * ks + 8 * g]);
+        }
+#pragma unroll
+        for (int prod = 0; prod < 3; ++prod)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+              const bf16x8_t af = __builtin_bit_cast(bf16x8_t, prod == 1 ? al[j][nt][ks] : ah[j][nt][ks]);
+              const bf16x8_t xf = prod == 2 ? xl[mt] : xh[mt];
+              acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, xf, acc[mt][nt], 0, 0, 0);
+            }
+      }
+      load_a(j, step + kF);  // the slot's fragments are consumed: refill with frame step + kF
+
+      // acc[mt][nt][r] = (X A_t)[m][ncol(nt) + r] with m = 16 mt + l16
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int m = 16 * mt + l16;
+          f32x4_t xn;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xn[r] = gm * (xr[mt][nt][r] - acc[mt][nt][r]) + umul * u[j][mt][nt][r];
+          if (active) xr[mt][nt] = xn;
+          put_split(cur ^ 1, m, ncol(nt), xr[mt][nt]);
+        }
+      if (active && p.states != nullptr) {
+        float* st = p.states + f * DD + (int64_t)srow0 * D;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            *(f32x4_t*)(st + (16 * mt + l16) * D + ncol(nt)) = xr[mt][nt];
+      }
+      load_u(j, step + kF);
+      cur ^= 1;
+      lds_barrier();  // a plain __syncthreads() would also wait for the prefetched frames
     }
-    load_u(nbase);
-    gm = gm_next;
-    cur ^= 1;
-    __syncthreads();
   }
 
   if (p.fin_last_only && c != p.nchunk - 1) return;
@@ -343,9 +372,7 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        fin[(int64_t)(srow0 + 16 * mt + 4 * g + r) * D + n0 + 16 * nt + l16] = xr[mt][nt][r];
+      *(f32x4_t*)(fin + (int64_t)(srow0 + 16 * mt + l16) * D + ncol(nt)) = xr[mt][nt];
 }
 
 }  // namespace
@@ -360,7 +387,7 @@ hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st) {
   if (scan_uses_mfma(sh)) {
     constexpr int MT = GDN_SCAN_MT;
     const int64_t blocks = xcd_grid(q.njobs, (int)(rows_total / (16 * MT)));
-    scan_mfma_d128<MT><<<dim3((unsigned)blocks), 256, 0, st>>>(q);
+    scan_mfma_d128<MT, GDN_SCAN_F><<<dim3((unsigned)blocks), 256, 0, st>>>(q);
     return hipGetLastError();
   }
   dim3 grid((unsigned)xcd_grid(q.njobs, (int)(rows_total / kR)));

@@ -267,22 +267,6 @@ __device__ __forceinline__ void dma4(const void* g, void* lds, bool active) {
 }
 #pragma clang diagnostic pop
 
-// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding): this wave's copies except
-// the n youngest have landed and its own LDS reads are complete.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | 0x70 | (((N >> 4) & 3) << 14));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads() (which would
-// also wait for every copy in flight); the empty asm statements keep the
-// compiler from moving memory accesses across it.
-__device__ __forceinline__ void bare_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // One MFMA operand fragment: lane gets the 8 consecutive tokens
 // k0 + 8*(lane/32) + 0..7 of feature f0 + (lane % 32) (k0 % 16 == 0,
@@ -435,30 +419,44 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   const int n = 32 * nt + (lane & 31);
   const int64_t obase = fh * out.fstride + (int64_t)split * out.sstride;
 
-  // 32 KB staged block -> dst. bf16 blocks sit swizzled in LDS (row n is
-  // 256 bytes; its 16-byte chunk j lives at position j ^ (n % 16)); fp32
-  // blocks are plain row-major.
-  auto flush = [&](void* dst, bool swz) {
+  // 32 KB staged block -> dst: 16-byte granule ci of dst comes from LDS byte
+  // offset lds_of(ci).
+  auto flush = [&](void* dst, auto lds_of) {
     wait_vmcnt_lgkm0<63>();  // lgkmcnt(0): this wave's LDS writes are done
     bare_barrier();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ci = 512 * i + tid;
-      const int lo = swz ? ((ci >> 4) << 8) + (((ci & 15) ^ ((ci >> 4) & 15)) << 4) : 16 * ci;
-      __builtin_nontemporal_store(*(const u32x4_t*)(stage + lo), (u32x4_t*)dst + ci);
+      __builtin_nontemporal_store(*(const u32x4_t*)(stage + lds_of(ci)), (u32x4_t*)dst + ci);
     }
     wait_vmcnt_lgkm0<63>();  // this wave's LDS reads are done before the block is refilled
     bare_barrier();
   };
+  // LDS placements: fp32 rows plain (row-major) or swizzled (row m: 16-byte
+  // chunk c at position c ^ (m % 16)); A^T rows n of 256 bytes, chunk kc at
+  // kc ^ (n % 16). The swizzles keep both the owners' writes and the
+  // granule-order reads free of bank conflicts.
+  auto plain = [](int ci) { return 16 * ci; };
+  auto u_frag = [](int ci) {  // granule ci of a 64-row half of U
+    const int m = 16 * (ci >> 9) + (ci & 15);
+    const int nc = 4 * ((ci >> 6) & 7) + ((ci >> 4) & 3);
+    return m * 512 + ((nc ^ (m & 15)) << 4);
+  };
+  auto a_frag = [](int ci) {  // granule ci of the hi or lo block of A
+    const int n = 16 * (ci >> 8) + (ci & 15);
+    const int kc = 4 * ((ci >> 6) & 3) + ((ci >> 4) & 3);
+    return n * 256 + ((kc ^ (n & 15)) << 4);
+  };
   // Owning waves: rows 64 hh .. 64 hh + 63 of their (scaled) fp32 result.
-  auto put_rows = [&](int hh) {
+  auto put_rows = [&](int hh, bool swz) {
     float* Sf = (float*)stage;
 #pragma unroll
     for (int mt2 = 0; mt2 < 2; ++mt2)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int m = 32 * mt2 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        Sf[m * D + n] = acc[2 * hh + mt2][q] * scale;
+        const int col = swz ? ((((n >> 2) ^ (m & 15)) << 2) | (n & 3)) : n;
+        Sf[m * D + col] = acc[2 * hh + mt2][q] * scale;
       }
   };
   // A waves: the hi (hl = 0) or lo (hl = 1) bf16 half of A, transposed
@@ -490,27 +488,31 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   };
 
   // The output pointers are kernel arguments, so every wave takes the same
-  // branches and meets the same barriers.
+  // branches and meets the same barriers. kSplitA: A as bf16 hi/lo and U, both
+  // in the scan's granule layout; otherwise fp32 row-major A and U.
   if (out.outA != nullptr) {
     if (kSplitA) {
 #pragma unroll
       for (int hl = 0; hl < 2; ++hl) {
         if (rowsK) put_split(hl);
-        flush((uint16_t*)(out.outA + obase) + hl * D * D, true);
+        flush((uint16_t*)(out.outA + obase) + hl * D * D, a_frag);
       }
     } else {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        if (rowsK) put_rows(hh);
-        flush(out.outA + obase + hh * 64 * D, false);
+        if (rowsK) put_rows(hh, false);
+        flush(out.outA + obase + hh * 64 * D, plain);
       }
     }
   }
   if (out.outU != nullptr) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      if (!rowsK) put_rows(hh);
-      flush(out.outU + obase + hh * 64 * D, false);
+      if (!rowsK) put_rows(hh, kSplitA);
+      if (kSplitA)
+        flush(out.outU + obase + hh * 64 * D, u_frag);
+      else
+        flush(out.outU + obase + hh * 64 * D, plain);
     }
   }
 }
@@ -626,8 +628,10 @@ reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, in
       uint32_t h1 = pack_bf16x2(v[2], v[3]);
       uint32_t l0 = pack_bf16x2(v[0] - bf16_to_f32(h0 & 0xFFFFu), v[1] - bf16_to_f32(h0 >> 16));
       uint32_t l1 = pack_bf16x2(v[2] - bf16_to_f32(h1 & 0xFFFFu), v[3] - bf16_to_f32(h1 >> 16));
-      *(uint2*)(hiT + nn * D + mm) = make_uint2(h0, h1);
-      *(uint2*)(loT + nn * D + mm) = make_uint2(l0, l1);
+      // split_a is only requested for D = 128 (granule layout)
+      const int64_t at = (int64_t)a_granule((int)nn, (int)(mm >> 3)) * 8 + (mm & 7);
+      *(uint2*)(hiT + at) = make_uint2(h0, h1);
+      *(uint2*)(loT + at) = make_uint2(l0, l1);
       continue;
     }
     const float4* src = (const float4*)(base + e);
@@ -643,7 +647,10 @@ reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, in
     const int64_t col = e % D;
     float* dst = row < D ? out.outA : out.outU;
     if (dst == nullptr) continue;
-    *(float4*)(dst + f * out.fstride + (row % D) * D + col) = s;
+    if (split_a && row >= D)
+      *(float4*)(dst + f * out.fstride + (int64_t)u_granule((int)(row - D), (int)(col >> 2)) * 4) = s;
+    else
+      *(float4*)(dst + f * out.fstride + (row % D) * D + col) = s;
   }
 }
 

@@ -307,3 +307,45 @@ def test_named_workload_full_size(idx, heads):
         for h in range(w.H):
             e = rel_fro(host(res["states"][0, h]), host(seq["states"][0, h]))
             assert e <= 1e-4, (h, e)
+
+
+# ------------------------------------------------------- batch invariance
+@pytest.mark.parametrize("mode", ["fwd", "bidir"])
+def test_batch_invariance_bitwise(mode):
+    """A head's results do not depend on the batch it is launched with: a
+    large call (B=2, H=3, FH=1200) and calls on single heads sliced out of it
+    give bit-identical states, final states and outputs; the large call also
+    matches the oracle."""
+    w = gi.workload(3).with_shape(B=2, H=3, T=200, S=64)
+    x, d = _gen(w)
+    s0 = _s0(w)
+    s0d = torch.from_numpy(s0).to(DEV)
+
+    def run(q, k, v, beta, gamma, s0_):
+        if mode == "bidir":
+            return gdn.gdn_scan_bidir_chunked(q, k, v, beta, gamma, 7, s0=s0_, n_time_chunks=3)
+        return gdn.gdn_scan_fwd(q, k, v, beta, gamma, s0=s0_, n_time_chunks=4)
+
+    say("batch invariance", mode, "full batch")
+    full = run(d["q"], d["k"], d["v"], d["beta"], d["gamma"], s0d)
+    torch.cuda.synchronize()
+    for (b, h) in [(0, 0), (1, 2)]:
+        say("batch invariance", mode, "head", (b, h))
+        one = run(*(d[n][b:b + 1, h:h + 1].contiguous() for n in ("q", "k", "v", "beta", "gamma")),
+                  s0d[b:b + 1, h:h + 1].contiguous())
+        torch.cuda.synchronize()
+        for n, t in one.items():
+            assert torch.equal(t[0, 0], full[n][b, h]), (b, h, n)
+    b, h = 1, 2
+    a = head_arrays(x, b, h)
+    s0h = s0[b, h][None, None].astype(np.float64)
+    if mode == "bidir":
+        ref = orc.scan_bidir_chunked(a["q"], a["k"], a["v"], a["beta"], a["gamma"], 7, s0=s0h)
+        names = ("states_fwd", "states_rev", "s_final", "o")
+    else:
+        ref = orc.scan_fwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"], s0=s0h)
+        names = ("states", "s_final", "o")
+    for n in names:
+        e = rel_fro(host(full[n][b, h]), ref[n][0, 0])
+        say(mode, n, f"{e:.2e}")
+        assert e <= tol(w), (n, e)
