@@ -391,6 +391,17 @@ gdn_status gdn_scan_bidir_chunked(const gdn_desc* desc, const void* q, const voi
   return run_path(sh, L.n_split, n_time_chunks, chunk_len, x, st);
 }
 
+gdn_status gdn_step(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                    const float* beta, const float* gamma, const float* carry_in,
+                    float* carry_out, void* o, float* states_fwd, float* states_rev, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (desc == nullptr) return GDN_EINVAL;
+  // the block is one reverse chunk; T = 0 passes the carry through
+  const int32_t chunk_len = desc->T > 0 ? desc->T : 1;
+  return gdn_scan_bidir_chunked(desc, q, k, v, beta, gamma, carry_in, chunk_len, states_fwd,
+                                states_rev, carry_out, o, 1, ws, ws_bytes, stream);
+}
+
 gdn_status gdn_compose(const gdn_desc* desc, const void* k, const void* v, const float* beta,
                        const float* gamma, const int32_t* chunk_offsets, int32_t P, float* C,
                        float* Hc, const float* s0, float* s_start, void* ws, size_t ws_bytes,

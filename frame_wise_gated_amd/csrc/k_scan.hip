@@ -283,8 +283,11 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
         al[j][nt][ks] = loT[gi];
       }
   };
+  // Composite C rows have no U term (umul = 0): their U loads re-read granules
+  // of the frame's A block, which the workgroup fetches anyway (cache hits,
+  // finite values), so that every workgroup issues the same load sequence.
   auto load_u = [&](int j, int step) {
-    const f32x4_t* Ug = (const f32x4_t*)(terms_of(step) + DD);
+    const f32x4_t* Ug = (const f32x4_t*)(terms_of(step) + (c_rows ? 0 : DD));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll

@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
     L.gdn_scan_bidir_chunked.restype = _st
     L.gdn_scan_bidir_chunked.argtypes = [P(gdn_desc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
                                          _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
+    L.gdn_step.restype = _st
+    L.gdn_step.argtypes = [P(gdn_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                           ctypes.c_size_t, _vp]
     L.gdn_compose.restype = _st
     L.gdn_compose.argtypes = [P(gdn_desc), _vp, _vp, _vp, _vp, P(ctypes.c_int32), ctypes.c_int32,
                               _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -223,6 +226,31 @@ def gdn_scan_bidir_chunked(q, k, v, beta, gamma, chunk_len, s0=None, n_time_chun
                                         int(n_time_chunks), _ptr(ws), nb, _stream(stream)),
            "gdn_scan_bidir_chunked")
     return {"states_fwd": states_fwd, "states_rev": states_rev, "s_final": s_final, "o": o}
+
+
+def gdn_step(q, k, v, beta, gamma, carry_in=None, carry_out=None, key_scale=0.0,
+             keys_prepared=False, want_o=True, want_states=False, o=None, states_fwd=None,
+             states_rev=None, ws=None, stream=None):
+    """One streaming block (k.shape[2] frames): bidirectional inside the block,
+    forward state carried in from `carry_in` and out to `carry_out` (which may
+    be the same tensor)."""
+    d = _desc_from(k, key_scale, keys_prepared)
+    B, H, T, S, D = k.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _need(t, n, k.shape, k.dtype)
+    _need(beta, "beta", (B, H, T, S), torch.float32)
+    _need(gamma, "gamma", (B, H, T), torch.float32)
+    _need(carry_in, "carry_in", (B, H, D, D), torch.float32)
+    _need(carry_out, "carry_out", (B, H, D, D), torch.float32)
+    carry_out = _out(carry_out, True, (B, H, D, D), torch.float32, k.device)
+    o = _out(o, want_o, k.shape, k.dtype, k.device)
+    states_fwd = _out(states_fwd, want_states, (B, H, T, D, D), torch.float32, k.device)
+    states_rev = _out(states_rev, want_states, (B, H, T, D, D), torch.float32, k.device)
+    ws, nb = _ws(ws, d, 1, k.device)
+    _check(lib().gdn_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gamma),
+                          _ptr(carry_in), _ptr(carry_out), _ptr(o), _ptr(states_fwd),
+                          _ptr(states_rev), _ptr(ws), nb, _stream(stream)), "gdn_step")
+    return {"carry_out": carry_out, "o": o, "states_fwd": states_fwd, "states_rev": states_rev}
 
 
 def gdn_compose(k, v, beta, gamma, chunk_offsets, s0=None, key_scale=0.0, keys_prepared=False,

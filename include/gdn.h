@@ -128,6 +128,24 @@ GDN_API gdn_status gdn_scan_bidir_chunked(const gdn_desc* desc, const void* q, c
                                   float* states_rev, float* s_final, void* o,
                                   int32_t n_time_chunks, void* ws, size_t ws_bytes, void* stream);
 
+/* Streaming chunk step: one block of desc->T frames, bidirectional inside the
+ * block (the reverse scan covers the whole block), with the causal forward
+ * state carried from block to block. This is how the released chunk-causal
+ * model runs (trdm.cn SANA-WM guide, sections 四.3 and 七: blocks of
+ * num_frame_per_block = 3 latent frames, chunk_size 3). S_{-1} = carry_in
+ * (NULL = zero state); carry_out receives S_{T-1} of the block; o, states_fwd
+ * and states_rev are the block's outputs as in gdn_scan_bidir_chunked.
+ * Equivalent to gdn_scan_bidir_chunked(chunk_len = T, n_time_chunks = 1,
+ * s0 = carry_in, s_final = carry_out): cutting a sequence into blocks of L
+ * frames and stepping through them gives the chunk-causal scan with
+ * chunk_len = L. carry_in and carry_out may be the same buffer (each state
+ * row is read before it is rewritten); no other output may alias an input.
+ * Workspace: gdn_workspace_bytes(desc, 1). */
+GDN_API gdn_status gdn_step(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                            const float* beta, const float* gamma, const float* carry_in,
+                            float* carry_out, void* o, float* states_fwd, float* states_rev,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* Affine composites of explicit time chunks (blog.hotdry.top SANA-WM post,
  * section "显存分片: Context-Parallel 的工程实现"): for chunk p = [a_p, a_{p+1}),
  * C_p = M_{a_p} ... M_{a_{p+1}-1} (ordered product) and H_p = the chunk scanned

@@ -21,7 +21,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = gdn.exported_names_in_header()
     assert set(names) == {"gdn_status_str", "gdn_workspace_bytes", "gdn_prepare", "gdn_frame_terms",
-                          "gdn_scan_fwd", "gdn_scan_bidir_chunked", "gdn_compose", "gdn_readout"}
+                          "gdn_scan_fwd", "gdn_scan_bidir_chunked", "gdn_compose", "gdn_readout",
+                          "gdn_step"}
     out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -109,6 +110,13 @@ def test_null_and_chunk_arguments(L):
         arr = (ctypes.c_int32 * len(offs))(*offs)
         assert L.gdn_compose(ctypes.byref(d), fake, fake, fake, fake, arr, len(offs) - 1, fake,
                              None, None, None, fake, 1 << 30, None) == gdn.GDN_EINVAL
+    # streaming step: NULL descriptor, missing gamma, workspace too small
+    assert L.gdn_step(None, fake, fake, fake, fake, fake, None, fake, fake, None, None, fake,
+                      1 << 30, None) == gdn.GDN_EINVAL
+    assert L.gdn_step(ctypes.byref(d), fake, fake, fake, fake, None, None, fake, fake, None, None,
+                      fake, 1 << 30, None) == gdn.GDN_EINVAL
+    assert L.gdn_step(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake, fake, None, None,
+                      fake, 16, None) == gdn.GDN_EWORKSPACE
     # prepare refuses already-prepared keys
     dp = gdn.make_desc(1, 1, 4, 12, 16, gdn.GDN_F32, keys_prepared=True)
     assert L.gdn_prepare(ctypes.byref(dp), fake, fake, None) == gdn.GDN_EINVAL

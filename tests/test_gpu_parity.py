@@ -349,3 +349,39 @@ def test_batch_invariance_bitwise(mode):
         e = rel_fro(host(full[n][b, h]), ref[n][0, 0])
         say(mode, n, f"{e:.2e}")
         assert e <= tol(w), (n, e)
+
+
+# ------------------------------------------------------ streaming chunk step
+def test_streaming_step_chain_equals_chunk_causal_scan():
+    """gdn_step over consecutive 3-frame blocks (the last one short), with the
+    forward state carried in place from block to block, reproduces the
+    chunk-causal bidirectional scan with chunk_len = 3 bit for bit, and the
+    oracle within the bf16 bar."""
+    w = gi.workload(5).with_shape(H=2, T=31, S=200)
+    x, d = _gen(w)
+    L = 3
+    say("step chain: one-shot chunk-causal scan")
+    ref = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], L)
+    carry = torch.zeros((w.B, w.H, w.D, w.D), dtype=torch.float32, device=DEV)
+    outs, fwd, rev = [], [], []
+    for a in range(0, w.T, L):
+        b = min(a + L, w.T)
+        say("step chain: block", a, b)
+        blk = {n: d[n][:, :, a:b].contiguous() for n in ("q", "k", "v", "beta", "gamma")}
+        r = gdn.gdn_step(blk["q"], blk["k"], blk["v"], blk["beta"], blk["gamma"], carry_in=carry,
+                         carry_out=carry, want_states=True)
+        outs.append(r["o"])
+        fwd.append(r["states_fwd"])
+        rev.append(r["states_rev"])
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs, dim=2), ref["o"])
+    assert torch.equal(torch.cat(fwd, dim=2), ref["states_fwd"])
+    assert torch.equal(torch.cat(rev, dim=2), ref["states_rev"])
+    assert torch.equal(carry, ref["s_final"])
+    a = head_arrays(x, 0, 1)
+    orc_ref = orc.scan_bidir_chunked(a["q"], a["k"], a["v"], a["beta"], a["gamma"], L)
+    for n in ("o", "states_fwd", "states_rev"):
+        e = rel_fro(host(torch.cat({"o": outs, "states_fwd": fwd, "states_rev": rev}[n], dim=2)[0, 1]),
+                    orc_ref[n][0, 0])
+        say("step chain vs oracle", n, f"{e:.2e}")
+        assert e <= tol(w), (n, e)
