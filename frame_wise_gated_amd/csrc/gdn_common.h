@@ -15,15 +15,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// 16-byte load of a large activation stream (k, v) that is read exactly once
-// per call, with the non-temporal hint (measured: phase 1 runs about 5% faster
-// on MI355X; the same hint on the readout's stores slows it down, so the
-// readout uses plain accesses).
-__device__ __forceinline__ uint4 ld_stream16(const void* p) {
-  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

@@ -9,216 +9,31 @@
 // followed by the scales c^2 (A rows) and c (U rows) in fp32. Every frame-head
 // is independent, so the grid is frame-parallel.
 //
-// MFMA path (bf16, D = 128): one workgroup per frame-head (or per token range
-// of it), 4 wave64s, v_mfma_f32_32x32x16_bf16 with fp32 accumulation. Tokens
-// are the contraction index but are the strided dimension in memory, so each
-// 64-token tile is transposed on its way to LDS: a thread loads 8 tokens x 8
-// features with eight coalesced 16-byte loads, transposes the 8x8 bf16 block
-// in registers and writes eight 16-byte rows "feature-major" into LDS, where
-// an MFMA operand fragment (8 consecutive tokens of one feature) is a single
-// 16-byte read. ReLU(k) is exact in bf16; beta . ReLU(k) is rounded to bf16
-// once (round to nearest even) to form the second operand.
+// MFMA path (bf16, D = 128): terms_dma_bf16_d128 below; any other shape runs
+// the fp32 vector path terms_generic.
 #include <algorithm>
 #include <type_traits>
 
 #include "gdn_common.h"
 
-#ifndef GDN_TERMS_DMA
-#define GDN_TERMS_DMA 1
-#endif
-
 namespace gdn {
 
 namespace {
 
-constexpr int kTS = 64;          // tokens per LDS tile
-constexpr int kChunks = kTS / 8; // 16-byte chunks (8 tokens) per LDS row
-
-// XOR swizzle of the 16-byte chunk inside a 128-byte LDS row. Row-consecutive
-// reads (8 lanes, same chunk) and the transposed writes (8 lanes, rows 8 apart)
-// both land in 8 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return chunk ^ ((row + (row >> 3)) & 7);
-}
-
-template <bool kSplitA>
-__global__ void __launch_bounds__(256, 2)
-terms_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                     const float* __restrict__ beta, int S, int n_split, float c, int prepared,
-                     TermsOut out) {
-  constexpr int D = 128;
-  // rows 0..127: ReLU(k)^T, rows 128..255: v^T, rows 256..383: (beta . ReLU(k))^T
-  __shared__ uint4 lds[(2 * D + D) * kChunks];
-
-  const int64_t fh = blockIdx.x / n_split;
-  const int split = blockIdx.x % n_split;
-  const int tiles = (S + kTS - 1) / kTS;
-  const int t_begin = (int)(((int64_t)split * tiles) / n_split);
-  const int t_end = (int)(((int64_t)(split + 1) * tiles) / n_split);
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const bool isK = tid < 128;           // waves 0,1 stage keys; waves 2,3 stage values
-  const int lt = tid & 127;
-  const int g = lt >> 4;                // token group: tokens 8g..8g+7 of the tile
-  const int db = lt & 15;               // feature block: features 8db..8db+7
-  const uint16_t* src = (isK ? k : v) + fh * (int64_t)S * D + 8 * db;
-  const float* bsrc = beta + fh * (int64_t)S;
-
-  uint4 x[8];
-  float bt[8];
-
-  auto load_tile = [&](int tile) {
-    const int s0 = tile * kTS + 8 * g;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int s = s0 + e;
-      x[e] = (s < S) ? ld_stream16(src + (int64_t)s * D) : make_uint4(0, 0, 0, 0);
-    }
-    if (isK) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bt[e] = (s0 + e < S) ? bsrc[s0 + e] : 0.f;
-    }
-  };
-
-  auto stage_tile = [&]() {
-    uint32_t xw[8][4];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      xw[e][0] = x[e].x;
-      xw[e][1] = x[e].y;
-      xw[e][2] = x[e].z;
-      xw[e][3] = x[e].w;
-      if (isK && !prepared) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) xw[e][p] = relu_bf16x2(xw[e][p]);
-      }
-    }
-    const int rbase = isK ? 0 : D;
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const int hw = f >> 1;
-      const int shf = (f & 1) * 16;
-      uint32_t lo[4], hi[4], y[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        lo[p] = (xw[2 * p][hw] >> shf) & 0xFFFFu;
-        hi[p] = (xw[2 * p + 1][hw] >> shf) & 0xFFFFu;
-        y[p] = lo[p] | (hi[p] << 16);
-      }
-      const int row = rbase + 8 * db + f;
-      lds[row * kChunks + swz(row, g)] = make_uint4(y[0], y[1], y[2], y[3]);
-      if (isK) {
-        uint32_t w[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-          w[p] = pack_bf16x2(bf16_to_f32(lo[p]) * bt[2 * p], bf16_to_f32(hi[p]) * bt[2 * p + 1]);
-        const int wrow = 2 * D + 8 * db + f;
-        lds[wrow * kChunks + swz(wrow, g)] = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    }
-  };
-
-  f32x16_t acc[2][4];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[mt][nt][j] = 0.f;
-
-  if (t_begin < t_end) load_tile(t_begin);
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    __syncthreads();  // every wave is done reading the previous tile
-    stage_tile();
-    if (tile + 1 < t_end) load_tile(tile + 1);  // in flight during the MFMAs below
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kTS / 16; ++kk) {
-      const int ch = 2 * kk + (lane >> 5);
-      bf16x8_t a[2], b[4];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int row = 64 * wave + 32 * mt + (lane & 31);
-        a[mt] = __builtin_bit_cast(bf16x8_t, lds[row * kChunks + swz(row, ch)]);
-      }
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int row = 2 * D + 32 * nt + (lane & 31);
-        b[nt] = __builtin_bit_cast(bf16x8_t, lds[row * kChunks + swz(row, ch)]);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
-    }
-  }
-
-  // Epilogue: 32x32 accumulator layout, lane holds column (lane & 31) and rows
-  // 8*(j/4) + 4*(lane/32) + (j%4) of each tile.
-  const bool rowsA = wave < 2;
-  const float scale = rowsA ? c * c : c;
-  float* dst = (rowsA ? out.outA : out.outU);
-  if (dst == nullptr) return;
-  dst += fh * out.fstride + (int64_t)split * out.sstride;
-  const int mbase = 64 * (wave & 1);
-  if (kSplitA && rowsA) {
-    // A^T as a bf16 hi/lo pair (A = hi + lo to ~2^-17 relative), [n][m] with m
-    // contiguous: the scan reads 8 consecutive m of one column as one fragment.
-    uint16_t* hiT = (uint16_t*)dst;
-    uint16_t* loT = hiT + D * D;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          const int m = mbase + 32 * mt + 8 * jg + 4 * (lane >> 5);
-          const int n = 32 * nt + (lane & 31);
-          float a[4];
-          uint32_t h[2], l[2];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] = acc[mt][nt][4 * jg + e] * scale;
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            h[e] = pack_bf16x2(a[2 * e], a[2 * e + 1]);
-            l[e] = pack_bf16x2(a[2 * e] - bf16_to_f32(h[e] & 0xFFFFu),
-                               a[2 * e + 1] - bf16_to_f32(h[e] >> 16));
-          }
-          *(uint2*)(hiT + n * D + m) = make_uint2(h[0], h[1]);
-          *(uint2*)(loT + n * D + m) = make_uint2(l[0], l[1]);
-        }
-    return;
-  }
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = mbase + 32 * mt + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-        const int n = 32 * nt + (lane & 31);
-        dst[m * D + n] = acc[mt][nt][j] * scale;
-      }
-}
-
-// ---------------------------------------------------------------------------
-// Deep-pipeline variant of the MFMA path. The bytes in flight per CU, not
-// the MFMA work, bound phase 1: with two register-staged workgroups per CU
-// (about 64 KB of loads outstanding) the k/v stream reaches ~5 TB/s, while
-// the same access pattern with more loads in flight reaches ~6.9 TB/s. Here
-// the loads bypass registers: global_load_lds_dwordx4 copies 16 bytes per
-// lane straight into a ring of kNst LDS stages (32 tokens of k and v each, in
-// their natural token-major layout, 16-byte chunks XOR-swizzled by token), so
-// kNst - 1 stages stay in flight while one is consumed. MFMA fragments (eight
-// consecutive tokens of one feature) are read with ds_read_b64_tr_b16, which
-// returns, for each 16-lane group, the columns of the 4 x 16 block its lanes
-// address: two reads give a lane its eight tokens. ReLU and beta . ReLU(k)
-// are formed per fragment in registers (beta rides along in the same ring).
-// 8 waves: wave w owns output columns 32(w%4)..+32 and the 128 rows of A
-// (w < 4) or of U (w >= 4), as four 32 x 32 tiles.
+// MFMA path. Phase 1 is bound by the HBM reads of k and v, and the bytes in
+// flight per CU decide how close it gets: with the loads staged through
+// registers (two workgroups per CU, about 64 KB outstanding) the stream
+// reaches about 5 TB/s, while the same access pattern with more in flight
+// reaches about 7 TB/s. Here the loads bypass registers: global_load_lds_dwordx4
+// copies 16 bytes per lane straight into a ring of kNst LDS stages (32 tokens
+// of k and v each), so kNst - 1 stages stay in flight while one is consumed.
+// MFMA fragments (eight consecutive tokens of one feature) are read with
+// ds_read_b64_tr_b16, which returns, for each 16-lane group, the columns of
+// the 4 x 16 block its lanes address: two reads give a lane its eight tokens.
+// A per-stage transform pass forms ReLU(k) in place and bf16(beta . ReLU(k))
+// (beta rides along in the same ring). 8 waves: wave w owns output columns
+// 32(w%4)..+32 and the 128 rows of A (w < 4) or of U (w >= 4), as four
+// 32 x 32 tiles.
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 #define GDN_LDS __attribute__((address_space(3)))
 #define GDN_GLB __attribute__((address_space(1)))
@@ -695,7 +510,6 @@ int terms_split(const Shape& sh) {
 hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const float* beta,
                         int n_split, TermsOut out, bool split_a, hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
-#if GDN_TERMS_DMA
   if (terms_use_mfma(sh)) {
     dim3 grid((unsigned)(sh.FH() * n_split));
     const uint16_t* kk = (const uint16_t*)k;
@@ -708,17 +522,6 @@ hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const flo
       terms_dma_bf16_d128<false, false><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out);
     else
       terms_dma_bf16_d128<false, true><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out);
-    return hipGetLastError();
-  }
-#endif
-  if (terms_use_mfma(sh)) {
-    dim3 grid((unsigned)(sh.FH() * n_split));
-    if (split_a)
-      terms_mfma_bf16_d128<true><<<grid, 256, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, beta,
-                                                       sh.S, n_split, sh.c, sh.prepared, out);
-    else
-      terms_mfma_bf16_d128<false><<<grid, 256, 0, st>>>((const uint16_t*)k, (const uint16_t*)v,
-                                                        beta, sh.S, n_split, sh.c, sh.prepared, out);
     return hipGetLastError();
   }
   if (sh.io == 1) return launch_generic<uint16_t>(sh, k, v, beta, n_split, out, st);
