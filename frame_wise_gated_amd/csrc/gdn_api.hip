@@ -120,13 +120,13 @@ Slice work_slice(const Layout& L, void* ws) {
 gdn_status run_terms(const Shape& sh, int n_split, const Slice& x, hipStream_t st) {
   const int64_t DD = (int64_t)sh.D * sh.D;
   gdn::TermsOut direct{x.terms, x.terms + DD, 2 * DD, 0};
-  const bool split_a = gdn::scan_uses_mfma(sh);
+  const bool scan_layout = gdn::scan_uses_mfma(sh);
   if (n_split == 1) {
-    GDN_HIP(gdn::launch_terms(sh, x.k, x.v, x.beta, 1, direct, split_a, st));
+    GDN_HIP(gdn::launch_terms(sh, x.k, x.v, x.beta, 1, direct, scan_layout, st));
   } else {
     gdn::TermsOut po{x.partial, x.partial + DD, (int64_t)n_split * 2 * DD, 2 * DD};
     GDN_HIP(gdn::launch_terms(sh, x.k, x.v, x.beta, n_split, po, false, st));
-    GDN_HIP(gdn::launch_reduce_partials(sh, x.partial, n_split, direct, split_a, st));
+    GDN_HIP(gdn::launch_reduce_partials(sh, x.partial, n_split, direct, scan_layout, st));
   }
   return GDN_OK;
 }

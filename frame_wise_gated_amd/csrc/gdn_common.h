@@ -87,11 +87,12 @@ __device__ __forceinline__ void xcd_job(int64_t linear, int per, int64_t* job, i
 }
 
 // Internal layout of the phase-1 terms read by the MFMA scan (bf16 inputs,
-// D = 128), per frame-head: A hi (32 KB), A lo (32 KB), U (64 KB, fp32).
+// D = 128), per frame-head slot of 2*D*D floats: bf16(A) (32 KB), 32 KB not
+// used, U (64 KB, fp32).
 // Both are stored as 16-byte granules in the order in which the scan's MFMA
 // lanes load them, so every 64-lane load instruction reads 1 KB of
 // consecutive bytes:
-//   A granule (n, kc): A[8kc .. 8kc+7][n] (bf16, hi or lo part), at granule
+//   A granule (n, kc): A[8kc .. 8kc+7][n] (bf16), at granule
 //     index ((n/16)*4 + kc/4)*64 + (kc%4)*16 + n%16;
 //   U granule (m, nc): U[m][4nc .. 4nc+3] (fp32), at granule index
 //     ((m/16)*8 + nc/4)*64 + (nc%4)*16 + m%16.
@@ -162,12 +163,12 @@ struct CombineParams {
 hipError_t launch_prepare(const Shape& sh, const void* k, void* k_hat, hipStream_t st);
 bool terms_use_mfma(const Shape& sh);
 int terms_split(const Shape& sh);
-// split_a: write A as the bf16 hi/lo pair and U in the granule layout the
+// scan_layout: write A in bf16 and U in fp32, both in the granule layout the
 // MFMA scan reads (MFMA path only); otherwise A and U are fp32 row-major.
 hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const float* beta,
-                        int n_split, TermsOut out, bool split_a, hipStream_t st);
+                        int n_split, TermsOut out, bool scan_layout, hipStream_t st);
 hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_split,
-                                  TermsOut out, bool split_a, hipStream_t st);
+                                  TermsOut out, bool scan_layout, hipStream_t st);
 bool scan_uses_mfma(const Shape& sh);
 hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st);
 hipError_t launch_combine(const Shape& sh, const CombineParams& p, hipStream_t st);

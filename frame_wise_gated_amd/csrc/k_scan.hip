@@ -21,7 +21,7 @@
 // Build-time tuning knobs of the MFMA scan: row block in 16-row MFMA tiles,
 // and frames of A_t / U_t prefetched in registers.
 #ifndef GDN_SCAN_MT
-#define GDN_SCAN_MT 4
+#define GDN_SCAN_MT 2
 #endif
 #ifndef GDN_SCAN_F
 #define GDN_SCAN_F 2
@@ -170,15 +170,20 @@ __global__ void __launch_bounds__(256) combine_rows_kernel(CombineParams p) {
 }
 
 // MFMA scan step for bf16 workloads with D = 128: the product X A_t of the
-// fp32 row block X (R = 16*MT rows) with the fp32 A_t runs on bf16 MFMA with
-// both operands split into a hi/lo bf16 pair,
-//   X A ~= Xh Ah + Xh Al + Xl Ah,     |X - Xh - Xl| <= 2^-17 |X|,
-// which keeps about 16 significant bits per product at three times the bf16
-// MFMA cost (still far above the fp32 MFMA rate). Accumulation, the decay and
-// the U_t update are fp32.
+// fp32 row block X (R = 16*MT rows) with A_t runs on bf16 MFMA, the state
+// split into a hi/lo bf16 pair and A_t rounded to bf16 once by phase 1:
+//   X A ~= Xh A' + Xl A',     |X - Xh - Xl| <= 2^-17 |X|,  A' = bf16(A).
+// The state therefore keeps about 16 significant bits through every step
+// (rounding the state itself to bf16 each frame would compound over the
+// frames), at twice the bf16 MFMA cost. A' perturbs the transition by at most
+// 2^-9 |A| elementwise, and since the transition is contractive
+// (tr A <= 1), that error stays at the 1e-4 level over a 121-frame scan
+// (measured with the float64 oracle: 6.5e-5 relative on the states of the
+// 60 s 720p layer). Accumulation, the decay and the U_t update are fp32, and
+// U_t stays fp32.
 //
-// The MFMA computes (X A)^T tiles: A_t^T (from phase 1 already split, in the
-// granule layout described with a_granule) is the first operand, one 16-byte
+// The MFMA computes (X A)^T tiles: bf16(A_t)^T (from phase 1, in the granule
+// layout described with a_granule) is the first operand, one 16-byte
 // load per fragment and 1 KB per wave, and the state rows are the second. A lane then owns
 // four consecutive columns n of one state row m, so its U_t entries, its
 // per-frame state store and its share of the split bf16 copy in LDS are
@@ -186,7 +191,7 @@ __global__ void __launch_bounds__(256) combine_rows_kernel(CombineParams p) {
 // registers for the whole scan; LDS holds only the split copy that the MFMA
 // reads (double-buffered, one barrier per frame).
 //
-// The per-frame step is short (96 MFMAs per wave for MT = 4) next to the
+// The per-frame step is short (64 MFMAs per wave for MT = 4) next to the
 // latency of a global load, so the A_t fragments and U_t entries of the next
 // kF frames live in a register ring: the loads of frame s + kF are issued as
 // soon as frame s has consumed the slot. Slot indices are compile-time (the
@@ -263,25 +268,21 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
   };
   auto terms_of = [&](int step) { return p.terms + (bh * p.T + frame_of(step)) * 2 * DD; };
 
-  // register ring: A_t^T fragments (hi, lo), U_t entries and gamma_t of kF
+  // register ring: A_t^T fragments, U_t entries and gamma_t of kF
   // frames. gamma rides with U_t: waiting for a load issued later than the
   // prefetches would wait for all of them (vmcnt counts in order).
-  uint4 ah[kF][2][4], al[kF][2][4];
+  uint4 af[kF][2][4];
   f32x4_t u[kF][MT][2];
   float gmr[kF];
   // granule layout of the terms (a_granule / u_granule): each load below is
   // 1 KB of consecutive bytes per wave
   auto load_a = [&](int j, int step) {
-    const uint4* hiT = (const uint4*)terms_of(step);
-    const uint4* loT = hiT + DD / 8;
+    const uint4* At = (const uint4*)terms_of(step);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int gi = ((2 * wave + nt) * 4 + ks) * 64 + lane;  // a_granule(n0 + 16nt + l16, 4ks + g)
-        ah[j][nt][ks] = hiT[gi];
-        al[j][nt][ks] = loT[gi];
-      }
+      for (int ks = 0; ks < 4; ++ks)  // a_granule(n0 + 16nt + l16, 4ks + g)
+        af[j][nt][ks] = At[((2 * wave + nt) * 4 + ks) * 64 + lane];
   };
   // Composite C rows have no U term (umul = 0): their U loads re-read granules
   // of the frame's A block, which the workgroup fetches anyway (cache hits,
@@ -317,8 +318,8 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       // per k-slice: the state fragments of every row tile first, then the
-      // three split products in an order that puts 2*MT independent MFMAs
-      // between two that accumulate into the same tile
+      // two products in an order that puts 2*MT independent MFMAs between two
+      // that accumulate into the same tile
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         bf16x8_t xh[MT], xl[MT];
@@ -329,14 +330,14 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
           xl[mt] = __builtin_bit_cast(bf16x8_t, *(const uint4*)&Xl[cur][m][32 * ks + 8 * g]);
         }
 #pragma unroll
-        for (int prod = 0; prod < 3; ++prod)
+        for (int prod = 0; prod < 2; ++prod)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-              const bf16x8_t af = __builtin_bit_cast(bf16x8_t, prod == 1 ? al[j][nt][ks] : ah[j][nt][ks]);
-              const bf16x8_t xf = prod == 2 ? xl[mt] : xh[mt];
-              acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, xf, acc[mt][nt], 0, 0, 0);
+              const bf16x8_t a_ = __builtin_bit_cast(bf16x8_t, af[j][nt][ks]);
+              acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_, prod == 0 ? xh[mt] : xl[mt],
+                                                                    acc[mt][nt], 0, 0, 0);
             }
       }
       load_a(j, step + kF);  // the slot's fragments are consumed: refill with frame step + kF

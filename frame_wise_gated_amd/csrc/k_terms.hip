@@ -100,7 +100,7 @@ __device__ __forceinline__ uint4 tr_frag(const uint8_t* base, int lb, int k0, in
 #else
 #define GDN_TERMS_WAVES_PER_EU 2  // one workgroup per CU (its ring fills the LDS)
 #endif
-template <bool kSplitA, bool kPrepared>
+template <bool kScanLayout, bool kPrepared>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(GDN_TERMS_WAVES_PER_EU, GDN_TERMS_WAVES_PER_EU)))
 terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -222,7 +222,7 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
 
   // Epilogue, staged through the idle ring so that every global store
   // instruction writes 1 KB of consecutive bytes: block by block (32 KB each:
-  // the hi or lo half of the split A, or 64 rows of an fp32 result), the
+  // bf16(A) in the scan's layout, or 64 rows of an fp32 result), the
   // owning waves drop their values into LDS, the workgroup meets, and all 512
   // threads copy the block out with 16-byte stores. Scattered 8-byte stores
   // straight from the MFMA accumulators cost phase 1 about a seventh of its
@@ -257,7 +257,7 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
     const int nc = 4 * ((ci >> 6) & 7) + ((ci >> 4) & 3);
     return m * 512 + ((nc ^ (m & 15)) << 4);
   };
-  auto a_frag = [](int ci) {  // granule ci of the hi or lo block of A
+  auto a_frag = [](int ci) {  // granule ci of bf16(A)
     const int n = 16 * (ci >> 8) + (ci & 15);
     const int kc = 4 * ((ci >> 6) & 3) + ((ci >> 4) & 3);
     return n * 256 + ((kc ^ (n & 15)) << 4);
@@ -274,44 +274,26 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
         Sf[m * D + col] = acc[2 * hh + mt2][q] * scale;
       }
   };
-  // A waves: the hi (hl = 0) or lo (hl = 1) bf16 half of A, transposed
-  // (row n holds A[0..D)[n]); hi = bf16(x), lo = bf16(x - hi). The hi pass
-  // leaves the scaled residual x - hi in the accumulators for the lo pass.
-  auto put_split = [&](int hl) {
+  // A waves: bf16(A) transposed (row n holds A[0..D)[n]) for the scan.
+  auto put_a_bf16 = [&]() {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
         const int m = 32 * mt + 8 * jg + 4 * (lane >> 5);
-        uint32_t w[2];
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          const int i0 = 4 * jg + 2 * q2;
-          if (hl == 0) {
-            const float x0 = acc[mt][i0] * scale;
-            const float x1 = acc[mt][i0 + 1] * scale;
-            w[q2] = pack_bf16x2(x0, x1);
-            acc[mt][i0] = x0 - bf16_to_f32(w[q2] & 0xFFFFu);
-            acc[mt][i0 + 1] = x1 - bf16_to_f32(w[q2] >> 16);
-          } else {
-            w[q2] = pack_bf16x2(acc[mt][i0], acc[mt][i0 + 1]);
-          }
-        }
-        *(uint2*)(stage + n * 256 + (((m >> 3) ^ (n & 15)) << 4) + 2 * (m & 7)) =
-            make_uint2(w[0], w[1]);
+        const uint32_t w0 = pack_bf16x2(acc[mt][4 * jg] * scale, acc[mt][4 * jg + 1] * scale);
+        const uint32_t w1 = pack_bf16x2(acc[mt][4 * jg + 2] * scale, acc[mt][4 * jg + 3] * scale);
+        *(uint2*)(stage + n * 256 + (((m >> 3) ^ (n & 15)) << 4) + 2 * (m & 7)) = make_uint2(w0, w1);
       }
   };
 
   // The output pointers are kernel arguments, so every wave takes the same
-  // branches and meets the same barriers. kSplitA: A as bf16 hi/lo and U, both
-  // in the scan's granule layout; otherwise fp32 row-major A and U.
+  // branches and meets the same barriers. kScanLayout: A in bf16 and U in
+  // fp32, both in the scan's granule layout; otherwise fp32 row-major A and U.
   if (out.outA != nullptr) {
-    if (kSplitA) {
-#pragma unroll
-      for (int hl = 0; hl < 2; ++hl) {
-        if (rowsK) put_split(hl);
-        flush((uint16_t*)(out.outA + obase) + hl * D * D, a_frag);
-      }
+    if (kScanLayout) {
+      if (rowsK) put_a_bf16();
+      flush(out.outA + obase, a_frag);
     } else {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -323,8 +305,8 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   if (out.outU != nullptr) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      if (!rowsK) put_rows(hh, kSplitA);
-      if (kSplitA)
+      if (!rowsK) put_rows(hh, kScanLayout);
+      if (kScanLayout)
         flush(out.outU + obase + hh * 64 * D, u_frag);
       else
         flush(out.outU + obase + hh * 64 * D, plain);
@@ -415,11 +397,12 @@ terms_generic(const TIn* __restrict__ k, const TIn* __restrict__ v, const float*
 }
 
 // Sum of the token-range partials in a fixed order (deterministic). With
-// split_a, the A half is written as the transposed bf16 hi/lo pair (as the
-// MFMA epilogue does): each thread then sums four consecutive m of one column.
+// scan_layout, the A half is written as bf16 in the scan's granule layout (as
+// the MFMA epilogue does): each thread then sums four consecutive m of one
+// column.
 __global__ void __launch_bounds__(256)
 reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, int64_t FH,
-                       TermsOut out, int split_a) {
+                       TermsOut out, int scan_layout) {
   const int64_t per = (int64_t)2 * D * D / 4;  // four-element groups per frame-head
   const int64_t n = FH * per;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -428,7 +411,7 @@ reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, in
     const int64_t f = i / per;
     const int64_t e = (i % per) * 4;
     const float* base = partial + (f * n_split) * 2 * D * D;
-    if (split_a && e < (int64_t)D * D) {
+    if (scan_layout && e < (int64_t)D * D) {
       // group = (column nn, rows mm..mm+3)
       const int64_t nn = e / D;
       const int64_t mm = e % D;
@@ -437,16 +420,10 @@ reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, in
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] += base[(int64_t)p * 2 * D * D + (mm + q) * D + nn];
       if (out.outA == nullptr) continue;
-      uint16_t* hiT = (uint16_t*)(out.outA + f * out.fstride);
-      uint16_t* loT = hiT + (int64_t)D * D;
-      uint32_t h0 = pack_bf16x2(v[0], v[1]);
-      uint32_t h1 = pack_bf16x2(v[2], v[3]);
-      uint32_t l0 = pack_bf16x2(v[0] - bf16_to_f32(h0 & 0xFFFFu), v[1] - bf16_to_f32(h0 >> 16));
-      uint32_t l1 = pack_bf16x2(v[2] - bf16_to_f32(h1 & 0xFFFFu), v[3] - bf16_to_f32(h1 >> 16));
-      // split_a is only requested for D = 128 (granule layout)
+      uint16_t* At = (uint16_t*)(out.outA + f * out.fstride);
+      // scan_layout is only requested for D = 128 (granule layout)
       const int64_t at = (int64_t)a_granule((int)nn, (int)(mm >> 3)) * 8 + (mm & 7);
-      *(uint2*)(hiT + at) = make_uint2(h0, h1);
-      *(uint2*)(loT + at) = make_uint2(l0, l1);
+      *(uint2*)(At + at) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       continue;
     }
     const float4* src = (const float4*)(base + e);
@@ -462,7 +439,7 @@ reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, in
     const int64_t col = e % D;
     float* dst = row < D ? out.outA : out.outU;
     if (dst == nullptr) continue;
-    if (split_a && row >= D)
+    if (scan_layout && row >= D)
       *(float4*)(dst + f * out.fstride + (int64_t)u_granule((int)(row - D), (int)(col >> 2)) * 4) = s;
     else
       *(float4*)(dst + f * out.fstride + (row % D) * D + col) = s;
@@ -508,15 +485,15 @@ int terms_split(const Shape& sh) {
 }
 
 hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const float* beta,
-                        int n_split, TermsOut out, bool split_a, hipStream_t st) {
+                        int n_split, TermsOut out, bool scan_layout, hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
   if (terms_use_mfma(sh)) {
     dim3 grid((unsigned)(sh.FH() * n_split));
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
-    if (split_a && !sh.prepared)
+    if (scan_layout && !sh.prepared)
       terms_dma_bf16_d128<true, false><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out);
-    else if (split_a)
+    else if (scan_layout)
       terms_dma_bf16_d128<true, true><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out);
     else if (!sh.prepared)
       terms_dma_bf16_d128<false, false><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out);
@@ -529,12 +506,12 @@ hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const flo
 }
 
 hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_split, TermsOut out,
-                                  bool split_a, hipStream_t st) {
+                                  bool scan_layout, hipStream_t st) {
   const int64_t n = sh.FH() * 2 * sh.D * sh.D / 4;
   if (n == 0) return hipSuccess;
   int64_t g = std::min<int64_t>((n + 255) / 256, 8192);
   reduce_partials_kernel<<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out,
-                                                      split_a ? 1 : 0);
+                                                      scan_layout ? 1 : 0);
   return hipGetLastError();
 }
 
