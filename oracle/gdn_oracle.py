@@ -32,7 +32,12 @@ Readings where the pages are silent (each also listed in the design notes):
 * the reverse scan of the chunk-causal variant is R_t = R_{t+1} M_t + U_t,
   started from zero after the last frame of each chunk, and the
   bidirectional readout is o = (S_t + R_t) q;
-* chunks of the reverse scan are [0, L), [L, 2L), ...; the last may be short.
+* chunks of the reverse scan are [0, L), [L, 2L), ...; the last may be short;
+* the optional RMSNorm that [P1] lists inside its fused kernel (section
+  "显存分片: Context-Parallel 的工程实现", the paragraph on the fused Triton
+  kernel: RMSNorm, ReLU, key scaling and the scan in one operator) normalises
+  each token of q and of k over the head dimension, before the key's ReLU and
+  scale, with epsilon 1e-6 and unit weight (the pages give neither).
 
 Every function here is pinned by tests under ``tests/`` (closed forms, brute
 force, exact rational arithmetic, invariants); none is "parity unpinned".
@@ -45,6 +50,8 @@ import math
 import numpy as np
 
 __all__ = [
+    "RMS_EPS",
+    "rms_norm",
     "default_key_scale",
     "prepare_keys",
     "frame_terms",
@@ -63,8 +70,21 @@ def default_key_scale(D: int, S: int) -> float:
     return 1.0 / math.sqrt(float(D) * float(S))
 
 
-def prepare_keys(k, key_scale: float | None = None):
-    """K_hat = ReLU(k) * c, elementwise, in float64.
+RMS_EPS = 1e-6
+
+
+def rms_norm(x, eps: float = RMS_EPS):
+    """Per-token RMS normalisation over the last axis (the head dimension):
+    x / sqrt(mean(x^2) + eps), unit weight. The RMSNorm step of the fused
+    operator in [P1] "显存分片: Context-Parallel 的工程实现"; axis, epsilon and
+    weight are this module's reading (see the module docstring)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def prepare_keys(k, key_scale: float | None = None, rmsnorm: bool = False):
+    """K_hat = ReLU(k) * c (with ``rmsnorm``: ReLU(rms_norm(k)) * c),
+    elementwise per token, in float64.
 
     [P1] "混合线性注意力": keys are scaled by 1/sqrt(D*S); [P2] 2.1 states the
     trace bound that this scaling buys. ``key_scale`` <= 0 or None selects the
@@ -73,6 +93,8 @@ def prepare_keys(k, key_scale: float | None = None):
     k = np.asarray(k, dtype=np.float64)
     if key_scale is None or key_scale <= 0:
         key_scale = default_key_scale(k.shape[-1], k.shape[-2])
+    if rmsnorm:
+        k = rms_norm(k)
     return np.maximum(k, 0.0) * float(key_scale)
 
 
@@ -103,10 +125,16 @@ def readout(state, q_t):
     return np.asarray(q_t, dtype=np.float64) @ state.T
 
 
-def _keys(k, key_scale, keys_prepared):
+def _keys(k, key_scale, keys_prepared, rmsnorm=False):
     if keys_prepared:
         return np.asarray(k, dtype=np.float64)
-    return prepare_keys(k, key_scale)
+    return prepare_keys(k, key_scale, rmsnorm)
+
+
+def _queries(q, rmsnorm):
+    if q is None:
+        return None
+    return rms_norm(q) if rmsnorm else np.asarray(q, dtype=np.float64)
 
 
 def _head_fwd(q, kh, v, beta, gamma, s0, t0, t1):
@@ -126,10 +154,11 @@ def _head_fwd(q, kh, v, beta, gamma, s0, t0, t1):
 
 
 def scan_fwd(q, k, v, beta, gamma, s0=None, key_scale=None, keys_prepared=False,
-             with_output=True):
+             with_output=True, qk_rmsnorm=False):
     """Causal frame scan S_t = S_{t-1} M_t + U_t with per-token readout.
 
     Inputs as in the module docstring; ``s0`` is [B, H, D, D] or None (zero).
+    ``qk_rmsnorm`` applies rms_norm to q and (unless ``keys_prepared``) to k.
     Returns a dict with ``states`` [B,H,T,D,D], ``s_final`` [B,H,D,D] and
     ``o`` [B,H,T,S,D] (absent when ``with_output`` is False or q is None).
     """
@@ -140,8 +169,8 @@ def scan_fwd(q, k, v, beta, gamma, s0=None, key_scale=None, keys_prepared=False,
     o = np.zeros((B, H, T, S, D)) if (with_output and q is not None) else None
     for b in range(B):
         for h in range(H):
-            kh = _keys(k[b, h], key_scale, keys_prepared)
-            qh = None if o is None else q[b, h]
+            kh = _keys(k[b, h], key_scale, keys_prepared, qk_rmsnorm)
+            qh = None if o is None else _queries(q[b, h], qk_rmsnorm)
             sinit = None if s0 is None else s0[b, h]
             fin, st, outs = _head_fwd(qh, kh, v[b, h], beta[b, h], gamma[b, h],
                                       sinit, 0, T)
@@ -162,7 +191,7 @@ def chunk_bounds(T: int, chunk_len: int):
 
 
 def scan_reverse_chunked(k, v, beta, gamma, chunk_len, key_scale=None,
-                         keys_prepared=False):
+                         keys_prepared=False, qk_rmsnorm=False):
     """Reverse temporal scan restarted at every chunk boundary ([P3], method).
 
     Inside chunk [a, b): R_{b-1} = U_{b-1} (zero state after the chunk's last
@@ -174,7 +203,7 @@ def scan_reverse_chunked(k, v, beta, gamma, chunk_len, key_scale=None,
     rev = np.zeros((B, H, T, D, D))
     for b in range(B):
         for h in range(H):
-            kh = _keys(k[b, h], key_scale, keys_prepared)
+            kh = _keys(k[b, h], key_scale, keys_prepared, qk_rmsnorm)
             for (a, e) in chunk_bounds(T, chunk_len):
                 R = np.zeros((D, D))
                 for t in range(e - 1, a - 1, -1):
@@ -185,27 +214,29 @@ def scan_reverse_chunked(k, v, beta, gamma, chunk_len, key_scale=None,
 
 
 def scan_bidir_chunked(q, k, v, beta, gamma, chunk_len, s0=None, key_scale=None,
-                       keys_prepared=False):
+                       keys_prepared=False, qk_rmsnorm=False):
     """Chunk-causal bidirectional scan: causal forward states plus the reverse
     chunk scan, read out together as o = (S_t + R_t) q.
 
     ``chunk_len`` >= T gives the full-sequence bidirectional variant.
     """
     fwd = scan_fwd(q, k, v, beta, gamma, s0=s0, key_scale=key_scale,
-                   keys_prepared=keys_prepared, with_output=False)
+                   keys_prepared=keys_prepared, with_output=False, qk_rmsnorm=qk_rmsnorm)
     rev = scan_reverse_chunked(k, v, beta, gamma, chunk_len, key_scale=key_scale,
-                               keys_prepared=keys_prepared)
+                               keys_prepared=keys_prepared, qk_rmsnorm=qk_rmsnorm)
     B, H, T, S, D = np.asarray(k).shape
     o = np.zeros((B, H, T, S, D))
     for b in range(B):
         for h in range(H):
             for t in range(T):
-                o[b, h, t] = readout(fwd["states"][b, h, t] + rev[b, h, t], q[b, h, t])
+                o[b, h, t] = readout(fwd["states"][b, h, t] + rev[b, h, t],
+                                     _queries(q[b, h, t], qk_rmsnorm))
     return {"states_fwd": fwd["states"], "states_rev": rev,
             "s_final": fwd["s_final"], "o": o}
 
 
-def compose(k, v, beta, gamma, offsets, key_scale=None, keys_prepared=False):
+def compose(k, v, beta, gamma, offsets, key_scale=None, keys_prepared=False,
+            qk_rmsnorm=False):
     """Per-chunk affine composites (C_p, H_p) with S_end = S_start C_p + H_p.
 
     [P1] "显存分片: Context-Parallel 的工程实现": C_p is the ordered product of
@@ -220,7 +251,7 @@ def compose(k, v, beta, gamma, offsets, key_scale=None, keys_prepared=False):
     Hc = np.zeros((B, H, P, D, D))
     for b in range(B):
         for h in range(H):
-            kh = _keys(k[b, h], key_scale, keys_prepared)
+            kh = _keys(k[b, h], key_scale, keys_prepared, qk_rmsnorm)
             for p in range(P):
                 Cp = np.eye(D)
                 Hp = np.zeros((D, D))

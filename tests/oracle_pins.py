@@ -434,6 +434,70 @@ def pin_readout_linear(orc):
     _close(fwd["o"][0, 0], o1, 1e-13, "forward readout")
 
 
+def pin_rmsnorm_values(orc):
+    """Per-token RMSNorm over the head dimension (reading of the fused
+    operator's RMSNorm, blog.hotdry.top SANA-WM post, section
+    "显存分片: Context-Parallel 的工程实现"): hand values on tokens of
+    different size, unit mean square up to epsilon, odd symmetry."""
+    eps = orc.RMS_EPS
+    x = np.array([[3.0, -4.0, 0.0, 0.0],      # mean square 25/4
+                  [1.0, 1.0, 1.0, 1.0],       # mean square 1
+                  [0.0, 0.0, 0.0, 2.0]])      # mean square 1
+    want = np.array([[3.0 / math.sqrt(6.25 + eps), -4.0 / math.sqrt(6.25 + eps), 0.0, 0.0],
+                     [1.0 / math.sqrt(1.0 + eps)] * 4,
+                     [0.0, 0.0, 0.0, 2.0 / math.sqrt(1.0 + eps)]])
+    _close(orc.rms_norm(x), want, 1e-15, "rms_norm hand values")
+    rng = np.random.default_rng(21)
+    y = rng.standard_normal((7, 16)) * rng.uniform(0.5, 50.0, (7, 1))
+    z = orc.rms_norm(y)
+    ms = np.mean(y * y, axis=-1)
+    _close(np.mean(z * z, axis=-1), ms / (ms + eps), 1e-13, "unit mean square")
+    _close(orc.rms_norm(-y), -z, 0.0, "odd symmetry")
+
+
+def pin_rmsnorm_in_the_scan(orc):
+    """With qk_rmsnorm, tokens whose entries are all +-a (mean square a^2)
+    are normalised to +-a/sqrt(a^2 + eps): the flag must equal the plain scan
+    on those hand-normalised q and k, on every route (forward, bidirectional,
+    composites), and per-token rescaling of q and k must not change the result
+    (far above epsilon), while without the flag it does."""
+    rng = np.random.default_rng(22)
+    B, H, T, S, D = 1, 2, 5, 6, 4
+    eps = orc.RMS_EPS
+    aq = rng.uniform(0.5, 2.0, (B, H, T, S, 1))
+    ak = rng.uniform(0.5, 2.0, (B, H, T, S, 1))
+    sq = rng.choice([-1.0, 1.0], (B, H, T, S, D))
+    sk = rng.choice([-1.0, 1.0], (B, H, T, S, D))
+    q, k = sq * aq, sk * ak
+    qn, kn = sq * aq / np.sqrt(aq * aq + eps), sk * ak / np.sqrt(ak * ak + eps)
+    v = rng.standard_normal((B, H, T, S, D))
+    b = rng.uniform(0, 1, (B, H, T, S))
+    g = rng.uniform(0.8, 1.0, (B, H, T))
+    s0 = rng.standard_normal((B, H, D, D))
+    r1 = orc.scan_fwd(q, k, v, b, g, s0=s0, qk_rmsnorm=True)
+    r0 = orc.scan_fwd(qn, kn, v, b, g, s0=s0)
+    for n in ("states", "s_final", "o"):
+        _close(r1[n], r0[n], 1e-12, "rmsnorm forward " + n)
+    r1 = orc.scan_bidir_chunked(q, k, v, b, g, 2, s0=s0, qk_rmsnorm=True)
+    r0 = orc.scan_bidir_chunked(qn, kn, v, b, g, 2, s0=s0)
+    for n in ("states_fwd", "states_rev", "o"):
+        _close(r1[n], r0[n], 1e-12, "rmsnorm bidirectional " + n)
+    c1 = orc.compose(k, v, b, g, [0, 2, 5], qk_rmsnorm=True)
+    c0 = orc.compose(kn, v, b, g, [0, 2, 5])
+    _close(c1[0], c0[0], 1e-12, "rmsnorm composite C")
+    _close(c1[1], c0[1], 1e-12, "rmsnorm composite H")
+    # scale invariance on generic tokens: two independent per-token rescalings
+    # by 100..1000 (epsilon then moves the result by < 1e-7 relative)
+    q, k, v, b, g = _rand_case(rng, T=4, S=5, D=4)
+    sc = [rng.uniform(100.0, 1000.0, x.shape[:-1] + (1,)) for x in (q, k, q, k)]
+    ra = orc.scan_fwd(q * sc[0], k * sc[1], v, b, g, qk_rmsnorm=True)
+    rb = orc.scan_fwd(q * sc[2], k * sc[3], v, b, g, qk_rmsnorm=True)
+    _close(ra["o"], rb["o"], 1e-6, "rmsnorm scale invariance")
+    rc = orc.scan_fwd(q * sc[2], k * sc[3], v, b, g)
+    assert np.linalg.norm(rc["o"] - rb["o"]) > 1e-3 * np.linalg.norm(rb["o"]), \
+        "without the flag, rescaled tokens must change the output"
+
+
 ALL_PINS = [
     pin_prepare_closed_form,
     pin_hand_example,
@@ -451,4 +515,6 @@ ALL_PINS = [
     pin_resume,
     pin_reverse_is_forward_on_reversed_chunk,
     pin_readout_linear,
+    pin_rmsnorm_values,
+    pin_rmsnorm_in_the_scan,
 ]

@@ -57,7 +57,8 @@ def _frame_terms_variant(kind):
     return f
 
 
-def _compose_reversed(k, v, beta, gamma, offsets, key_scale=None, keys_prepared=False):
+def _compose_reversed(k, v, beta, gamma, offsets, key_scale=None, keys_prepared=False,
+                      qk_rmsnorm=False):
     k = np.asarray(k)
     B, H, T, S, D = k.shape
     P = len(offsets) - 1
@@ -65,7 +66,7 @@ def _compose_reversed(k, v, beta, gamma, offsets, key_scale=None, keys_prepared=
     Hc = np.zeros((B, H, P, D, D))
     for b in range(B):
         for h in range(H):
-            kh = orc._keys(k[b, h], key_scale, keys_prepared)
+            kh = orc._keys(k[b, h], key_scale, keys_prepared, qk_rmsnorm)
             for p in range(P):
                 Cp, Hp = np.eye(D), np.zeros((D, D))
                 for t in range(offsets[p], offsets[p + 1]):
@@ -91,13 +92,14 @@ def _combine_swapped(C, Hc, s0=None):
     return s_start, s_end
 
 
-def _reverse_off_by_one(k, v, beta, gamma, chunk_len, key_scale=None, keys_prepared=False):
+def _reverse_off_by_one(k, v, beta, gamma, chunk_len, key_scale=None, keys_prepared=False,
+                        qk_rmsnorm=False):
     k = np.asarray(k)
     B, H, T, S, D = k.shape
     rev = np.zeros((B, H, T, D, D))
     for b in range(B):
         for h in range(H):
-            kh = orc._keys(k[b, h], key_scale, keys_prepared)
+            kh = orc._keys(k[b, h], key_scale, keys_prepared, qk_rmsnorm)
             for (a, e) in orc.chunk_bounds(T, chunk_len):
                 R = np.zeros((D, D))
                 for t in range(e - 1, a - 1, -1):
@@ -123,12 +125,23 @@ MUTANTS = {
     "readout_transposed": ("readout", lambda st, q: np.asarray(q, dtype=np.float64) @ st),
     "scale_1_over_sqrt_S": ("default_key_scale", lambda D, S: 1.0 / math.sqrt(S)),
     "scale_1_over_D": ("default_key_scale", lambda D, S: 1.0 / D / math.sqrt(S)),
-    "no_relu": ("prepare_keys", lambda k, key_scale=None: np.asarray(k, dtype=np.float64)
+    "no_relu": ("prepare_keys", lambda k, key_scale=None, rmsnorm=False:
+                np.asarray(orc.rms_norm(k) if rmsnorm else k, dtype=np.float64)
                 * (key_scale if key_scale and key_scale > 0
                    else 1.0 / math.sqrt(np.shape(k)[-1] * np.shape(k)[-2]))),
     "reverse_not_reset": ("chunk_bounds", lambda T, L: [(0, T)]),
     "reverse_wrong_gates": ("scan_reverse_chunked", _reverse_off_by_one),
     "compose_reversed_product": ("compose", _compose_reversed),
+    "rms_over_tokens": ("rms_norm", lambda x, eps=orc.RMS_EPS: np.asarray(x, dtype=np.float64)
+                        / np.sqrt(np.mean(np.asarray(x, dtype=np.float64) ** 2, axis=-2,
+                                          keepdims=True) + eps)),
+    "rms_sum_not_mean": ("rms_norm", lambda x, eps=orc.RMS_EPS: np.asarray(x, dtype=np.float64)
+                         / np.sqrt(np.sum(np.asarray(x, dtype=np.float64) ** 2, axis=-1,
+                                          keepdims=True) + eps)),
+    "rms_no_sqrt": ("rms_norm", lambda x, eps=orc.RMS_EPS: np.asarray(x, dtype=np.float64)
+                    / (np.mean(np.asarray(x, dtype=np.float64) ** 2, axis=-1, keepdims=True) + eps)),
+    "rms_q_ignored": ("_queries", lambda q, rmsnorm: None if q is None
+                      else np.asarray(q, dtype=np.float64)),
     "combine_left_multiply": ("combine", _combine_swapped),
 }
 
