@@ -122,6 +122,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=4, help="named workload 2..5 (default 4)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--qk-rmsnorm", action="store_true",
+                    help="fuse the per-token RMSNorm of q and k (GDN_QK_RMSNORM)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phases", action="store_true", help="skip the per-phase timing loops")
@@ -173,7 +175,8 @@ def main():
     st_rev = torch.empty_like(st_fwd) if w.mode == "bidir" else None
     s_fin = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
     o = torch.empty_like(q)
-    desc = gdn.make_desc(B, H, T, S, D, gdn.GDN_BF16 if bf else gdn.GDN_F32)
+    norm = bool(args.qk_rmsnorm)
+    desc = gdn.make_desc(B, H, T, S, D, gdn.GDN_BF16 if bf else gdn.GDN_F32, qk_rmsnorm=norm)
     ws = gdn.workspace(desc, w.time_chunks, dev)
     stream = torch.cuda.current_stream()
 
@@ -181,10 +184,10 @@ def main():
         if w.mode == "bidir":
             gdn.gdn_scan_bidir_chunked(q, k, v, beta, gamma, w.chunk_len, n_time_chunks=w.time_chunks,
                                        states_fwd=st_fwd, states_rev=st_rev, s_final=s_fin, o=o,
-                                       ws=ws, stream=stream)
+                                       ws=ws, stream=stream, qk_rmsnorm=norm)
         else:
             gdn.gdn_scan_fwd(q, k, v, beta, gamma, n_time_chunks=w.time_chunks, states=st_fwd,
-                             s_final=s_fin, o=o, ws=ws, stream=stream)
+                             s_final=s_fin, o=o, ws=ws, stream=stream, qk_rmsnorm=norm)
 
     def timed(fn, reps):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -222,7 +225,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if bf else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "H": H, "T": T, "S": S, "D": D,
+        "config": {"workload": w.name + ("_qk_rmsnorm" if norm else ""), "B": B, "H": H, "T": T,
+                   "S": S, "D": D,
                    "scan": w.mode, "time_chunks": w.time_chunks, "chunk_len": w.chunk_len,
                    "parallelism": "single GPU"},
     }
@@ -235,8 +239,10 @@ def main():
         A = torch.empty((B, H, T, D, D), dtype=torch.float32, device=dev)
         U = torch.empty_like(A)
         reps = max(args.steps, 5)
-        t_terms = timed(lambda: gdn.gdn_frame_terms(k, v, beta, A=A, U=U, ws=ws, stream=stream), reps)
-        t_read = timed(lambda: gdn.gdn_readout(q, st_fwd, st_rev, o=o, stream=stream), reps)
+        t_terms = timed(lambda: gdn.gdn_frame_terms(k, v, beta, A=A, U=U, ws=ws, stream=stream,
+                                                    qk_rmsnorm=norm), reps)
+        t_read = timed(lambda: gdn.gdn_readout(q, st_fwd, st_rev, o=o, stream=stream,
+                                               qk_rmsnorm=norm), reps)
         phases = {
             "terms": (t_terms, pf["terms_bytes"] * fh, pf["terms_flop"] * fh),
             "readout": (t_read, pf["readout_bytes"] * fh, pf["readout_flop"] * fh),
@@ -261,7 +267,7 @@ def main():
         }
         del A, U
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not norm:
         print("[bench] cpu baseline (float64 oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -22,7 +22,7 @@ gdn_status check_desc(const gdn_desc* d, Shape* sh) {
   if (d == nullptr) return GDN_EINVAL;
   if (d->B < 0 || d->H < 0 || d->T < 0 || d->S < 1 || d->D < 1) return GDN_EINVAL;
   if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) return GDN_EINVAL;
-  if ((d->flags & ~GDN_KEYS_PREPARED) != 0) return GDN_EINVAL;
+  if ((d->flags & ~(GDN_KEYS_PREPARED | GDN_QK_RMSNORM)) != 0) return GDN_EINVAL;
   if (!(std::isfinite(d->key_scale))) return GDN_EINVAL;
   if (d->D != 16 && d->D != 32 && d->D != 64 && d->D != 128) return GDN_EUNSUPPORTED;
   // element counts must stay far from 64-bit overflow
@@ -35,6 +35,7 @@ gdn_status check_desc(const gdn_desc* d, Shape* sh) {
   sh->D = d->D;
   sh->io = d->io_dtype;
   sh->prepared = (d->flags & GDN_KEYS_PREPARED) ? 1 : 0;
+  sh->qk_norm = (d->flags & GDN_QK_RMSNORM) ? 1 : 0;
   if (sh->prepared) {
     sh->c = 1.0f;
   } else if (d->key_scale > 0.f) {

@@ -86,6 +86,44 @@ __device__ __forceinline__ void xcd_job(int64_t linear, int per, int64_t* job, i
   *member = (int)(slot % per);
 }
 
+// Epsilon of the optional per-token RMSNorm of q and k.
+constexpr float kRmsEps = 1e-6f;
+
+// 1 / sqrt(mean square + eps) from a sum of squares over D entries
+// (v_rsq_f32: about one ulp; the argument is at least eps, never denormal).
+__device__ __forceinline__ float rms_inv(float sum_sq, int D) {
+  return __builtin_amdgcn_rsqf(sum_sq * (1.0f / (float)D) + kRmsEps);
+}
+
+// Sum of squares of two packed bf16 values added to acc (v_dot2_f32_bf16;
+// the bf16 products are exact in fp32).
+__device__ __forceinline__ float sumsq_bf16x2(uint32_t w, float acc) {
+  const bf16x2_t a = __builtin_bit_cast(bf16x2_t, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(a, a, acc, false);
+}
+
+// Cross-lane sums in VALU (no LDS round trip). The gfx950 swaps exchange
+// rows (permlane16_swap: 16-lane rows 0<->1 and 2<->3 between its two
+// operands) or halves (permlane32_swap: lanes 0..31 <-> 32..63); called with
+// the same value twice, the two results hold a lane's value and its partner's,
+// so their sum is the pair sum in every lane.
+__device__ __forceinline__ float sum_lane_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(p[0]) + __int_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_lane_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(p[0]) + __int_as_float(p[1]);
+}
+// Sum over the 16 lanes of the wave congruent to this one mod 4: DPP row
+// rotations by 4 and 8 sum the four such lanes of each 16-lane row, then the
+// row swaps add the other rows.
+__device__ __forceinline__ float sum_lanes_mod4(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  return sum_lane_xor32(sum_lane_xor16(x));
+}
+
 // Internal layout of the phase-1 terms read by the MFMA scan (bf16 inputs,
 // D = 128), per frame-head slot of 2*D*D floats: bf16(A) (32 KB), 32 KB not
 // used, U (64 KB, fp32).
@@ -111,6 +149,7 @@ struct Shape {
   int io;          // 0 = fp32, 1 = bf16
   float c;         // key scale applied to ReLU(k) (1 for prepared keys)
   int prepared;    // keys already hold K_hat: no ReLU
+  int qk_norm;     // RMS-normalise q (and k unless prepared) per token over D
   int64_t BH() const { return (int64_t)B * H; }
   int64_t FH() const { return (int64_t)B * H * T; }
 };

@@ -1,4 +1,5 @@
-// Elementwise kernels: key preparation K_hat = ReLU(k) * c, fp32 copy and fill.
+// Key preparation K_hat = ReLU(k) * c (optionally after a per-token RMSNorm),
+// fp32 copy and fill.
 //
 // Key scaling: blog.hotdry.top SANA-WM post, section "混合线性注意力" (keys are
 // scaled by 1/sqrt(D*S) so that the frame transition cannot expand the state).
@@ -51,6 +52,46 @@ __global__ void __launch_bounds__(256) zero_f32_kernel(float* __restrict__ d, in
   for (; i < n; i += stride) d[i] = 0.f;
 }
 
+// K_hat = ReLU(k / rms(k)) * c with the per-token RMSNorm over D: each lane
+// handles one 16-byte chunk, the kL lanes of a token are consecutive (kL
+// divides 64, so a token never straddles two waves, and a token's lanes are
+// active together), and the sum of squares is reduced with lane swaps.
+template <bool kBf16, int kL>
+__global__ void __launch_bounds__(256) prepare_norm_kernel(const uint4* __restrict__ k,
+                                                           uint4* __restrict__ out, int64_t n16,
+                                                           int D, float c) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n16; i += stride) {
+    const uint4 x = k[i];
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    float f[8];
+    constexpr int kN = kBf16 ? 8 : 4;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if (kBf16) {
+        f[2 * p] = bf16_to_f32(w[p] & 0xFFFFu);
+        f[2 * p + 1] = bf16_to_f32(w[p] >> 16);
+      } else {
+        f[p] = __uint_as_float(w[p]);
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < kN; ++e) ss += f[e] * f[e];
+#pragma unroll
+    for (int off = 1; off < kL; off <<= 1) ss += __shfl_xor(ss, off);
+    const float rc = rms_inv(ss, D) * c;
+#pragma unroll
+    for (int e = 0; e < kN; ++e) f[e] = (f[e] > 0.f ? f[e] : 0.f) * rc;
+    uint32_t r[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      r[p] = kBf16 ? pack_bf16x2(f[2 * p], f[2 * p + 1]) : __float_as_uint(f[p]);
+    out[i] = make_uint4(r[0], r[1], r[2], r[3]);
+  }
+}
+
 int grid_for(int64_t n) {
   int64_t g = (n + 255) / 256;
   if (g > 4096) g = 4096;
@@ -63,6 +104,35 @@ int grid_for(int64_t n) {
 hipError_t launch_prepare(const Shape& sh, const void* k, void* k_hat, hipStream_t st) {
   int64_t n = sh.FH() * sh.S * sh.D;
   if (n == 0) return hipSuccess;
+  if (sh.qk_norm) {
+    // 16-byte chunks: D * (2 or 4) / 16 lanes per token, a power of two <= 32
+    const int64_t n16 = n * (sh.io == 1 ? 2 : 4) / 16;
+    const int lanes = sh.D * (sh.io == 1 ? 2 : 4) / 16;
+    const uint4* src = (const uint4*)k;
+    uint4* dst = (uint4*)k_hat;
+    const int g = grid_for(n16);
+#define GDN_PREP_NORM(BF, L) \
+  prepare_norm_kernel<BF, L><<<g, 256, 0, st>>>(src, dst, n16, sh.D, sh.c)
+    if (sh.io == 1) {
+      switch (lanes) {
+        case 2: GDN_PREP_NORM(true, 2); break;
+        case 4: GDN_PREP_NORM(true, 4); break;
+        case 8: GDN_PREP_NORM(true, 8); break;
+        case 16: GDN_PREP_NORM(true, 16); break;
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      switch (lanes) {
+        case 4: GDN_PREP_NORM(false, 4); break;
+        case 8: GDN_PREP_NORM(false, 8); break;
+        case 16: GDN_PREP_NORM(false, 16); break;
+        case 32: GDN_PREP_NORM(false, 32); break;
+        default: return hipErrorInvalidValue;
+      }
+    }
+#undef GDN_PREP_NORM
+    return hipGetLastError();
+  }
   if (sh.io == 1) {
     // D is a multiple of 16, so n is a multiple of 8 and rows are 16-byte aligned.
     int64_t n8 = n / 8;

@@ -34,6 +34,7 @@ __device__ __forceinline__ uint4 ld_q(const uint16_t* q, int s, int S, int j) {
 // consecutive rows read at the same logical chunk hit eight distinct bank groups.
 __device__ __forceinline__ int rswz(int row, int chunk) { return chunk ^ (row & 7); }
 
+template <bool kNorm>
 __global__ void __launch_bounds__(256, 2)
 readout_mfma_bf16_d128(const uint16_t* __restrict__ q, const float* __restrict__ sa,
                        const float* __restrict__ sb, uint16_t* __restrict__ o, int S, int64_t FH,
@@ -94,6 +95,20 @@ readout_mfma_bf16_d128(const uint16_t* __restrict__ q, const float* __restrict__
     bf16x8_t bq[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) bq[kk] = __builtin_bit_cast(bf16x8_t, qb[kk]);
+    // RMSNorm of q: this lane holds 64 of token l32's 128 features, the
+    // other 64 sit in lane l32 + 32 of the other half
+    float rq = 1.f;
+    if (kNorm) {
+      float ss = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        ss = sumsq_bf16x2(qb[kk].x, ss);
+        ss = sumsq_bf16x2(qb[kk].y, ss);
+        ss = sumsq_bf16x2(qb[kk].z, ss);
+        ss = sumsq_bf16x2(qb[kk].w, ss);
+      }
+      rq = rms_inv(sum_lane_xor32(ss), D);
+    }
     const int nxt = tile + wstride;
     if (nxt < ntiles) {
       const int sn = nxt * kTokPerWave + l32;
@@ -113,6 +128,10 @@ readout_mfma_bf16_d128(const uint16_t* __restrict__ q, const float* __restrict__
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, Sl[row * 16 + rswz(row, 2 * kk + half)]);
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[kk], acc[mt], 0, 0, 0);
       }
+    if (kNorm) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt] *= rq;  // o = S (q / rms(q)) = (S q) / rms(q)
+    }
     // Accumulator (i, s): lane holds token s = l32 and value dims
     // 32mt + 8jg + 4half + (0..3). Stage as rows of tokens, then write the
     // 32 x 256-byte tile (contiguous in HBM) with 16-byte stores.
@@ -145,11 +164,12 @@ readout_mfma_bf16_d128(const uint16_t* __restrict__ q, const float* __restrict__
 template <typename TIn, int D>
 __global__ void __launch_bounds__(256)
 readout_generic(const TIn* __restrict__ q, const float* __restrict__ sa,
-                const float* __restrict__ sb, TIn* __restrict__ o, int S, int ntile) {
+                const float* __restrict__ sb, TIn* __restrict__ o, int S, int ntile, int norm) {
   constexpr int TT = 2048 / D;        // tokens per tile
   constexpr int OPT = TT * D / 256;   // outputs per thread
   __shared__ float St[D][D];
   __shared__ float Qs[TT][D];
+  __shared__ float rq[TT];  // per-token factor 1/rms(q) (1 without norm)
   const int64_t fh = blockIdx.x / ntile;
   const int tile = blockIdx.x % ntile;
   const int tid = threadIdx.x;
@@ -175,6 +195,16 @@ readout_generic(const TIn* __restrict__ q, const float* __restrict__ sa,
     Qs[s][j] = x;
   }
   __syncthreads();
+  if (tid < TT) {
+    float f = 1.f;
+    if (norm) {
+      float ss = 0.f;
+      for (int j = 0; j < D; ++j) ss += Qs[tid][j] * Qs[tid][j];
+      f = rms_inv(ss, D);
+    }
+    rq[tid] = f;
+  }
+  __syncthreads();
   TIn* of = o + fh * (int64_t)S * D;
 #pragma unroll
   for (int r = 0; r < OPT; ++r) {
@@ -184,6 +214,7 @@ readout_generic(const TIn* __restrict__ q, const float* __restrict__ sa,
     float acc = 0.f;
 #pragma unroll 8
     for (int j = 0; j < D; ++j) acc = fmaf(St[j][i], Qs[s][j], acc);
+    acc *= rq[s];
     if (s0 + s < S) {
       if constexpr (sizeof(TIn) == 2)
         ((uint16_t*)of)[(int64_t)(s0 + s) * D + i] = (uint16_t)(pack_bf16x2(acc, 0.f) & 0xFFFFu);
@@ -202,10 +233,10 @@ hipError_t launch_readout_generic(const Shape& sh, const void* q, const float* s
   const TIn* qq = (const TIn*)q;
   TIn* oo = (TIn*)o;
   switch (sh.D) {
-    case 16: readout_generic<TIn, 16><<<grid, 256, 0, st>>>(qq, sa, sb, oo, sh.S, ntile); break;
-    case 32: readout_generic<TIn, 32><<<grid, 256, 0, st>>>(qq, sa, sb, oo, sh.S, ntile); break;
-    case 64: readout_generic<TIn, 64><<<grid, 256, 0, st>>>(qq, sa, sb, oo, sh.S, ntile); break;
-    case 128: readout_generic<TIn, 128><<<grid, 256, 0, st>>>(qq, sa, sb, oo, sh.S, ntile); break;
+    case 16: readout_generic<TIn, 16><<<grid, 256, 0, st>>>(qq, sa, sb, oo, sh.S, ntile, sh.qk_norm); break;
+    case 32: readout_generic<TIn, 32><<<grid, 256, 0, st>>>(qq, sa, sb, oo, sh.S, ntile, sh.qk_norm); break;
+    case 64: readout_generic<TIn, 64><<<grid, 256, 0, st>>>(qq, sa, sb, oo, sh.S, ntile, sh.qk_norm); break;
+    case 128: readout_generic<TIn, 128><<<grid, 256, 0, st>>>(qq, sa, sb, oo, sh.S, ntile, sh.qk_norm); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -222,8 +253,12 @@ hipError_t launch_readout(const Shape& sh, const void* q, const float* sa, const
     if (nb > kBlocksPerFrameHead) nb = kBlocksPerFrameHead;
     const int64_t groups = (sh.FH() + kXcd - 1) / kXcd;
     dim3 grid((unsigned)(groups * kXcd * nb));
-    readout_mfma_bf16_d128<<<grid, 256, 0, st>>>((const uint16_t*)q, sa, sb, (uint16_t*)o, sh.S,
-                                                 sh.FH(), nb);
+    if (sh.qk_norm)
+      readout_mfma_bf16_d128<true><<<grid, 256, 0, st>>>((const uint16_t*)q, sa, sb, (uint16_t*)o,
+                                                         sh.S, sh.FH(), nb);
+    else
+      readout_mfma_bf16_d128<false><<<grid, 256, 0, st>>>((const uint16_t*)q, sa, sb, (uint16_t*)o,
+                                                          sh.S, sh.FH(), nb);
     return hipGetLastError();
   }
   if (sh.io == 1) return launch_readout_generic<uint16_t>(sh, q, sa, sb, o, st);

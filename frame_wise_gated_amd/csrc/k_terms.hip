@@ -100,7 +100,7 @@ __device__ __forceinline__ uint4 tr_frag(const uint8_t* base, int lb, int k0, in
 #else
 #define GDN_TERMS_WAVES_PER_EU 2  // one workgroup per CU (its ring fills the LDS)
 #endif
-template <bool kScanLayout, bool kPrepared>
+template <bool kScanLayout, bool kPrepared, bool kNorm>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(GDN_TERMS_WAVES_PER_EU, GDN_TERMS_WAVES_PER_EU)))
 terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -155,6 +155,26 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
     const float* gates = (const float*)(Ks + 2 * kKvBytes);
     uint4 x = *(const uint4*)(Ks + 16 * tid);
     const float b = (st * kTsd + ttok < S) ? gates[ttok] : 0.f;
+    if (kNorm && !kPrepared) {
+      // RMSNorm of the raw key over its 128 features: the token's 16 chunks
+      // sit in the lanes congruent to this one mod 4 of the same wave
+      const uint32_t w0[4] = {x.x, x.y, x.z, x.w};
+      float ss = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ss = sumsq_bf16x2(w0[q], ss);
+      const float r = rms_inv(sum_lanes_mod4(ss), D);
+      uint32_t kq[4], o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t z = relu_bf16x2_pk(w0[q]);
+        const float lo = __uint_as_float(z << 16) * r, hi = __uint_as_float(z & 0xFFFF0000u) * r;
+        kq[q] = pack_bf16x2(lo, hi);         // first operand of the A rows: ReLU(k) / rms(k)
+        o[q] = pack_bf16x2(lo * b, hi * b);  // beta . ReLU(k) / rms(k), rounded once
+      }
+      *(uint4*)(Ks + 16 * tid) = make_uint4(kq[0], kq[1], kq[2], kq[3]);
+      *(uint4*)(wbuf[st & 1] + 16 * tid) = make_uint4(o[0], o[1], o[2], o[3]);
+      return;
+    }
     if (!kPrepared) {
       x.x = relu_bf16x2_pk(x.x);
       x.y = relu_bf16x2_pk(x.y);
@@ -328,11 +348,12 @@ __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, int64_t i) {
 template <typename TIn, int D>
 __global__ void __launch_bounds__(256)
 terms_generic(const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ beta,
-              int S, int n_split, float c, int prepared, TermsOut out) {
+              int S, int n_split, float c, int prepared, int norm, TermsOut out) {
   constexpr int TSG = 16;
   constexpr int OPT = 2 * D * D / 256;
   __shared__ float Ls[TSG][2 * D];
   __shared__ float Ws[TSG][D];
+  __shared__ float rn[TSG];  // per-token key factor c (times 1/rms(k) with norm)
 
   const int64_t fh = blockIdx.x / n_split;
   const int split = blockIdx.x % n_split;
@@ -349,6 +370,19 @@ terms_generic(const TIn* __restrict__ k, const TIn* __restrict__ v, const float*
 
   for (int s0 = s_begin; s0 < s_end; s0 += TSG) {
     __syncthreads();
+    if (tid < TSG) {
+      float f = c;
+      if (norm && !prepared && s0 + tid < s_end) {
+        float ss = 0.f;
+        for (int j = 0; j < D; ++j) {
+          const float kv = ld<TIn>(kf, (int64_t)(s0 + tid) * D + j);
+          ss += kv * kv;
+        }
+        f = c * rms_inv(ss, D);
+      }
+      rn[tid] = f;
+    }
+    __syncthreads();
     for (int idx = tid; idx < TSG * 2 * D; idx += 256) {
       const int s = idx / (2 * D);
       const int m = idx % (2 * D);
@@ -357,7 +391,7 @@ terms_generic(const TIn* __restrict__ k, const TIn* __restrict__ v, const float*
       if (tok < s_end) {
         if (m < D) {
           float kv = ld<TIn>(kf, (int64_t)tok * D + m);
-          val = prepared ? kv : (kv > 0.f ? kv : 0.f) * c;
+          val = prepared ? kv : (kv > 0.f ? kv : 0.f) * rn[s];
         } else {
           val = ld<TIn>(vf, (int64_t)tok * D + (m - D));
         }
@@ -371,7 +405,7 @@ terms_generic(const TIn* __restrict__ k, const TIn* __restrict__ v, const float*
       float val = 0.f;
       if (tok < s_end) {
         float kv = ld<TIn>(kf, (int64_t)tok * D + n);
-        val = bf[tok] * (prepared ? kv : (kv > 0.f ? kv : 0.f) * c);
+        val = bf[tok] * (prepared ? kv : (kv > 0.f ? kv : 0.f) * rn[s]);
       }
       Ws[s][n] = val;
     }
@@ -454,16 +488,20 @@ hipError_t launch_generic(const Shape& sh, const void* k, const void* v, const f
   const TIn* vv = (const TIn*)v;
   switch (sh.D) {
     case 16:
-      terms_generic<TIn, 16><<<grid, 256, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, sh.prepared, out);
+      terms_generic<TIn, 16><<<grid, 256, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, sh.prepared,
+                                                  sh.qk_norm, out);
       break;
     case 32:
-      terms_generic<TIn, 32><<<grid, 256, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, sh.prepared, out);
+      terms_generic<TIn, 32><<<grid, 256, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, sh.prepared,
+                                                  sh.qk_norm, out);
       break;
     case 64:
-      terms_generic<TIn, 64><<<grid, 256, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, sh.prepared, out);
+      terms_generic<TIn, 64><<<grid, 256, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, sh.prepared,
+                                                  sh.qk_norm, out);
       break;
     case 128:
-      terms_generic<TIn, 128><<<grid, 256, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, sh.prepared, out);
+      terms_generic<TIn, 128><<<grid, 256, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, sh.prepared,
+                                                  sh.qk_norm, out);
       break;
     default:
       return hipErrorInvalidValue;
@@ -491,14 +529,19 @@ hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const flo
     dim3 grid((unsigned)(sh.FH() * n_split));
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
-    if (scan_layout && !sh.prepared)
-      terms_dma_bf16_d128<true, false><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out);
-    else if (scan_layout)
-      terms_dma_bf16_d128<true, true><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out);
-    else if (!sh.prepared)
-      terms_dma_bf16_d128<false, false><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out);
-    else
-      terms_dma_bf16_d128<false, true><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out);
+    const bool norm = sh.qk_norm && !sh.prepared;  // prepared keys are used as given
+#define GDN_TERMS_DMA(L, P, N) \
+  terms_dma_bf16_d128<L, P, N><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out)
+    if (scan_layout) {
+      if (sh.prepared) GDN_TERMS_DMA(true, true, false);
+      else if (norm) GDN_TERMS_DMA(true, false, true);
+      else GDN_TERMS_DMA(true, false, false);
+    } else {
+      if (sh.prepared) GDN_TERMS_DMA(false, true, false);
+      else if (norm) GDN_TERMS_DMA(false, false, true);
+      else GDN_TERMS_DMA(false, false, false);
+    }
+#undef GDN_TERMS_DMA
     return hipGetLastError();
   }
   if (sh.io == 1) return launch_generic<uint16_t>(sh, k, v, beta, n_split, out, st);

@@ -21,7 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "gdn.h")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = range(5)
 GDN_F32, GDN_BF16 = 0, 1
-GDN_KEYS_RAW, GDN_KEYS_PREPARED = 0, 1
+GDN_KEYS_RAW, GDN_KEYS_PREPARED, GDN_QK_RMSNORM = 0, 1, 2
 GDN_MAX_TIME_CHUNKS = 256
 
 
@@ -108,12 +108,14 @@ def _stream(stream) -> int | None:
     return getattr(stream, "cuda_stream", stream)
 
 
-def make_desc(B, H, T, S, D, io_dtype, key_scale=0.0, keys_prepared=False) -> gdn_desc:
-    return gdn_desc(B, H, T, S, D, io_dtype, float(key_scale),
-                    GDN_KEYS_PREPARED if keys_prepared else GDN_KEYS_RAW)
+def make_desc(B, H, T, S, D, io_dtype, key_scale=0.0, keys_prepared=False,
+              qk_rmsnorm=False) -> gdn_desc:
+    flags = (GDN_KEYS_PREPARED if keys_prepared else GDN_KEYS_RAW) | \
+        (GDN_QK_RMSNORM if qk_rmsnorm else 0)
+    return gdn_desc(B, H, T, S, D, io_dtype, float(key_scale), flags)
 
 
-def _desc_from(k: torch.Tensor, key_scale, keys_prepared) -> gdn_desc:
+def _desc_from(k: torch.Tensor, key_scale, keys_prepared, qk_rmsnorm=False) -> gdn_desc:
     if k.dim() != 5:
         raise ValueError("k must be [B, H, T, S, D]")
     if k.dtype == torch.float32:
@@ -123,7 +125,7 @@ def _desc_from(k: torch.Tensor, key_scale, keys_prepared) -> gdn_desc:
     else:
         raise ValueError(f"unsupported io dtype {k.dtype}")
     B, H, T, S, D = k.shape
-    return make_desc(B, H, T, S, D, io, key_scale, keys_prepared)
+    return make_desc(B, H, T, S, D, io, key_scale, keys_prepared, qk_rmsnorm)
 
 
 def _need(t: torch.Tensor | None, name: str, shape, dtype) -> None:
@@ -158,8 +160,8 @@ def _ws(ws, desc, n_time_chunks, device):
     return ws, ws.numel() * ws.element_size()
 
 
-def gdn_prepare(k, k_hat=None, key_scale=0.0, stream=None):
-    d = _desc_from(k, key_scale, False)
+def gdn_prepare(k, k_hat=None, key_scale=0.0, qk_rmsnorm=False, stream=None):
+    d = _desc_from(k, key_scale, False, qk_rmsnorm)
     k_hat = _out(k_hat, True, k.shape, k.dtype, k.device)
     _need(k, "k", k.shape, k.dtype)
     _need(k_hat, "k_hat", k.shape, k.dtype)
@@ -168,8 +170,8 @@ def gdn_prepare(k, k_hat=None, key_scale=0.0, stream=None):
 
 
 def gdn_frame_terms(k, v, beta, A=None, U=None, key_scale=0.0, keys_prepared=False, ws=None,
-                    stream=None):
-    d = _desc_from(k, key_scale, keys_prepared)
+                    stream=None, qk_rmsnorm=False):
+    d = _desc_from(k, key_scale, keys_prepared, qk_rmsnorm)
     B, H, T, S, D = k.shape
     for t, n in ((k, "k"), (v, "v")):
         _need(t, n, k.shape, k.dtype)
@@ -184,8 +186,8 @@ def gdn_frame_terms(k, v, beta, A=None, U=None, key_scale=0.0, keys_prepared=Fal
 
 def gdn_scan_fwd(q, k, v, beta, gamma, s0=None, n_time_chunks=1, key_scale=0.0,
                  keys_prepared=False, want_states=True, want_s_final=True, want_o=True,
-                 states=None, s_final=None, o=None, ws=None, stream=None):
-    d = _desc_from(k, key_scale, keys_prepared)
+                 states=None, s_final=None, o=None, ws=None, stream=None, qk_rmsnorm=False):
+    d = _desc_from(k, key_scale, keys_prepared, qk_rmsnorm)
     B, H, T, S, D = k.shape
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _need(t, n, k.shape, k.dtype)
@@ -207,8 +209,8 @@ def gdn_scan_fwd(q, k, v, beta, gamma, s0=None, n_time_chunks=1, key_scale=0.0,
 def gdn_scan_bidir_chunked(q, k, v, beta, gamma, chunk_len, s0=None, n_time_chunks=1,
                            key_scale=0.0, keys_prepared=False, want_states=True, want_s_final=True,
                            want_o=True, states_fwd=None, states_rev=None, s_final=None, o=None,
-                           ws=None, stream=None):
-    d = _desc_from(k, key_scale, keys_prepared)
+                           ws=None, stream=None, qk_rmsnorm=False):
+    d = _desc_from(k, key_scale, keys_prepared, qk_rmsnorm)
     B, H, T, S, D = k.shape
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _need(t, n, k.shape, k.dtype)
@@ -230,11 +232,11 @@ def gdn_scan_bidir_chunked(q, k, v, beta, gamma, chunk_len, s0=None, n_time_chun
 
 def gdn_step(q, k, v, beta, gamma, carry_in=None, carry_out=None, key_scale=0.0,
              keys_prepared=False, want_o=True, want_states=False, o=None, states_fwd=None,
-             states_rev=None, ws=None, stream=None):
+             states_rev=None, ws=None, stream=None, qk_rmsnorm=False):
     """One streaming block (k.shape[2] frames): bidirectional inside the block,
     forward state carried in from `carry_in` and out to `carry_out` (which may
     be the same tensor)."""
-    d = _desc_from(k, key_scale, keys_prepared)
+    d = _desc_from(k, key_scale, keys_prepared, qk_rmsnorm)
     B, H, T, S, D = k.shape
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _need(t, n, k.shape, k.dtype)
@@ -255,8 +257,8 @@ def gdn_step(q, k, v, beta, gamma, carry_in=None, carry_out=None, key_scale=0.0,
 
 def gdn_compose(k, v, beta, gamma, chunk_offsets, s0=None, key_scale=0.0, keys_prepared=False,
                 want_C=True, want_H=True, want_s_start=True, C=None, Hc=None, s_start=None,
-                ws=None, stream=None):
-    d = _desc_from(k, key_scale, keys_prepared)
+                ws=None, stream=None, qk_rmsnorm=False):
+    d = _desc_from(k, key_scale, keys_prepared, qk_rmsnorm)
     B, H, T, S, D = k.shape
     P = len(chunk_offsets) - 1
     offs = (ctypes.c_int32 * (P + 1))(*[int(x) for x in chunk_offsets])
@@ -273,8 +275,8 @@ def gdn_compose(k, v, beta, gamma, chunk_offsets, s0=None, key_scale=0.0, keys_p
     return {"C": C, "Hc": Hc, "s_start": s_start}
 
 
-def gdn_readout(q, states, states_add=None, o=None, stream=None):
-    d = _desc_from(q, 0.0, False)
+def gdn_readout(q, states, states_add=None, o=None, qk_rmsnorm=False, stream=None):
+    d = _desc_from(q, 0.0, False, qk_rmsnorm)
     B, H, T, S, D = q.shape
     _need(q, "q", q.shape, q.dtype)
     _need(states, "states", (B, H, T, D, D), torch.float32)

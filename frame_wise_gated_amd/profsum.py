@@ -31,14 +31,26 @@ def _one(pattern: str) -> str:
 
 
 def _short(name: str) -> str:
-    name = name.split("(")[0]
-    for key in ("terms_dma_bf16_d128", "terms_generic", "reduce_partials", "scan_mfma_d128",
-                "scan_rows_kernel", "combine_rows_kernel", "readout_mfma_bf16_d128",
-                "readout_generic", "prepare_bf16_kernel", "prepare_f32_kernel",
-                "copy_f32_kernel", "zero_f32_kernel"):
-        if key in name:
-            return key
-    return name[:48]
+    """Kernel base name, with its template arguments when the trace kept them
+    (rocprofv3 without -T), e.g. terms_dma_bf16_d128<true, false>."""
+    keys = ("terms_dma_bf16_d128", "terms_generic", "reduce_partials", "scan_mfma_d128",
+            "scan_rows_kernel", "combine_rows_kernel", "readout_mfma_bf16_d128",
+            "readout_generic", "prepare_bf16_kernel", "prepare_f32_kernel",
+            "copy_f32_kernel", "zero_f32_kernel")
+    for key in keys:
+        at = name.find(key)
+        if at < 0:
+            continue
+        rest = name[at + len(key):]
+        if rest.startswith("<"):
+            depth = 0
+            for i, ch in enumerate(rest):
+                depth += ch == "<"
+                depth -= ch == ">"
+                if depth == 0:
+                    return key + rest[:i + 1]
+        return key
+    return name.split("(")[0][:48]
 
 
 def trace(d: str, skip: int) -> list[str]:
@@ -47,10 +59,10 @@ def trace(d: str, skip: int) -> list[str]:
     for r in rows:
         key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) if "Grid_Size_X" in r else int(r["Grid_Size"]))
         agg[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    out = [f"{'kernel':28s} {'grid':>9s} {'calls':>5s} {'mean_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    out = [f"{'kernel':40s} {'grid':>9s} {'calls':>5s} {'mean_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
     for (name, grid), v in sorted(agg.items()):
         v = v[skip:] if len(v) > skip else v
-        out.append(f"{name:28s} {grid:9d} {len(v):5d} {sum(v) / len(v):9.1f} {min(v):9.1f} {max(v):9.1f}")
+        out.append(f"{name:40s} {grid:9d} {len(v):5d} {sum(v) / len(v):9.1f} {min(v):9.1f} {max(v):9.1f}")
     return out
 
 
@@ -60,11 +72,11 @@ def pmc(d: str, scale: float) -> list[str]:
     for r in rows:
         agg[(_short(r["Kernel_Name"]), int(r["Grid_Size"]), r["Counter_Name"])].append(
             float(r["Counter_Value"]))
-    out = [f"{'kernel':28s} {'grid':>9s} {'counter':>11s} {'calls':>5s} {'mean_KiB':>12s} "
+    out = [f"{'kernel':40s} {'grid':>9s} {'counter':>11s} {'calls':>5s} {'mean_KiB':>12s} "
            f"{'x' + format(scale, 'g'):>5s} {'MB':>10s}"]
     for (name, grid, ctr), v in sorted(agg.items()):
         m = sum(v) / len(v)
-        out.append(f"{name:28s} {grid:9d} {ctr:>11s} {len(v):5d} {m:12.1f} {'':>5s} "
+        out.append(f"{name:40s} {grid:9d} {ctr:>11s} {len(v):5d} {m:12.1f} {'':>5s} "
                    f"{m * 1024 * scale / 1e6:10.2f}")
     return out
 

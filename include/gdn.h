@@ -67,9 +67,16 @@ typedef enum {
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
-/* flags */
+/* flags (may be combined with |) */
 #define GDN_KEYS_RAW 0u       /* kernels apply ReLU and the key scale to k */
 #define GDN_KEYS_PREPARED 1u  /* k already holds K_hat; no ReLU, no scale */
+/* RMS-normalise every token of q, and of k unless GDN_KEYS_PREPARED, over the
+ * head dim before use: x / sqrt(mean_d x_d^2 + 1e-6), unit weight, ahead of
+ * the key's ReLU and scale. The RMSNorm of the fused operator in
+ * blog.hotdry.top SANA-WM post, section "显存分片: Context-Parallel 的工程实现";
+ * the pages give no axis, epsilon or weight, so these are this library's
+ * reading. Fused into the kernels' load paths (no extra HBM pass). */
+#define GDN_QK_RMSNORM 2u
 
 #define GDN_MAX_TIME_CHUNKS 256
 
@@ -77,7 +84,7 @@ typedef struct {
   int32_t B, H, T, S, D;  /* batch, heads, frames, tokens per frame, head dim (Dk = Dv) */
   int32_t io_dtype;       /* gdn_dtype of q, k, v, o, k_hat */
   float key_scale;        /* <= 0 selects 1/sqrt(D*S) */
-  uint32_t flags;         /* GDN_KEYS_RAW or GDN_KEYS_PREPARED */
+  uint32_t flags;         /* GDN_KEYS_RAW or GDN_KEYS_PREPARED, optionally | GDN_QK_RMSNORM */
 } gdn_desc;
 
 /* Human-readable name of a status code (static string; never NULL). */
@@ -89,8 +96,8 @@ GDN_API const char* gdn_status_str(int32_t status);
  * left unchanged). */
 GDN_API gdn_status gdn_workspace_bytes(const gdn_desc* desc, int32_t n_time_chunks, size_t* bytes);
 
-/* K_hat = ReLU(k) * c, elementwise, written in io_dtype (bf16: round to
- * nearest even of the fp32 product). Key scaling: blog.hotdry.top SANA-WM post,
+/* K_hat = ReLU(k) * c (with GDN_QK_RMSNORM: ReLU(k / rms(k)) * c, per token),
+ * written in io_dtype (bf16: round to nearest even of the fp32 product). Key scaling: blog.hotdry.top SANA-WM post,
  * section "混合线性注意力", paragraph on the 1/sqrt(D*S) factor. Requires
  * flags = GDN_KEYS_RAW. k and k_hat: [B,H,T,S,D]; may not overlap. */
 GDN_API gdn_status gdn_prepare(const gdn_desc* desc, const void* k, void* k_hat, void* stream);

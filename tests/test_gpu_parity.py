@@ -385,3 +385,102 @@ def test_streaming_step_chain_equals_chunk_causal_scan():
                     orc_ref[n][0, 0])
         say("step chain vs oracle", n, f"{e:.2e}")
         assert e <= tol(w), (n, e)
+
+
+# ------------------------------------------------------ fused q/k RMSNorm
+def _gen_rescaled(w, seed=0):
+    """Seeded inputs whose q and k tokens are rescaled by factors in
+    [0.2, 5] (then rounded to the io dtype again), so that a missing or wrong
+    per-token normalisation changes the result far beyond the bar."""
+    x = gi.batch_inputs(w, seed)
+    rng = np.random.default_rng([77, seed])
+    for n in ("q", "k"):
+        fac = rng.uniform(0.2, 5.0, x[n].shape[:-1] + (1,)).astype(np.float32)
+        val = x[n] * fac
+        if w.io == "bf16":
+            x[n + "_bits"] = gi.f32_to_bf16_bits(val)
+            x[n] = gi.bf16_bits_to_f32(x[n + "_bits"])
+        else:
+            x[n] = val.astype(np.float32)
+    return x, upload(x, w)
+
+
+@pytest.mark.parametrize("io,D", [("bf16", 16), ("bf16", 128), ("f32", 16), ("f32", 128)])
+def test_prepare_rmsnorm(io, D):
+    w = gi.workload(2).with_shape(T=2, S=77, D=D, io=io)
+    x, d = _gen_rescaled(w)
+    say("prepare rmsnorm", io, D)
+    kh = host(gdn.gdn_prepare(d["k"], qk_rmsnorm=True))
+    torch.cuda.synchronize()
+    ref = orc.prepare_keys(x["k"], rmsnorm=True)
+    assert (kh[ref == 0.0] == 0.0).all()
+    rel = np.abs(kh - ref) / np.maximum(np.abs(ref), 1e-300)
+    # bf16: one rounding of an fp32 value (2^-9) plus fp32 arithmetic; fp32: the
+    # fp32 sum of squares (a few ulp), sqrt, reciprocal and two products
+    bound = 2.0 ** -8 if io == "bf16" else 3e-6
+    assert rel[ref != 0].max() <= bound * 1.01, rel[ref != 0].max()
+
+
+RMS_CASES = {
+    # name: (workload, mode, P or chunk_len, keys_prepared)
+    "bf16_D128_fwd_P2": (gi.workload(2).with_shape(H=2, T=5, S=700), "fwd", 2, False),
+    "bf16_D128_bidir_L2": (gi.workload(5).with_shape(H=2, T=5, S=600), "bidir", 2, False),
+    "bf16_D128_split_S2100": (gi.workload(2).with_shape(T=2, S=2100), "fwd", 1, False),
+    "bf16_D64_fwd": (gi.workload(2).with_shape(D=64, T=4, S=130), "fwd", 1, False),
+    "f32_D16_fwd_P2": (gi.workload(1), "fwd", 2, False),
+    "f32_D128_bidir_L3": (gi.workload(1).with_shape(D=128, S=60, T=4), "bidir", 3, False),
+    "bf16_D128_prepared_keys": (gi.workload(2).with_shape(T=3, S=300), "fwd", 1, True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RMS_CASES))
+def test_scan_rmsnorm(name):
+    """GDN_QK_RMSNORM fused into phase 1 (keys) and the readout (queries)."""
+    w, mode, par, prepared = RMS_CASES[name]
+    x, d = _gen_rescaled(w)
+    if prepared:
+        # keys given as K_hat (normalised, ReLU'd and scaled by the oracle);
+        # the flag then normalises q only
+        kh = orc.prepare_keys(x["k"], rmsnorm=True)
+        if w.io == "bf16":
+            bits = gi.f32_to_bf16_bits(kh.astype(np.float32))
+            x["k"] = gi.bf16_bits_to_f32(bits)
+            d["k"] = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+        else:
+            x["k"] = kh.astype(np.float32)
+            d["k"] = torch.from_numpy(x["k"]).to(DEV)
+    say("scan rmsnorm", name)
+    if mode == "bidir":
+        res = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], par,
+                                         keys_prepared=prepared, qk_rmsnorm=True)
+    else:
+        res = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], n_time_chunks=par,
+                               keys_prepared=prepared, qk_rmsnorm=True)
+    torch.cuda.synchronize()
+    for (b, h) in [(0, w.H - 1)]:
+        a = head_arrays(x, b, h)
+        if mode == "bidir":
+            ref = orc.scan_bidir_chunked(a["q"], a["k"], a["v"], a["beta"], a["gamma"], par,
+                                         keys_prepared=prepared, qk_rmsnorm=True)
+            names = ("states_fwd", "states_rev", "o")
+        else:
+            ref = orc.scan_fwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"],
+                               keys_prepared=prepared, qk_rmsnorm=True)
+            names = ("states", "s_final", "o")
+        for n in names:
+            e = rel_fro(host(res[n][b, h]), ref[n][0, 0])
+            say(name, n, f"{e:.2e}")
+            assert e <= tol(w), (n, e)
+
+
+def test_frame_terms_rmsnorm():
+    w = gi.workload(2).with_shape(H=2, T=2, S=1000)
+    x, d = _gen_rescaled(w)
+    say("frame terms rmsnorm")
+    A, U = gdn.gdn_frame_terms(d["k"], d["v"], d["beta"], qk_rmsnorm=True)
+    torch.cuda.synchronize()
+    kh = orc.prepare_keys(x["k"][0, 1], rmsnorm=True)
+    for t in range(w.T):
+        Ar, Ur = orc.frame_terms(kh[t], x["v"][0, 1, t], x["beta"][0, 1, t])
+        assert rel_fro(host(A[0, 1, t]), Ar) <= tol(w)
+        assert rel_fro(host(U[0, 1, t]), Ur) <= tol(w)
