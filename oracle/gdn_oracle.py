@@ -62,6 +62,7 @@ __all__ = [
     "compose",
     "combine",
     "readout",
+    "scan_fwd_bwd",
 ]
 
 
@@ -283,3 +284,75 @@ def combine(C, Hc, s0=None):
                 X = X @ C[b, h, p] + Hc[b, h, p]
             s_end[b, h] = X
     return s_start, s_end
+
+
+def scan_fwd_bwd(q, k, v, beta, gamma, do, ds_final=None, s0=None, key_scale=None,
+                 keys_prepared=False):
+    """Reverse-mode gradients of the causal frame scan.
+
+    The scalar is L = sum_{t,s} <do_{t,s}, o_{t,s}> + <ds_final, S_{T-1}>,
+    with o_{t,s} = S_t q_{t,s} and S_t = S_{t-1} M_t + U_t as in scan_fwd
+    ([P1] "混合线性注意力"). The chain rule is taken step by step through the
+    forward definition, frames in reverse order. With G the gradient of L with
+    respect to S_t:
+
+        G      += sum_s do_{t,s} q_{t,s}^T            (readout of frame t)
+        dq_t,s  = S_t^T do_{t,s}
+        dU_t    = G
+        dM_t    = S_{t-1}^T G                        (S_t = S_{t-1} M_t + U_t)
+        dgamma_t = <dM_t, I - A_t>,   dA_t = -gamma_t dM_t
+        G       = G M_t^T                            (gradient reaching S_{t-1})
+
+    and, through A_t = sum_s beta_s k_s k_s^T and U_t = sum_s beta_s v_s k_s^T
+    (k the prepared keys), dk_s = beta_s (dA + dA^T) k_s + beta_s G^T v_s,
+    dbeta_s = k_s^T dA k_s + v_s^T G k_s, dv_s = beta_s G k_s; raw keys then
+    pass through the key scale and the ReLU (gradient zero where k <= 0).
+    Returns dq, dk, dv [B,H,T,S,D], dbeta [B,H,T,S], dgamma [B,H,T] and
+    ds0 [B,H,D,D] (the gradient reaching the initial state).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, H, T, S, D = k.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dbeta = np.zeros_like(beta)
+    dgamma = np.zeros_like(gamma)
+    ds0 = np.zeros((B, H, D, D))
+    c = None
+    if not keys_prepared:
+        c = key_scale if (key_scale is not None and key_scale > 0) else default_key_scale(D, S)
+    for b in range(B):
+        for h in range(H):
+            kh = _keys(k[b, h], key_scale, keys_prepared)
+            sinit = None if s0 is None else s0[b, h]
+            _, states, _ = _head_fwd(None, kh, v[b, h], beta[b, h], gamma[b, h], sinit, 0, T)
+            G = np.zeros((D, D)) if ds_final is None else np.array(ds_final[b, h], dtype=np.float64)
+            for t in range(T - 1, -1, -1):
+                St = states[t]
+                if t > 0:
+                    Sp = states[t - 1]
+                else:
+                    Sp = np.zeros((D, D)) if sinit is None else np.asarray(sinit, dtype=np.float64)
+                G = G + do[b, h, t].T @ q[b, h, t]
+                dq[b, h, t] = do[b, h, t] @ St
+                A, _ = frame_terms(kh[t], v[b, h, t], beta[b, h, t])
+                dM = Sp.T @ G
+                dgamma[b, h, t] = np.sum(dM * (np.eye(D) - A))
+                dA = -gamma[b, h, t] * dM
+                Ksym = dA + dA.T
+                kt, vt, bt = kh[t], v[b, h, t], beta[b, h, t]
+                dkh = bt[:, None] * (kt @ Ksym.T + vt @ G)
+                dv[b, h, t] = bt[:, None] * (kt @ G.T)
+                dbeta[b, h, t] = np.einsum("si,ij,sj->s", kt, dA, kt) + np.einsum("si,ij,sj->s", vt, G, kt)
+                if keys_prepared:
+                    dk[b, h, t] = dkh
+                else:
+                    dk[b, h, t] = dkh * c * (k[b, h, t] > 0)
+                G = G @ transition(A, gamma[b, h, t]).T
+            ds0[b, h] = G
+    return {"dq": dq, "dk": dk, "dv": dv, "dbeta": dbeta, "dgamma": dgamma, "ds0": ds0}

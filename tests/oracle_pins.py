@@ -498,6 +498,68 @@ def pin_rmsnorm_in_the_scan(orc):
         "without the flag, rescaled tokens must change the output"
 
 
+def _loss(orc, q, k, v, b, g, s0, do, dsf):
+    r = orc.scan_fwd(q, k, v, b, g, s0=s0)
+    return float(np.sum(r["o"] * do) + np.sum(r["s_final"] * dsf))
+
+
+def pin_backward_finite_differences(orc):
+    """Every gradient of L = <do, o> + <ds_final, S_{T-1}> matches a central
+    finite difference of the forward oracle, element by element (no use of
+    the chain-rule formulas). Keys are kept away from the ReLU kink."""
+    rng = np.random.default_rng(31)
+    B, H, T, S, D = 1, 2, 3, 4, 3
+    q = rng.standard_normal((B, H, T, S, D))
+    k = rng.standard_normal((B, H, T, S, D))
+    k = np.where(np.abs(k) < 0.1, 0.1 * np.sign(k + 1e-30) + k, k)
+    v = rng.standard_normal((B, H, T, S, D))
+    b = rng.uniform(0.1, 1.0, (B, H, T, S))
+    g = rng.uniform(0.8, 1.0, (B, H, T))
+    s0 = rng.standard_normal((B, H, D, D))
+    do = rng.standard_normal((B, H, T, S, D))
+    dsf = rng.standard_normal((B, H, D, D))
+    grads = orc.scan_fwd_bwd(q, k, v, b, g, do, ds_final=dsf, s0=s0)
+    args = {"q": q, "k": k, "v": v, "beta": b, "gamma": g, "s0": s0}
+    names = {"q": "dq", "k": "dk", "v": "dv", "beta": "dbeta", "gamma": "dgamma", "s0": "ds0"}
+    h = 1e-6
+    for name, arr in args.items():
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = _loss(orc, q, k, v, b, g, s0, do, dsf)
+            arr[idx] = old - h
+            lm = _loss(orc, q, k, v, b, g, s0, do, dsf)
+            arr[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        got = grads[names[name]]
+        err = np.max(np.abs(got - fd)) / max(1.0, np.max(np.abs(fd)))
+        assert err < 1e-6, f"backward {names[name]}: finite-difference mismatch {err:.3e}"
+
+
+def pin_backward_pure_decay(orc):
+    """beta = 0: S_t = (prod_{tau<=t} gamma_tau) S0, so the gradient reaching S0
+    is sum_t (prod_{tau<=t} gamma_tau) E_t with E_t = sum_s do_{t,s} q_{t,s}^T,
+    and dgamma_t = sum_{t'>=t} (prod_{tau<=t'} gamma_tau / gamma_t) <E_t', S0>;
+    v and the gates get zero gradient."""
+    rng = np.random.default_rng(32)
+    q, k, v, b, g = _rand_case(rng, T=4, S=5, D=3)
+    b[:] = 0.0
+    B, H, T, S, D = q.shape
+    s0 = rng.standard_normal((B, H, D, D))
+    do = rng.standard_normal(q.shape)
+    r = orc.scan_fwd_bwd(q, k, v, b, g, do, s0=s0)
+    E = np.einsum("tsi,tsj->tij", do[0, 0], q[0, 0])
+    pg = np.cumprod(g[0, 0])
+    want_ds0 = sum(pg[t] * E[t] for t in range(T))
+    _close(r["ds0"][0, 0], want_ds0, 1e-12, "beta = 0: ds0")
+    for t in range(T):
+        want = sum(pg[u] / g[0, 0, t] * np.sum(E[u] * s0[0, 0]) for u in range(t, T))
+        _close(r["dgamma"][0, 0, t], want, 1e-12, "beta = 0: dgamma")
+    _close(r["dv"], np.zeros_like(v), 0.0, "beta = 0: dv")
+    _close(r["dk"], np.zeros_like(k), 0.0, "beta = 0: dk")
+
+
 ALL_PINS = [
     pin_prepare_closed_form,
     pin_hand_example,
@@ -517,4 +579,6 @@ ALL_PINS = [
     pin_readout_linear,
     pin_rmsnorm_values,
     pin_rmsnorm_in_the_scan,
+    pin_backward_finite_differences,
+    pin_backward_pure_decay,
 ]

@@ -111,6 +111,49 @@ def _reverse_off_by_one(k, v, beta, gamma, chunk_len, key_scale=None, keys_prepa
     return rev
 
 
+def _bwd_variant(kind):
+    """scan_fwd_bwd with one planted mistake."""
+    def f(q, k, v, beta, gamma, do, ds_final=None, s0=None, key_scale=None, keys_prepared=False):
+        q, k, v, beta, gamma, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, beta, gamma, do))
+        B, H, T, S, D = k.shape
+        out = {n: np.zeros_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dbeta", beta),
+                                                  ("dgamma", gamma))}
+        out["ds0"] = np.zeros((B, H, D, D))
+        c = orc.default_key_scale(D, S)
+        for b in range(B):
+            for h in range(H):
+                kh = orc._keys(k[b, h], key_scale, keys_prepared)
+                sinit = None if s0 is None else s0[b, h]
+                _, states, _ = orc._head_fwd(None, kh, v[b, h], beta[b, h], gamma[b, h], sinit, 0, T)
+                G = np.zeros((D, D))
+                if ds_final is not None and kind != "no_ds_final":
+                    G = np.array(ds_final[b, h], dtype=np.float64)
+                for t in range(T - 1, -1, -1):
+                    St = states[t]
+                    Sp = states[t - 1] if t > 0 else (np.zeros((D, D)) if sinit is None else sinit)
+                    if kind == "dM_uses_S_t":
+                        Sp = St
+                    G = G + do[b, h, t].T @ q[b, h, t]
+                    out["dq"][b, h, t] = do[b, h, t] @ (Sp if kind == "dq_uses_prev" else St)
+                    A, _ = orc.frame_terms(kh[t], v[b, h, t], beta[b, h, t])
+                    dM = Sp.T @ G
+                    out["dgamma"][b, h, t] = np.sum(dM * (np.eye(D) - A))
+                    dA = -gamma[b, h, t] * dM
+                    Ksym = dA if kind == "dk_not_symmetrised" else dA + dA.T
+                    kt, vt, bt = kh[t], v[b, h, t], beta[b, h, t]
+                    out["dv"][b, h, t] = bt[:, None] * (kt @ G.T)
+                    db = np.einsum("si,ij,sj->s", kt, dA, kt)
+                    if kind != "dbeta_no_U_term":
+                        db = db + np.einsum("si,ij,sj->s", vt, G, kt)
+                    out["dbeta"][b, h, t] = db
+                    out["dk"][b, h, t] = bt[:, None] * (kt @ Ksym.T + vt @ G) * c * (k[b, h, t] > 0)
+                    if kind != "G_not_propagated":
+                        G = G @ orc.transition(A, gamma[b, h, t]).T
+                out["ds0"][b, h] = G
+        return out
+    return f
+
+
 MUTANTS = {
     "U_transposed": ("frame_terms", _frame_terms_variant("U_transposed")),
     "U_no_beta": ("frame_terms", _frame_terms_variant("U_no_beta")),
@@ -132,6 +175,12 @@ MUTANTS = {
     "reverse_not_reset": ("chunk_bounds", lambda T, L: [(0, T)]),
     "reverse_wrong_gates": ("scan_reverse_chunked", _reverse_off_by_one),
     "compose_reversed_product": ("compose", _compose_reversed),
+    "bwd_dM_uses_S_t": ("scan_fwd_bwd", _bwd_variant("dM_uses_S_t")),
+    "bwd_dq_uses_prev": ("scan_fwd_bwd", _bwd_variant("dq_uses_prev")),
+    "bwd_dk_not_symmetrised": ("scan_fwd_bwd", _bwd_variant("dk_not_symmetrised")),
+    "bwd_dbeta_no_U_term": ("scan_fwd_bwd", _bwd_variant("dbeta_no_U_term")),
+    "bwd_G_not_propagated": ("scan_fwd_bwd", _bwd_variant("G_not_propagated")),
+    "bwd_no_ds_final": ("scan_fwd_bwd", _bwd_variant("no_ds_final")),
     "rms_over_tokens": ("rms_norm", lambda x, eps=orc.RMS_EPS: np.asarray(x, dtype=np.float64)
                         / np.sqrt(np.mean(np.asarray(x, dtype=np.float64) ** 2, axis=-2,
                                           keepdims=True) + eps)),
