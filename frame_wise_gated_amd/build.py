@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.hip", "k_misc.hip", "k_terms.hip", "k_scan.hip", "k_readout.hip"]
+SOURCES = ["gdn_api.hip", "k_misc.hip", "k_terms.hip", "k_scan.hip", "k_readout.hip", "k_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

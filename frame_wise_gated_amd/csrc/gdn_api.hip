@@ -76,6 +76,36 @@ Layout layout(const Shape& sh, int P) {
   return L;
 }
 
+// Workspace of the backward pass: phase-1 terms (A), split partials, E_t,
+// the adjoint states G, the per-frame P_t, G_{T-1} per head and a ones gate.
+struct BwdLayout {
+  size_t terms = 0, partial = 0, E = 0, G = 0, P = 0, ginit = 0, ones = 0;
+  size_t total = 0;
+  int n_split = 1;
+};
+
+BwdLayout bwd_layout(const Shape& sh) {
+  BwdLayout L;
+  const size_t DD = (size_t)sh.D * sh.D * sizeof(float);
+  const size_t FH = (size_t)sh.FH();
+  L.n_split = gdn::terms_split(sh);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  L.terms = take(FH * 2 * DD);
+  L.partial = take(L.n_split > 1 ? FH * L.n_split * 2 * DD : 0);
+  L.E = take(FH * DD);
+  L.G = take(FH * DD);
+  L.P = take(FH * DD);
+  L.ginit = take((size_t)sh.BH() * DD);
+  L.ones = take(FH * (size_t)sh.S * sizeof(float));
+  L.total = off;
+  return L;
+}
+
 template <typename T>
 T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
@@ -449,6 +479,106 @@ gdn_status gdn_compose(const gdn_desc* desc, const void* k, const void* v, const
     gdn::CombineParams cp{Cb, Hb, s0, s_start, P};
     GDN_HIP(gdn::launch_combine(sh, cp, st));
   }
+  return GDN_OK;
+}
+
+gdn_status gdn_bwd_workspace_bytes(const gdn_desc* desc, size_t* bytes) {
+  Shape sh;
+  gdn_status s = check_desc(desc, &sh);
+  if (s != GDN_OK) return s;
+  if (bytes == nullptr) return GDN_EINVAL;
+  *bytes = bwd_layout(sh).total;
+  return GDN_OK;
+}
+
+gdn_status gdn_scan_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                        const float* beta, const float* gamma, const float* s0,
+                        const float* states, const void* d_o, const float* ds_final, void* dq,
+                        void* dk, void* dv, float* dbeta, float* dgamma, float* ds0, void* ws,
+                        size_t ws_bytes, void* stream) {
+  Shape sh;
+  gdn_status s = check_desc(desc, &sh);
+  if (s != GDN_OK) return s;
+  if (sh.qk_norm) return GDN_EUNSUPPORTED;
+  for (const void* p : {q, k, v, (const void*)s0, (const void*)states, d_o, (const void*)ds_final,
+                        (const void*)dq, (const void*)dk, (const void*)dv, (const void*)ds0})
+    if (!aligned16(p)) return GDN_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  if (sh.BH() == 0) return GDN_OK;
+  const int64_t DD = (int64_t)sh.D * sh.D;
+  if (sh.T == 0) {
+    // no frames: L depends on s0 only through S_{-1} = s0 = S_{T-1}
+    if (ds0 == nullptr) return GDN_OK;
+    if (ds_final) GDN_HIP(gdn::launch_copy_f32(ds_final, ds0, sh.BH() * DD, st));
+    else GDN_HIP(gdn::launch_zero_f32(ds0, sh.BH() * DD, st));
+    return GDN_OK;
+  }
+  if (!q || !k || !v || !beta || !gamma || !states || !d_o) return GDN_EINVAL;
+  const BwdLayout L = bwd_layout(sh);
+  if (ws_bytes < L.total) return GDN_EWORKSPACE;
+  if (ws == nullptr || ((uintptr_t)ws % kAlign) != 0) return GDN_EINVAL;
+  const bool mfma = gdn::scan_uses_mfma(sh);  // layout of the internal terms and E
+  float* terms = at<float>(ws, L.terms);
+  float* part = at<float>(ws, L.partial);
+  float* E = at<float>(ws, L.E);
+  float* G = at<float>(ws, L.G);
+  float* P = at<float>(ws, L.P);
+  float* ginit = at<float>(ws, L.ginit);
+  float* ones = at<float>(ws, L.ones);
+  // A_t of every frame (the U half is not needed)
+  {
+    gdn::TermsOut direct{terms, nullptr, 2 * DD, 0};
+    if (L.n_split == 1) {
+      GDN_HIP(gdn::launch_terms(sh, k, v, beta, 1, direct, mfma, st));
+    } else {
+      gdn::TermsOut po{part, part + DD, (int64_t)L.n_split * 2 * DD, 2 * DD};
+      GDN_HIP(gdn::launch_terms(sh, k, v, beta, L.n_split, po, false, st));
+      GDN_HIP(gdn::launch_reduce_partials(sh, part, L.n_split, direct, mfma, st));
+    }
+  }
+  // E_t = d_o_t^T q_t: the phase-1 contraction with q as prepared keys, d_o
+  // as values and unit gates (the U half of its output)
+  {
+    GDN_HIP(gdn::launch_fill_f32(ones, sh.FH() * sh.S, 1.f, st));
+    Shape shq = sh;
+    shq.prepared = 1;
+    shq.c = 1.f;
+    gdn::TermsOut eout{nullptr, E, DD, 0};
+    if (L.n_split == 1) {
+      GDN_HIP(gdn::launch_terms(shq, q, d_o, ones, 1, eout, mfma, st));
+    } else {
+      gdn::TermsOut po{part, part + DD, (int64_t)L.n_split * 2 * DD, 2 * DD};
+      GDN_HIP(gdn::launch_terms(shq, q, d_o, ones, L.n_split, po, false, st));
+      GDN_HIP(gdn::launch_reduce_partials(shq, part, L.n_split, eout, mfma, st));
+    }
+  }
+  GDN_HIP(gdn::launch_grad_init(sh, E, ds_final, ginit, mfma, st));
+  // adjoint recurrence: frames T-1 .. 0 from G_{T-1}, adding E_{f-1} after
+  // frame f's transition, so the state after frame f is G_{f-1} (stored in
+  // slot f) and after frame 0 it is dL/dS0
+  {
+    gdn::ScanParams p;
+    memset(&p, 0, sizeof(p));
+    p.terms = terms;
+    p.gamma = gamma;
+    p.T = sh.T;
+    p.nchunk = 1;
+    p.mode = gdn::SCAN_REVERSE;
+    p.usrc = E;
+    p.ushift = -1;
+    p.init = ginit;
+    p.init_bh_stride = DD;
+    p.states = G;
+    p.finA = ds0;
+    p.fin_bh_stride = DD;
+    p.fin_last_only = 1;
+    p.offsets[0] = 0;
+    p.offsets[1] = sh.T;
+    GDN_HIP(gdn::launch_scan(sh, p, st));
+  }
+  GDN_HIP(gdn::launch_frame_grad(sh, states, s0, G, ginit, terms, mfma, gamma, P, dgamma, st));
+  if (dq || dk || dv || dbeta)
+    GDN_HIP(gdn::launch_token_grad(sh, k, v, beta, d_o, states, G, ginit, P, dq, dk, dv, dbeta, st));
   return GDN_OK;
 }
 

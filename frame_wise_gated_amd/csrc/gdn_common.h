@@ -166,7 +166,7 @@ struct TermsOut {
 enum ScanMode : int {
   SCAN_FORWARD = 0,  // rows = D, frames ascending, U added
   SCAN_COMPOSE = 1,  // rows = 2D: C rows (identity start, no U) then H rows (zero start, U)
-  SCAN_REVERSE = 2,  // rows = D, frames descending, U added, zero start
+  SCAN_REVERSE = 2,  // rows = D, frames descending, U added, start from init (or zero)
 };
 
 struct ScanParams {
@@ -176,7 +176,12 @@ struct ScanParams {
   int T;
   int nchunk;           // chunks per head
   int mode;             // ScanMode
-  const float* init;    // nullable start states: base + bh*init_bh_stride + c*init_c_stride
+  const float* usrc;    // nullable: U of frame f comes from usrc slot bh*T + f + ushift
+                        // (same layout as the terms' U, slots of DD floats) and is zero
+                        // when f + ushift < 0; NULL = the terms' own U
+  int ushift;
+  const float* init;    // nullable start states (FORWARD and REVERSE):
+                        // base + bh*init_bh_stride + c*init_c_stride
   int64_t init_bh_stride;
   int64_t init_c_stride;
   float* states;        // nullable [FH][D][D] per-frame states
@@ -215,5 +220,17 @@ hipError_t launch_readout(const Shape& sh, const void* q, const float* st_a, con
                           void* o, hipStream_t st);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st);
 hipError_t launch_zero_f32(float* dst, int64_t n, hipStream_t st);
+hipError_t launch_fill_f32(float* dst, int64_t n, float value, hipStream_t st);
+// Backward pass (k_bwd.hip).
+hipError_t launch_grad_init(const Shape& sh, const float* E, const float* ds_final, float* ginit,
+                            bool granule, hipStream_t st);
+hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* s0,
+                             const float* gbuf, const float* ginit, const float* terms,
+                             bool a_granule_bf16, const float* gamma, float* P, float* dgamma,
+                             hipStream_t st);
+hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, const float* beta,
+                             const void* dout, const float* states, const float* gbuf,
+                             const float* ginit, const float* P, void* dq, void* dk, void* dv,
+                             float* dbeta, hipStream_t st);
 
 }  // namespace gdn

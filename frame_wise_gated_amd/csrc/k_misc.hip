@@ -46,10 +46,10 @@ __global__ void __launch_bounds__(256) copy_f32_kernel(const float* __restrict__
   for (; i < n; i += stride) d[i] = s[i];
 }
 
-__global__ void __launch_bounds__(256) zero_f32_kernel(float* __restrict__ d, int64_t n) {
+__global__ void __launch_bounds__(256) fill_f32_kernel(float* __restrict__ d, int64_t n, float x) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (; i < n; i += stride) d[i] = 0.f;
+  for (; i < n; i += stride) d[i] = x;
 }
 
 // K_hat = ReLU(k / rms(k)) * c with the per-token RMSNorm over D: each lane
@@ -149,10 +149,14 @@ hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_zero_f32(float* dst, int64_t n, hipStream_t st) {
+hipError_t launch_fill_f32(float* dst, int64_t n, float value, hipStream_t st) {
   if (n == 0) return hipSuccess;
-  zero_f32_kernel<<<grid_for(n), 256, 0, st>>>(dst, n);
+  fill_f32_kernel<<<grid_for(n), 256, 0, st>>>(dst, n, value);
   return hipGetLastError();
+}
+
+hipError_t launch_zero_f32(float* dst, int64_t n, hipStream_t st) {
+  return launch_fill_f32(dst, n, 0.f, st);
 }
 
 }  // namespace gdn

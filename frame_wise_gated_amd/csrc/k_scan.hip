@@ -63,7 +63,7 @@ __global__ void __launch_bounds__(256) scan_rows_kernel(ScanParams p) {
     float x0 = 0.f;
     if (p.mode == SCAN_COMPOSE) {
       x0 = (c_rows && (srow0 + i) == n) ? 1.f : 0.f;
-    } else if (p.mode == SCAN_FORWARD && p.init != nullptr) {
+    } else if (p.init != nullptr) {
       x0 = p.init[bh * p.init_bh_stride + (int64_t)c * p.init_c_stride + (int64_t)(srow0 + i) * D + n];
     }
     Xs[0][i][n] = x0;
@@ -80,6 +80,12 @@ __global__ void __launch_bounds__(256) scan_rows_kernel(ScanParams p) {
     const int64_t f = bh * p.T + t;
     const float* At = p.terms + f * 2 * DD;
     const float* Ut = At + DD;
+    bool u_on = use_u;
+    if (p.usrc != nullptr) {
+      const int fs = t + p.ushift;
+      u_on = use_u && fs >= 0 && fs < p.T;
+      Ut = p.usrc + (bh * p.T + (u_on ? fs : 0)) * DD;
+    }
     const float g = p.gamma[f];
     float acc[RPT];
 #pragma unroll
@@ -94,7 +100,7 @@ __global__ void __launch_bounds__(256) scan_rows_kernel(ScanParams p) {
     for (int r = 0; r < RPT; ++r) {
       const int i = ig + RG * r;
       float xn = g * (Xs[cur][i][n] - acc[r]);
-      if (use_u) xn += Ut[(int64_t)(srow0 + i) * D + n];
+      if (u_on) xn += Ut[(int64_t)(srow0 + i) * D + n];
       Xs[cur ^ 1][i][n] = xn;
       if (p.states != nullptr) p.states[f * DD + (int64_t)(srow0 + i) * D + n] = xn;
     }
@@ -250,7 +256,7 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
       if (p.mode == SCAN_COMPOSE) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) x0[r] = (c_rows && srow0 + m == n + r) ? 1.f : 0.f;
-      } else if (p.mode == SCAN_FORWARD && p.init != nullptr) {
+      } else if (p.init != nullptr) {
         x0 = *(const f32x4_t*)(p.init + bh * p.init_bh_stride + (int64_t)c * p.init_c_stride +
                               (int64_t)(srow0 + m) * D + n);
       }
@@ -274,6 +280,7 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
   uint4 af[kF][2][4];
   f32x4_t u[kF][MT][2];
   float gmr[kF];
+  float umr[kF];  // 1 when the frame's U term applies, 0 otherwise
   // granule layout of the terms (a_granule / u_granule): each load below is
   // 1 KB of consecutive bytes per wave
   auto load_a = [&](int j, int step) {
@@ -289,6 +296,14 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
   // finite values), so that every workgroup issues the same load sequence.
   auto load_u = [&](int j, int step) {
     const f32x4_t* Ug = (const f32x4_t*)(terms_of(step) + (c_rows ? 0 : DD));
+    umr[j] = umul;
+    if (p.usrc != nullptr && !c_rows) {
+      // U of frame f from the shifted source slot (zero outside [0, T))
+      const int fs = frame_of(step) + p.ushift;
+      const bool on = fs >= 0 && fs < p.T;
+      umr[j] = on ? 1.f : 0.f;
+      Ug = (const f32x4_t*)(p.usrc + (bh * p.T + (on ? fs : 0)) * DD);
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -350,7 +365,7 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
           const int m = 16 * mt + l16;
           f32x4_t xn;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) xn[r] = gm * (xr[mt][nt][r] - acc[mt][nt][r]) + umul * u[j][mt][nt][r];
+          for (int r = 0; r < 4; ++r) xn[r] = gm * (xr[mt][nt][r] - acc[mt][nt][r]) + umr[j] * u[j][mt][nt][r];
           if (active) xr[mt][nt] = xn;
           put_split(cur ^ 1, m, ncol(nt), xr[mt][nt]);
         }

@@ -166,6 +166,31 @@ GDN_API gdn_status gdn_compose(const gdn_desc* desc, const void* k, const void* 
                        float* Hc, const float* s0, float* s_start, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* Workspace in bytes that gdn_scan_bwd needs for `desc`. Host-only. */
+GDN_API gdn_status gdn_bwd_workspace_bytes(const gdn_desc* desc, size_t* bytes);
+
+/* Backward pass of the causal frame scan (gdn_scan_fwd): reverse-mode
+ * gradients of L = sum <d_o, o> + <ds_final, S_{T-1}> through the rule of
+ * blog.hotdry.top SANA-WM post, section "混合线性注意力". With
+ * G_t = dL/dS_t: G_{T-1} = E_{T-1} + ds_final, G_t = E_t + G_{t+1} M_{t+1}
+ * (E_t = d_o_t^T q_t, M symmetric), and per frame dM_t = S_{t-1}^T G_t,
+ * dgamma_t = <dM_t, I - A_t>; per token dq = S_t^T do,
+ * dk_hat = beta ((dA + dA^T) k_hat + G_t^T v) with dA = -gamma_t dM_t,
+ * dv = beta G_t k_hat, dbeta = k_hat^T dA k_hat + v^T G_t k_hat; raw keys
+ * then get the key scale and the ReLU mask (zero where k <= 0).
+ * Inputs: the forward's q, k, v, beta, gamma, s0 (NULL = zero) and its
+ * per-frame states [B,H,T,D,D] (required), d_o [B,H,T,S,D] (io dtype,
+ * required), ds_final [B,H,D,D] (NULL = zero). Outputs (each may be NULL):
+ * dq, dk, dv [B,H,T,S,D] (io dtype), dbeta [B,H,T,S], dgamma [B,H,T],
+ * ds0 [B,H,D,D] (fp32). The adjoint recurrence runs sequentially over the
+ * frames. GDN_QK_RMSNORM is not supported here (GDN_EUNSUPPORTED).
+ * Workspace: gdn_bwd_workspace_bytes. */
+GDN_API gdn_status gdn_scan_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                                const float* beta, const float* gamma, const float* s0,
+                                const float* states, const void* d_o, const float* ds_final,
+                                void* dq, void* dk, void* dv, float* dbeta, float* dgamma,
+                                float* ds0, void* ws, size_t ws_bytes, void* stream);
+
 /* Phase 3 alone: o_{t,s} = (states_t + states_add_t) q_{t,s} for every token
  * of every frame (states_add may be NULL). The readout with the state after
  * frame t is this library's reading of the frame-wise rule (the pages give the

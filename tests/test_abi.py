@@ -22,7 +22,7 @@ def test_exports_every_declared_symbol(L):
     names = gdn.exported_names_in_header()
     assert set(names) == {"gdn_status_str", "gdn_workspace_bytes", "gdn_prepare", "gdn_frame_terms",
                           "gdn_scan_fwd", "gdn_scan_bidir_chunked", "gdn_compose", "gdn_readout",
-                          "gdn_step"}
+                          "gdn_step", "gdn_scan_bwd", "gdn_bwd_workspace_bytes"}
     out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -119,6 +119,17 @@ def test_null_and_chunk_arguments(L):
                       fake, 1 << 30, None) == gdn.GDN_EINVAL
     assert L.gdn_step(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake, fake, None, None,
                       fake, 16, None) == gdn.GDN_EWORKSPACE
+    # backward: RMSNorm unsupported, missing states, workspace too small
+    dn = gdn.make_desc(1, 1, 4, 12, 16, gdn.GDN_F32, qk_rmsnorm=True)
+    bwd = lambda dd, states, nb: L.gdn_scan_bwd(ctypes.byref(dd), fake, fake, fake, fake, fake, None,
+                                                states, fake, None, fake, fake, fake, fake, fake,
+                                                None, fake, nb, None)
+    assert bwd(dn, fake, 1 << 30) == gdn.GDN_EUNSUPPORTED
+    assert bwd(d, None, 1 << 30) == gdn.GDN_EINVAL
+    assert bwd(d, fake, 16) == gdn.GDN_EWORKSPACE
+    nbw = ctypes.c_size_t(0)
+    assert L.gdn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(nbw)) == gdn.GDN_OK
+    assert nbw.value > 0
     # prepare refuses already-prepared keys
     dp = gdn.make_desc(1, 1, 4, 12, 16, gdn.GDN_F32, keys_prepared=True)
     assert L.gdn_prepare(ctypes.byref(dp), fake, fake, None) == gdn.GDN_EINVAL

@@ -484,3 +484,76 @@ def test_frame_terms_rmsnorm():
         Ar, Ur = orc.frame_terms(kh[t], x["v"][0, 1, t], x["beta"][0, 1, t])
         assert rel_fro(host(A[0, 1, t]), Ar) <= tol(w)
         assert rel_fro(host(U[0, 1, t]), Ur) <= tol(w)
+
+
+# --------------------------------------------------------------- backward
+BWD_CASES = {
+    # name: (workload, with s0 / ds_final, keys_prepared)
+    "f32_D16_s0_dsf": (gi.workload(1), True, False),
+    "f32_D16_plain": (gi.workload(1).with_shape(B=2, H=2), False, False),
+    "bf16_D128_s0_dsf": (gi.workload(2).with_shape(H=2, T=6, S=300), True, False),
+    "bf16_D128_split_S2100": (gi.workload(2).with_shape(T=3, S=2100), True, False),
+    "bf16_D64": (gi.workload(2).with_shape(D=64, T=5, S=130), True, False),
+    "f32_D128_prepared": (gi.workload(1).with_shape(D=128, S=40, T=4), True, True),
+}
+
+
+def _bwd_inputs(w, x, d, extras, seed=5):
+    rng = np.random.default_rng([88, seed])
+    do = rng.standard_normal((w.B, w.H, w.T, w.S, w.D)).astype(np.float32)
+    if w.io == "bf16":
+        do_bits = gi.f32_to_bf16_bits(do)
+        do = gi.bf16_bits_to_f32(do_bits)
+        do_d = torch.from_numpy(do_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    else:
+        do_d = torch.from_numpy(do).to(DEV)
+    s0 = dsf = None
+    if extras:
+        s0 = (0.5 * rng.standard_normal((w.B, w.H, w.D, w.D))).astype(np.float32)
+        dsf = rng.standard_normal((w.B, w.H, w.D, w.D)).astype(np.float32)
+    return do, do_d, s0, dsf
+
+
+@pytest.mark.parametrize("name", sorted(BWD_CASES))
+def test_scan_bwd(name):
+    """Gradients of L = <do, o> + <ds_final, S_T-1> through the whole path
+    (phase 1, adjoint scan, per-frame and per-token kernels) against the
+    float64 oracle's reverse-mode gradients, per head."""
+    w, extras, prepared = BWD_CASES[name]
+    x, d = _gen(w)
+    if prepared:
+        kh = orc.prepare_keys(x["k"]).astype(np.float32)
+        x["k"] = kh
+        d["k"] = torch.from_numpy(kh).to(DEV)
+    do, do_d, s0, dsf = _bwd_inputs(w, x, d, extras)
+    dev = lambda a: None if a is None else torch.from_numpy(a).to(DEV)
+    say("scan_bwd", name, "forward")
+    fwd = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], s0=dev(s0),
+                           keys_prepared=prepared, want_o=False)
+    say("scan_bwd", name, "backward")
+    g = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], do_d,
+                         s0=dev(s0), ds_final=dev(dsf), keys_prepared=prepared)
+    torch.cuda.synchronize()
+    for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
+        a = head_arrays(x, b, h)
+        ref = orc.scan_fwd_bwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"],
+                               do[b, h][None, None].astype(np.float64),
+                               ds_final=None if dsf is None else dsf[b, h][None, None].astype(np.float64),
+                               s0=None if s0 is None else s0[b, h][None, None].astype(np.float64),
+                               keys_prepared=prepared)
+        for n in ("dq", "dk", "dv", "dbeta", "dgamma", "ds0"):
+            e = rel_fro(host(g[n][b, h]), ref[n][0, 0])
+            say(name, (b, h), n, f"{e:.2e}")
+            assert e <= tol(w), (n, e)
+
+
+def test_scan_bwd_no_frames():
+    w = gi.workload(1).with_shape(T=0)
+    x, d = _gen(w)
+    dsf = torch.randn((w.B, w.H, w.D, w.D), device=DEV)
+    states = torch.empty((w.B, w.H, 0, w.D, w.D), device=DEV)
+    say("scan_bwd T=0")
+    g = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], states, d["q"],
+                         ds_final=dsf, want=("ds0",))
+    torch.cuda.synchronize()
+    assert torch.equal(g["ds0"], dsf)
