@@ -216,8 +216,9 @@ hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_s
 bool scan_uses_mfma(const Shape& sh);
 hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st);
 hipError_t launch_combine(const Shape& sh, const CombineParams& p, hipStream_t st);
+// transpose_state (bf16, D = 128 only): o = states^T q, for the backward pass.
 hipError_t launch_readout(const Shape& sh, const void* q, const float* st_a, const float* st_b,
-                          void* o, hipStream_t st);
+                          void* o, hipStream_t st, bool transpose_state = false);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st);
 hipError_t launch_zero_f32(float* dst, int64_t n, hipStream_t st);
 hipError_t launch_fill_f32(float* dst, int64_t n, float value, hipStream_t st);
@@ -232,5 +233,6 @@ hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, cons
                              const void* dout, const float* states, const float* gbuf,
                              const float* ginit, const float* P, void* dq, void* dk, void* dv,
                              float* dbeta, hipStream_t st);
+bool token_grad_uses_mfma(const Shape& sh);
 
 }  // namespace gdn

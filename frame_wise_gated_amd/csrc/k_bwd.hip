@@ -179,6 +179,245 @@ __global__ void __launch_bounds__(256) token_grad_generic(
   if (on && i == 0 && dbeta != nullptr) dbeta[f * S + s] = red[tl][0];
 }
 
+// MFMA path of the per-token gradients (bf16, D = 128), dq excluded (it is
+// the readout with the state transposed). Per frame-head, P_t, G_t and
+// G_t^T are staged once in LDS as bf16 MFMA "A" operands (rows i,
+// contraction j contiguous, chunk-swizzled like the readout's state); each
+// wave streams 32-token tiles of k and v as "B" operands:
+//   pass 1: Y1 = P ReLU(k) c, Y2 = G^T v  ->  dk = beta c [k > 0] (Y1 + Y2),
+//           dbeta = k_hat . (Y1 / 2 + Y2)   (v^T G k_hat = k_hat . G^T v);
+//   pass 2: Y3 = G ReLU(k) c              ->  dv = beta Y3.
+// The accumulators hold tokens as columns; each result tile goes through a
+// per-wave LDS buffer so that a row pass can combine it with the token's raw
+// key (mask, dbeta) and write 16-byte chunks of contiguous token rows.
+constexpr int kTgTok = 32;    // tokens per wave tile
+constexpr int kTgWaves = 4;
+constexpr int kTgXcd = 8;
+
+__device__ __forceinline__ int tswz(int row, int chunk) { return chunk ^ (row & 7); }
+
+__device__ __forceinline__ uint4 ld_row16(const uint16_t* base, int s, int S, int j) {
+  return (s < S) ? *(const uint4*)(base + (int64_t)s * 128 + j) : make_uint4(0, 0, 0, 0);
+}
+
+// Sum over the 16 lanes of a DPP row (rotations by 1, 2, 4, 8).
+__device__ __forceinline__ float sum_row16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  return x;
+}
+
+template <bool kPrepared>
+__global__ void __launch_bounds__(256, 1)
+token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                          const float* __restrict__ beta, const float* __restrict__ gbuf,
+                          const float* __restrict__ ginit, const float* __restrict__ P,
+                          uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                          float* __restrict__ dbeta, int S, int T, int64_t FH, int nb, float c) {
+  constexpr int D = 128;
+  constexpr int64_t DD = (int64_t)D * D;
+  __shared__ uint4 Pl[D * 16], Gl[D * 16], GTl[D * 16];           // 3 x 32 KB
+  __shared__ uint4 Zs[kTgWaves][kTgTok * 16], Ws[kTgWaves][kTgTok * 16];  // 2 x 4 x 8 KB
+
+  const int xcd = blockIdx.x % kTgXcd;
+  const int slot = blockIdx.x / kTgXcd;
+  const int64_t fh = (int64_t)(slot / nb) * kTgXcd + xcd;
+  const int b = slot % nb;
+  if (fh >= FH) return;
+  const int64_t bh = fh / T;
+  const int t = (int)(fh % T);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  {
+    const float* Pt = P + fh * DD;
+    const float* Gt = t == T - 1 ? ginit + bh * DD : gbuf + (fh + 1) * DD;
+    for (int cc = tid; cc < D * 16; cc += 256) {
+      const int i = cc >> 4;
+      const int ch = cc & 15;
+      const int64_t off = (int64_t)i * D + 8 * ch;
+      const float4 p0 = *(const float4*)(Pt + off), p1 = *(const float4*)(Pt + off + 4);
+      const float4 g0 = *(const float4*)(Gt + off), g1 = *(const float4*)(Gt + off + 4);
+      Pl[i * 16 + tswz(i, ch)] = make_uint4(pack_bf16x2(p0.x, p0.y), pack_bf16x2(p0.z, p0.w),
+                                            pack_bf16x2(p1.x, p1.y), pack_bf16x2(p1.z, p1.w));
+      Gl[i * 16 + tswz(i, ch)] = make_uint4(pack_bf16x2(g0.x, g0.y), pack_bf16x2(g0.z, g0.w),
+                                            pack_bf16x2(g1.x, g1.y), pack_bf16x2(g1.z, g1.w));
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = Gt[(int64_t)(8 * ch + e) * D + i];
+      GTl[i * 16 + tswz(i, ch)] = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                             pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+    }
+  }
+  __syncthreads();
+
+  const uint16_t* kf = k + fh * (int64_t)S * D;
+  const uint16_t* vf = v + fh * (int64_t)S * D;
+  const float* bf = beta + fh * (int64_t)S;
+  uint16_t* dkf = dk ? dk + fh * (int64_t)S * D : nullptr;
+  uint16_t* dvf = dv ? dv + fh * (int64_t)S * D : nullptr;
+  float* dbf = dbeta ? dbeta + fh * (int64_t)S : nullptr;
+  const int ntiles = (S + kTgTok - 1) / kTgTok;
+  const int wstride = nb * kTgWaves;
+  int tile = b * kTgWaves + wave;
+  if (tile >= ntiles) return;
+  uint4* zs = Zs[wave];
+  uint4* ws = Ws[wave];
+  const float ck = kPrepared ? 1.f : c;  // key scale carried by the products of ReLU(k)
+
+  uint4 kb[8], vb[8];
+  {
+    const int s = tile * kTgTok + l32;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      kb[kk] = ld_row16(kf, s, S, 16 * kk + 8 * half);
+      vb[kk] = ld_row16(vf, s, S, 16 * kk + 8 * half);
+    }
+  }
+  // staged tile -> per-row pass over the 32 tokens: lane handles 16-byte
+  // chunk (lane & 15) of rows 4 it + lane / 16
+  for (; tile < ntiles; tile += wstride) {
+    bf16x8_t bk[8], bv[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      uint4 x = kb[kk];
+      if (!kPrepared) {
+        x.x = relu_bf16x2_pk(x.x);
+        x.y = relu_bf16x2_pk(x.y);
+        x.z = relu_bf16x2_pk(x.z);
+        x.w = relu_bf16x2_pk(x.w);
+      }
+      bk[kk] = __builtin_bit_cast(bf16x8_t, x);
+      bv[kk] = __builtin_bit_cast(bf16x8_t, vb[kk]);
+    }
+    const int s0 = tile * kTgTok;
+    const int nxt = tile + wstride;
+    if (nxt < ntiles) {
+      const int sn = nxt * kTgTok + l32;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        kb[kk] = ld_row16(kf, sn, S, 16 * kk + 8 * half);
+        vb[kk] = ld_row16(vf, sn, S, 16 * kk + 8 * half);
+      }
+    }
+    // ---- pass 1: Y1 = P k_hat, Y2 = G^T v
+    {
+      f32x16_t y1[4], y2[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) y1[mt][j] = y2[mt][j] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int row = 32 * mt + l32;
+          const int at = row * 16 + tswz(row, 2 * kk + half);
+          y1[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, Pl[at]), bk[kk],
+                                                           y1[mt], 0, 0, 0);
+          y2[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, GTl[at]), bv[kk],
+                                                           y2[mt], 0, 0, 0);
+        }
+      // accumulator (i, s): token s = l32, rows i = 32 mt + 8 jg + 4 half + (0..3)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          float z[4], w[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a1 = y1[mt][4 * jg + r] * ck, a2 = y2[mt][4 * jg + r];
+            z[r] = a1 + a2;
+            w[r] = 0.5f * a1 + a2;
+          }
+          const int at = l32 * 16 + tswz(l32, 4 * mt + jg);
+          ((uint2*)&zs[at])[half] = make_uint2(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]));
+          ((uint2*)&ws[at])[half] = make_uint2(pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]));
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll 2
+    for (int it = 0; it < 8; ++it) {
+      const int row = 4 * it + (lane >> 4);
+      const int ch = lane & 15;
+      const int s = s0 + row;
+      const bool on = s < S;
+      const uint4 zc = zs[row * 16 + tswz(row, ch)];
+      const uint4 wc = ws[row * 16 + tswz(row, ch)];
+      const uint4 kc = ld_row16(kf, s, S, 8 * ch);
+      const float bt = on ? bf[s] : 0.f;
+      const uint32_t zw[4] = {zc.x, zc.y, zc.z, zc.w};
+      const uint32_t ww[4] = {wc.x, wc.y, wc.z, wc.w};
+      const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
+      uint32_t out[4];
+      float part = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float k0 = __uint_as_float(kw[q] << 16), k1 = __uint_as_float(kw[q] & 0xFFFF0000u);
+        const float z0 = __uint_as_float(zw[q] << 16), z1 = __uint_as_float(zw[q] & 0xFFFF0000u);
+        const float w0 = __uint_as_float(ww[q] << 16), w1 = __uint_as_float(ww[q] & 0xFFFF0000u);
+        float h0, h1, m0, m1;
+        if (kPrepared) {
+          h0 = k0; h1 = k1; m0 = m1 = 1.f;
+        } else {
+          h0 = (k0 > 0.f ? k0 : 0.f) * c; h1 = (k1 > 0.f ? k1 : 0.f) * c;
+          m0 = k0 > 0.f ? c : 0.f; m1 = k1 > 0.f ? c : 0.f;
+        }
+        part += h0 * w0 + h1 * w1;
+        out[q] = pack_bf16x2(bt * m0 * z0, bt * m1 * z1);
+      }
+      part = sum_row16(part);  // the 16 lanes of this token row
+      if (on && dkf) *(uint4*)(dkf + (int64_t)s * D + 8 * ch) = make_uint4(out[0], out[1], out[2], out[3]);
+      if (on && dbf && ch == 0) dbf[s] = part;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- pass 2: Y3 = G k_hat, dv = beta Y3
+    if (dvf) {
+      f32x16_t y3[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) y3[mt][j] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int row = 32 * mt + l32;
+          y3[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, Gl[row * 16 + tswz(row, 2 * kk + half)]), bk[kk], y3[mt], 0, 0, 0);
+        }
+      const int sl = s0 + l32;
+      const float bt = (sl < S ? bf[sl] : 0.f) * ck;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int at = l32 * 16 + tswz(l32, 4 * mt + jg);
+          ((uint2*)&zs[at])[half] =
+              make_uint2(pack_bf16x2(bt * y3[mt][4 * jg], bt * y3[mt][4 * jg + 1]),
+                         pack_bf16x2(bt * y3[mt][4 * jg + 2], bt * y3[mt][4 * jg + 3]));
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int row = 4 * it + (lane >> 4);
+        const int ch = lane & 15;
+        if (s0 + row < S) *(uint4*)(dvf + (int64_t)(s0 + row) * D + 8 * ch) = zs[row * 16 + tswz(row, ch)];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+}
+
 int grid_cap(int64_t n) {
   int64_t g = (n + 255) / 256;
   return (int)(g < 1 ? 1 : (g > 4096 ? 4096 : g));
@@ -216,11 +455,35 @@ hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* 
   return hipGetLastError();
 }
 
+bool token_grad_uses_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
+
 hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, const float* beta,
                              const void* dout, const float* states, const float* gbuf,
                              const float* ginit, const float* P, void* dq, void* dk, void* dv,
                              float* dbeta, hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
+  if (token_grad_uses_mfma(sh)) {
+    // dq = states^T do: the readout with the state staged transposed
+    if (dq) {
+      hipError_t e = launch_readout(sh, dout, states, nullptr, dq, st, true);
+      if (e != hipSuccess) return e;
+    }
+    if (!dk && !dv && !dbeta) return hipSuccess;
+    const int ntiles = (sh.S + kTgTok - 1) / kTgTok;
+    int nb = (ntiles + kTgWaves - 1) / kTgWaves;
+    if (nb > 2) nb = 2;
+    const int64_t groups = (sh.FH() + kTgXcd - 1) / kTgXcd;
+    dim3 grid((unsigned)(groups * kTgXcd * nb));
+    const uint16_t* kk = (const uint16_t*)k;
+    const uint16_t* vv = (const uint16_t*)v;
+    if (sh.prepared)
+      token_grad_mfma_bf16_d128<true><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P, (uint16_t*)dk,
+                                                            (uint16_t*)dv, dbeta, sh.S, sh.T, sh.FH(), nb, sh.c);
+    else
+      token_grad_mfma_bf16_d128<false><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P, (uint16_t*)dk,
+                                                             (uint16_t*)dv, dbeta, sh.S, sh.T, sh.FH(), nb, sh.c);
+    return hipGetLastError();
+  }
   const int tpw = 256 / sh.D;
   const int ntile = (sh.S + tpw - 1) / tpw;
   dim3 grid((unsigned)(sh.FH() * ntile));

@@ -34,7 +34,7 @@ __device__ __forceinline__ uint4 ld_q(const uint16_t* q, int s, int S, int j) {
 // consecutive rows read at the same logical chunk hit eight distinct bank groups.
 __device__ __forceinline__ int rswz(int row, int chunk) { return chunk ^ (row & 7); }
 
-template <bool kNorm>
+template <bool kNorm, bool kTransposeState>
 __global__ void __launch_bounds__(256, 2)
 readout_mfma_bf16_d128(const uint16_t* __restrict__ q, const float* __restrict__ sa,
                        const float* __restrict__ sb, uint16_t* __restrict__ o, int S, int64_t FH,
@@ -55,8 +55,21 @@ readout_mfma_bf16_d128(const uint16_t* __restrict__ q, const float* __restrict__
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // Stage the (summed) state once per workgroup: fp32 -> bf16, coalesced.
-  {
+  // Stage the (summed) state once per workgroup: fp32 -> bf16, coalesced
+  // (kTransposeState: row i of the staged matrix is column i of the state,
+  // gathered with strided reads; the backward pass uses it for dq = S^T do).
+  if (kTransposeState) {
+    const float* s1 = sa + fh * D * D;
+    for (int c = tid; c < D * 16; c += 256) {
+      const int i = c >> 4;
+      const int ch = c & 15;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = s1[(int64_t)(8 * ch + e) * D + i];
+      Sl[i * 16 + rswz(i, ch)] = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                            pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+    }
+  } else {
     const float* s1 = sa + fh * D * D;
     const float* s2 = sb ? sb + fh * D * D : nullptr;
     for (int c = tid; c < D * 16; c += 256) {
@@ -245,7 +258,8 @@ hipError_t launch_readout_generic(const Shape& sh, const void* q, const float* s
 }  // namespace
 
 hipError_t launch_readout(const Shape& sh, const void* q, const float* sa, const float* sb, void* o,
-                          hipStream_t st) {
+                          hipStream_t st, bool transpose_state) {
+  if (transpose_state && !(sh.io == 1 && sh.D == 128)) return hipErrorInvalidValue;
   if (sh.FH() == 0) return hipSuccess;
   if (sh.io == 1 && sh.D == 128) {
     const int ntiles = (sh.S + kTokPerWave - 1) / kTokPerWave;
@@ -253,12 +267,15 @@ hipError_t launch_readout(const Shape& sh, const void* q, const float* sa, const
     if (nb > kBlocksPerFrameHead) nb = kBlocksPerFrameHead;
     const int64_t groups = (sh.FH() + kXcd - 1) / kXcd;
     dim3 grid((unsigned)(groups * kXcd * nb));
-    if (sh.qk_norm)
-      readout_mfma_bf16_d128<true><<<grid, 256, 0, st>>>((const uint16_t*)q, sa, sb, (uint16_t*)o,
-                                                         sh.S, sh.FH(), nb);
+    if (transpose_state)
+      readout_mfma_bf16_d128<false, true><<<grid, 256, 0, st>>>((const uint16_t*)q, sa, nullptr,
+                                                                (uint16_t*)o, sh.S, sh.FH(), nb);
+    else if (sh.qk_norm)
+      readout_mfma_bf16_d128<true, false><<<grid, 256, 0, st>>>((const uint16_t*)q, sa, sb,
+                                                                (uint16_t*)o, sh.S, sh.FH(), nb);
     else
-      readout_mfma_bf16_d128<false><<<grid, 256, 0, st>>>((const uint16_t*)q, sa, sb, (uint16_t*)o,
-                                                          sh.S, sh.FH(), nb);
+      readout_mfma_bf16_d128<false, false><<<grid, 256, 0, st>>>((const uint16_t*)q, sa, sb,
+                                                                 (uint16_t*)o, sh.S, sh.FH(), nb);
     return hipGetLastError();
   }
   if (sh.io == 1) return launch_readout_generic<uint16_t>(sh, q, sa, sb, o, st);

@@ -557,3 +557,29 @@ def test_scan_bwd_no_frames():
                          ds_final=dsf, want=("ds0",))
     torch.cuda.synchronize()
     assert torch.equal(g["ds0"], dsf)
+
+
+def test_scan_bwd_layer_full_size():
+    """Backward of the 16-head 720p layer (T = 11, S = 3600) at full size in
+    the MFMA configuration, checked on two sampled heads."""
+    w = gi.workload(3)
+    heads = [(0, 2), (0, 13)]
+    say("generate", w.name)
+    x = gi.batch_inputs(w, 0, keep_f32=False)
+    d = upload(x, w)
+    rng = np.random.default_rng([88, 9])
+    do_bits = gi.f32_to_bf16_bits(rng.standard_normal((w.B, w.H, w.T, w.S, w.D)).astype(np.float32))
+    do_d = torch.from_numpy(do_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    say("forward + backward", w.name)
+    fwd = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], want_o=False)
+    g = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], do_d)
+    torch.cuda.synchronize()
+    for (b, h) in heads:
+        s = gi.head_inputs(w, 0, b, h)
+        a = {n: np.asarray(s[n], dtype=np.float64)[None, None] for n in ("q", "k", "v", "beta", "gamma")}
+        dof = gi.bf16_bits_to_f32(do_bits[b, h]).astype(np.float64)[None, None]
+        ref = orc.scan_fwd_bwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"], dof)
+        for n in ("dq", "dk", "dv", "dbeta", "dgamma", "ds0"):
+            e = rel_fro(host(g[n][b, h]), ref[n][0, 0])
+            say(w.name, (b, h), n, f"{e:.2e}")
+            assert e <= tol(w), (n, e)
