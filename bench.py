@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phases", action="store_true", help="skip the per-phase timing loops")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the backward pass (causal workloads only)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -266,6 +268,33 @@ def main():
             "mfma_frac": nflop / (t / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
         }
         del A, U
+
+    if not args.no_backward and w.mode != "bidir" and not norm:
+        # backward of the same layer: gradients of <d_o, o> for a random d_o
+        print("[bench] backward", file=sys.stderr, flush=True)
+        gen = torch.Generator(device=dev).manual_seed(args.seed + 1)
+        d_o = torch.randn(q.shape, device=dev, dtype=torch.float32, generator=gen).to(q.dtype)
+        grads = {n: torch.empty_like(q) for n in ("dq", "dk", "dv")}
+        grads["dbeta"] = torch.empty_like(beta)
+        grads["dgamma"] = torch.empty_like(gamma)
+        grads["ds0"] = torch.empty_like(s_fin)
+        bws = torch.empty(gdn.gdn_bwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+        bstep = lambda: gdn.gdn_scan_bwd(q, k, v, beta, gamma, st_fwd, d_o, out=grads, ws=bws,
+                                         stream=stream)
+        for _ in range(2):
+            bstep()
+        t_bwd = timed(bstep, max(args.steps // 2, 3))
+        # algorithmic bytes: q, k, v, d_o, beta, gamma and the forward states in;
+        # dq, dk, dv, dbeta, dgamma out
+        bw_bytes = fh * (4 * S * D * (2 if bf else 4) + 4 * S + 4 + 4 * D * D
+                         + 3 * S * D * (2 if bf else 4) + 4 * S + 4)
+        out["backward"] = {
+            "ms_per_call": t_bwd,
+            "layer_frames_per_s": T / (t_bwd / 1e3),
+            "algorithmic_bytes": bw_bytes,
+            "hbm_frac": bw_bytes / (t_bwd / 1e3) / 1e9 / HBM_PEAK_GBS,
+        }
+        del grads, bws, d_o
 
     if not args.no_cpu_baseline and not norm:
         print("[bench] cpu baseline (float64 oracle)", file=sys.stderr, flush=True)

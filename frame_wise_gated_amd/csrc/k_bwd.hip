@@ -196,8 +196,13 @@ constexpr int kTgXcd = 8;
 
 __device__ __forceinline__ int tswz(int row, int chunk) { return chunk ^ (row & 7); }
 
+// 16 bytes of token row min(s, S - 1) (features j .. j + 7). Rows past the
+// end repeat the last token: an MFMA output column depends only on its own
+// token and those columns are never stored, so no zeroing is needed, and the
+// load stays unconditional (a select on it becomes an exec-masked load, which
+// makes the compiler drain every prefetch at the loop's back edge).
 __device__ __forceinline__ uint4 ld_row16(const uint16_t* base, int s, int S, int j) {
-  return (s < S) ? *(const uint4*)(base + (int64_t)s * 128 + j) : make_uint4(0, 0, 0, 0);
+  return *(const uint4*)(base + (int64_t)min(s, S - 1) * 128 + j);
 }
 
 // Sum over the 16 lanes of a DPP row (rotations by 1, 2, 4, 8).
@@ -215,7 +220,8 @@ token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __rest
                           const float* __restrict__ beta, const float* __restrict__ gbuf,
                           const float* __restrict__ ginit, const float* __restrict__ P,
                           uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-                          float* __restrict__ dbeta, int S, int T, int64_t FH, int nb, float c) {
+                          float* __restrict__ dbeta, uint8_t* __restrict__ trash, int S, int T,
+                          int64_t FH, int nb, float c) {
   constexpr int D = 128;
   constexpr int64_t DD = (int64_t)D * D;
   __shared__ uint4 Pl[D * 16], Gl[D * 16], GTl[D * 16];           // 3 x 32 KB
@@ -229,7 +235,9 @@ token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __rest
   const int64_t bh = fh / T;
   const int t = (int)(fh % T);
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // the wave index is uniform across the wave: read it into a scalar so that
+  // the tile loop below is uniform control flow (no exec-masked loads)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int l32 = lane & 31;
@@ -270,19 +278,41 @@ token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __rest
   uint4* ws = Ws[wave];
   const float ck = kPrepared ? 1.f : c;  // key scale carried by the products of ReLU(k)
 
-  uint4 kb[8], vb[8];
-  {
-    const int s = tile * kTgTok + l32;
+  // B operands of the tile (token l32, features 16 kk + 8 half ..) and, for
+  // the row passes, the raw key chunk (8 ch ..) and gate of rows 4 it + lane/16;
+  // all prefetched one tile ahead
+  const int rch = lane & 15;
+  const int rrow = lane >> 4;
+  uint4 kb[8], vb[8], kr[8];
+  float br[8], bl;
+  auto fetch = [&](int tl) {
+    const int s = tl * kTgTok + l32;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       kb[kk] = ld_row16(kf, s, S, 16 * kk + 8 * half);
       vb[kk] = ld_row16(vf, s, S, 16 * kk + 8 * half);
     }
-  }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int sr = tl * kTgTok + 4 * it + rrow;
+      kr[it] = ld_row16(kf, sr, S, 8 * rch);
+      br[it] = bf[min(sr, S - 1)];  // rows past the end are never stored
+    }
+    bl = bf[min(tl * kTgTok + l32, S - 1)];  // gate of this lane's token column
+  };
+  fetch(tile);
   // staged tile -> per-row pass over the 32 tokens: lane handles 16-byte
   // chunk (lane & 15) of rows 4 it + lane / 16
   for (; tile < ntiles; tile += wstride) {
     bf16x8_t bk[8], bv[8];
+    uint4 krc[8];
+    float brc[8];
+    const float blc = bl;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      krc[it] = kr[it];
+      brc[it] = br[it];
+    }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       uint4 x = kb[kk];
@@ -297,14 +327,7 @@ token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __rest
     }
     const int s0 = tile * kTgTok;
     const int nxt = tile + wstride;
-    if (nxt < ntiles) {
-      const int sn = nxt * kTgTok + l32;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        kb[kk] = ld_row16(kf, sn, S, 16 * kk + 8 * half);
-        vb[kk] = ld_row16(vf, sn, S, 16 * kk + 8 * half);
-      }
-    }
+    if (nxt < ntiles) fetch(nxt);
     // ---- pass 1: Y1 = P k_hat, Y2 = G^T v
     {
       f32x16_t y1[4], y2[4];
@@ -312,17 +335,28 @@ token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __rest
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) y1[mt][j] = y2[mt][j] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
+      uint4 pa[2][4], ga[2][4];
+      auto frag1 = [&](int buf, int kk) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const int row = 32 * mt + l32;
           const int at = row * 16 + tswz(row, 2 * kk + half);
-          y1[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, Pl[at]), bk[kk],
-                                                           y1[mt], 0, 0, 0);
-          y2[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, GTl[at]), bv[kk],
-                                                           y2[mt], 0, 0, 0);
+          pa[buf][mt] = Pl[at];
+          ga[buf][mt] = GTl[at];
         }
+      };
+      frag1(0, 0);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        if (kk + 1 < 8) frag1((kk + 1) & 1, kk + 1);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          y1[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, pa[kk & 1][mt]),
+                                                           bk[kk], y1[mt], 0, 0, 0);
+          y2[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ga[kk & 1][mt]),
+                                                           bv[kk], y2[mt], 0, 0, 0);
+        }
+      }
       // accumulator (i, s): token s = l32, rows i = 32 mt + 8 jg + 4 half + (0..3)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -342,16 +376,16 @@ token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __rest
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll 2
+#pragma unroll
     for (int it = 0; it < 8; ++it) {
-      const int row = 4 * it + (lane >> 4);
-      const int ch = lane & 15;
+      const int row = 4 * it + rrow;
+      const int ch = rch;
       const int s = s0 + row;
       const bool on = s < S;
       const uint4 zc = zs[row * 16 + tswz(row, ch)];
       const uint4 wc = ws[row * 16 + tswz(row, ch)];
-      const uint4 kc = ld_row16(kf, s, S, 8 * ch);
-      const float bt = on ? bf[s] : 0.f;
+      const uint4 kc = krc[it];
+      const float bt = brc[it];
       const uint32_t zw[4] = {zc.x, zc.y, zc.z, zc.w};
       const uint32_t ww[4] = {wc.x, wc.y, wc.z, wc.w};
       const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
@@ -373,8 +407,13 @@ token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __rest
         out[q] = pack_bf16x2(bt * m0 * z0, bt * m1 * z1);
       }
       part = sum_row16(part);  // the 16 lanes of this token row
-      if (on && dkf) *(uint4*)(dkf + (int64_t)s * D + 8 * ch) = make_uint4(out[0], out[1], out[2], out[3]);
-      if (on && dbf && ch == 0) dbf[s] = part;
+      // Every store is issued; rows past the end go to a scratch area (a store
+      // under a per-lane condition would make the compiler drain the prefetch)
+      uint8_t* tr = trash + 16 * lane;
+      if (dkf)
+        *(uint4*)(on ? (uint8_t*)(dkf + (int64_t)s * D + 8 * ch) : tr) =
+            make_uint4(out[0], out[1], out[2], out[3]);
+      if (dbf) *(float*)(on ? (uint8_t*)(dbf + s) : tr) = part;  // the row's 16 lanes agree
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -385,16 +424,24 @@ token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __rest
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) y3[mt][j] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
+      uint4 gf[2][4];
+      auto frag3 = [&](int buf, int kk) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const int row = 32 * mt + l32;
-          y3[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, Gl[row * 16 + tswz(row, 2 * kk + half)]), bk[kk], y3[mt], 0, 0, 0);
+          gf[buf][mt] = Gl[row * 16 + tswz(row, 2 * kk + half)];
         }
-      const int sl = s0 + l32;
-      const float bt = (sl < S ? bf[sl] : 0.f) * ck;
+      };
+      frag3(0, 0);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        if (kk + 1 < 8) frag3((kk + 1) & 1, kk + 1);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          y3[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, gf[kk & 1][mt]),
+                                                           bk[kk], y3[mt], 0, 0, 0);
+      }
+      const float bt = blc * ck;  // columns past the end are never stored
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -410,12 +457,96 @@ token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __rest
       for (int it = 0; it < 8; ++it) {
         const int row = 4 * it + (lane >> 4);
         const int ch = lane & 15;
-        if (s0 + row < S) *(uint4*)(dvf + (int64_t)(s0 + row) * D + 8 * ch) = zs[row * 16 + tswz(row, ch)];
+        const bool on = s0 + row < S;
+        *(uint4*)(on ? (uint8_t*)(dvf + (int64_t)(s0 + row) * D + 8 * ch) : trash + 16 * lane) =
+            zs[row * 16 + tswz(row, ch)];
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
+}
+
+// MFMA path of the per-frame gradients (D = 128): dM = S_prev^T G on fp32
+// MFMA (v_mfma_f32_32x32x2_f32: exact fp32 products), wave w owns rows
+// 32w .. 32w + 31 of dM as four 32 x 32 tiles. The A operand of lane l is
+// S_prev[i][32w + l % 32] with i = 2 ks + l / 32, the B operand
+// G[i][32 nb + l % 32]; both are conflict-free row reads of the staged
+// matrices.
+__global__ void __launch_bounds__(256, 1)
+frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__ s0,
+                     const float* __restrict__ gbuf, const float* __restrict__ ginit,
+                     const float* __restrict__ terms, int a_granule_bf16,
+                     const float* __restrict__ gamma, float* __restrict__ P,
+                     float* __restrict__ dgamma, int T) {
+  constexpr int D = 128;
+  constexpr int LDT = D + 4;  // padded row for the transposed read of dM
+  constexpr int64_t DD = (int64_t)D * D;
+  __shared__ float Ss[D][LDT];
+  __shared__ float Gs[D][D];
+  __shared__ float red[4];
+  const int64_t f = blockIdx.x;
+  const int64_t bh = f / T;
+  const int t = (int)(f % T);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hk = lane >> 5;
+  const float* Sp = t > 0 ? states + (f - 1) * DD : (s0 ? s0 + bh * DD : nullptr);
+  const float* Gt = t == T - 1 ? ginit + bh * DD : gbuf + (f + 1) * DD;
+  for (int e = tid; e < D * D / 4; e += 256) {
+    const int r = e / (D / 4), c4 = 4 * (e % (D / 4));
+    const float4 sv = Sp ? *(const float4*)(Sp + (int64_t)r * D + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    Ss[r][c4] = sv.x; Ss[r][c4 + 1] = sv.y; Ss[r][c4 + 2] = sv.z; Ss[r][c4 + 3] = sv.w;
+    *(float4*)&Gs[r][c4] = *(const float4*)(Gt + (int64_t)r * D + c4);
+  }
+  __syncthreads();
+  f32x16_t acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[nb][j] = 0.f;
+#pragma unroll 4
+  for (int ks = 0; ks < D / 2; ++ks) {
+    const int i = 2 * ks + hk;
+    const float a = Ss[i][32 * wave + l32];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Gs[i][32 * nb + l32], acc[nb], 0, 0, 0);
+  }
+  // acc[nb][j] = dM[a][b], a = 32 wave + 8 (j / 4) + 4 hk + j % 4, b = 32 nb + l32
+  const float* At = terms + f * 2 * DD;
+  float part = 0.f;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int a = 32 * wave + 8 * (j >> 2) + 4 * hk + (j & 3), b = 32 * nb + l32;
+      const float av = a_granule_bf16
+                           ? bf16_to_f32(((const uint16_t*)At)[(int64_t)a_granule(b, a >> 3) * 8 + (a & 7)])
+                           : At[(int64_t)a * D + b];
+      part += acc[nb][j] * ((a == b ? 1.f : 0.f) - av);
+    }
+  part = sum_lane_xor32(sum_lane_xor16(sum_row16(part)));
+  if (lane == 0) red[wave] = part;
+  __syncthreads();  // every wave is done reading Ss
+  const float g = gamma[f];
+  if (tid == 0 && dgamma != nullptr) dgamma[f] = red[0] + red[1] + red[2] + red[3];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      Ss[32 * wave + 8 * (j >> 2) + 4 * hk + (j & 3)][32 * nb + l32] = acc[nb][j];
+  __syncthreads();
+  float* Pf = P + f * DD;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int a = 32 * wave + 8 * (j >> 2) + 4 * hk + (j & 3), b = 32 * nb + l32;
+      Pf[(int64_t)a * D + b] = -g * (acc[nb][j] + Ss[b][a]);
+    }
 }
 
 int grid_cap(int64_t n) {
@@ -441,6 +572,11 @@ hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* 
   if (sh.FH() == 0) return hipSuccess;
   dim3 grid((unsigned)sh.FH());
   const int ag = a_granule_bf16 ? 1 : 0;
+  if (sh.D == 128) {
+    frame_grad_mfma_d128<<<grid, 256, 0, st>>>(states, s0, gbuf, ginit, terms, ag, gamma, P, dgamma,
+                                               sh.T);
+    return hipGetLastError();
+  }
 #define GDN_FG(DV)                                                                              \
   frame_grad_kernel<DV><<<grid, 256, 0, st>>>(states, s0, gbuf, ginit, terms, ag, gamma, P, \
                                               dgamma, sh.T)
@@ -460,7 +596,7 @@ bool token_grad_uses_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
 hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, const float* beta,
                              const void* dout, const float* states, const float* gbuf,
                              const float* ginit, const float* P, void* dq, void* dk, void* dv,
-                             float* dbeta, hipStream_t st) {
+                             float* dbeta, void* trash, hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
   if (token_grad_uses_mfma(sh)) {
     // dq = states^T do: the readout with the state staged transposed
@@ -476,12 +612,15 @@ hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, cons
     dim3 grid((unsigned)(groups * kTgXcd * nb));
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
+    if (trash == nullptr) return hipErrorInvalidValue;
     if (sh.prepared)
       token_grad_mfma_bf16_d128<true><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P, (uint16_t*)dk,
-                                                            (uint16_t*)dv, dbeta, sh.S, sh.T, sh.FH(), nb, sh.c);
+                                                            (uint16_t*)dv, dbeta, (uint8_t*)trash, sh.S,
+                                                            sh.T, sh.FH(), nb, sh.c);
     else
       token_grad_mfma_bf16_d128<false><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P, (uint16_t*)dk,
-                                                             (uint16_t*)dv, dbeta, sh.S, sh.T, sh.FH(), nb, sh.c);
+                                                             (uint16_t*)dv, dbeta, (uint8_t*)trash, sh.S,
+                                                             sh.T, sh.FH(), nb, sh.c);
     return hipGetLastError();
   }
   const int tpw = 256 / sh.D;
