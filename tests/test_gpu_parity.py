@@ -495,6 +495,7 @@ BWD_CASES = {
     "bf16_D128_split_S2100": (gi.workload(2).with_shape(T=3, S=2100), True, False),
     "bf16_D64": (gi.workload(2).with_shape(D=64, T=5, S=130), True, False),
     "f32_D128_prepared": (gi.workload(1).with_shape(D=128, S=40, T=4), True, True),
+    "bf16_D128_prepared": (gi.workload(2).with_shape(H=2, T=4, S=170), True, True),
 }
 
 
@@ -523,8 +524,13 @@ def test_scan_bwd(name):
     x, d = _gen(w)
     if prepared:
         kh = orc.prepare_keys(x["k"]).astype(np.float32)
+        if w.io == "bf16":  # both sides take the bf16-rounded prepared keys
+            bits = gi.f32_to_bf16_bits(kh)
+            kh = gi.bf16_bits_to_f32(bits)
+            d["k"] = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+        else:
+            d["k"] = torch.from_numpy(kh).to(DEV)
         x["k"] = kh
-        d["k"] = torch.from_numpy(kh).to(DEV)
     do, do_d, s0, dsf = _bwd_inputs(w, x, d, extras)
     dev = lambda a: None if a is None else torch.from_numpy(a).to(DEV)
     say("scan_bwd", name, "forward")
