@@ -79,7 +79,7 @@ Layout layout(const Shape& sh, int P) {
 // Workspace of the backward pass: phase-1 terms (A), split partials, E_t,
 // the adjoint states G, the per-frame P_t, G_{T-1} per head and a ones gate.
 struct BwdLayout {
-  size_t terms = 0, partial = 0, E = 0, G = 0, P = 0, ginit = 0, ones = 0, trash = 0;
+  size_t terms = 0, partial = 0, E = 0, G = 0, P = 0, ginit = 0, ones = 0;
   size_t total = 0;
   int n_split = 1;
 };
@@ -102,7 +102,6 @@ BwdLayout bwd_layout(const Shape& sh) {
   L.P = take(FH * DD);
   L.ginit = take((size_t)sh.BH() * DD);
   L.ones = take(FH * (size_t)sh.S * sizeof(float));
-  L.trash = take(1024);
   L.total = off;
   return L;
 }
@@ -579,8 +578,7 @@ gdn_status gdn_scan_bwd(const gdn_desc* desc, const void* q, const void* k, cons
   }
   GDN_HIP(gdn::launch_frame_grad(sh, states, s0, G, ginit, terms, mfma, gamma, P, dgamma, st));
   if (dq || dk || dv || dbeta)
-    GDN_HIP(gdn::launch_token_grad(sh, k, v, beta, d_o, states, G, ginit, P, dq, dk, dv, dbeta,
-                                   at<void>(ws, L.trash), st));
+    GDN_HIP(gdn::launch_token_grad(sh, k, v, beta, d_o, states, G, ginit, P, dq, dk, dv, dbeta, st));
   return GDN_OK;
 }
 

@@ -232,8 +232,7 @@ hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* 
 hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, const float* beta,
                              const void* dout, const float* states, const float* gbuf,
                              const float* ginit, const float* P, void* dq, void* dk, void* dv,
-                             float* dbeta, void* trash, hipStream_t st);
-// trash: >= 1 KB of device scratch that absorbs the stores of rows past the end
+                             float* dbeta, hipStream_t st);
 bool token_grad_uses_mfma(const Shape& sh);
 
 }  // namespace gdn

@@ -214,13 +214,16 @@ __device__ __forceinline__ float sum_row16(float x) {
   return x;
 }
 
-template <bool kPrepared>
+// kAll: dk, dv and dbeta are all wanted, so no store sits behind a pointer
+// test (on a path without stores the prefetch loads would be the youngest
+// memory operations, and the loop's back edge would wait for all of them).
+template <bool kPrepared, bool kAll>
 __global__ void __launch_bounds__(256, 1)
 token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                           const float* __restrict__ beta, const float* __restrict__ gbuf,
                           const float* __restrict__ ginit, const float* __restrict__ P,
                           uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-                          float* __restrict__ dbeta, uint8_t* __restrict__ trash, int S, int T,
+                          float* __restrict__ dbeta, int S, int T,
                           int64_t FH, int nb, float c) {
   constexpr int D = 128;
   constexpr int64_t DD = (int64_t)D * D;
@@ -381,7 +384,6 @@ token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __rest
       const int row = 4 * it + rrow;
       const int ch = rch;
       const int s = s0 + row;
-      const bool on = s < S;
       const uint4 zc = zs[row * 16 + tswz(row, ch)];
       const uint4 wc = ws[row * 16 + tswz(row, ch)];
       const uint4 kc = krc[it];
@@ -407,18 +409,18 @@ token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __rest
         out[q] = pack_bf16x2(bt * m0 * z0, bt * m1 * z1);
       }
       part = sum_row16(part);  // the 16 lanes of this token row
-      // Every store is issued; rows past the end go to a scratch area (a store
-      // under a per-lane condition would make the compiler drain the prefetch)
-      uint8_t* tr = trash + 16 * lane;
-      if (dkf)
-        *(uint4*)(on ? (uint8_t*)(dkf + (int64_t)s * D + 8 * ch) : tr) =
-            make_uint4(out[0], out[1], out[2], out[3]);
-      if (dbf) *(float*)(on ? (uint8_t*)(dbf + s) : tr) = part;  // the row's 16 lanes agree
+      // Every store is issued (a store under a per-lane condition makes the
+      // compiler drain the prefetch). A row past the end was computed from
+      // clamped copies of row S - 1, so it holds exactly row S - 1's values
+      // and is written there again.
+      const int sc = min(s, S - 1);
+      if (kAll || dkf) *(uint4*)(dkf + (int64_t)sc * D + 8 * ch) = make_uint4(out[0], out[1], out[2], out[3]);
+      if (kAll || dbf) dbf[sc] = part;  // the row's 16 lanes agree
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // ---- pass 2: Y3 = G k_hat, dv = beta Y3
-    if (dvf) {
+    if (kAll || dvf) {
       f32x16_t y3[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -457,9 +459,8 @@ token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __rest
       for (int it = 0; it < 8; ++it) {
         const int row = 4 * it + (lane >> 4);
         const int ch = lane & 15;
-        const bool on = s0 + row < S;
-        *(uint4*)(on ? (uint8_t*)(dvf + (int64_t)(s0 + row) * D + 8 * ch) : trash + 16 * lane) =
-            zs[row * 16 + tswz(row, ch)];
+        const int sc = min(s0 + row, S - 1);  // see the dk store
+        *(uint4*)(dvf + (int64_t)sc * D + 8 * ch) = zs[row * 16 + tswz(row, ch)];
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -596,7 +597,7 @@ bool token_grad_uses_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
 hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, const float* beta,
                              const void* dout, const float* states, const float* gbuf,
                              const float* ginit, const float* P, void* dq, void* dk, void* dv,
-                             float* dbeta, void* trash, hipStream_t st) {
+                             float* dbeta, hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
   if (token_grad_uses_mfma(sh)) {
     // dq = states^T do: the readout with the state staged transposed
@@ -612,15 +613,19 @@ hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, cons
     dim3 grid((unsigned)(groups * kTgXcd * nb));
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
-    if (trash == nullptr) return hipErrorInvalidValue;
-    if (sh.prepared)
-      token_grad_mfma_bf16_d128<true><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P, (uint16_t*)dk,
-                                                            (uint16_t*)dv, dbeta, (uint8_t*)trash, sh.S,
-                                                            sh.T, sh.FH(), nb, sh.c);
-    else
-      token_grad_mfma_bf16_d128<false><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P, (uint16_t*)dk,
-                                                             (uint16_t*)dv, dbeta, (uint8_t*)trash, sh.S,
-                                                             sh.T, sh.FH(), nb, sh.c);
+    const bool all = dk && dv && dbeta;
+#define GDN_TOKEN_GRAD(PR, ALL)                                                                \
+  token_grad_mfma_bf16_d128<PR, ALL><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P,       \
+                                                           (uint16_t*)dk, (uint16_t*)dv, dbeta, \
+                                                           sh.S, sh.T, sh.FH(), nb, sh.c)
+    if (sh.prepared) {
+      if (all) GDN_TOKEN_GRAD(true, true);
+      else GDN_TOKEN_GRAD(true, false);
+    } else {
+      if (all) GDN_TOKEN_GRAD(false, true);
+      else GDN_TOKEN_GRAD(false, false);
+    }
+#undef GDN_TOKEN_GRAD
     return hipGetLastError();
   }
   const int tpw = 256 / sh.D;

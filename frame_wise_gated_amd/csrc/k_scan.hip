@@ -23,6 +23,9 @@
 #ifndef GDN_SCAN_MT
 #define GDN_SCAN_MT 2
 #endif
+#ifndef GDN_SCAN_MT_COMPOSE
+#define GDN_SCAN_MT_COMPOSE GDN_SCAN_MT
+#endif
 #ifndef GDN_SCAN_F
 #define GDN_SCAN_F 2
 #endif
@@ -123,11 +126,19 @@ template <int D>
 constexpr int combine_rows() { return (256 / D) > 4 ? (256 / D) : 4; }
 
 // combine: s_start[q+1] = s_start[q] C_q + H_q, for one head's CR-row block.
+// Thread (n, ig) forms column n of its rows. Column n of C_q is read from
+// global memory (L2) in blocks of kCJ entries whose loads are all issued before
+// the first use, so a step waits for D / kCJ round trips rather than one per
+// few entries; the state rows come from LDS.
+#ifndef GDN_COMBINE_J
+#define GDN_COMBINE_J 64
+#endif
 template <int D>
 __global__ void __launch_bounds__(256) combine_rows_kernel(CombineParams p) {
   constexpr int CR = combine_rows<D>();  // state rows per workgroup
   constexpr int RG = 256 / D;
   constexpr int RPT = CR / RG;
+  constexpr int kCJ = D < GDN_COMBINE_J ? D : GDN_COMBINE_J;
   __shared__ float Xs[2][CR][D];
   constexpr int nrb = D / CR;
   int64_t bh;
@@ -158,18 +169,18 @@ __global__ void __launch_bounds__(256) combine_rows_kernel(CombineParams p) {
     if (q == p.P - 1) break;
     float acc[RPT];
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) acc[r] = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < D; ++j) {
-      const float cv = Cq[(int64_t)j * D + n];
+    for (int r = 0; r < RPT; ++r) acc[r] = Hq[(int64_t)(row0 + ig + RG * r) * D + n];
+    for (int j0 = 0; j0 < D; j0 += kCJ) {
+      float cv[kCJ];
 #pragma unroll
-      for (int r = 0; r < RPT; ++r) acc[r] = fmaf(Xs[cur][ig + RG * r][j], cv, acc[r]);
+      for (int jj = 0; jj < kCJ; ++jj) cv[jj] = Cq[(int64_t)(j0 + jj) * D + n];
+#pragma unroll
+      for (int jj = 0; jj < kCJ; ++jj)
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) acc[r] = fmaf(Xs[cur][ig + RG * r][j0 + jj], cv[jj], acc[r]);
     }
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      const int i = ig + RG * r;
-      Xs[cur ^ 1][i][n] = acc[r] + Hq[(int64_t)(row0 + i) * D + n];
-    }
+    for (int r = 0; r < RPT; ++r) Xs[cur ^ 1][ig + RG * r][n] = acc[r];
     cur ^= 1;
     __syncthreads();
   }
@@ -404,9 +415,15 @@ hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st) {
   q.njobs = sh.BH() * p.nchunk;
   if (q.njobs == 0) return hipSuccess;
   if (scan_uses_mfma(sh)) {
-    constexpr int MT = GDN_SCAN_MT;
-    const int64_t blocks = xcd_grid(q.njobs, (int)(rows_total / (16 * MT)));
-    scan_mfma_d128<MT, GDN_SCAN_F><<<dim3((unsigned)blocks), 256, 0, st>>>(q);
+    if (p.mode == SCAN_COMPOSE) {
+      constexpr int MT = GDN_SCAN_MT_COMPOSE;
+      const int64_t blocks = xcd_grid(q.njobs, (int)(rows_total / (16 * MT)));
+      scan_mfma_d128<MT, GDN_SCAN_F><<<dim3((unsigned)blocks), 256, 0, st>>>(q);
+    } else {
+      constexpr int MT = GDN_SCAN_MT;
+      const int64_t blocks = xcd_grid(q.njobs, (int)(rows_total / (16 * MT)));
+      scan_mfma_d128<MT, GDN_SCAN_F><<<dim3((unsigned)blocks), 256, 0, st>>>(q);
+    }
     return hipGetLastError();
   }
   dim3 grid((unsigned)xcd_grid(q.njobs, (int)(rows_total / kR)));

@@ -38,13 +38,15 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 #define GDN_LDS __attribute__((address_space(3)))
 #define GDN_GLB __attribute__((address_space(1)))
 
+// Three stages (two in flight while one is consumed) keep two workgroups per
+// CU within the LDS (2 x 65920 B); on MI355X phase 1 ran 8 % faster than with
+// two stages, and four stages (one workgroup per CU) were no faster than two.
 #ifndef GDN_TERMS_NST
-#define GDN_TERMS_NST 2
+#define GDN_TERMS_NST 3
 #endif
 constexpr int kTsd = 32;                        // tokens per stage
-constexpr int kNst = GDN_TERMS_NST;             // stages in the ring (power of two)
+constexpr int kNst = GDN_TERMS_NST;             // stages in the ring
 constexpr int kKvBytes = kTsd * 256;            // one stage of k (or v): 32 rows x 256 B
-constexpr int kStageBytes = 2 * kKvBytes + 4 * kTsd;
 
 // LDS layout of a stage tensor: token block b (tokens 4b..4b+3) occupies
 // bytes [1024 b, 1024 b + 1024), chunk-major inside: 16-byte chunk c (features
@@ -95,22 +97,27 @@ __device__ __forceinline__ uint4 tr_frag(const uint8_t* base, int lb, int k0, in
   return make_uint4(a.x, a.y, b.x, b.y);
 }
 
-#if GDN_TERMS_NST <= 4
+#if GDN_TERMS_NST <= 3
 #define GDN_TERMS_WAVES_PER_EU 4  // two 8-wave workgroups per CU: at most 128 VGPRs
 #else
 #define GDN_TERMS_WAVES_PER_EU 2  // one workgroup per CU (its ring fills the LDS)
 #endif
-template <bool kScanLayout, bool kPrepared, bool kNorm>
+// kAOnly: only A_t is wanted (U_t is not written), so v is never read: the
+// copies move k and the gates only and the U waves skip the products.
+template <bool kScanLayout, bool kPrepared, bool kNorm, bool kAOnly>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(GDN_TERMS_WAVES_PER_EU, GDN_TERMS_WAVES_PER_EU)))
 terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     const float* __restrict__ beta, int S, int n_split, float c,
                     TermsOut out) {
   constexpr int D = 128;
-  static_assert((kNst & (kNst - 1)) == 0, "ring depth is a power of two");
   // ring slot: k block, v block, then the stage's 32 gates; wbuf[st % 2]
   // holds the second operand bf16(beta . ReLU(k)) of stage st
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kNst][kStageBytes];
+  // Without v a slot is half as large, and the same LDS holds twice the stages.
+  constexpr int kNs = kAOnly ? 2 * kNst : kNst;
+  constexpr int kGateOff = (kAOnly ? 1 : 2) * kKvBytes;
+  constexpr int kSlot = kGateOff + 4 * kTsd;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kNs][kSlot];
   __shared__ __attribute__((aligned(16))) uint8_t wbuf[2][kKvBytes];
 
   const int64_t fh = blockIdx.x / n_split;
@@ -127,19 +134,21 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   const float* bf = beta + fh * (int64_t)S;
 
   // DMA of stage `st` into its ring slot: wave w copies tokens 4w..4w+3 of
-  // k and of v (one 1 KB instruction each) and their 4 gates. Lane L of a
+  // k and of v (one 1 KB instruction each; k only when kAOnly) and their 4
+  // gates. Lane L of a
   // copy instruction fills LDS slot L of its block: chunk L/4 of token
   // 4w + L%4. Tokens past the end are clamped to the last token (valid
   // memory); their gate is zeroed by the transform pass.
   const int dtok = 4 * wave + (lane & 3);            // token within the stage
   const int dchunk = lane >> 2;
+  constexpr int kOps = kAOnly ? 2 : 3;  // copy instructions per wave and stage
   auto issue = [&](int st) {
-    uint8_t* slot = ring[st & (kNst - 1)];
+    uint8_t* slot = ring[st % kNs];
     const int t = min(st * kTsd + dtok, S - 1);
     const int64_t off = (int64_t)t * D + 8 * dchunk;
     dma16(kf + off, slot + 1024 * wave);
-    dma16(vf + off, slot + kKvBytes + 1024 * wave);
-    dma4(bf + t, slot + 2 * kKvBytes + 16 * wave, lane < 4);
+    if (!kAOnly) dma16(vf + off, slot + kKvBytes + 1024 * wave);
+    dma4(bf + t, slot + kGateOff + 16 * wave, lane < 4);
   };
   const int lb = tr_lane_base(lane);
 
@@ -151,8 +160,8 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   // (the second operand of every row).
   const int ttok = 4 * (tid >> 6) + (tid & 3);       // == dtok
   auto transform = [&](int st) {
-    uint8_t* Ks = ring[st & (kNst - 1)];
-    const float* gates = (const float*)(Ks + 2 * kKvBytes);
+    uint8_t* Ks = ring[st % kNs];
+    const float* gates = (const float*)(Ks + kGateOff);
     uint4 x = *(const uint4*)(Ks + 16 * tid);
     const float b = (st * kTsd + ttok < S) ? gates[ttok] : 0.f;
     if (kNorm && !kPrepared) {
@@ -204,7 +213,7 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
     for (int q = 0; q < 16; ++q) acc[mt][q] = 0.f;
 
   auto compute = [&](int st) {
-    const uint8_t* Ks = ring[st & (kNst - 1)];
+    const uint8_t* Ks = ring[st % kNs];
 #pragma unroll
     for (int kk = 0; kk < kTsd / 16; ++kk) {
       const int k0 = 16 * kk;
@@ -220,23 +229,23 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
     }
   };
 
-  // Pipeline: kNst - 1 stages in flight, one barrier per stage. Each step
+  // Pipeline: kNs - 1 stages in flight, one barrier per stage. Each step
   // waits for this wave's copies of stage st (and its own LDS reads of the
   // step before), transforms its share of stage st, waits for those LDS
   // writes, and meets every other wave: then all of stage st is transformed,
   // and every wave has finished consuming stage st - 1, so its ring slot can
-  // be refilled with stage st + kNst - 1 (past the end the copy re-reads the
+  // be refilled with stage st + kNs - 1 (past the end the copy re-reads the
   // last token: harmless) and wbuf[(st + 1) % 2] rewritten in the next step.
   // Then the wave consumes stage st.
 #pragma unroll
-  for (int i = 0; i < kNst - 1; ++i) issue(st_begin + i);
+  for (int i = 0; i < kNs - 1; ++i) issue(st_begin + i);
   for (int st = st_begin; st < st_end; ++st) {
-    wait_vmcnt_lgkm0<(kNst - 2) * 3>();
+    wait_vmcnt_lgkm0<(kNs - 2) * kOps>();
     transform(st);
-    wait_vmcnt_lgkm0<(kNst - 2) * 3>();  // lgkmcnt(0): this wave's transform writes are done
+    wait_vmcnt_lgkm0<(kNs - 2) * kOps>();  // lgkmcnt(0): this wave's transform writes are done
     bare_barrier();
-    issue(st + kNst - 1);
-    compute(st);
+    issue(st + kNs - 1);
+    if (!kAOnly || rowsK) compute(st);
   }
   wait_vmcnt_lgkm0<0>();  // no copy may still be landing in LDS when the workgroup retires
 
@@ -247,7 +256,7 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   // threads copy the block out with 16-byte stores. Scattered 8-byte stores
   // straight from the MFMA accumulators cost phase 1 about a seventh of its
   // time on MI355X.
-  static_assert(kNst * kStageBytes >= 32768, "epilogue staging needs 32 KB of ring");
+  static_assert(kNs * kSlot >= 32768, "epilogue staging needs 32 KB of ring");
   uint8_t* const stage = &ring[0][0];
   bare_barrier();  // every wave has finished reading the ring
   const float scale = rowsK ? c * c : c;
@@ -322,7 +331,7 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
       }
     }
   }
-  if (out.outU != nullptr) {
+  if (!kAOnly && out.outU != nullptr) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       if (!rowsK) put_rows(hh, kScanLayout);
@@ -530,16 +539,19 @@ hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const flo
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
     const bool norm = sh.qk_norm && !sh.prepared;  // prepared keys are used as given
-#define GDN_TERMS_DMA(L, P, N) \
-  terms_dma_bf16_d128<L, P, N><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out)
-    if (scan_layout) {
-      if (sh.prepared) GDN_TERMS_DMA(true, true, false);
-      else if (norm) GDN_TERMS_DMA(true, false, true);
-      else GDN_TERMS_DMA(true, false, false);
+#define GDN_TERMS_DMA(L, P, N, AO) \
+  terms_dma_bf16_d128<L, P, N, AO><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out)
+    if (scan_layout && out.outU == nullptr && !norm) {  // A_t alone (the backward's recompute)
+      if (sh.prepared) GDN_TERMS_DMA(true, true, false, true);
+      else GDN_TERMS_DMA(true, false, false, true);
+    } else if (scan_layout) {
+      if (sh.prepared) GDN_TERMS_DMA(true, true, false, false);
+      else if (norm) GDN_TERMS_DMA(true, false, true, false);
+      else GDN_TERMS_DMA(true, false, false, false);
     } else {
-      if (sh.prepared) GDN_TERMS_DMA(false, true, false);
-      else if (norm) GDN_TERMS_DMA(false, false, true);
-      else GDN_TERMS_DMA(false, false, false);
+      if (sh.prepared) GDN_TERMS_DMA(false, true, false, false);
+      else if (norm) GDN_TERMS_DMA(false, false, true, false);
+      else GDN_TERMS_DMA(false, false, false, false);
     }
 #undef GDN_TERMS_DMA
     return hipGetLastError();
