@@ -538,15 +538,22 @@ gdn_status gdn_scan_bwd(const gdn_desc* desc, const void* q, const void* k, cons
   }
   // E_t = d_o_t^T q_t: the phase-1 contraction with q as prepared keys, d_o
   // as values and unit gates (the U half of its output)
+  bool fused_dq = false;
   {
-    GDN_HIP(gdn::launch_fill_f32(ones, sh.FH() * sh.S, 1.f, st));
     Shape shq = sh;
     shq.prepared = 1;
     shq.c = 1.f;
     gdn::TermsOut eout{nullptr, E, DD, 0};
-    if (L.n_split == 1) {
+    if (dq != nullptr && gdn::edq_fused(shq)) {
+      // one pass over q and d_o forms E_t and dq = S_t^T do together (one
+      // workgroup per frame-head, whatever split phase 1 uses)
+      GDN_HIP(gdn::launch_edq(shq, q, d_o, states, dq, E, st));
+      fused_dq = true;
+    } else if (L.n_split == 1) {
+      GDN_HIP(gdn::launch_fill_f32(ones, sh.FH() * sh.S, 1.f, st));
       GDN_HIP(gdn::launch_terms(shq, q, d_o, ones, 1, eout, mfma, st));
     } else {
+      GDN_HIP(gdn::launch_fill_f32(ones, sh.FH() * sh.S, 1.f, st));
       gdn::TermsOut po{part, part + DD, (int64_t)L.n_split * 2 * DD, 2 * DD};
       GDN_HIP(gdn::launch_terms(shq, q, d_o, ones, L.n_split, po, false, st));
       GDN_HIP(gdn::launch_reduce_partials(shq, part, L.n_split, eout, mfma, st));
@@ -578,7 +585,8 @@ gdn_status gdn_scan_bwd(const gdn_desc* desc, const void* q, const void* k, cons
   }
   GDN_HIP(gdn::launch_frame_grad(sh, states, s0, G, ginit, terms, mfma, gamma, P, dgamma, st));
   if (dq || dk || dv || dbeta)
-    GDN_HIP(gdn::launch_token_grad(sh, k, v, beta, d_o, states, G, ginit, P, dq, dk, dv, dbeta, st));
+    GDN_HIP(gdn::launch_token_grad(sh, k, v, beta, d_o, states, G, ginit, P, fused_dq ? nullptr : dq,
+                                   dk, dv, dbeta, st));
   return GDN_OK;
 }
 

@@ -211,6 +211,11 @@ int terms_split(const Shape& sh);
 // MFMA scan reads (MFMA path only); otherwise A and U are fp32 row-major.
 hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const float* beta,
                         int n_split, TermsOut out, bool scan_layout, hipStream_t st);
+// Backward pass: E_t = d_o_t^T q_t (into E, the scan's granule layout) and
+// dq = S_t^T do (bf16) in one pass over q and d_o (bf16, D = 128 only).
+bool edq_fused(const Shape& sh);
+hipError_t launch_edq(const Shape& sh, const void* q, const void* d_o, const float* states, void* dq,
+                      float* E, hipStream_t st);
 hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_split,
                                   TermsOut out, bool scan_layout, hipStream_t st);
 bool scan_uses_mfma(const Shape& sh);

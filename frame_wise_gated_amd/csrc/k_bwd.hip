@@ -496,11 +496,39 @@ frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__
   const int hk = lane >> 5;
   const float* Sp = t > 0 ? states + (f - 1) * DD : (s0 ? s0 + bh * DD : nullptr);
   const float* Gt = t == T - 1 ? ginit + bh * DD : gbuf + (f + 1) * DD;
-  for (int e = tid; e < D * D / 4; e += 256) {
-    const int r = e / (D / 4), c4 = 4 * (e % (D / 4));
-    const float4 sv = Sp ? *(const float4*)(Sp + (int64_t)r * D + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
-    Ss[r][c4] = sv.x; Ss[r][c4 + 1] = sv.y; Ss[r][c4 + 2] = sv.z; Ss[r][c4 + 3] = sv.w;
-    *(float4*)&Gs[r][c4] = *(const float4*)(Gt + (int64_t)r * D + c4);
+  const float* At = terms + f * 2 * DD;
+  // A_t entries of this lane's accumulators (see the epilogue), loaded before
+  // the products so that their latency is hidden: in the bf16 granule layout
+  // the four entries a = 32 w + 8 jg + 4 hk + 0..3 of column b = 32 nb + l32
+  // are one 8-byte piece of granule (b, 4 w + jg)
+  uint2 ag[4][4];
+  if (a_granule_bf16) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg)
+        ag[nb][jg] = *(const uint2*)((const uint16_t*)At +
+                                     (int64_t)a_granule(32 * nb + l32, 4 * wave + jg) * 8 + 4 * hk);
+  }
+  // S_prev and G_t into LDS: all 32 loads of a thread are issued before the
+  // first LDS write, so the staging costs one memory round trip
+  {
+    constexpr int kPer = D * D / 4 / 256;
+    float4 sv[kPer], gv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e / (D / 4), c4 = 4 * (e % (D / 4));
+      sv[u] = Sp ? *(const float4*)(Sp + (int64_t)r * D + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      gv[u] = *(const float4*)(Gt + (int64_t)r * D + c4);
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e / (D / 4), c4 = 4 * (e % (D / 4));
+      Ss[r][c4] = sv[u].x; Ss[r][c4 + 1] = sv[u].y; Ss[r][c4 + 2] = sv[u].z; Ss[r][c4 + 3] = sv[u].w;
+      *(float4*)&Gs[r][c4] = gv[u];
+    }
   }
   __syncthreads();
   f32x16_t acc[4];
@@ -517,16 +545,16 @@ frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__
       acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Gs[i][32 * nb + l32], acc[nb], 0, 0, 0);
   }
   // acc[nb][j] = dM[a][b], a = 32 wave + 8 (j / 4) + 4 hk + j % 4, b = 32 nb + l32
-  const float* At = terms + f * 2 * DD;
   float part = 0.f;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int a = 32 * wave + 8 * (j >> 2) + 4 * hk + (j & 3), b = 32 * nb + l32;
-      const float av = a_granule_bf16
-                           ? bf16_to_f32(((const uint16_t*)At)[(int64_t)a_granule(b, a >> 3) * 8 + (a & 7)])
-                           : At[(int64_t)a * D + b];
+      const uint2 w = ag[nb][j >> 2];
+      const uint32_t pair = (j & 2) ? w.y : w.x;
+      const float av = a_granule_bf16 ? bf16_to_f32((j & 1) ? (pair >> 16) : (pair & 0xFFFFu))
+                                      : At[(int64_t)a * D + b];
       part += acc[nb][j] * ((a == b ? 1.f : 0.f) - av);
     }
   part = sum_lane_xor32(sum_lane_xor16(sum_row16(part)));
@@ -592,6 +620,12 @@ hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* 
   return hipGetLastError();
 }
 
+// Workgroups per frame-head in the token-gradient kernel (each stages P_t and
+// G_t once).
+#ifndef GDN_TG_NB
+#define GDN_TG_NB 1
+#endif
+
 bool token_grad_uses_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
 
 hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, const float* beta,
@@ -608,7 +642,7 @@ hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, cons
     if (!dk && !dv && !dbeta) return hipSuccess;
     const int ntiles = (sh.S + kTgTok - 1) / kTgTok;
     int nb = (ntiles + kTgWaves - 1) / kTgWaves;
-    if (nb > 2) nb = 2;
+    if (nb > GDN_TG_NB) nb = GDN_TG_NB;
     const int64_t groups = (sh.FH() + kTgXcd - 1) / kTgXcd;
     dim3 grid((unsigned)(groups * kTgXcd * nb));
     const uint16_t* kk = (const uint16_t*)k;

@@ -104,21 +104,34 @@ __device__ __forceinline__ uint4 tr_frag(const uint8_t* base, int lb, int k0, in
 #endif
 // kAOnly: only A_t is wanted (U_t is not written), so v is never read: the
 // copies move k and the gates only and the U waves skip the products.
-template <bool kScanLayout, bool kPrepared, bool kNorm, bool kAOnly>
+//
+// kDq (backward pass): k holds the queries, v the output gradients d_o, and
+// the gates are 1, so U = d_o^T q is E_t; the A waves instead form the query
+// gradient dq_s = S_t^T do_s of every token of the stage from S_t^T staged
+// in LDS, so d_o is read once for both. Waves 4-7 issue all copies (their
+// vmcnt then counts copies only and the explicit waits stay exact) and
+// waves 0-3 issue all dq stores; wbuf (unused without gates) stages each
+// stage's dq tile so that the stores are whole 256-byte rows.
+#ifndef GDN_EDQ_NST
+#define GDN_EDQ_NST 6
+#endif
+template <bool kScanLayout, bool kPrepared, bool kNorm, bool kAOnly, bool kDq>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(GDN_TERMS_WAVES_PER_EU, GDN_TERMS_WAVES_PER_EU)))
 terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     const float* __restrict__ beta, int S, int n_split, float c,
-                    TermsOut out) {
+                    TermsOut out, const float* __restrict__ sdq, uint16_t* __restrict__ dq) {
   constexpr int D = 128;
+  static_assert(!kDq || (kScanLayout && kPrepared && !kNorm && !kAOnly), "dq mode of the E pass");
   // ring slot: k block, v block, then the stage's 32 gates; wbuf[st % 2]
   // holds the second operand bf16(beta . ReLU(k)) of stage st
   // Without v a slot is half as large, and the same LDS holds twice the stages.
-  constexpr int kNs = kAOnly ? 2 * kNst : kNst;
+  constexpr int kNs = kDq ? GDN_EDQ_NST : (kAOnly ? 2 * kNst : kNst);
   constexpr int kGateOff = (kAOnly ? 1 : 2) * kKvBytes;
   constexpr int kSlot = kGateOff + 4 * kTsd;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kNs][kSlot];
   __shared__ __attribute__((aligned(16))) uint8_t wbuf[2][kKvBytes];
+  __shared__ uint4 Sl[kDq ? D * 16 : 1];  // kDq: S_t^T in bf16, row i = column i of S_t
 
   const int64_t fh = blockIdx.x / n_split;
   const int split = blockIdx.x % n_split;
@@ -131,7 +144,22 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   const int lane = tid & 63;
   const uint16_t* kf = k + fh * (int64_t)S * D;
   const uint16_t* vf = v + fh * (int64_t)S * D;
-  const float* bf = beta + fh * (int64_t)S;
+  const float* bf = kDq ? nullptr : beta + fh * (int64_t)S;
+
+  // S_t^T -> LDS (kDq), 16-byte chunk ch of row i at chunk position ch ^ (i % 8)
+  if (kDq) {
+    const float* s1 = sdq + fh * D * D;
+#pragma unroll
+    for (int u = 0; u < D * 16 / 512; ++u) {
+      const int cidx = tid + 512 * u;
+      const int i = cidx >> 4, ch = cidx & 15;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = s1[(int64_t)(8 * ch + e) * D + i];
+      Sl[i * 16 + (ch ^ (i & 7))] = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                                pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+    }
+  }
 
   // DMA of stage `st` into its ring slot: wave w copies tokens 4w..4w+3 of
   // k and of v (one 1 KB instruction each; k only when kAOnly) and their 4
@@ -141,9 +169,22 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   // memory); their gate is zeroed by the transform pass.
   const int dtok = 4 * wave + (lane & 3);            // token within the stage
   const int dchunk = lane >> 2;
-  constexpr int kOps = kAOnly ? 2 : 3;  // copy instructions per wave and stage
+  constexpr int kOps = kDq ? 4 : (kAOnly ? 2 : 3);  // copy instructions per (copying) wave and stage
   auto issue = [&](int st) {
     uint8_t* slot = ring[st % kNs];
+    if (kDq) {  // waves 4-7: token blocks 2 (w - 4) and 2 (w - 4) + 1 of q and d_o
+      if (wave >= 4) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int blk = 2 * (wave - 4) + h;
+          const int t = min(st * kTsd + 4 * blk + (lane & 3), S - 1);
+          const int64_t off = (int64_t)t * D + 8 * dchunk;
+          dma16(kf + off, slot + 1024 * blk);
+          dma16(vf + off, slot + kKvBytes + 1024 * blk);
+        }
+      }
+      return;
+    }
     const int t = min(st * kTsd + dtok, S - 1);
     const int64_t off = (int64_t)t * D + 8 * dchunk;
     dma16(kf + off, slot + 1024 * wave);
@@ -220,12 +261,61 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
       uint4 fa[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) fa[mt] = tr_frag(Ks, lb, k0, aoff + 32 * mt);
-      const uint4 fb = tr_frag(wbuf[st & 1], lb, k0, 32 * nt);
+      // kDq: the gates are 1 and the keys prepared, so the second operand is q itself
+      const uint4 fb = tr_frag(kDq ? Ks : wbuf[st & 1], lb, k0, 32 * nt);
       const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, fb);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[mt]), bw,
                                                           acc[mt], 0, 0, 0);
+    }
+  };
+
+  // kDq, waves 0-3: the dq tile of stage st (its 32 tokens x features
+  // 32 w .. 32 w + 31) as (dq^T) = S_t^T . do^T on MFMA: the first operand is
+  // row i of S_t^T, the second token l32's d_o chunk, both 16-byte LDS reads.
+  // Lane (half, l32) ends with features 32 w + 8 jg + 4 half + 0..3 of token
+  // l32 and drops them, in bf16, into wbuf[st % 2] as row-major [token][feature]
+  // (16-byte chunk c of row r at position c ^ (r % 16)).
+  const int half = (lane >> 5) & 1;
+  const int l32 = lane & 31;
+  auto compute_dq = [&](int st) {
+    const uint8_t* Vs = ring[st % kNs] + kKvBytes;
+    const int i = 32 * wave + l32;
+    f32x16_t dacc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) dacc[q] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int ch = 2 * kk + half;
+      const uint4 fa = Sl[i * 16 + (ch ^ (i & 7))];
+      const uint4 fb = *(const uint4*)(Vs + 1024 * (l32 >> 2) + 64 * ch + 16 * (l32 & 3));
+      dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa),
+                                                     __builtin_bit_cast(bf16x8_t, fb), dacc, 0, 0, 0);
+    }
+    uint8_t* stg = wbuf[st & 1];
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      const int cc = 4 * wave + jg;
+      *(uint2*)(stg + l32 * 256 + ((cc ^ (l32 & 15)) << 4) + 8 * half) =
+          make_uint2(pack_bf16x2(dacc[4 * jg], dacc[4 * jg + 1]),
+                     pack_bf16x2(dacc[4 * jg + 2], dacc[4 * jg + 3]));
+    }
+  };
+  // Stores of the staged dq tile of stage st by waves 0-3 (two 16-byte row
+  // pieces per thread). Tokens past the end were computed from clamped copies
+  // of row S - 1, so they carry exactly row S - 1's values and are written
+  // there again.
+  uint16_t* dqf = kDq ? dq + fh * (int64_t)S * D : nullptr;
+  auto store_dq = [&](int st) {
+    const uint8_t* stg = wbuf[st & 1];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int idx = tid + 256 * r;
+      const int row = idx >> 4, ch = idx & 15;
+      const uint4 x = *(const uint4*)(stg + row * 256 + ((ch ^ (row & 15)) << 4));
+      const int sr = min(st * kTsd + row, S - 1);
+      *(uint4*)(dqf + (int64_t)sr * D + 8 * ch) = x;
     }
   };
 
@@ -239,7 +329,39 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   // Then the wave consumes stage st.
 #pragma unroll
   for (int i = 0; i < kNs - 1; ++i) issue(st_begin + i);
-  for (int st = st_begin; st < st_end; ++st) {
+  if (kDq) {
+    for (int st = st_begin; st < st_end; ++st) {
+      if (wave >= 4) {
+        wait_vmcnt_lgkm0<(kNs - 2) * kOps>();  // this wave's copies of stage st
+        if ((st + 1) * kTsd > S) {
+          // tokens past the end hold copies of row S - 1 and have no gate
+          // to silence them: zero their q bytes (this lane's own copies) so
+          // that they add nothing to E_t (their dq is row S - 1's, see below)
+          uint8_t* slot = ring[st % kNs];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int blk = 2 * (wave - 4) + h;
+            if (st * kTsd + 4 * blk + (lane & 3) >= S) *(uint4*)(slot + 1024 * blk + 16 * lane) = make_uint4(0, 0, 0, 0);
+          }
+          wait_vmcnt_lgkm0<63>();
+        }
+      } else {
+        wait_vmcnt_lgkm0<63>();  // lgkmcnt(0): staged dq is written
+      }
+      bare_barrier();
+      if (wave >= 4) {
+        issue(st + kNs - 1);
+        compute(st);
+      } else {
+        if (st > st_begin) store_dq(st - 1);
+        compute_dq(st);
+      }
+    }
+    wait_vmcnt_lgkm0<0>();
+    bare_barrier();
+    if (wave < 4 && st_end > st_begin) store_dq(st_end - 1);
+  }
+  for (int st = st_begin; !kDq && st < st_end; ++st) {
     wait_vmcnt_lgkm0<(kNs - 2) * kOps>();
     transform(st);
     wait_vmcnt_lgkm0<(kNs - 2) * kOps>();  // lgkmcnt(0): this wave's transform writes are done
@@ -539,8 +661,9 @@ hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const flo
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
     const bool norm = sh.qk_norm && !sh.prepared;  // prepared keys are used as given
-#define GDN_TERMS_DMA(L, P, N, AO) \
-  terms_dma_bf16_d128<L, P, N, AO><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, out)
+#define GDN_TERMS_DMA(L, P, N, AO)                                                           \
+  terms_dma_bf16_d128<L, P, N, AO, false><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, \
+                                                                out, nullptr, nullptr)
     if (scan_layout && out.outU == nullptr && !norm) {  // A_t alone (the backward's recompute)
       if (sh.prepared) GDN_TERMS_DMA(true, true, false, true);
       else GDN_TERMS_DMA(true, false, false, true);
@@ -558,6 +681,18 @@ hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const flo
   }
   if (sh.io == 1) return launch_generic<uint16_t>(sh, k, v, beta, n_split, out, st);
   return launch_generic<float>(sh, k, v, beta, n_split, out, st);
+}
+
+bool edq_fused(const Shape& sh) { return terms_use_mfma(sh); }
+
+hipError_t launch_edq(const Shape& sh, const void* q, const void* d_o, const float* states, void* dq,
+                      float* E, hipStream_t st) {
+  if (sh.FH() == 0) return hipSuccess;
+  if (!edq_fused(sh)) return hipErrorInvalidValue;
+  TermsOut out{nullptr, E, (int64_t)sh.D * sh.D, 0};
+  terms_dma_bf16_d128<true, true, false, false, true><<<dim3((unsigned)sh.FH()), 512, 0, st>>>(
+      (const uint16_t*)q, (const uint16_t*)d_o, nullptr, sh.S, 1, 1.f, out, states, (uint16_t*)dq);
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_split, TermsOut out,

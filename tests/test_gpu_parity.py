@@ -553,6 +553,66 @@ def test_scan_bwd(name):
             assert e <= tol(w), (n, e)
 
 
+def test_scan_bwd_fused_dq_pass_matches_separate_passes():
+    """With dq wanted, E_t and dq come from one pass over q and d_o; without
+    it, E_t comes from the plain phase-1 pass. Both form E_t from the same
+    bf16 operands in the same order, so every other gradient is bitwise
+    equal; dq itself is checked against the oracle in test_scan_bwd."""
+    w = gi.workload(2).with_shape(H=2, T=5, S=333)
+    x, d = _gen(w)
+    do, do_d, s0, dsf = _bwd_inputs(w, x, d, True)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    say("scan_bwd fused vs separate E")
+    fwd = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], s0=dev(s0), want_o=False)
+    full = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], do_d,
+                            s0=dev(s0), ds_final=dev(dsf))
+    part = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], do_d,
+                            s0=dev(s0), ds_final=dev(dsf),
+                            want=("dk", "dv", "dbeta", "dgamma", "ds0"))
+    torch.cuda.synchronize()
+    for n in ("dk", "dv", "dbeta", "dgamma", "ds0"):
+        assert torch.equal(full[n], part[n]), n
+    assert part["dq"] is None
+
+
+def test_scan_bwd_layer_60s_fused_dq():
+    """The 60 s 720p layer (T = 121, S = 3600, 16 heads) in the launch
+    configuration the benchmark times. The oracle is too slow at this size, so
+    the fused E_t + dq pass is checked by properties that hold at any size:
+    the other gradients are bitwise equal to those of the unfused E pass
+    (which the oracle checks at smaller sizes), and dq of sampled tokens
+    equals S_t^T do computed on the host from the same fp32 states."""
+    w = gi.workload(4)
+    say("generate", w.name)
+    x = gi.batch_inputs(w, 0, threads=16, keep_f32=False)
+    d = upload(x, w)
+    del x
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(1234)
+    do_d = torch.randn(d["q"].shape, generator=gen, device=DEV).to(torch.bfloat16)
+    say("forward", w.name)
+    fwd = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"],
+                           n_time_chunks=w.time_chunks, want_o=False)
+    say("backward with dq (fused E pass)", w.name)
+    full = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], do_d)
+    torch.cuda.synchronize()
+    say("backward without dq", w.name)
+    part = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], do_d,
+                            want=("dk", "dv", "dbeta", "dgamma", "ds0"))
+    torch.cuda.synchronize()
+    for n in ("dk", "dv", "dbeta", "dgamma", "ds0"):
+        assert torch.equal(full[n], part[n]), n
+    del part
+    rng = np.random.default_rng(77)
+    for _ in range(24):
+        h, t = int(rng.integers(w.H)), int(rng.integers(w.T))
+        s = int(rng.integers(w.S)) if rng.random() < 0.75 else w.S - 1 - int(rng.integers(20))
+        St = host(fwd["states"][0, h, t])
+        ref = St.T @ host(do_d[0, h, t, s])
+        e = rel_fro(host(full["dq"][0, h, t, s]), ref)
+        assert e <= tol(w), ((h, t, s), e)
+
+
 def test_scan_bwd_no_frames():
     w = gi.workload(1).with_shape(T=0)
     x, d = _gen(w)
