@@ -40,7 +40,9 @@ Readings where the pages are silent (each also listed in the design notes):
   scale, with epsilon 1e-6 and unit weight (the pages give neither).
 
 Every function here is pinned by tests under ``tests/`` (closed forms, brute
-force, exact rational arithmetic, invariants); none is "parity unpinned".
+force, exact rational arithmetic, invariants, and for the two backward
+functions central finite differences of the forward definitions); none is
+"parity unpinned".
 """
 
 from __future__ import annotations
@@ -63,6 +65,7 @@ __all__ = [
     "combine",
     "readout",
     "scan_fwd_bwd",
+    "scan_bidir_bwd",
 ]
 
 
@@ -356,3 +359,86 @@ def scan_fwd_bwd(q, k, v, beta, gamma, do, ds_final=None, s0=None, key_scale=Non
                 G = G @ transition(A, gamma[b, h, t]).T
             ds0[b, h] = G
     return {"dq": dq, "dk": dk, "dv": dv, "dbeta": dbeta, "dgamma": dgamma, "ds0": ds0}
+
+
+def scan_bidir_bwd(q, k, v, beta, gamma, chunk_len, do, ds_final=None, s0=None,
+                   key_scale=None, keys_prepared=False):
+    """Reverse-mode gradients of the chunk-causal bidirectional scan.
+
+    The scalar is L = sum_{t,s} <do_{t,s}, o_{t,s}> + <ds_final, S_{T-1}> with
+    o_{t,s} = (S_t + R_t) q_{t,s} (scan_bidir_chunked: the causal states S_t
+    and the reverse states R_t of the chunk holding t, [P3] method). The chain
+    rule runs through both recurrences of the definition:
+
+    * causal part, frames in reverse order (as in scan_fwd_bwd): G_t, the
+      gradient of L with respect to S_t, is E_t + G_{t+1} M_{t+1}^T (plus
+      ds_final at t = T-1), E_t = sum_s do_{t,s} q_{t,s}^T; S_t = S_{t-1} M_t
+      + U_t adds G_t to dU_t and S_{t-1}^T G_t to dM_t;
+    * reverse part, inside each chunk [a, e) in forward order: R_t feeds o_t
+      and R_{t-1} = R_t M_{t-1} + U_{t-1}, so its gradient is F_a = E_a and
+      F_t = E_t + F_{t-1} M_{t-1}^T; R_t = R_{t+1} M_t + U_t adds F_t to dU_t
+      and, when t + 1 < e, R_{t+1}^T F_t to dM_t (the chunk's last frame starts
+      from a zero state).
+
+    Then per frame and token exactly as in scan_fwd_bwd with dU_t in place of
+    G: dgamma_t = <dM_t, I - A_t>, dA_t = -gamma_t dM_t, dk_s = beta_s (dA +
+    dA^T) k_s + beta_s dU^T v_s, dbeta_s = k_s^T dA k_s + v_s^T dU k_s,
+    dv_s = beta_s dU k_s, and dq_{t,s} = (S_t + R_t)^T do_{t,s}. Raw keys pass
+    through the key scale and the ReLU. Returns the same dict as scan_fwd_bwd.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, H, T, S, D = k.shape
+    fwd = scan_fwd(None, k, v, beta, gamma, s0=s0, key_scale=key_scale,
+                   keys_prepared=keys_prepared, with_output=False)
+    rev = scan_reverse_chunked(k, v, beta, gamma, chunk_len, key_scale=key_scale,
+                               keys_prepared=keys_prepared)
+    out = {n: np.zeros_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dbeta", beta),
+                                              ("dgamma", gamma))}
+    out["ds0"] = np.zeros((B, H, D, D))
+    c = None
+    if not keys_prepared:
+        c = key_scale if (key_scale is not None and key_scale > 0) else default_key_scale(D, S)
+    for b in range(B):
+        for h in range(H):
+            kh = _keys(k[b, h], key_scale, keys_prepared)
+            St = fwd["states"][b, h]
+            Rt = rev[b, h]
+            sinit = np.zeros((D, D)) if s0 is None else np.asarray(s0[b, h], dtype=np.float64)
+            A = [frame_terms(kh[t], v[b, h, t], beta[b, h, t])[0] for t in range(T)]
+            M = [transition(A[t], gamma[b, h, t]) for t in range(T)]
+            E = [do[b, h, t].T @ q[b, h, t] for t in range(T)]
+            dU = [np.zeros((D, D)) for _ in range(T)]
+            dM = [np.zeros((D, D)) for _ in range(T)]
+            # causal part
+            G = np.zeros((D, D)) if ds_final is None else np.array(ds_final[b, h], dtype=np.float64)
+            for t in range(T - 1, -1, -1):
+                G = G + E[t]
+                Sp = St[t - 1] if t > 0 else sinit
+                dU[t] += G
+                dM[t] += Sp.T @ G
+                G = G @ M[t].T
+            out["ds0"][b, h] = G
+            # reverse part, chunk by chunk
+            for (a, e) in chunk_bounds(T, chunk_len):
+                F = np.zeros((D, D))
+                for t in range(a, e):
+                    F = E[t] if t == a else E[t] + F @ M[t - 1].T
+                    dU[t] += F
+                    if t + 1 < e:
+                        dM[t] += Rt[t + 1].T @ F
+            for t in range(T):
+                out["dq"][b, h, t] = do[b, h, t] @ (St[t] + Rt[t])
+                out["dgamma"][b, h, t] = np.sum(dM[t] * (np.eye(D) - A[t]))
+                dA = -gamma[b, h, t] * dM[t]
+                kt, vt, bt = kh[t], v[b, h, t], beta[b, h, t]
+                dkh = bt[:, None] * (kt @ (dA + dA.T).T + vt @ dU[t])
+                out["dv"][b, h, t] = bt[:, None] * (kt @ dU[t].T)
+                out["dbeta"][b, h, t] = (np.einsum("si,ij,sj->s", kt, dA, kt)
+                                         + np.einsum("si,ij,sj->s", vt, dU[t], kt))
+                out["dk"][b, h, t] = dkh if keys_prepared else dkh * c * (k[b, h, t] > 0)
+    return out

@@ -560,6 +560,61 @@ def pin_backward_pure_decay(orc):
     _close(r["dk"], np.zeros_like(k), 0.0, "beta = 0: dk")
 
 
+def _loss_bidir(orc, q, k, v, b, g, s0, do, dsf, L):
+    r = orc.scan_bidir_chunked(q, k, v, b, g, L, s0=s0)
+    return float(np.sum(r["o"] * do) + np.sum(r["s_final"] * dsf))
+
+
+def pin_bidir_backward_finite_differences(orc):
+    """Every gradient of L = <do, o> + <ds_final, S_{T-1}> for the chunk-causal
+    bidirectional scan (o = (S_t + R_t) q) matches a central finite difference
+    of the forward oracle, element by element. T = 5 with chunk length 2 has
+    two full chunks and a one-frame chunk."""
+    rng = np.random.default_rng(33)
+    B, H, T, S, D, L = 1, 1, 5, 3, 3, 2
+    q = rng.standard_normal((B, H, T, S, D))
+    k = rng.standard_normal((B, H, T, S, D))
+    k = np.where(np.abs(k) < 0.1, 0.1 * np.sign(k + 1e-30) + k, k)
+    v = rng.standard_normal((B, H, T, S, D))
+    b = rng.uniform(0.1, 1.0, (B, H, T, S))
+    g = rng.uniform(0.8, 1.0, (B, H, T))
+    s0 = rng.standard_normal((B, H, D, D))
+    do = rng.standard_normal((B, H, T, S, D))
+    dsf = rng.standard_normal((B, H, D, D))
+    grads = orc.scan_bidir_bwd(q, k, v, b, g, L, do, ds_final=dsf, s0=s0)
+    args = {"q": q, "k": k, "v": v, "beta": b, "gamma": g, "s0": s0}
+    names = {"q": "dq", "k": "dk", "v": "dv", "beta": "dbeta", "gamma": "dgamma", "s0": "ds0"}
+    h = 1e-6
+    for name, arr in args.items():
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = _loss_bidir(orc, q, k, v, b, g, s0, do, dsf, L)
+            arr[idx] = old - h
+            lm = _loss_bidir(orc, q, k, v, b, g, s0, do, dsf, L)
+            arr[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        got = grads[names[name]]
+        err = np.max(np.abs(got - fd)) / max(1.0, np.max(np.abs(fd)))
+        assert err < 1e-6, f"bidirectional backward {names[name]}: finite-difference mismatch {err:.3e}"
+
+
+def pin_bidir_backward_without_readout(orc):
+    """With do = 0 only <ds_final, S_{T-1}> remains, which the reverse states
+    do not reach: the bidirectional gradients equal the causal ones."""
+    rng = np.random.default_rng(34)
+    q, k, v, b, g = _rand_case(rng, T=4, S=5, D=3)
+    B, H, T, S, D = q.shape
+    s0 = rng.standard_normal((B, H, D, D))
+    dsf = rng.standard_normal((B, H, D, D))
+    do = np.zeros(q.shape)
+    bi = orc.scan_bidir_bwd(q, k, v, b, g, 2, do, ds_final=dsf, s0=s0)
+    ca = orc.scan_fwd_bwd(q, k, v, b, g, do, ds_final=dsf, s0=s0)
+    for n in ("dq", "dk", "dv", "dbeta", "dgamma", "ds0"):
+        _close(bi[n], ca[n], 1e-12, f"do = 0: {n}")
+
+
 ALL_PINS = [
     pin_prepare_closed_form,
     pin_hand_example,
@@ -581,4 +636,6 @@ ALL_PINS = [
     pin_rmsnorm_in_the_scan,
     pin_backward_finite_differences,
     pin_backward_pure_decay,
+    pin_bidir_backward_finite_differences,
+    pin_bidir_backward_without_readout,
 ]

@@ -154,6 +154,65 @@ def _bwd_variant(kind):
     return f
 
 
+def _bidir_bwd_variant(kind):
+    """scan_bidir_bwd with one planted mistake."""
+    def f(q, k, v, beta, gamma, chunk_len, do, ds_final=None, s0=None, key_scale=None,
+          keys_prepared=False):
+        q, k, v, beta, gamma, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, beta, gamma, do))
+        B, H, T, S, D = k.shape
+        fwd = orc.scan_fwd(None, k, v, beta, gamma, s0=s0, key_scale=key_scale,
+                           keys_prepared=keys_prepared, with_output=False)
+        rev = orc.scan_reverse_chunked(k, v, beta, gamma, chunk_len, key_scale=key_scale,
+                                       keys_prepared=keys_prepared)
+        out = {n: np.zeros_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dbeta", beta),
+                                                  ("dgamma", gamma))}
+        out["ds0"] = np.zeros((B, H, D, D))
+        c = orc.default_key_scale(D, S)
+        for b in range(B):
+            for h in range(H):
+                kh = orc._keys(k[b, h], key_scale, keys_prepared)
+                St, Rt = fwd["states"][b, h], rev[b, h]
+                sinit = np.zeros((D, D)) if s0 is None else np.asarray(s0[b, h], dtype=np.float64)
+                A = [orc.frame_terms(kh[t], v[b, h, t], beta[b, h, t])[0] for t in range(T)]
+                M = [orc.transition(A[t], gamma[b, h, t]) for t in range(T)]
+                E = [do[b, h, t].T @ q[b, h, t] for t in range(T)]
+                dU = [np.zeros((D, D)) for _ in range(T)]
+                dM = [np.zeros((D, D)) for _ in range(T)]
+                G = np.zeros((D, D)) if ds_final is None else np.array(ds_final[b, h], dtype=np.float64)
+                for t in range(T - 1, -1, -1):
+                    G = G + E[t]
+                    dU[t] += G
+                    dM[t] += (St[t - 1] if t > 0 else sinit).T @ G
+                    G = G @ M[t].T
+                out["ds0"][b, h] = G
+                F = np.zeros((D, D))
+                for (a, e) in orc.chunk_bounds(T, chunk_len):
+                    for t in range(a, e):
+                        if t == a and kind != "F_not_reset":
+                            F = E[t]
+                        elif t == 0:
+                            F = E[t]
+                        else:
+                            F = E[t] + F @ M[t if kind == "F_same_frame_M" else t - 1].T
+                        if kind != "dU_no_F":
+                            dU[t] += F
+                        if t + 1 < e and kind != "dM_no_R_term":
+                            dM[t] += Rt[t + 1].T @ F
+                for t in range(T):
+                    Sq = St[t] if kind == "dq_causal_only" else St[t] + Rt[t]
+                    out["dq"][b, h, t] = do[b, h, t] @ Sq
+                    out["dgamma"][b, h, t] = np.sum(dM[t] * (np.eye(D) - A[t]))
+                    dA = -gamma[b, h, t] * dM[t]
+                    kt, vt, bt = kh[t], v[b, h, t], beta[b, h, t]
+                    dkh = bt[:, None] * (kt @ (dA + dA.T).T + vt @ dU[t])
+                    out["dv"][b, h, t] = bt[:, None] * (kt @ dU[t].T)
+                    out["dbeta"][b, h, t] = (np.einsum("si,ij,sj->s", kt, dA, kt)
+                                             + np.einsum("si,ij,sj->s", vt, dU[t], kt))
+                    out["dk"][b, h, t] = dkh if keys_prepared else dkh * c * (k[b, h, t] > 0)
+        return out
+    return f
+
+
 MUTANTS = {
     "U_transposed": ("frame_terms", _frame_terms_variant("U_transposed")),
     "U_no_beta": ("frame_terms", _frame_terms_variant("U_no_beta")),
@@ -192,6 +251,11 @@ MUTANTS = {
     "rms_q_ignored": ("_queries", lambda q, rmsnorm: None if q is None
                       else np.asarray(q, dtype=np.float64)),
     "combine_left_multiply": ("combine", _combine_swapped),
+    "bidir_bwd_F_not_reset": ("scan_bidir_bwd", _bidir_bwd_variant("F_not_reset")),
+    "bidir_bwd_F_same_frame_M": ("scan_bidir_bwd", _bidir_bwd_variant("F_same_frame_M")),
+    "bidir_bwd_dM_no_R_term": ("scan_bidir_bwd", _bidir_bwd_variant("dM_no_R_term")),
+    "bidir_bwd_dq_causal_only": ("scan_bidir_bwd", _bidir_bwd_variant("dq_causal_only")),
+    "bidir_bwd_dU_no_F": ("scan_bidir_bwd", _bidir_bwd_variant("dU_no_F")),
 }
 
 
