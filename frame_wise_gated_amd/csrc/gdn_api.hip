@@ -77,14 +77,16 @@ Layout layout(const Shape& sh, int P) {
 }
 
 // Workspace of the backward pass: phase-1 terms (A), split partials, E_t,
-// the adjoint states G, the per-frame P_t, G_{T-1} per head and a ones gate.
+// the adjoint states G, the per-frame P_t, G_{T-1} per head and a ones gate;
+// for the chunk-causal scan (n_rev chunks) also the reverse-state adjoint F
+// and its value at every chunk start.
 struct BwdLayout {
-  size_t terms = 0, partial = 0, E = 0, G = 0, P = 0, ginit = 0, ones = 0;
+  size_t terms = 0, partial = 0, E = 0, G = 0, P = 0, ginit = 0, ones = 0, F = 0, finit = 0;
   size_t total = 0;
   int n_split = 1;
 };
 
-BwdLayout bwd_layout(const Shape& sh) {
+BwdLayout bwd_layout(const Shape& sh, int64_t n_rev = 0) {
   BwdLayout L;
   const size_t DD = (size_t)sh.D * sh.D * sizeof(float);
   const size_t FH = (size_t)sh.FH();
@@ -102,6 +104,8 @@ BwdLayout bwd_layout(const Shape& sh) {
   L.P = take(FH * DD);
   L.ginit = take((size_t)sh.BH() * DD);
   L.ones = take(FH * (size_t)sh.S * sizeof(float));
+  L.F = take(n_rev > 0 ? FH * DD : 0);
+  L.finit = take((size_t)sh.BH() * (size_t)n_rev * DD);
   L.total = off;
   return L;
 }
@@ -491,17 +495,39 @@ gdn_status gdn_bwd_workspace_bytes(const gdn_desc* desc, size_t* bytes) {
   return GDN_OK;
 }
 
-gdn_status gdn_scan_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
-                        const float* beta, const float* gamma, const float* s0,
-                        const float* states, const void* d_o, const float* ds_final, void* dq,
-                        void* dk, void* dv, float* dbeta, float* dgamma, float* ds0, void* ws,
-                        size_t ws_bytes, void* stream) {
+gdn_status gdn_bidir_bwd_workspace_bytes(const gdn_desc* desc, int32_t chunk_len, size_t* bytes) {
+  Shape sh;
+  gdn_status s = check_desc(desc, &sh);
+  if (s != GDN_OK) return s;
+  if (bytes == nullptr || chunk_len < 1) return GDN_EINVAL;
+  const int64_t n_rev = sh.T > 0 ? ((int64_t)sh.T + chunk_len - 1) / chunk_len : 0;
+  if (n_rev > gdn::kMaxChunks) return GDN_EUNSUPPORTED;
+  *bytes = bwd_layout(sh, n_rev).total;
+  return GDN_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Both backward passes. chunk_len == 0: the causal scan; otherwise the
+// chunk-causal bidirectional scan with reverse states `rev`.
+gdn_status run_bwd(const gdn_desc* desc, int32_t chunk_len, const void* q, const void* k,
+                   const void* v, const float* beta, const float* gamma, const float* s0,
+                   const float* states, const float* rev, const void* d_o, const float* ds_final,
+                   void* dq, void* dk, void* dv, float* dbeta, float* dgamma, float* ds0, void* ws,
+                   size_t ws_bytes, void* stream) {
   Shape sh;
   gdn_status s = check_desc(desc, &sh);
   if (s != GDN_OK) return s;
   if (sh.qk_norm) return GDN_EUNSUPPORTED;
-  for (const void* p : {q, k, v, (const void*)s0, (const void*)states, d_o, (const void*)ds_final,
-                        (const void*)dq, (const void*)dk, (const void*)dv, (const void*)ds0})
+  const bool bidir = chunk_len > 0;
+  if (chunk_len < 0) return GDN_EINVAL;
+  const int64_t n_rev = bidir && sh.T > 0 ? ((int64_t)sh.T + chunk_len - 1) / chunk_len : 0;
+  if (n_rev > gdn::kMaxChunks) return GDN_EUNSUPPORTED;
+  for (const void* p : {q, k, v, (const void*)s0, (const void*)states, (const void*)rev, d_o,
+                        (const void*)ds_final, (const void*)dq, (const void*)dk, (const void*)dv,
+                        (const void*)ds0})
     if (!aligned16(p)) return GDN_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   if (sh.BH() == 0) return GDN_OK;
@@ -514,7 +540,8 @@ gdn_status gdn_scan_bwd(const gdn_desc* desc, const void* q, const void* k, cons
     return GDN_OK;
   }
   if (!q || !k || !v || !beta || !gamma || !states || !d_o) return GDN_EINVAL;
-  const BwdLayout L = bwd_layout(sh);
+  if (bidir && !rev) return GDN_EINVAL;
+  const BwdLayout L = bwd_layout(sh, n_rev);
   if (ws_bytes < L.total) return GDN_EWORKSPACE;
   if (ws == nullptr || ((uintptr_t)ws % kAlign) != 0) return GDN_EINVAL;
   const bool mfma = gdn::scan_uses_mfma(sh);  // layout of the internal terms and E
@@ -545,9 +572,9 @@ gdn_status gdn_scan_bwd(const gdn_desc* desc, const void* q, const void* k, cons
     shq.c = 1.f;
     gdn::TermsOut eout{nullptr, E, DD, 0};
     if (dq != nullptr && gdn::edq_fused(shq)) {
-      // one pass over q and d_o forms E_t and dq = S_t^T do together (one
-      // workgroup per frame-head, whatever split phase 1 uses)
-      GDN_HIP(gdn::launch_edq(shq, q, d_o, states, dq, E, st));
+      // one pass over q and d_o forms E_t and dq = (S_t [+ R_t])^T do together
+      // (one workgroup per frame-head, whatever split phase 1 uses)
+      GDN_HIP(gdn::launch_edq(shq, q, d_o, states, bidir ? rev : nullptr, dq, E, st));
       fused_dq = true;
     } else if (L.n_split == 1) {
       GDN_HIP(gdn::launch_fill_f32(ones, sh.FH() * sh.S, 1.f, st));
@@ -583,11 +610,68 @@ gdn_status gdn_scan_bwd(const gdn_desc* desc, const void* q, const void* k, cons
     p.offsets[1] = sh.T;
     GDN_HIP(gdn::launch_scan(sh, p, st));
   }
-  GDN_HIP(gdn::launch_frame_grad(sh, states, s0, G, ginit, terms, mfma, gamma, P, dgamma, st));
+  gdn::RevGrad rg;
+  if (bidir) {
+    // adjoint of the reverse states, forward inside every chunk [a, e):
+    // F_a = E_a and F_{t+1} = F_t M_t + E_{t+1}. The scan starts each chunk
+    // from E_a, steps frames a .. e-1 adding E_{f+1} after frame f's
+    // transition and stores F_{f+1} in slot f (the last step of a chunk
+    // leaves a value nobody reads).
+    float* F = at<float>(ws, L.F);
+    float* finit = at<float>(ws, L.finit);
+    GDN_HIP(gdn::launch_chunk_init(sh, E, chunk_len, (int)n_rev, finit, mfma, st));
+    gdn::ScanParams p;
+    memset(&p, 0, sizeof(p));
+    p.terms = terms;
+    p.gamma = gamma;
+    p.T = sh.T;
+    p.nchunk = (int)n_rev;
+    p.mode = gdn::SCAN_FORWARD;
+    p.usrc = E;
+    p.ushift = 1;
+    p.init = finit;
+    p.init_bh_stride = n_rev * DD;
+    p.init_c_stride = DD;
+    p.states = F;
+    for (int c = 0; c <= (int)n_rev; ++c)
+      p.offsets[c] = (int)std::min<int64_t>((int64_t)c * chunk_len, sh.T);
+    GDN_HIP(gdn::launch_scan(sh, p, st));
+    rg.rev = rev;
+    rg.fbuf = F;
+    rg.finit = finit;
+    rg.L = chunk_len;
+    rg.nchunk = (int)n_rev;
+  }
+  GDN_HIP(gdn::launch_frame_grad(sh, states, s0, G, ginit, terms, mfma, gamma, P, dgamma, rg, st));
   if (dq || dk || dv || dbeta)
-    GDN_HIP(gdn::launch_token_grad(sh, k, v, beta, d_o, states, G, ginit, P, fused_dq ? nullptr : dq,
-                                   dk, dv, dbeta, st));
+    GDN_HIP(gdn::launch_token_grad(sh, k, v, beta, d_o, states, bidir ? rev : nullptr, G, ginit, P,
+                                   fused_dq ? nullptr : dq, dk, dv, dbeta, st));
   return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_scan_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                        const float* beta, const float* gamma, const float* s0,
+                        const float* states, const void* d_o, const float* ds_final, void* dq,
+                        void* dk, void* dv, float* dbeta, float* dgamma, float* ds0, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return run_bwd(desc, 0, q, k, v, beta, gamma, s0, states, nullptr, d_o, ds_final, dq, dk, dv,
+                 dbeta, dgamma, ds0, ws, ws_bytes, stream);
+}
+
+gdn_status gdn_scan_bidir_chunked_bwd(const gdn_desc* desc, int32_t chunk_len, const void* q,
+                                      const void* k, const void* v, const float* beta,
+                                      const float* gamma, const float* s0,
+                                      const float* states_fwd, const float* states_rev,
+                                      const void* d_o, const float* ds_final, void* dq, void* dk,
+                                      void* dv, float* dbeta, float* dgamma, float* ds0, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  if (chunk_len < 1) return GDN_EINVAL;
+  return run_bwd(desc, chunk_len, q, k, v, beta, gamma, s0, states_fwd, states_rev, d_o, ds_final,
+                 dq, dk, dv, dbeta, dgamma, ds0, ws, ws_bytes, stream);
 }
 
 gdn_status gdn_readout(const gdn_desc* desc, const void* q, const float* states,

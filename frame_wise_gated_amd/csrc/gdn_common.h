@@ -203,6 +203,16 @@ struct CombineParams {
   int64_t BH;           // set by launch_combine
 };
 
+// Reverse-state adjoint of the chunk-causal bidirectional scan for the
+// per-frame gradients; rev == nullptr means the causal scan alone.
+struct RevGrad {
+  const float* rev = nullptr;    // [FH][D][D] reverse states R_t
+  const float* fbuf = nullptr;   // [FH][D][D]: slot f holds F_{t+1} (unused at chunk ends)
+  const float* finit = nullptr;  // [BH][nchunk][D][D]: F at each chunk's first frame
+  int L = 0;                     // chunk length
+  int nchunk = 0;
+};
+
 // Launchers (defined in the k_*.hip files). Each returns hipGetLastError().
 hipError_t launch_prepare(const Shape& sh, const void* k, void* k_hat, hipStream_t st);
 bool terms_use_mfma(const Shape& sh);
@@ -214,8 +224,9 @@ hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const flo
 // Backward pass: E_t = d_o_t^T q_t (into E, the scan's granule layout) and
 // dq = S_t^T do (bf16) in one pass over q and d_o (bf16, D = 128 only).
 bool edq_fused(const Shape& sh);
-hipError_t launch_edq(const Shape& sh, const void* q, const void* d_o, const float* states, void* dq,
-                      float* E, hipStream_t st);
+// states2 (nullable): reverse states summed into the state of dq.
+hipError_t launch_edq(const Shape& sh, const void* q, const void* d_o, const float* states,
+                      const float* states2, void* dq, float* E, hipStream_t st);
 hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_split,
                                   TermsOut out, bool scan_layout, hipStream_t st);
 bool scan_uses_mfma(const Shape& sh);
@@ -230,14 +241,19 @@ hipError_t launch_fill_f32(float* dst, int64_t n, float value, hipStream_t st);
 // Backward pass (k_bwd.hip).
 hipError_t launch_grad_init(const Shape& sh, const float* E, const float* ds_final, float* ginit,
                             bool granule, hipStream_t st);
-hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* s0,
-                             const float* gbuf, const float* ginit, const float* terms,
-                             bool a_granule_bf16, const float* gamma, float* P, float* dgamma,
+// F_t at every chunk start (= E of the chunk's first frame), row-major.
+hipError_t launch_chunk_init(const Shape& sh, const float* E, int L, int nchunk, float* finit,
+                             bool granule, hipStream_t st);
+// With rg.rev set, G_t (in gbuf / ginit) is replaced in place by G_t + F_t.
+hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* s0, float* gbuf,
+                             float* ginit, const float* terms, bool a_granule_bf16,
+                             const float* gamma, float* P, float* dgamma, const RevGrad& rg,
                              hipStream_t st);
+// states2 (nullable): reverse states summed into the state of dq.
 hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, const float* beta,
-                             const void* dout, const float* states, const float* gbuf,
-                             const float* ginit, const float* P, void* dq, void* dk, void* dv,
-                             float* dbeta, hipStream_t st);
+                             const void* dout, const float* states, const float* states2,
+                             const float* gbuf, const float* ginit, const float* P, void* dq,
+                             void* dk, void* dv, float* dbeta, hipStream_t st);
 bool token_grad_uses_mfma(const Shape& sh);
 
 }  // namespace gdn

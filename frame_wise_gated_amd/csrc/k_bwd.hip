@@ -38,14 +38,50 @@ __global__ void __launch_bounds__(256) grad_init_kernel(const float* __restrict_
   }
 }
 
+// F at the first frame of every chunk of the bidirectional backward:
+// finit[bh][c] = E_{c L} (row-major output; E in the scan's granule layout
+// when `granule`).
+__global__ void __launch_bounds__(256) chunk_init_kernel(const float* __restrict__ E,
+                                                         float* __restrict__ finit, int T, int D,
+                                                         int L, int nchunk, int64_t BH,
+                                                         int granule) {
+  const int64_t DD = (int64_t)D * D;
+  const int64_t n_all = BH * nchunk * DD;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_all;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t bc = i / DD;
+    const int64_t bh = bc / nchunk;
+    const int c = (int)(bc % nchunk);
+    const int e = (int)(i % DD);
+    const int m = e / D, n = e % D;
+    const float* Ea = E + (bh * T + (int64_t)c * L) * DD;
+    finit[i] = granule ? Ea[(int64_t)u_granule(m, n >> 2) * 4 + (n & 3)] : Ea[e];
+  }
+}
+
+// Chunk-causal backward, per frame t of chunk [a, e): F_t (first frame: the
+// chunk's start value; later frames: slot f - 1 of the F scan), and whether a
+// reverse state R_{t+1} of the same chunk exists.
+__device__ __forceinline__ const float* rev_adjoint(const RevGrad& rg, int64_t f, int64_t bh,
+                                                    int t, int T, int64_t DD, bool* more) {
+  const int c = t / rg.L;
+  const int a = c * rg.L;
+  *more = t + 1 < min(a + rg.L, T);
+  return t == a ? rg.finit + (bh * rg.nchunk + c) * DD : rg.fbuf + (f - 1) * DD;
+}
+
 // Per frame-head: dM = S_prev^T G (fp32), dgamma = tr(dM) - <dM, A>,
 // P = -gamma (dM + dM^T). 256 threads as a 16 x 16 grid, each owning a
 // B x B block of dM (B = D / 16); S_prev and G staged in LDS.
+// Chunk-causal scan (rg.rev set): dM also gets R_{t+1}^T F_t, and G_t is
+// replaced in place by G_t + F_t (the gradient reaching U_t) for the token
+// kernel; no other workgroup reads frame t's slot.
 template <int D>
 __global__ void __launch_bounds__(256) frame_grad_kernel(
-    const float* __restrict__ states, const float* __restrict__ s0, const float* __restrict__ gbuf,
-    const float* __restrict__ ginit, const float* __restrict__ terms, int a_granule_bf16,
-    const float* __restrict__ gamma, float* __restrict__ P, float* __restrict__ dgamma, int T) {
+    const float* __restrict__ states, const float* __restrict__ s0, float* __restrict__ gbuf,
+    float* __restrict__ ginit, const float* __restrict__ terms, int a_granule_bf16,
+    const float* __restrict__ gamma, float* __restrict__ P, float* __restrict__ dgamma, int T,
+    RevGrad rg) {
   constexpr int B = D / 16;
   constexpr int64_t DD = (int64_t)D * D;
   __shared__ float Ss[D][D];
@@ -56,7 +92,7 @@ __global__ void __launch_bounds__(256) frame_grad_kernel(
   const int t = (int)(f % T);
   const int tid = threadIdx.x;
   const float* Sp = t > 0 ? states + (f - 1) * DD : (s0 ? s0 + bh * DD : nullptr);
-  const float* Gt = t == T - 1 ? ginit + bh * DD : gbuf + (f + 1) * DD;
+  float* Gt = t == T - 1 ? ginit + bh * DD : gbuf + (f + 1) * DD;
   for (int e = tid; e < D * D; e += 256) {
     Ss[e / D][e % D] = Sp ? Sp[e] : 0.f;
     Gs[e / D][e % D] = Gt[e];
@@ -68,16 +104,33 @@ __global__ void __launch_bounds__(256) frame_grad_kernel(
   for (int x = 0; x < B; ++x)
 #pragma unroll
     for (int y = 0; y < B; ++y) acc[x][y] = 0.f;
-  for (int i = 0; i < D; ++i) {
-    float sa[B], gb[B];
+  auto product = [&]() {  // acc += Ss^T Gs
+    for (int i = 0; i < D; ++i) {
+      float sa[B], gb[B];
 #pragma unroll
-    for (int x = 0; x < B; ++x) sa[x] = Ss[i][a0 + x];
+      for (int x = 0; x < B; ++x) sa[x] = Ss[i][a0 + x];
 #pragma unroll
-    for (int y = 0; y < B; ++y) gb[y] = Gs[i][b0 + y];
+      for (int y = 0; y < B; ++y) gb[y] = Gs[i][b0 + y];
 #pragma unroll
-    for (int x = 0; x < B; ++x)
+      for (int x = 0; x < B; ++x)
 #pragma unroll
-      for (int y = 0; y < B; ++y) acc[x][y] = fmaf(sa[x], gb[y], acc[x][y]);
+        for (int y = 0; y < B; ++y) acc[x][y] = fmaf(sa[x], gb[y], acc[x][y]);
+    }
+  };
+  product();
+  if (rg.rev != nullptr) {
+    bool more;
+    const float* Ft = rev_adjoint(rg, f, bh, t, T, DD, &more);
+    const float* Rn = rg.rev + (f + 1) * DD;
+    __syncthreads();  // every thread is done with Ss and Gs
+    for (int e = tid; e < D * D; e += 256) {
+      const float fv = Ft[e];
+      Gt[e] = Gs[e / D][e % D] + fv;
+      Gs[e / D][e % D] = fv;
+      if (more) Ss[e / D][e % D] = Rn[e];
+    }
+    __syncthreads();
+    if (more) product();
   }
   // <dM, I - A>
   const float* At = terms + f * 2 * DD;
@@ -125,7 +178,8 @@ __global__ void __launch_bounds__(256) frame_grad_kernel(
 template <typename TIn, int D>
 __global__ void __launch_bounds__(256) token_grad_generic(
     const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ beta,
-    const TIn* __restrict__ dout, const float* __restrict__ states, const float* __restrict__ gbuf,
+    const TIn* __restrict__ dout, const float* __restrict__ states,
+    const float* __restrict__ states2, const float* __restrict__ gbuf,
     const float* __restrict__ ginit, const float* __restrict__ P, TIn* __restrict__ dq,
     TIn* __restrict__ dk, TIn* __restrict__ dv, float* __restrict__ dbeta, int S, int T,
     int ntile, float c, int prepared) {
@@ -154,11 +208,13 @@ __global__ void __launch_bounds__(256) token_grad_generic(
   ds[tl][i] = on ? ld(dout, row + i) : 0.f;
   __syncthreads();
   const float* St = states + f * DD;
+  const float* S2t = states2 ? states2 + f * DD : nullptr;
   const float* Gt = t == T - 1 ? ginit + bh * DD : gbuf + (f + 1) * DD;
   const float* Pt = P + f * DD;
   float dqv = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
   for (int j = 0; j < D; ++j) {
-    dqv = fmaf(St[(int64_t)j * D + i], ds[tl][j], dqv);
+    const float sji = St[(int64_t)j * D + i] + (S2t ? S2t[(int64_t)j * D + i] : 0.f);
+    dqv = fmaf(sji, ds[tl][j], dqv);
     y1 = fmaf(Pt[(int64_t)i * D + j], kh[tl][j], y1);
     y2 = fmaf(Gt[(int64_t)j * D + i], vs[tl][j], y2);
     y3 = fmaf(Gt[(int64_t)i * D + j], kh[tl][j], y3);
@@ -476,10 +532,10 @@ token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __rest
 // matrices.
 __global__ void __launch_bounds__(256, 1)
 frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__ s0,
-                     const float* __restrict__ gbuf, const float* __restrict__ ginit,
+                     float* __restrict__ gbuf, float* __restrict__ ginit,
                      const float* __restrict__ terms, int a_granule_bf16,
                      const float* __restrict__ gamma, float* __restrict__ P,
-                     float* __restrict__ dgamma, int T) {
+                     float* __restrict__ dgamma, int T, RevGrad rg) {
   constexpr int D = 128;
   constexpr int LDT = D + 4;  // padded row for the transposed read of dM
   constexpr int64_t DD = (int64_t)D * D;
@@ -495,7 +551,7 @@ frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__
   const int l32 = lane & 31;
   const int hk = lane >> 5;
   const float* Sp = t > 0 ? states + (f - 1) * DD : (s0 ? s0 + bh * DD : nullptr);
-  const float* Gt = t == T - 1 ? ginit + bh * DD : gbuf + (f + 1) * DD;
+  float* Gt = t == T - 1 ? ginit + bh * DD : gbuf + (f + 1) * DD;
   const float* At = terms + f * 2 * DD;
   // A_t entries of this lane's accumulators (see the epilogue), loaded before
   // the products so that their latency is hidden: in the bf16 granule layout
@@ -536,13 +592,43 @@ frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[nb][j] = 0.f;
+  auto product = [&]() {  // acc += Ss^T Gs
 #pragma unroll 4
-  for (int ks = 0; ks < D / 2; ++ks) {
-    const int i = 2 * ks + hk;
-    const float a = Ss[i][32 * wave + l32];
+    for (int ks = 0; ks < D / 2; ++ks) {
+      const int i = 2 * ks + hk;
+      const float a = Ss[i][32 * wave + l32];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Gs[i][32 * nb + l32], acc[nb], 0, 0, 0);
+      for (int nb = 0; nb < 4; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Gs[i][32 * nb + l32], acc[nb], 0, 0, 0);
+    }
+  };
+  product();
+  // chunk-causal scan: + R_{t+1}^T F_t, and G_t + F_t written over G_t
+  if (rg.rev != nullptr) {
+    bool more;
+    const float* Ft = rev_adjoint(rg, f, bh, t, T, DD, &more);
+    const float* Rn = rg.rev + (f + 1) * DD;
+    constexpr int kPer = D * D / 4 / 256;
+    float4 fv[kPer], rv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + 256 * u;
+      fv[u] = *(const float4*)(Ft + 4 * (int64_t)e);
+      rv[u] = more ? *(const float4*)(Rn + 4 * (int64_t)e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();  // every wave is done with Ss and Gs
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e / (D / 4), c4 = 4 * (e % (D / 4));
+      const float4 g4 = *(const float4*)&Gs[r][c4];
+      *(float4*)(Gt + 4 * (int64_t)e) =
+          make_float4(g4.x + fv[u].x, g4.y + fv[u].y, g4.z + fv[u].z, g4.w + fv[u].w);
+      *(float4*)&Gs[r][c4] = fv[u];
+      Ss[r][c4] = rv[u].x; Ss[r][c4 + 1] = rv[u].y; Ss[r][c4 + 2] = rv[u].z; Ss[r][c4 + 3] = rv[u].w;
+    }
+    __syncthreads();
+    if (more) product();
   }
   // acc[nb][j] = dM[a][b], a = 32 wave + 8 (j / 4) + 4 hk + j % 4, b = 32 nb + l32
   float part = 0.f;
@@ -594,21 +680,34 @@ hipError_t launch_grad_init(const Shape& sh, const float* E, const float* ds_fin
   return hipGetLastError();
 }
 
-hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* s0,
-                             const float* gbuf, const float* ginit, const float* terms,
-                             bool a_granule_bf16, const float* gamma, float* P, float* dgamma,
+hipError_t launch_chunk_init(const Shape& sh, const float* E, int L, int nchunk, float* finit,
+                             bool granule, hipStream_t st) {
+  const int64_t n = sh.BH() * nchunk * sh.D * sh.D;
+  if (n == 0) return hipSuccess;
+  if (L < 1 || (int64_t)(nchunk - 1) * L >= sh.T) return hipErrorInvalidValue;
+  chunk_init_kernel<<<grid_cap(n), 256, 0, st>>>(E, finit, sh.T, sh.D, L, nchunk, sh.BH(),
+                                                 granule ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* s0, float* gbuf,
+                             float* ginit, const float* terms, bool a_granule_bf16,
+                             const float* gamma, float* P, float* dgamma, const RevGrad& rg,
                              hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
+  if (rg.rev != nullptr && (rg.L < 1 || rg.fbuf == nullptr || rg.finit == nullptr ||
+                            (int64_t)rg.nchunk * rg.L < sh.T))
+    return hipErrorInvalidValue;
   dim3 grid((unsigned)sh.FH());
   const int ag = a_granule_bf16 ? 1 : 0;
   if (sh.D == 128) {
     frame_grad_mfma_d128<<<grid, 256, 0, st>>>(states, s0, gbuf, ginit, terms, ag, gamma, P, dgamma,
-                                               sh.T);
+                                               sh.T, rg);
     return hipGetLastError();
   }
 #define GDN_FG(DV)                                                                              \
   frame_grad_kernel<DV><<<grid, 256, 0, st>>>(states, s0, gbuf, ginit, terms, ag, gamma, P, \
-                                              dgamma, sh.T)
+                                              dgamma, sh.T, rg)
   switch (sh.D) {
     case 16: GDN_FG(16); break;
     case 32: GDN_FG(32); break;
@@ -629,12 +728,14 @@ hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* 
 bool token_grad_uses_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
 
 hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, const float* beta,
-                             const void* dout, const float* states, const float* gbuf,
-                             const float* ginit, const float* P, void* dq, void* dk, void* dv,
-                             float* dbeta, hipStream_t st) {
+                             const void* dout, const float* states, const float* states2,
+                             const float* gbuf, const float* ginit, const float* P, void* dq,
+                             void* dk, void* dv, float* dbeta, hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
   if (token_grad_uses_mfma(sh)) {
-    // dq = states^T do: the readout with the state staged transposed
+    // dq = states^T do: the readout with the state staged transposed (the
+    // summed states of the bidirectional scan go through the fused E pass)
+    if (dq && states2) return hipErrorInvalidValue;
     if (dq) {
       hipError_t e = launch_readout(sh, dout, states, nullptr, dq, st, true);
       if (e != hipSuccess) return e;
@@ -667,7 +768,7 @@ hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, cons
   dim3 grid((unsigned)(sh.FH() * ntile));
 #define GDN_TG(TT, DV)                                                                        \
   token_grad_generic<TT, DV><<<grid, 256, 0, st>>>(                                          \
-      (const TT*)k, (const TT*)v, beta, (const TT*)dout, states, gbuf, ginit, P, (TT*)dq, \
+      (const TT*)k, (const TT*)v, beta, (const TT*)dout, states, states2, gbuf, ginit, P, (TT*)dq, \
       (TT*)dk, (TT*)dv, dbeta, sh.S, sh.T, ntile, sh.c, sh.prepared)
   if (sh.io == 1) {
     switch (sh.D) {

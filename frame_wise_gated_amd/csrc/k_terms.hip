@@ -120,7 +120,8 @@ __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(GDN_TERMS_WAVES_PER_EU, GDN_TERMS_WAVES_PER_EU)))
 terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     const float* __restrict__ beta, int S, int n_split, float c,
-                    TermsOut out, const float* __restrict__ sdq, uint16_t* __restrict__ dq) {
+                    TermsOut out, const float* __restrict__ sdq, const float* __restrict__ sdq2,
+                    uint16_t* __restrict__ dq) {
   constexpr int D = 128;
   static_assert(!kDq || (kScanLayout && kPrepared && !kNorm && !kAOnly), "dq mode of the E pass");
   // ring slot: k block, v block, then the stage's 32 gates; wbuf[st % 2]
@@ -146,16 +147,19 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   const uint16_t* vf = v + fh * (int64_t)S * D;
   const float* bf = kDq ? nullptr : beta + fh * (int64_t)S;
 
-  // S_t^T -> LDS (kDq), 16-byte chunk ch of row i at chunk position ch ^ (i % 8)
+  // S_t^T -> LDS (kDq; S_t + R_t with the reverse states of the bidirectional
+  // scan), 16-byte chunk ch of row i at chunk position ch ^ (i % 8)
   if (kDq) {
     const float* s1 = sdq + fh * D * D;
+    const float* s2 = sdq2 ? sdq2 + fh * D * D : nullptr;
 #pragma unroll
     for (int u = 0; u < D * 16 / 512; ++u) {
       const int cidx = tid + 512 * u;
       const int i = cidx >> 4, ch = cidx & 15;
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = s1[(int64_t)(8 * ch + e) * D + i];
+      for (int e = 0; e < 8; ++e)
+        x[e] = s1[(int64_t)(8 * ch + e) * D + i] + (s2 ? s2[(int64_t)(8 * ch + e) * D + i] : 0.f);
       Sl[i * 16 + (ch ^ (i & 7))] = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
                                                 pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
     }
@@ -663,7 +667,7 @@ hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const flo
     const bool norm = sh.qk_norm && !sh.prepared;  // prepared keys are used as given
 #define GDN_TERMS_DMA(L, P, N, AO)                                                           \
   terms_dma_bf16_d128<L, P, N, AO, false><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, \
-                                                                out, nullptr, nullptr)
+                                                                out, nullptr, nullptr, nullptr)
     if (scan_layout && out.outU == nullptr && !norm) {  // A_t alone (the backward's recompute)
       if (sh.prepared) GDN_TERMS_DMA(true, true, false, true);
       else GDN_TERMS_DMA(true, false, false, true);
@@ -685,13 +689,14 @@ hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const flo
 
 bool edq_fused(const Shape& sh) { return terms_use_mfma(sh); }
 
-hipError_t launch_edq(const Shape& sh, const void* q, const void* d_o, const float* states, void* dq,
-                      float* E, hipStream_t st) {
+hipError_t launch_edq(const Shape& sh, const void* q, const void* d_o, const float* states,
+                      const float* states2, void* dq, float* E, hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
   if (!edq_fused(sh)) return hipErrorInvalidValue;
   TermsOut out{nullptr, E, (int64_t)sh.D * sh.D, 0};
   terms_dma_bf16_d128<true, true, false, false, true><<<dim3((unsigned)sh.FH()), 512, 0, st>>>(
-      (const uint16_t*)q, (const uint16_t*)d_o, nullptr, sh.S, 1, 1.f, out, states, (uint16_t*)dq);
+      (const uint16_t*)q, (const uint16_t*)d_o, nullptr, sh.S, 1, 1.f, out, states, states2,
+      (uint16_t*)dq);
   return hipGetLastError();
 }
 

@@ -87,6 +87,11 @@ def lib() -> ctypes.CDLL:
     L.gdn_bwd_workspace_bytes.argtypes = [P(gdn_desc), P(ctypes.c_size_t)]
     L.gdn_scan_bwd.restype = _st
     L.gdn_scan_bwd.argtypes = [P(gdn_desc)] + [_vp] * 15 + [_vp, ctypes.c_size_t, _vp]
+    L.gdn_bidir_bwd_workspace_bytes.restype = _st
+    L.gdn_bidir_bwd_workspace_bytes.argtypes = [P(gdn_desc), ctypes.c_int32, P(ctypes.c_size_t)]
+    L.gdn_scan_bidir_chunked_bwd.restype = _st
+    L.gdn_scan_bidir_chunked_bwd.argtypes = ([P(gdn_desc), ctypes.c_int32] + [_vp] * 16
+                                             + [_vp, ctypes.c_size_t, _vp])
     L.gdn_readout.restype = _st
     L.gdn_readout.argtypes = [P(gdn_desc), _vp, _vp, _vp, _vp, _vp]
     _lib = L
@@ -315,6 +320,49 @@ def gdn_scan_bwd(q, k, v, beta, gamma, states, d_o, s0=None, ds_final=None, key_
                               _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
                               _ptr(out["dgamma"]), _ptr(out["ds0"]), _ptr(ws), nb, _stream(stream)),
            "gdn_scan_bwd")
+    return out
+
+
+def gdn_bidir_bwd_workspace_bytes(desc: gdn_desc, chunk_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_bidir_bwd_workspace_bytes(ctypes.byref(desc), int(chunk_len), ctypes.byref(n)),
+           "gdn_bidir_bwd_workspace_bytes")
+    return int(n.value)
+
+
+def gdn_scan_bidir_chunked_bwd(q, k, v, beta, gamma, chunk_len, states_fwd, states_rev, d_o,
+                               s0=None, ds_final=None, key_scale=0.0, keys_prepared=False,
+                               want=("dq", "dk", "dv", "dbeta", "dgamma", "ds0"), out=None,
+                               ws=None, stream=None):
+    """Gradients of the chunk-causal bidirectional scan; `states_fwd` and
+    `states_rev` are the forward call's states. Returns a dict with the
+    requested gradients."""
+    d = _desc_from(k, key_scale, keys_prepared)
+    B, H, T, S, D = k.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (d_o, "d_o")):
+        _need(t, n, k.shape, k.dtype)
+    _need(beta, "beta", (B, H, T, S), torch.float32)
+    _need(gamma, "gamma", (B, H, T), torch.float32)
+    _need(states_fwd, "states_fwd", (B, H, T, D, D), torch.float32)
+    _need(states_rev, "states_rev", (B, H, T, D, D), torch.float32)
+    _need(s0, "s0", (B, H, D, D), torch.float32)
+    _need(ds_final, "ds_final", (B, H, D, D), torch.float32)
+    shapes = {"dq": (k.shape, k.dtype), "dk": (k.shape, k.dtype), "dv": (k.shape, k.dtype),
+              "dbeta": ((B, H, T, S), torch.float32), "dgamma": ((B, H, T), torch.float32),
+              "ds0": ((B, H, D, D), torch.float32)}
+    out = dict(out or {})
+    for n, (shp, dt) in shapes.items():
+        _need(out.get(n), n, shp, dt)
+        out[n] = _out(out.get(n), n in want, shp, dt, k.device)
+    if ws is None:
+        ws = torch.empty(max(gdn_bidir_bwd_workspace_bytes(d, chunk_len), 1), dtype=torch.uint8,
+                         device=k.device)
+    nb = ws.numel() * ws.element_size()
+    _check(lib().gdn_scan_bidir_chunked_bwd(
+        ctypes.byref(d), int(chunk_len), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gamma),
+        _ptr(s0), _ptr(states_fwd), _ptr(states_rev), _ptr(d_o), _ptr(ds_final), _ptr(out["dq"]),
+        _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dgamma"]),
+        _ptr(out["ds0"]), _ptr(ws), nb, _stream(stream)), "gdn_scan_bidir_chunked_bwd")
     return out
 
 

@@ -191,6 +191,35 @@ GDN_API gdn_status gdn_scan_bwd(const gdn_desc* desc, const void* q, const void*
                                 void* dq, void* dk, void* dv, float* dbeta, float* dgamma,
                                 float* ds0, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace in bytes that gdn_scan_bidir_chunked_bwd needs for `desc` and
+ * `chunk_len` (>= 1). Host-only. */
+GDN_API gdn_status gdn_bidir_bwd_workspace_bytes(const gdn_desc* desc, int32_t chunk_len,
+                                                 size_t* bytes);
+
+/* Backward pass of the chunk-causal bidirectional scan
+ * (gdn_scan_bidir_chunked; hyper.ai paper page 2605.15178, method section:
+ * the reverse scan restarts at every chunk boundary): gradients of
+ * L = sum <d_o, o> + <ds_final, S_{T-1}> with o = (S_t + R_t) q. The causal
+ * adjoint G is that of gdn_scan_bwd; the reverse states R get their own
+ * adjoint, forward in time inside each chunk [a, e): F_a = E_a,
+ * F_t = E_t + F_{t-1} M_{t-1}. Then dU_t = G_t + F_t,
+ * dM_t = S_{t-1}^T G_t + R_{t+1}^T F_t (the second term only when t + 1 < e),
+ * dq = (S_t + R_t)^T do, and the per-frame and per-token rules of
+ * gdn_scan_bwd with dU_t in place of G_t.
+ * Inputs: as gdn_scan_bwd plus chunk_len (>= 1, as in the forward call) and
+ * the forward's states_fwd and states_rev [B,H,T,D,D] (both required).
+ * Outputs as gdn_scan_bwd (each may be NULL). More than 256 chunks:
+ * GDN_EUNSUPPORTED. GDN_QK_RMSNORM is not supported here.
+ * Workspace: gdn_bidir_bwd_workspace_bytes. */
+GDN_API gdn_status gdn_scan_bidir_chunked_bwd(const gdn_desc* desc, int32_t chunk_len,
+                                              const void* q, const void* k, const void* v,
+                                              const float* beta, const float* gamma,
+                                              const float* s0, const float* states_fwd,
+                                              const float* states_rev, const void* d_o,
+                                              const float* ds_final, void* dq, void* dk, void* dv,
+                                              float* dbeta, float* dgamma, float* ds0, void* ws,
+                                              size_t ws_bytes, void* stream);
+
 /* Phase 3 alone: o_{t,s} = (states_t + states_add_t) q_{t,s} for every token
  * of every frame (states_add may be NULL). The readout with the state after
  * frame t is this library's reading of the frame-wise rule (the pages give the

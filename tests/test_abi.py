@@ -22,7 +22,8 @@ def test_exports_every_declared_symbol(L):
     names = gdn.exported_names_in_header()
     assert set(names) == {"gdn_status_str", "gdn_workspace_bytes", "gdn_prepare", "gdn_frame_terms",
                           "gdn_scan_fwd", "gdn_scan_bidir_chunked", "gdn_compose", "gdn_readout",
-                          "gdn_step", "gdn_scan_bwd", "gdn_bwd_workspace_bytes"}
+                          "gdn_step", "gdn_scan_bwd", "gdn_bwd_workspace_bytes",
+                          "gdn_scan_bidir_chunked_bwd", "gdn_bidir_bwd_workspace_bytes"}
     out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -130,6 +131,23 @@ def test_null_and_chunk_arguments(L):
     nbw = ctypes.c_size_t(0)
     assert L.gdn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(nbw)) == gdn.GDN_OK
     assert nbw.value > 0
+    # bidirectional backward: chunk_len < 1, missing reverse states, RMSNorm,
+    # workspace too small, more than 256 chunks; its workspace holds the causal one
+    bbw = lambda dd, L_, rev, nb: L.gdn_scan_bidir_chunked_bwd(
+        ctypes.byref(dd), L_, fake, fake, fake, fake, fake, None, fake, rev, fake, None, fake, fake,
+        fake, fake, fake, None, fake, nb, None)
+    assert bbw(d, 0, fake, 1 << 30) == gdn.GDN_EINVAL
+    assert bbw(d, 2, None, 1 << 30) == gdn.GDN_EINVAL
+    assert bbw(dn, 2, fake, 1 << 30) == gdn.GDN_EUNSUPPORTED
+    assert bbw(d, 2, fake, 16) == gdn.GDN_EWORKSPACE
+    dlong = gdn.make_desc(1, 1, 300, 12, 16, gdn.GDN_F32)
+    assert bbw(dlong, 1, fake, 1 << 30) == gdn.GDN_EUNSUPPORTED
+    nbb = ctypes.c_size_t(0)
+    assert L.gdn_bidir_bwd_workspace_bytes(ctypes.byref(d), 0, ctypes.byref(nbb)) == gdn.GDN_EINVAL
+    assert L.gdn_bidir_bwd_workspace_bytes(ctypes.byref(dlong), 1, ctypes.byref(nbb)) == \
+        gdn.GDN_EUNSUPPORTED
+    assert L.gdn_bidir_bwd_workspace_bytes(ctypes.byref(d), 2, ctypes.byref(nbb)) == gdn.GDN_OK
+    assert nbb.value > nbw.value
     # prepare refuses already-prepared keys
     dp = gdn.make_desc(1, 1, 4, 12, 16, gdn.GDN_F32, keys_prepared=True)
     assert L.gdn_prepare(ctypes.byref(dp), fake, fake, None) == gdn.GDN_EINVAL

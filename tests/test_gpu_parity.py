@@ -613,6 +613,86 @@ def test_scan_bwd_layer_60s_fused_dq():
         assert e <= tol(w), ((h, t, s), e)
 
 
+BIDIR_BWD_CASES = {
+    # name: (workload, chunk_len, with s0 / ds_final, keys_prepared)
+    "f32_D16_L2_s0_dsf": (gi.workload(1), 2, True, False),
+    "f32_D16_L3_plain": (gi.workload(1).with_shape(B=2, H=2), 3, False, False),
+    "f32_D16_L1": (gi.workload(1), 1, True, False),
+    "f32_D16_L_ge_T": (gi.workload(1), 20, True, False),
+    "f32_D128_L2_prepared": (gi.workload(1).with_shape(D=128, S=40, T=4), 2, True, True),
+    "bf16_D128_L3_s0_dsf": (gi.workload(2).with_shape(H=2, T=7, S=300), 3, True, False),
+    "bf16_D128_L2_split_S2100": (gi.workload(2).with_shape(T=3, S=2100), 2, True, False),
+    "bf16_D64_L2": (gi.workload(2).with_shape(D=64, T=5, S=130), 2, True, False),
+    "bf16_D128_L3_prepared": (gi.workload(2).with_shape(H=2, T=5, S=170), 3, True, True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BIDIR_BWD_CASES))
+def test_scan_bidir_bwd(name):
+    """Gradients of L = <do, o> + <ds_final, S_T-1> for the chunk-causal
+    bidirectional scan (o = (S_t + R_t) q) against the float64 oracle."""
+    w, L, extras, prepared = BIDIR_BWD_CASES[name]
+    x, d = _gen(w)
+    if prepared:
+        kh = orc.prepare_keys(x["k"]).astype(np.float32)
+        if w.io == "bf16":
+            bits = gi.f32_to_bf16_bits(kh)
+            kh = gi.bf16_bits_to_f32(bits)
+            d["k"] = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+        else:
+            d["k"] = torch.from_numpy(kh).to(DEV)
+        x["k"] = kh
+    do, do_d, s0, dsf = _bwd_inputs(w, x, d, extras)
+    dev = lambda a: None if a is None else torch.from_numpy(a).to(DEV)
+    say("scan_bidir_bwd", name, "forward")
+    fwd = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], L,
+                                     s0=dev(s0), keys_prepared=prepared, want_o=False)
+    say("scan_bidir_bwd", name, "backward")
+    g = gdn.gdn_scan_bidir_chunked_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], L,
+                                       fwd["states_fwd"], fwd["states_rev"], do_d, s0=dev(s0),
+                                       ds_final=dev(dsf), keys_prepared=prepared)
+    torch.cuda.synchronize()
+    for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
+        a = head_arrays(x, b, h)
+        ref = orc.scan_bidir_bwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"], L,
+                                 do[b, h][None, None].astype(np.float64),
+                                 ds_final=None if dsf is None else dsf[b, h][None, None].astype(np.float64),
+                                 s0=None if s0 is None else s0[b, h][None, None].astype(np.float64),
+                                 keys_prepared=prepared)
+        for n in ("dq", "dk", "dv", "dbeta", "dgamma", "ds0"):
+            e = rel_fro(host(g[n][b, h]), ref[n][0, 0])
+            say(name, (b, h), n, f"{e:.2e}")
+            assert e <= tol(w), (n, e)
+
+
+def test_scan_bidir_bwd_layer_full_size():
+    """Backward of the chunk-causal 16-head 720p layer (T = 11, S = 3600,
+    chunks of 3 frames) at full size in the MFMA configuration, sampled heads."""
+    w = gi.workload(3)
+    L = 3
+    heads = [(0, 5), (0, 11)]
+    say("generate", w.name)
+    x = gi.batch_inputs(w, 0, keep_f32=False)
+    d = upload(x, w)
+    rng = np.random.default_rng([88, 10])
+    do_bits = gi.f32_to_bf16_bits(rng.standard_normal((w.B, w.H, w.T, w.S, w.D)).astype(np.float32))
+    do_d = torch.from_numpy(do_bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    say("forward + backward (bidirectional)", w.name)
+    fwd = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], L, want_o=False)
+    g = gdn.gdn_scan_bidir_chunked_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], L,
+                                       fwd["states_fwd"], fwd["states_rev"], do_d)
+    torch.cuda.synchronize()
+    for (b, h) in heads:
+        s = gi.head_inputs(w, 0, b, h)
+        a = {n: np.asarray(s[n], dtype=np.float64)[None, None] for n in ("q", "k", "v", "beta", "gamma")}
+        dof = gi.bf16_bits_to_f32(do_bits[b, h]).astype(np.float64)[None, None]
+        ref = orc.scan_bidir_bwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"], L, dof)
+        for n in ("dq", "dk", "dv", "dbeta", "dgamma", "ds0"):
+            e = rel_fro(host(g[n][b, h]), ref[n][0, 0])
+            say(w.name, "bidir", (b, h), n, f"{e:.2e}")
+            assert e <= tol(w), (n, e)
+
+
 def test_scan_bwd_no_frames():
     w = gi.workload(1).with_shape(T=0)
     x, d = _gen(w)
