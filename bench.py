@@ -128,7 +128,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phases", action="store_true", help="skip the per-phase timing loops")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip timing the backward pass (causal workloads only)")
+                    help="skip timing the backward pass")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -269,8 +269,9 @@ def main():
         }
         del A, U
 
-    if not args.no_backward and w.mode != "bidir" and not norm:
+    if not args.no_backward and not norm:
         # backward of the same layer: gradients of <d_o, o> for a random d_o
+        # (the chunk-causal backward for the bidirectional workload)
         print("[bench] backward", file=sys.stderr, flush=True)
         gen = torch.Generator(device=dev).manual_seed(args.seed + 1)
         d_o = torch.randn(q.shape, device=dev, dtype=torch.float32, generator=gen).to(q.dtype)
@@ -278,15 +279,24 @@ def main():
         grads["dbeta"] = torch.empty_like(beta)
         grads["dgamma"] = torch.empty_like(gamma)
         grads["ds0"] = torch.empty_like(s_fin)
-        bws = torch.empty(gdn.gdn_bwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
-        bstep = lambda: gdn.gdn_scan_bwd(q, k, v, beta, gamma, st_fwd, d_o, out=grads, ws=bws,
-                                         stream=stream)
+        if w.mode == "bidir":
+            bws = torch.empty(gdn.gdn_bidir_bwd_workspace_bytes(desc, w.chunk_len), dtype=torch.uint8,
+                              device=dev)
+            bstep = lambda: gdn.gdn_scan_bidir_chunked_bwd(q, k, v, beta, gamma, w.chunk_len, st_fwd,
+                                                           st_rev, d_o, out=grads, ws=bws,
+                                                           stream=stream)
+        else:
+            bws = torch.empty(gdn.gdn_bwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+            bstep = lambda: gdn.gdn_scan_bwd(q, k, v, beta, gamma, st_fwd, d_o, out=grads, ws=bws,
+                                             stream=stream)
         for _ in range(2):
             bstep()
         t_bwd = timed(bstep, max(args.steps // 2, 3))
-        # algorithmic bytes: q, k, v, d_o, beta, gamma and the forward states in;
-        # dq, dk, dv, dbeta, dgamma out
-        bw_bytes = fh * (4 * S * D * (2 if bf else 4) + 4 * S + 4 + 4 * D * D
+        # algorithmic bytes: q, k, v, d_o, beta, gamma and the forward states
+        # (both directions for the bidirectional scan) in; dq, dk, dv, dbeta,
+        # dgamma out
+        n_states = 2 if w.mode == "bidir" else 1
+        bw_bytes = fh * (4 * S * D * (2 if bf else 4) + 4 * S + 4 + n_states * 4 * D * D
                          + 3 * S * D * (2 if bf else 4) + 4 * S + 4)
         out["backward"] = {
             "ms_per_call": t_bwd,
