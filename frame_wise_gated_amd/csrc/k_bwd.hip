@@ -14,6 +14,7 @@
 //   dbeta = 1/2 k^T P_t k + v^T G_t k,
 // followed by the key scale and the ReLU mask for raw keys.
 #include "gdn_common.h"
+#include "gdn_dma.h"
 
 namespace gdn {
 
@@ -235,32 +236,6 @@ __global__ void __launch_bounds__(256) token_grad_generic(
   if (on && i == 0 && dbeta != nullptr) dbeta[f * S + s] = red[tl][0];
 }
 
-// MFMA path of the per-token gradients (bf16, D = 128), dq excluded (it is
-// the readout with the state transposed). Per frame-head, P_t, G_t and
-// G_t^T are staged once in LDS as bf16 MFMA "A" operands (rows i,
-// contraction j contiguous, chunk-swizzled like the readout's state); each
-// wave streams 32-token tiles of k and v as "B" operands:
-//   pass 1: Y1 = P ReLU(k) c, Y2 = G^T v  ->  dk = beta c [k > 0] (Y1 + Y2),
-//           dbeta = k_hat . (Y1 / 2 + Y2)   (v^T G k_hat = k_hat . G^T v);
-//   pass 2: Y3 = G ReLU(k) c              ->  dv = beta Y3.
-// The accumulators hold tokens as columns; each result tile goes through a
-// per-wave LDS buffer so that a row pass can combine it with the token's raw
-// key (mask, dbeta) and write 16-byte chunks of contiguous token rows.
-constexpr int kTgTok = 32;    // tokens per wave tile
-constexpr int kTgWaves = 4;
-constexpr int kTgXcd = 8;
-
-__device__ __forceinline__ int tswz(int row, int chunk) { return chunk ^ (row & 7); }
-
-// 16 bytes of token row min(s, S - 1) (features j .. j + 7). Rows past the
-// end repeat the last token: an MFMA output column depends only on its own
-// token and those columns are never stored, so no zeroing is needed, and the
-// load stays unconditional (a select on it becomes an exec-masked load, which
-// makes the compiler drain every prefetch at the loop's back edge).
-__device__ __forceinline__ uint4 ld_row16(const uint16_t* base, int s, int S, int j) {
-  return *(const uint4*)(base + (int64_t)min(s, S - 1) * 128 + j);
-}
-
 // Sum over the 16 lanes of a DPP row (rotations by 1, 2, 4, 8).
 __device__ __forceinline__ float sum_row16(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));
@@ -270,258 +245,198 @@ __device__ __forceinline__ float sum_row16(float x) {
   return x;
 }
 
-// kAll: dk, dv and dbeta are all wanted, so no store sits behind a pointer
-// test (on a path without stores the prefetch loads would be the youngest
-// memory operations, and the loop's back edge would wait for all of them).
-template <bool kPrepared, bool kAll>
-__global__ void __launch_bounds__(256, 1)
-token_grad_mfma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                          const float* __restrict__ beta, const float* __restrict__ gbuf,
-                          const float* __restrict__ ginit, const float* __restrict__ P,
-                          uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-                          float* __restrict__ dbeta, int S, int T,
-                          int64_t FH, int nb, float c) {
+// Weights-stationary MFMA path of the per-token gradients (bf16, D = 128).
+// Wave w keeps rows 32 w .. 32 w + 31 of P_t, G_t^T and G_t as bf16 MFMA
+// "A" fragments in registers (96 VGPRs) for the whole frame, and the frame's
+// tokens stream through a ring of 32-token LDS stages filled by direct
+// global -> LDS copies, so no register holds a prefetch and k is read once for
+// both the MFMA operand and the row pass. Per stage every wave forms its 32
+// rows of Y1 = P relu(k), Y2 = G^T v and Y3 = G relu(k) for the 32 tokens and
+// drops Z = c Y1 + Y2, W = c Y1 / 2 + Y2 and beta c Y3 into LDS (bf16, token
+// rows); then a row pass forms dk = beta c [k > 0] Z (prepared keys:
+// beta Z), dbeta = k_hat . W and dv = beta c Y3 and writes whole 16-byte row
+// chunks. Waves 0-1 issue every copy (their vmcnt counts copies only, so the
+// explicit waits are exact) and waves 2-3 run the row pass and issue every
+// store. Two workgroups fit a CU (74 KB of LDS each).
+constexpr int kWsTok = 32;                       // tokens per stage
+constexpr int kWsNst = 3;                        // ring stages
+constexpr int kWsKv = kWsTok * 256;              // one stage of k (or v): 32 rows x 256 B
+constexpr int kWsSlot = 2 * kWsKv + 4 * kWsTok;  // k, v, the stage's gates
+
+// byte offset of 16-byte chunk ch of token row r in a stage tensor: row r at
+// 256 r, chunk ch at position ch ^ (r % 16), so 16 consecutive rows read at
+// one chunk, or one row read at 16 chunks, hit distinct banks
+__device__ __forceinline__ int ws_at(int r, int ch) { return r * 256 + ((ch ^ (r & 15)) << 4); }
+
+__device__ __forceinline__ bf16x8_t pack8(float4 a, float4 b) {
+  return __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
+                                                 pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w)));
+}
+
+template <bool kPrepared>
+__global__ void __launch_bounds__(256, 2)
+token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                        const float* __restrict__ beta, const float* __restrict__ gbuf,
+                        const float* __restrict__ ginit, const float* __restrict__ P,
+                        uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                        float* __restrict__ dbeta, int S, int T, int nb, float c) {
   constexpr int D = 128;
   constexpr int64_t DD = (int64_t)D * D;
-  __shared__ uint4 Pl[D * 16], Gl[D * 16], GTl[D * 16];           // 3 x 32 KB
-  __shared__ uint4 Zs[kTgWaves][kTgTok * 16], Ws[kTgWaves][kTgTok * 16];  // 2 x 4 x 8 KB
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWsNst][kWsSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t Zs[kWsKv];
+  __shared__ __attribute__((aligned(16))) uint8_t Wsb[kWsKv];
+  __shared__ __attribute__((aligned(16))) uint8_t Vsb[kWsKv];
 
-  const int xcd = blockIdx.x % kTgXcd;
-  const int slot = blockIdx.x / kTgXcd;
-  const int64_t fh = (int64_t)(slot / nb) * kTgXcd + xcd;
-  const int b = slot % nb;
-  if (fh >= FH) return;
-  const int64_t bh = fh / T;
-  const int t = (int)(fh % T);
+  const int64_t f = blockIdx.x / nb;  // frame-head
+  const int part = blockIdx.x % nb;
+  const int64_t bh = f / T;
+  const int t = (int)(f % T);
+  const int stages = (S + kWsTok - 1) / kWsTok;
+  const int st_begin = (int)((int64_t)part * stages / nb);
+  const int st_end = (int)((int64_t)(part + 1) * stages / nb);
   const int tid = threadIdx.x;
-  // the wave index is uniform across the wave: read it into a scalar so that
-  // the tile loop below is uniform control flow (no exec-masked loads)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
+  const int l32 = lane & 31, h = lane >> 5;
+  const uint16_t* kf = k + f * (int64_t)S * D;
+  const uint16_t* vf = v + f * (int64_t)S * D;
+  const float* bf = beta + f * (int64_t)S;
+  const float ck = kPrepared ? 1.f : c;  // key scale carried by the products of relu(k)
 
-  {
-    const float* Pt = P + fh * DD;
-    const float* Gt = t == T - 1 ? ginit + bh * DD : gbuf + (fh + 1) * DD;
-    for (int cc = tid; cc < D * 16; cc += 256) {
-      const int i = cc >> 4;
-      const int ch = cc & 15;
-      const int64_t off = (int64_t)i * D + 8 * ch;
-      const float4 p0 = *(const float4*)(Pt + off), p1 = *(const float4*)(Pt + off + 4);
-      const float4 g0 = *(const float4*)(Gt + off), g1 = *(const float4*)(Gt + off + 4);
-      Pl[i * 16 + tswz(i, ch)] = make_uint4(pack_bf16x2(p0.x, p0.y), pack_bf16x2(p0.z, p0.w),
-                                            pack_bf16x2(p1.x, p1.y), pack_bf16x2(p1.z, p1.w));
-      Gl[i * 16 + tswz(i, ch)] = make_uint4(pack_bf16x2(g0.x, g0.y), pack_bf16x2(g0.z, g0.w),
-                                            pack_bf16x2(g1.x, g1.y), pack_bf16x2(g1.z, g1.w));
-      float x[8];
+  // this wave's rows of P_t, G_t^T, G_t: fragment kk holds columns
+  // 16 kk + 8 h .. + 7 of row 32 w + l32
+  const float* Pt = P + f * DD;
+  const float* Gt = t == T - 1 ? ginit + bh * DD : gbuf + (f + 1) * DD;
+  const int row = 32 * wave + l32;
+  bf16x8_t pa[8], gta[8], ga[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = Gt[(int64_t)(8 * ch + e) * D + i];
-      GTl[i * 16 + tswz(i, ch)] = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                             pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
-    }
+  for (int kk = 0; kk < 8; ++kk) {
+    const int j0 = 16 * kk + 8 * h;
+    pa[kk] = pack8(*(const float4*)(Pt + row * D + j0), *(const float4*)(Pt + row * D + j0 + 4));
+    ga[kk] = pack8(*(const float4*)(Gt + row * D + j0), *(const float4*)(Gt + row * D + j0 + 4));
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = Gt[(j0 + e) * D + row];
+    gta[kk] = pack8(make_float4(x[0], x[1], x[2], x[3]), make_float4(x[4], x[5], x[6], x[7]));
   }
-  __syncthreads();
 
-  const uint16_t* kf = k + fh * (int64_t)S * D;
-  const uint16_t* vf = v + fh * (int64_t)S * D;
-  const float* bf = beta + fh * (int64_t)S;
-  uint16_t* dkf = dk ? dk + fh * (int64_t)S * D : nullptr;
-  uint16_t* dvf = dv ? dv + fh * (int64_t)S * D : nullptr;
-  float* dbf = dbeta ? dbeta + fh * (int64_t)S : nullptr;
-  const int ntiles = (S + kTgTok - 1) / kTgTok;
-  const int wstride = nb * kTgWaves;
-  int tile = b * kTgWaves + wave;
-  if (tile >= ntiles) return;
-  uint4* zs = Zs[wave];
-  uint4* ws = Ws[wave];
-  const float ck = kPrepared ? 1.f : c;  // key scale carried by the products of ReLU(k)
-
-  // B operands of the tile (token l32, features 16 kk + 8 half ..) and, for
-  // the row passes, the raw key chunk (8 ch ..) and gate of rows 4 it + lane/16;
-  // all prefetched one tile ahead
-  const int rch = lane & 15;
-  const int rrow = lane >> 4;
-  uint4 kb[8], vb[8], kr[8];
-  float br[8], bl;
-  auto fetch = [&](int tl) {
-    const int s = tl * kTgTok + l32;
+  // copies of stage st (waves 0-1): wave w fills 4-token blocks 4 w .. 4 w + 3
+  // of k and v (lane i of a block's instruction lands at byte 16 i of the
+  // block, i.e. row 4 blk + i / 16 at chunk position i % 16, so it loads the
+  // chunk (i % 16) ^ (row % 16)) and the gates of tokens 16 w .. 16 w + 15.
+  // Tokens past the end copy row S - 1.
+  constexpr int kOps = 9;  // copy instructions per copying wave and stage
+  auto issue = [&](int st) {
+    uint8_t* slot = ring[st % kWsNst];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      kb[kk] = ld_row16(kf, s, S, 16 * kk + 8 * half);
-      vb[kk] = ld_row16(vf, s, S, 16 * kk + 8 * half);
+    for (int b = 0; b < 4; ++b) {
+      const int blk = 4 * wave + b;
+      const int r = 4 * blk + (lane >> 4);
+      const int ch = (lane & 15) ^ (r & 15);
+      const int64_t off = (int64_t)min(st * kWsTok + r, S - 1) * D + 8 * ch;
+      dma16(kf + off, slot + 1024 * blk);
+      dma16(vf + off, slot + kWsKv + 1024 * blk);
     }
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int sr = tl * kTgTok + 4 * it + rrow;
-      kr[it] = ld_row16(kf, sr, S, 8 * rch);
-      br[it] = bf[min(sr, S - 1)];  // rows past the end are never stored
-    }
-    bl = bf[min(tl * kTgTok + l32, S - 1)];  // gate of this lane's token column
+    dma4(bf + min(st * kWsTok + 16 * wave + (lane & 15), S - 1), slot + 2 * kWsKv + 64 * wave,
+         lane < 16);
   };
-  fetch(tile);
-  // staged tile -> per-row pass over the 32 tokens: lane handles 16-byte
-  // chunk (lane & 15) of rows 4 it + lane / 16
-  for (; tile < ntiles; tile += wstride) {
-    bf16x8_t bk[8], bv[8];
-    uint4 krc[8];
-    float brc[8];
-    const float blc = bl;
+  if (wave < 2) {
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      krc[it] = kr[it];
-      brc[it] = br[it];
-    }
+    for (int i = 0; i < kWsNst - 1; ++i) issue(st_begin + i);
+  }
+  uint16_t* dkf = dk ? dk + f * (int64_t)S * D : nullptr;
+  uint16_t* dvf = dv ? dv + f * (int64_t)S * D : nullptr;
+  float* dbf = dbeta ? dbeta + f * (int64_t)S : nullptr;
+
+  for (int st = st_begin; st < st_end; ++st) {
+    if (wave < 2) wait_vmcnt_lgkm0<(kWsNst - 2) * kOps>();  // this wave's copies of stage st
+    else wait_vmcnt_lgkm0<63>();                             // lgkmcnt(0)
+    bare_barrier();  // stage st has landed; stage st - 1's slot and the staging are free
+    if (wave < 2) issue(st + kWsNst - 1);
+    const uint8_t* slot = ring[st % kWsNst];
+    const float* gates = (const float*)(slot + 2 * kWsKv);
+    f32x16_t y1, y2, y3;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) y1[j] = y2[j] = y3[j] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      uint4 x = kb[kk];
+      const int at = ws_at(l32, 2 * kk + h);
+      uint4 kb = *(const uint4*)(slot + at);
+      const uint4 vb = *(const uint4*)(slot + kWsKv + at);
       if (!kPrepared) {
-        x.x = relu_bf16x2_pk(x.x);
-        x.y = relu_bf16x2_pk(x.y);
-        x.z = relu_bf16x2_pk(x.z);
-        x.w = relu_bf16x2_pk(x.w);
+        kb.x = relu_bf16x2_pk(kb.x);
+        kb.y = relu_bf16x2_pk(kb.y);
+        kb.z = relu_bf16x2_pk(kb.z);
+        kb.w = relu_bf16x2_pk(kb.w);
       }
-      bk[kk] = __builtin_bit_cast(bf16x8_t, x);
-      bv[kk] = __builtin_bit_cast(bf16x8_t, vb[kk]);
+      const bf16x8_t kv8 = __builtin_bit_cast(bf16x8_t, kb);
+      y1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], kv8, y1, 0, 0, 0);
+      y2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gta[kk], __builtin_bit_cast(bf16x8_t, vb), y2, 0, 0, 0);
+      y3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[kk], kv8, y3, 0, 0, 0);
     }
-    const int s0 = tile * kTgTok;
-    const int nxt = tile + wstride;
-    if (nxt < ntiles) fetch(nxt);
-    // ---- pass 1: Y1 = P k_hat, Y2 = G^T v
-    {
-      f32x16_t y1[4], y2[4];
+    // lane (h, l32): token l32, features 32 w + 8 jg + 4 h + 0..3
+    const float bc = gates[l32] * ck;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+    for (int jg = 0; jg < 4; ++jg) {
+      float z[4], w4[4], d[4];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) y1[mt][j] = y2[mt][j] = 0.f;
-      uint4 pa[2][4], ga[2][4];
-      auto frag1 = [&](int buf, int kk) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const int row = 32 * mt + l32;
-          const int at = row * 16 + tswz(row, 2 * kk + half);
-          pa[buf][mt] = Pl[at];
-          ga[buf][mt] = GTl[at];
-        }
-      };
-      frag1(0, 0);
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        if (kk + 1 < 8) frag1((kk + 1) & 1, kk + 1);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          y1[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, pa[kk & 1][mt]),
-                                                           bk[kk], y1[mt], 0, 0, 0);
-          y2[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ga[kk & 1][mt]),
-                                                           bv[kk], y2[mt], 0, 0, 0);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const float a1 = y1[4 * jg + r] * ck, a2 = y2[4 * jg + r];
+        z[r] = a1 + a2;
+        w4[r] = 0.5f * a1 + a2;
+        d[r] = bc * y3[4 * jg + r];
       }
-      // accumulator (i, s): token s = l32, rows i = 32 mt + 8 jg + 4 half + (0..3)
+      const int at = ws_at(l32, 4 * wave + jg) + 8 * h;
+      *(uint2*)(Zs + at) = make_uint2(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]));
+      *(uint2*)(Wsb + at) = make_uint2(pack_bf16x2(w4[0], w4[1]), pack_bf16x2(w4[2], w4[3]));
+      *(uint2*)(Vsb + at) = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+    }
+    wait_vmcnt_lgkm0<63>();  // lgkmcnt(0): the staged tiles are written
+    bare_barrier();
+    if (wave >= 2) {
+      // row pass: thread u handles chunk u % 16 of rows u / 16 + 8 m; the 16
+      // chunks of a row sit in one DPP row of 16 lanes. Rows past the end
+      // were computed from copies of row S - 1, hold its values and are
+      // written there again.
+      const int u = tid - 128;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int m = 0; m < 4; ++m) {
+        const int i = u + 128 * m;
+        const int r = i >> 4, ch = i & 15;
+        const int at = ws_at(r, ch);
+        const uint4 zc = *(const uint4*)(Zs + at);
+        const uint4 wc = *(const uint4*)(Wsb + at);
+        const uint4 kc = *(const uint4*)(slot + at);
+        const float bt = gates[r];
+        const uint32_t zw[4] = {zc.x, zc.y, zc.z, zc.w};
+        const uint32_t ww[4] = {wc.x, wc.y, wc.z, wc.w};
+        const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
+        uint32_t out[4];
+        float partial = 0.f;
 #pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          float z[4], w[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float a1 = y1[mt][4 * jg + r] * ck, a2 = y2[mt][4 * jg + r];
-            z[r] = a1 + a2;
-            w[r] = 0.5f * a1 + a2;
+        for (int q = 0; q < 4; ++q) {
+          const float k0 = __uint_as_float(kw[q] << 16), k1 = __uint_as_float(kw[q] & 0xFFFF0000u);
+          const float z0 = __uint_as_float(zw[q] << 16), z1 = __uint_as_float(zw[q] & 0xFFFF0000u);
+          const float w0 = __uint_as_float(ww[q] << 16), w1 = __uint_as_float(ww[q] & 0xFFFF0000u);
+          float h0, h1, m0, m1;
+          if (kPrepared) {
+            h0 = k0; h1 = k1; m0 = m1 = 1.f;
+          } else {
+            h0 = (k0 > 0.f ? k0 : 0.f) * c; h1 = (k1 > 0.f ? k1 : 0.f) * c;
+            m0 = k0 > 0.f ? c : 0.f; m1 = k1 > 0.f ? c : 0.f;
           }
-          const int at = l32 * 16 + tswz(l32, 4 * mt + jg);
-          ((uint2*)&zs[at])[half] = make_uint2(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]));
-          ((uint2*)&ws[at])[half] = make_uint2(pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]));
+          partial += h0 * w0 + h1 * w1;
+          out[q] = pack_bf16x2(bt * m0 * z0, bt * m1 * z1);
         }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int row = 4 * it + rrow;
-      const int ch = rch;
-      const int s = s0 + row;
-      const uint4 zc = zs[row * 16 + tswz(row, ch)];
-      const uint4 wc = ws[row * 16 + tswz(row, ch)];
-      const uint4 kc = krc[it];
-      const float bt = brc[it];
-      const uint32_t zw[4] = {zc.x, zc.y, zc.z, zc.w};
-      const uint32_t ww[4] = {wc.x, wc.y, wc.z, wc.w};
-      const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
-      uint32_t out[4];
-      float part = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float k0 = __uint_as_float(kw[q] << 16), k1 = __uint_as_float(kw[q] & 0xFFFF0000u);
-        const float z0 = __uint_as_float(zw[q] << 16), z1 = __uint_as_float(zw[q] & 0xFFFF0000u);
-        const float w0 = __uint_as_float(ww[q] << 16), w1 = __uint_as_float(ww[q] & 0xFFFF0000u);
-        float h0, h1, m0, m1;
-        if (kPrepared) {
-          h0 = k0; h1 = k1; m0 = m1 = 1.f;
-        } else {
-          h0 = (k0 > 0.f ? k0 : 0.f) * c; h1 = (k1 > 0.f ? k1 : 0.f) * c;
-          m0 = k0 > 0.f ? c : 0.f; m1 = k1 > 0.f ? c : 0.f;
-        }
-        part += h0 * w0 + h1 * w1;
-        out[q] = pack_bf16x2(bt * m0 * z0, bt * m1 * z1);
+        partial = sum_row16(partial);
+        const int64_t sr = min(st * kWsTok + r, S - 1);
+        if (dkf) *(uint4*)(dkf + sr * D + 8 * ch) = make_uint4(out[0], out[1], out[2], out[3]);
+        if (dvf) *(uint4*)(dvf + sr * D + 8 * ch) = *(const uint4*)(Vsb + at);
+        if (dbf && ch == 0) dbf[sr] = partial;
       }
-      part = sum_row16(part);  // the 16 lanes of this token row
-      // Every store is issued (a store under a per-lane condition makes the
-      // compiler drain the prefetch). A row past the end was computed from
-      // clamped copies of row S - 1, so it holds exactly row S - 1's values
-      // and is written there again.
-      const int sc = min(s, S - 1);
-      if (kAll || dkf) *(uint4*)(dkf + (int64_t)sc * D + 8 * ch) = make_uint4(out[0], out[1], out[2], out[3]);
-      if (kAll || dbf) dbf[sc] = part;  // the row's 16 lanes agree
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- pass 2: Y3 = G k_hat, dv = beta Y3
-    if (kAll || dvf) {
-      f32x16_t y3[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) y3[mt][j] = 0.f;
-      uint4 gf[2][4];
-      auto frag3 = [&](int buf, int kk) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const int row = 32 * mt + l32;
-          gf[buf][mt] = Gl[row * 16 + tswz(row, 2 * kk + half)];
-        }
-      };
-      frag3(0, 0);
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        if (kk + 1 < 8) frag3((kk + 1) & 1, kk + 1);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          y3[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, gf[kk & 1][mt]),
-                                                           bk[kk], y3[mt], 0, 0, 0);
-      }
-      const float bt = blc * ck;  // columns past the end are never stored
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          const int at = l32 * 16 + tswz(l32, 4 * mt + jg);
-          ((uint2*)&zs[at])[half] =
-              make_uint2(pack_bf16x2(bt * y3[mt][4 * jg], bt * y3[mt][4 * jg + 1]),
-                         pack_bf16x2(bt * y3[mt][4 * jg + 2], bt * y3[mt][4 * jg + 3]));
-        }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int row = 4 * it + (lane >> 4);
-        const int ch = lane & 15;
-        const int sc = min(s0 + row, S - 1);  // see the dk store
-        *(uint4*)(dvf + (int64_t)sc * D + 8 * ch) = zs[row * 16 + tswz(row, ch)];
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
+  wait_vmcnt_lgkm0<0>();  // no copy may still be landing in LDS when the workgroup retires
 }
 
 // MFMA path of the per-frame gradients (D = 128): dM = S_prev^T G on fp32
@@ -719,11 +634,6 @@ hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* 
   return hipGetLastError();
 }
 
-// Workgroups per frame-head in the token-gradient kernel (each stages P_t and
-// G_t once).
-#ifndef GDN_TG_NB
-#define GDN_TG_NB 1
-#endif
 
 bool token_grad_uses_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
 
@@ -741,26 +651,16 @@ hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, cons
       if (e != hipSuccess) return e;
     }
     if (!dk && !dv && !dbeta) return hipSuccess;
-    const int ntiles = (sh.S + kTgTok - 1) / kTgTok;
-    int nb = (ntiles + kTgWaves - 1) / kTgWaves;
-    if (nb > GDN_TG_NB) nb = GDN_TG_NB;
-    const int64_t groups = (sh.FH() + kTgXcd - 1) / kTgXcd;
-    dim3 grid((unsigned)(groups * kTgXcd * nb));
+    // one workgroup per frame-head; two fit a CU
+    dim3 grid((unsigned)sh.FH());
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
-    const bool all = dk && dv && dbeta;
-#define GDN_TOKEN_GRAD(PR, ALL)                                                                \
-  token_grad_mfma_bf16_d128<PR, ALL><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P,       \
-                                                           (uint16_t*)dk, (uint16_t*)dv, dbeta, \
-                                                           sh.S, sh.T, sh.FH(), nb, sh.c)
-    if (sh.prepared) {
-      if (all) GDN_TOKEN_GRAD(true, true);
-      else GDN_TOKEN_GRAD(true, false);
-    } else {
-      if (all) GDN_TOKEN_GRAD(false, true);
-      else GDN_TOKEN_GRAD(false, false);
-    }
-#undef GDN_TOKEN_GRAD
+    if (sh.prepared)
+      token_grad_ws_bf16_d128<true><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P, (uint16_t*)dk,
+                                                           (uint16_t*)dv, dbeta, sh.S, sh.T, 1, sh.c);
+    else
+      token_grad_ws_bf16_d128<false><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P, (uint16_t*)dk,
+                                                            (uint16_t*)dv, dbeta, sh.S, sh.T, 1, sh.c);
     return hipGetLastError();
   }
   const int tpw = 256 / sh.D;

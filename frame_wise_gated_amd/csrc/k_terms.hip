@@ -15,6 +15,7 @@
 #include <type_traits>
 
 #include "gdn_common.h"
+#include "gdn_dma.h"
 
 namespace gdn {
 
@@ -35,8 +36,6 @@ namespace {
 // 32(w%4)..+32 and the 128 rows of A (w < 4) or of U (w >= 4), as four
 // 32 x 32 tiles.
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
-#define GDN_LDS __attribute__((address_space(3)))
-#define GDN_GLB __attribute__((address_space(1)))
 
 // Three stages (two in flight while one is consumed) keep two workgroups per
 // CU within the LDS (2 x 65920 B); on MI355X phase 1 ran 8 % faster than with
@@ -60,29 +59,6 @@ __device__ __forceinline__ int tr_lane_base(int lane) {
   return 2048 * (G >> 1) + 64 * (2 * (G & 1) + ((j & 3) >> 1)) + 16 * (j >> 2) + 8 * (j & 1);
 }
 
-// Global -> LDS copies, issued as inline asm: lane i's bytes land at
-// lds + 16 i (dma16) or lds + 4 i (dma4). The instruction has no result
-// register. The compiler does not track these copies (when it does, it cannot
-// tell the ring slots apart and waits for every copy in flight before any LDS
-// read), so every wait for them is explicit; its own vmcnt waits can only
-// over-wait because of them.
-// M0 is a reserved register: clobbering it in asm is only sound because no
-// other instruction of the kernels that use these helpers reads M0 (checked in
-// their ISA: the only M0 writes are the ones below).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GDN_LDS void*)lds);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(m0), "v"(g)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* g, void* lds, bool active) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GDN_LDS void*)lds);
-  if (active)
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0), "v"(g)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 
 // One MFMA operand fragment: lane gets the 8 consecutive tokens

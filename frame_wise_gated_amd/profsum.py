@@ -38,6 +38,7 @@ def _short(name: str) -> str:
             "readout_generic", "prepare_bf16_kernel", "prepare_f32_kernel",
             "copy_f32_kernel", "zero_f32_kernel", "fill_f32_kernel", "grad_init_kernel",
             "frame_grad_mfma_d128", "frame_grad_kernel", "token_grad_mfma_bf16_d128",
+            "token_grad_ws_bf16_d128", "chunk_init_kernel",
             "token_grad_generic", "prepare_norm_kernel")
     for key in keys:
         at = name.find(key)

@@ -575,6 +575,29 @@ def test_scan_bwd_fused_dq_pass_matches_separate_passes():
     assert part["dq"] is None
 
 
+def test_scan_bwd_subsets_of_outputs():
+    """Any subset of the gradients may be requested; each requested one is
+    bitwise equal to the same gradient of a call that wants all of them."""
+    w = gi.workload(2).with_shape(H=2, T=4, S=200)
+    x, d = _gen(w)
+    do, do_d, s0, dsf = _bwd_inputs(w, x, d, True)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    fwd = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], s0=dev(s0), want_o=False)
+    say("scan_bwd all outputs")
+    full = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], do_d,
+                            s0=dev(s0), ds_final=dev(dsf))
+    for want in (("dbeta",), ("dv", "ds0"), ("dk", "dgamma"), ("dq", "dv")):
+        say("scan_bwd outputs", want)
+        g = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], do_d,
+                             s0=dev(s0), ds_final=dev(dsf), want=want)
+        torch.cuda.synchronize()
+        for n in ("dq", "dk", "dv", "dbeta", "dgamma", "ds0"):
+            if n in want:
+                assert torch.equal(g[n], full[n]), (want, n)
+            else:
+                assert g[n] is None
+
+
 def test_scan_bwd_layer_60s_fused_dq():
     """The 60 s 720p layer (T = 121, S = 3600, 16 heads) in the launch
     configuration the benchmark times. The oracle is too slow at this size, so
