@@ -93,7 +93,7 @@ __device__ __forceinline__ uint4 tr_frag(const uint8_t* base, int lb, int k0, in
 #endif
 template <bool kScanLayout, bool kPrepared, bool kNorm, bool kAOnly, bool kDq>
 __global__ void __launch_bounds__(512)
-__attribute__((amdgpu_waves_per_eu(GDN_TERMS_WAVES_PER_EU, GDN_TERMS_WAVES_PER_EU)))
+__attribute__((amdgpu_waves_per_eu(kDq ? 2 : GDN_TERMS_WAVES_PER_EU, kDq ? 2 : GDN_TERMS_WAVES_PER_EU)))
 terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     const float* __restrict__ beta, int S, int n_split, float c,
                     TermsOut out, const float* __restrict__ sdq, const float* __restrict__ sdq2,
