@@ -29,6 +29,10 @@
 #ifndef GDN_SCAN_F
 #define GDN_SCAN_F 2
 #endif
+// bf16 D = 128: the combine on MFMA (1) or on fp32 vector FMAs (0)
+#ifndef GDN_COMBINE_MFMA
+#define GDN_COMBINE_MFMA 1
+#endif
 
 namespace gdn {
 
@@ -183,6 +187,118 @@ __global__ void __launch_bounds__(256) combine_rows_kernel(CombineParams p) {
     for (int r = 0; r < RPT; ++r) Xs[cur ^ 1][ig + RG * r][n] = acc[r];
     cur ^= 1;
     __syncthreads();
+  }
+}
+
+// MFMA combine for bf16 workloads (D = 128): the same recurrence
+// s_start[q+1] = s_start[q] C_q + H_q with the products on bf16 MFMA as three
+// terms of hi/lo splits (Xh Ch + Xl Ch + Xh Cl; |X - Xh - Xl| <= 2^-17 |X|,
+// likewise C), fp32 accumulation: about 16 significant bits per product, as
+// in the scan's own steps. A workgroup owns a 32-row block of one head's
+// start states (four per head) and wave w forms columns 32 w .. 32 w + 31.
+// C_q sits in LDS transposed (row n holds column n of C_q, 16-byte chunk c at
+// position c ^ (n % 16)) so that the second operand is a row read; C_{q+1}
+// and this lane's entries of H_{q+1} are loaded into registers while step q
+// computes, so a step costs LDS staging, 24 MFMAs per wave and two barriers.
+__global__ void __launch_bounds__(256, 1) combine_mfma_d128(CombineParams p) {
+  constexpr int D = 128;
+  constexpr int64_t DD = (int64_t)D * D;
+  constexpr int R = 32;
+  __shared__ uint4 Cth[D * 16], Ctl[D * 16];
+  __shared__ uint4 Xh[R * 16], Xl[R * 16];
+  int64_t bh;
+  int rb;
+  xcd_job(blockIdx.x, D / R, &bh, &rb);
+  if (bh >= p.BH) return;
+  const int row0 = rb * R;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int n = 32 * wave + l32;  // this lane's output column
+  auto at = [](int r, int c) { return r * 16 + (c ^ (r & 15)); };
+  auto hi_lo = [](float a, float b, uint32_t* hi, uint32_t* lo) {
+    *hi = pack_bf16x2(a, b);
+    *lo = pack_bf16x2(a - bf16_to_f32(*hi & 0xFFFFu), b - bf16_to_f32(*hi >> 16));
+  };
+  // X_0 = s0 (or 0): thread t holds row t / 8, columns 16 (t % 8) .. + 15
+  {
+    const int i = tid >> 3, c0 = 2 * (tid & 7);
+    float x[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      x[e] = p.s0 ? p.s0[bh * DD + (int64_t)(row0 + i) * D + 8 * c0 + e] : 0.f;
+    float* out0 = p.s_start + (bh * p.P) * DD + (int64_t)(row0 + i) * D + 8 * c0;
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) *(float4*)(out0 + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hi_lo(x[8 * cc + 2 * q], x[8 * cc + 2 * q + 1], &hw[q], &lw[q]);
+      Xh[at(i, c0 + cc)] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      Xl[at(i, c0 + cc)] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+  }
+  if (p.P < 2) return;
+  // C_q in registers: thread t holds column t % 128, rows 64 (t / 128) .. + 63;
+  // H_q: this lane's output entries (rows 8 jg + 4 h + r, column n)
+  const int cn = tid & 127, cj0 = 64 * (tid >> 7);
+  float cv[64], hq[16], hn[16];
+  auto fetch = [&](int q, float* hdst) {
+    const float* Cq = p.C + (bh * p.P + q) * DD;
+#pragma unroll
+    for (int e = 0; e < 64; ++e) cv[e] = Cq[(int64_t)(cj0 + e) * D + cn];
+    const float* Hq = p.Hc + (bh * p.P + q) * DD;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      hdst[j] = Hq[(int64_t)(row0 + 8 * (j >> 2) + 4 * h + (j & 3)) * D + n];
+  };
+  fetch(0, hq);
+  for (int q = 0; q + 1 < p.P; ++q) {
+    // C_q^T (hi, lo) into LDS from the registers
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hi_lo(cv[8 * c + 2 * e], cv[8 * c + 2 * e + 1], &hw[e], &lw[e]);
+      Cth[at(cn, cj0 / 8 + c)] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      Ctl[at(cn, cj0 / 8 + c)] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+    if (q + 2 < p.P) fetch(q + 1, hn);
+    __syncthreads();  // C_q^T and X_q are in LDS
+    f32x16_t acc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int c = 2 * kk + h;
+      const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, Xh[at(l32, c)]);
+      const bf16x8_t al = __builtin_bit_cast(bf16x8_t, Xl[at(l32, c)]);
+      const bf16x8_t bh8 = __builtin_bit_cast(bf16x8_t, Cth[at(n, c)]);
+      const bf16x8_t bl8 = __builtin_bit_cast(bf16x8_t, Ctl[at(n, c)]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh8, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh8, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl8, acc, 0, 0, 0);
+    }
+    __syncthreads();  // every wave is done reading C_q^T and X_q
+    // X_{q+1} = acc + H_q: to s_start[q+1] and, split, to LDS
+    float* outq = p.s_start + (bh * p.P + q + 1) * DD;
+    uint16_t* xh16 = (uint16_t*)Xh;
+    uint16_t* xl16 = (uint16_t*)Xl;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int i = 8 * (j >> 2) + 4 * h + (j & 3);
+      const float x = acc[j] + hq[j];
+      outq[(int64_t)(row0 + i) * D + n] = x;
+      const uint32_t hw = pack_bf16x2(x, 0.f) & 0xFFFFu;
+      const uint32_t lw = pack_bf16x2(x - bf16_to_f32(hw), 0.f) & 0xFFFFu;
+      const int e = at(i, n >> 3) * 8 + (n & 7);
+      xh16[e] = (uint16_t)hw;
+      xl16[e] = (uint16_t)lw;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) hq[j] = hn[j];
   }
 }
 
@@ -448,6 +564,10 @@ hipError_t launch_combine(const Shape& sh, const CombineParams& p, hipStream_t s
   if (sh.BH() == 0 || p.P == 0) return hipSuccess;
   CombineParams q = p;
   q.BH = sh.BH();
+  if (GDN_COMBINE_MFMA && scan_uses_mfma(sh)) {
+    combine_mfma_d128<<<dim3((unsigned)xcd_grid(q.BH, 4)), 256, 0, st>>>(q);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)xcd_grid(q.BH, sh.D / rows));
   switch (sh.D) {
     case 16: combine_rows_kernel<16><<<grid, 256, 0, st>>>(q); break;

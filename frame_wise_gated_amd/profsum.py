@@ -34,7 +34,7 @@ def _short(name: str) -> str:
     """Kernel base name, with its template arguments when the trace kept them
     (rocprofv3 without -T), e.g. terms_dma_bf16_d128<true, false>."""
     keys = ("terms_dma_bf16_d128", "terms_generic", "reduce_partials", "scan_mfma_d128",
-            "scan_rows_kernel", "combine_rows_kernel", "readout_mfma_bf16_d128",
+            "scan_rows_kernel", "combine_rows_kernel", "combine_mfma_d128", "readout_mfma_bf16_d128",
             "readout_generic", "prepare_bf16_kernel", "prepare_f32_kernel",
             "copy_f32_kernel", "zero_f32_kernel", "fill_f32_kernel", "grad_init_kernel",
             "frame_grad_mfma_d128", "frame_grad_kernel", "token_grad_mfma_bf16_d128",
