@@ -29,6 +29,9 @@
 #ifndef GDN_SCAN_F
 #define GDN_SCAN_F 2
 #endif
+#ifndef GDN_SCAN_F_COMPOSE
+#define GDN_SCAN_F_COMPOSE GDN_SCAN_F
+#endif
 // bf16 D = 128: the combine on MFMA (1) or on fp32 vector FMAs (0)
 #ifndef GDN_COMBINE_MFMA
 #define GDN_COMBINE_MFMA 1
@@ -534,7 +537,7 @@ hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st) {
     if (p.mode == SCAN_COMPOSE) {
       constexpr int MT = GDN_SCAN_MT_COMPOSE;
       const int64_t blocks = xcd_grid(q.njobs, (int)(rows_total / (16 * MT)));
-      scan_mfma_d128<MT, GDN_SCAN_F><<<dim3((unsigned)blocks), 256, 0, st>>>(q);
+      scan_mfma_d128<MT, GDN_SCAN_F_COMPOSE><<<dim3((unsigned)blocks), 256, 0, st>>>(q);
     } else {
       constexpr int MT = GDN_SCAN_MT;
       const int64_t blocks = xcd_grid(q.njobs, (int)(rows_total / (16 * MT)));
