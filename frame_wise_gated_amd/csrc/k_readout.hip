@@ -13,7 +13,7 @@
 // state once in LDS as bf16 and its four waves stream 32-token tiles of q;
 // each output tile goes through a per-wave LDS buffer so that the 8 KB tile
 // (contiguous in HBM) is written with fully coalesced 16-byte stores. The
-// workgroup -> frame-head mapping keeps both workgroups of a frame-head on one
+// workgroup -> frame-head mapping keeps all workgroups of a frame-head on one
 // XCD, so the state comes from HBM once.
 #include "gdn_common.h"
 
@@ -23,7 +23,15 @@ namespace {
 
 constexpr int kTokPerWave = 32;
 constexpr int kWavesPerBlock = 4;
-constexpr int kBlocksPerFrameHead = 2;
+// Workgroups per frame-head (their tiles interleave). HBM serves a mixed
+// read/write stream faster when the concurrently active workgroups touch a
+// narrower address window: on MI355X, 4 per frame-head ran the 60 s layer's
+// readout in 722 us against 735 us with 2; 8 and 16 lost more to staging the
+// state once per workgroup than they gained.
+#ifndef GDN_READOUT_NB
+#define GDN_READOUT_NB 4
+#endif
+constexpr int kBlocksPerFrameHead = GDN_READOUT_NB;
 constexpr int kXcd = 8;
 
 __device__ __forceinline__ uint4 ld_q(const uint16_t* q, int s, int S, int j) {
