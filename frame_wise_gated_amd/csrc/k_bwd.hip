@@ -279,7 +279,7 @@ token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restri
                         const float* __restrict__ beta, const float* __restrict__ gbuf,
                         const float* __restrict__ ginit, const float* __restrict__ P,
                         uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-                        float* __restrict__ dbeta, int S, int T, int nb, float c) {
+                        float* __restrict__ dbeta, int S, int T, int64_t FH, int nb, float c) {
   constexpr int D = 128;
   constexpr int64_t DD = (int64_t)D * D;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWsNst][kWsSlot];
@@ -287,13 +287,18 @@ token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restri
   __shared__ __attribute__((aligned(16))) uint8_t Wsb[kWsKv];
   __shared__ __attribute__((aligned(16))) uint8_t Vsb[kWsKv];
 
-  const int64_t f = blockIdx.x / nb;  // frame-head
-  const int part = blockIdx.x % nb;
+  // nb workgroups per frame-head, all on one XCD (consecutive workgroups go
+  // to consecutive XCDs); part p takes stages p, p + nb, p + 2 nb, .. so the
+  // frame-head's workgroups sweep it together
+  const int xcd = blockIdx.x % 8;
+  const int slot_id = blockIdx.x / 8;
+  const int64_t f = (int64_t)(slot_id / nb) * 8 + xcd;  // frame-head
+  const int part = slot_id % nb;
+  if (f >= FH) return;
   const int64_t bh = f / T;
   const int t = (int)(f % T);
   const int stages = (S + kWsTok - 1) / kWsTok;
-  const int st_begin = (int)((int64_t)part * stages / nb);
-  const int st_end = (int)((int64_t)(part + 1) * stages / nb);
+  const int nmine = stages > part ? (stages - part + nb - 1) / nb : 0;  // stages of this part
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -326,8 +331,10 @@ token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restri
   // chunk (i % 16) ^ (row % 16)) and the gates of tokens 16 w .. 16 w + 15.
   // Tokens past the end copy row S - 1.
   constexpr int kOps = 9;  // copy instructions per copying wave and stage
-  auto issue = [&](int st) {
-    uint8_t* slot = ring[st % kWsNst];
+  // j-th stage of this part: tokens 32 (part + j nb) ..; ring slot j % kWsNst
+  auto issue = [&](int j) {
+    const int st = part + j * nb;
+    uint8_t* slot = ring[j % kWsNst];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int blk = 4 * wave + b;
@@ -342,18 +349,19 @@ token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restri
   };
   if (wave < 2) {
 #pragma unroll
-    for (int i = 0; i < kWsNst - 1; ++i) issue(st_begin + i);
+    for (int i = 0; i < kWsNst - 1; ++i) issue(i);
   }
   uint16_t* dkf = dk ? dk + f * (int64_t)S * D : nullptr;
   uint16_t* dvf = dv ? dv + f * (int64_t)S * D : nullptr;
   float* dbf = dbeta ? dbeta + f * (int64_t)S : nullptr;
 
-  for (int st = st_begin; st < st_end; ++st) {
-    if (wave < 2) wait_vmcnt_lgkm0<(kWsNst - 2) * kOps>();  // this wave's copies of stage st
+  for (int j = 0; j < nmine; ++j) {
+    const int st = part + j * nb;
+    if (wave < 2) wait_vmcnt_lgkm0<(kWsNst - 2) * kOps>();  // this wave's copies of stage j
     else wait_vmcnt_lgkm0<63>();                             // lgkmcnt(0)
-    bare_barrier();  // stage st has landed; stage st - 1's slot and the staging are free
-    if (wave < 2) issue(st + kWsNst - 1);
-    const uint8_t* slot = ring[st % kWsNst];
+    bare_barrier();  // stage j has landed; stage j - 1's slot and the staging are free
+    if (wave < 2) issue(j + kWsNst - 1);
+    const uint8_t* slot = ring[j % kWsNst];
     const float* gates = (const float*)(slot + 2 * kWsKv);
     f32x16_t y1, y2, y3;
 #pragma unroll
@@ -635,6 +643,14 @@ hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* 
 }
 
 
+// Workgroups per frame-head of the token-gradient kernel. More than one
+// narrows the window of active addresses but reloads the P and G fragments
+// per workgroup; on MI355X 1 ran fastest (1.73 ms against 1.75 ms with 2 and
+// 1.79 ms with 4 on the 60 s layer).
+#ifndef GDN_TG_NB
+#define GDN_TG_NB 1
+#endif
+
 bool token_grad_uses_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
 
 hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, const float* beta,
@@ -651,16 +667,20 @@ hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, cons
       if (e != hipSuccess) return e;
     }
     if (!dk && !dv && !dbeta) return hipSuccess;
-    // one workgroup per frame-head; two fit a CU
-    dim3 grid((unsigned)sh.FH());
+    // GDN_TG_NB workgroups per frame-head on one XCD; two fit a CU
+    const int nb = GDN_TG_NB;
+    const int64_t groups = (sh.FH() + 7) / 8;
+    dim3 grid((unsigned)(groups * 8 * nb));
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
     if (sh.prepared)
       token_grad_ws_bf16_d128<true><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P, (uint16_t*)dk,
-                                                           (uint16_t*)dv, dbeta, sh.S, sh.T, 1, sh.c);
+                                                           (uint16_t*)dv, dbeta, sh.S, sh.T, sh.FH(),
+                                                           nb, sh.c);
     else
       token_grad_ws_bf16_d128<false><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P, (uint16_t*)dk,
-                                                            (uint16_t*)dv, dbeta, sh.S, sh.T, 1, sh.c);
+                                                            (uint16_t*)dv, dbeta, sh.S, sh.T, sh.FH(),
+                                                            nb, sh.c);
     return hipGetLastError();
   }
   const int tpw = 256 / sh.D;
