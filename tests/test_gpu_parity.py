@@ -309,6 +309,64 @@ def test_named_workload_full_size(idx, heads):
             assert e <= 1e-4, (h, e)
 
 
+# ------------------------------------------------------------ graph capture
+def test_graph_capture_replays():
+    """The library allocates nothing and clears memory with kernels, so its
+    calls can be captured in a HIP graph: a captured forward scan (composites)
+    and a captured backward, replayed several times with eager work and
+    synchronisations in between, give bit-identical results to eager calls."""
+    w = gi.workload(2).with_shape(H=2, T=9, S=300)
+    x, d = _gen(w)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    s0 = dev(_s0(w))
+    do, do_d, _, dsf = _bwd_inputs(w, x, d, True)
+    dsf = dev(dsf)
+    B, H, T, S, D = w.B, w.H, w.T, w.S, w.D
+    desc = gdn.make_desc(B, H, T, S, D, gdn.GDN_BF16)
+    ws = gdn.workspace(desc, 3, DEV)
+    bws = torch.empty(gdn.gdn_bwd_workspace_bytes(desc), dtype=torch.uint8, device=DEV)
+    st = torch.empty((B, H, T, D, D), device=DEV)
+    sf = torch.empty((B, H, D, D), device=DEV)
+    o = torch.empty_like(d["q"])
+    gout = {n: torch.empty_like(d["q"]) for n in ("dq", "dk", "dv")}
+    gout["dbeta"] = torch.empty_like(d["beta"])
+    gout["dgamma"] = torch.empty_like(d["gamma"])
+    gout["ds0"] = torch.empty_like(sf)
+
+    def call():
+        gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], s0=s0, n_time_chunks=3,
+                         states=st, s_final=sf, o=o, ws=ws)
+        gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], st, do_d, s0=s0,
+                         ds_final=dsf, out=gout, ws=bws)
+
+    say("graph capture: eager reference")
+    call()
+    torch.cuda.synchronize()
+    ref = {"states": st.clone(), "s_final": sf.clone(), "o": o.clone()}
+    ref.update({n: t.clone() for n, t in gout.items()})
+    say("graph capture: capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    outs = {"states": st, "s_final": sf, "o": o, **gout}
+    for rep in range(3):
+        for t in outs.values():  # eager work between the replays
+            t.fill_(float("nan")) if t.dtype.is_floating_point else t.zero_()
+        torch.cuda.synchronize()
+        say("graph capture: replay", rep)
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, t in outs.items():
+            assert torch.equal(t, ref[n]), (rep, n)
+
+
 # ------------------------------------------------------- batch invariance
 @pytest.mark.parametrize("mode", ["fwd", "bidir"])
 def test_batch_invariance_bitwise(mode):
