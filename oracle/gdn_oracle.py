@@ -54,6 +54,7 @@ import numpy as np
 __all__ = [
     "RMS_EPS",
     "rms_norm",
+    "rms_norm_bwd",
     "default_key_scale",
     "prepare_keys",
     "frame_terms",
@@ -84,6 +85,17 @@ def rms_norm(x, eps: float = RMS_EPS):
     weight are this module's reading (see the module docstring)."""
     x = np.asarray(x, dtype=np.float64)
     return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def rms_norm_bwd(x, dy, eps: float = RMS_EPS):
+    """Gradient through y = rms_norm(x) per token: with r = (mean(x^2) +
+    eps)^(-1/2), dy_i/dx_j = r delta_ij - r^3 x_i x_j / D, so
+    dx = r dy - r^3 (x . dy) x / D (the derivative of the definition above)."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    D = x.shape[-1]
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return r * dy - r ** 3 * np.sum(x * dy, axis=-1, keepdims=True) * x / D
 
 
 def prepare_keys(k, key_scale: float | None = None, rmsnorm: bool = False):
@@ -290,7 +302,7 @@ def combine(C, Hc, s0=None):
 
 
 def scan_fwd_bwd(q, k, v, beta, gamma, do, ds_final=None, s0=None, key_scale=None,
-                 keys_prepared=False):
+                 keys_prepared=False, qk_rmsnorm=False):
     """Reverse-mode gradients of the causal frame scan.
 
     The scalar is L = sum_{t,s} <do_{t,s}, o_{t,s}> + <ds_final, S_{T-1}>,
@@ -310,6 +322,9 @@ def scan_fwd_bwd(q, k, v, beta, gamma, do, ds_final=None, s0=None, key_scale=Non
     (k the prepared keys), dk_s = beta_s (dA + dA^T) k_s + beta_s G^T v_s,
     dbeta_s = k_s^T dA k_s + v_s^T G k_s, dv_s = beta_s G k_s; raw keys then
     pass through the key scale and the ReLU (gradient zero where k <= 0).
+    With ``qk_rmsnorm`` the readout and E use the normalised queries and the
+    keys are normalised before the ReLU (scan_fwd); dq and dk then pass back
+    through rms_norm_bwd.
     Returns dq, dk, dv [B,H,T,S,D], dbeta [B,H,T,S], dgamma [B,H,T] and
     ds0 [B,H,D,D] (the gradient reaching the initial state).
     """
@@ -331,7 +346,9 @@ def scan_fwd_bwd(q, k, v, beta, gamma, do, ds_final=None, s0=None, key_scale=Non
         c = key_scale if (key_scale is not None and key_scale > 0) else default_key_scale(D, S)
     for b in range(B):
         for h in range(H):
-            kh = _keys(k[b, h], key_scale, keys_prepared)
+            kh = _keys(k[b, h], key_scale, keys_prepared, qk_rmsnorm)
+            qh = _queries(q[b, h], qk_rmsnorm)
+            kt_pre = rms_norm(k[b, h]) if qk_rmsnorm else k[b, h]  # keys before the ReLU
             sinit = None if s0 is None else s0[b, h]
             _, states, _ = _head_fwd(None, kh, v[b, h], beta[b, h], gamma[b, h], sinit, 0, T)
             G = np.zeros((D, D)) if ds_final is None else np.array(ds_final[b, h], dtype=np.float64)
@@ -341,8 +358,9 @@ def scan_fwd_bwd(q, k, v, beta, gamma, do, ds_final=None, s0=None, key_scale=Non
                     Sp = states[t - 1]
                 else:
                     Sp = np.zeros((D, D)) if sinit is None else np.asarray(sinit, dtype=np.float64)
-                G = G + do[b, h, t].T @ q[b, h, t]
-                dq[b, h, t] = do[b, h, t] @ St
+                G = G + do[b, h, t].T @ qh[t]
+                dqh = do[b, h, t] @ St
+                dq[b, h, t] = rms_norm_bwd(q[b, h, t], dqh) if qk_rmsnorm else dqh
                 A, _ = frame_terms(kh[t], v[b, h, t], beta[b, h, t])
                 dM = Sp.T @ G
                 dgamma[b, h, t] = np.sum(dM * (np.eye(D) - A))
@@ -355,14 +373,15 @@ def scan_fwd_bwd(q, k, v, beta, gamma, do, ds_final=None, s0=None, key_scale=Non
                 if keys_prepared:
                     dk[b, h, t] = dkh
                 else:
-                    dk[b, h, t] = dkh * c * (k[b, h, t] > 0)
+                    dpre = dkh * c * (kt_pre[t] > 0)
+                    dk[b, h, t] = rms_norm_bwd(k[b, h, t], dpre) if qk_rmsnorm else dpre
                 G = G @ transition(A, gamma[b, h, t]).T
             ds0[b, h] = G
     return {"dq": dq, "dk": dk, "dv": dv, "dbeta": dbeta, "dgamma": dgamma, "ds0": ds0}
 
 
 def scan_bidir_bwd(q, k, v, beta, gamma, chunk_len, do, ds_final=None, s0=None,
-                   key_scale=None, keys_prepared=False):
+                   key_scale=None, keys_prepared=False, qk_rmsnorm=False):
     """Reverse-mode gradients of the chunk-causal bidirectional scan.
 
     The scalar is L = sum_{t,s} <do_{t,s}, o_{t,s}> + <ds_final, S_{T-1}> with
@@ -384,7 +403,8 @@ def scan_bidir_bwd(q, k, v, beta, gamma, chunk_len, do, ds_final=None, s0=None,
     G: dgamma_t = <dM_t, I - A_t>, dA_t = -gamma_t dM_t, dk_s = beta_s (dA +
     dA^T) k_s + beta_s dU^T v_s, dbeta_s = k_s^T dA k_s + v_s^T dU k_s,
     dv_s = beta_s dU k_s, and dq_{t,s} = (S_t + R_t)^T do_{t,s}. Raw keys pass
-    through the key scale and the ReLU. Returns the same dict as scan_fwd_bwd.
+    through the key scale and the ReLU; ``qk_rmsnorm`` as in scan_fwd_bwd.
+    Returns the same dict as scan_fwd_bwd.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -394,9 +414,9 @@ def scan_bidir_bwd(q, k, v, beta, gamma, chunk_len, do, ds_final=None, s0=None,
     do = np.asarray(do, dtype=np.float64)
     B, H, T, S, D = k.shape
     fwd = scan_fwd(None, k, v, beta, gamma, s0=s0, key_scale=key_scale,
-                   keys_prepared=keys_prepared, with_output=False)
+                   keys_prepared=keys_prepared, with_output=False, qk_rmsnorm=qk_rmsnorm)
     rev = scan_reverse_chunked(k, v, beta, gamma, chunk_len, key_scale=key_scale,
-                               keys_prepared=keys_prepared)
+                               keys_prepared=keys_prepared, qk_rmsnorm=qk_rmsnorm)
     out = {n: np.zeros_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dbeta", beta),
                                               ("dgamma", gamma))}
     out["ds0"] = np.zeros((B, H, D, D))
@@ -405,13 +425,15 @@ def scan_bidir_bwd(q, k, v, beta, gamma, chunk_len, do, ds_final=None, s0=None,
         c = key_scale if (key_scale is not None and key_scale > 0) else default_key_scale(D, S)
     for b in range(B):
         for h in range(H):
-            kh = _keys(k[b, h], key_scale, keys_prepared)
+            kh = _keys(k[b, h], key_scale, keys_prepared, qk_rmsnorm)
+            qh = _queries(q[b, h], qk_rmsnorm)
+            k_pre = rms_norm(k[b, h]) if qk_rmsnorm else k[b, h]  # keys before the ReLU
             St = fwd["states"][b, h]
             Rt = rev[b, h]
             sinit = np.zeros((D, D)) if s0 is None else np.asarray(s0[b, h], dtype=np.float64)
             A = [frame_terms(kh[t], v[b, h, t], beta[b, h, t])[0] for t in range(T)]
             M = [transition(A[t], gamma[b, h, t]) for t in range(T)]
-            E = [do[b, h, t].T @ q[b, h, t] for t in range(T)]
+            E = [do[b, h, t].T @ qh[t] for t in range(T)]
             dU = [np.zeros((D, D)) for _ in range(T)]
             dM = [np.zeros((D, D)) for _ in range(T)]
             # causal part
@@ -432,7 +454,8 @@ def scan_bidir_bwd(q, k, v, beta, gamma, chunk_len, do, ds_final=None, s0=None,
                     if t + 1 < e:
                         dM[t] += Rt[t + 1].T @ F
             for t in range(T):
-                out["dq"][b, h, t] = do[b, h, t] @ (St[t] + Rt[t])
+                dqh = do[b, h, t] @ (St[t] + Rt[t])
+                out["dq"][b, h, t] = rms_norm_bwd(q[b, h, t], dqh) if qk_rmsnorm else dqh
                 out["dgamma"][b, h, t] = np.sum(dM[t] * (np.eye(D) - A[t]))
                 dA = -gamma[b, h, t] * dM[t]
                 kt, vt, bt = kh[t], v[b, h, t], beta[b, h, t]
@@ -440,5 +463,9 @@ def scan_bidir_bwd(q, k, v, beta, gamma, chunk_len, do, ds_final=None, s0=None,
                 out["dv"][b, h, t] = bt[:, None] * (kt @ dU[t].T)
                 out["dbeta"][b, h, t] = (np.einsum("si,ij,sj->s", kt, dA, kt)
                                          + np.einsum("si,ij,sj->s", vt, dU[t], kt))
-                out["dk"][b, h, t] = dkh if keys_prepared else dkh * c * (k[b, h, t] > 0)
+                if keys_prepared:
+                    out["dk"][b, h, t] = dkh
+                else:
+                    dpre = dkh * c * (k_pre[t] > 0)
+                    out["dk"][b, h, t] = rms_norm_bwd(k[b, h, t], dpre) if qk_rmsnorm else dpre
     return out

@@ -498,8 +498,8 @@ def pin_rmsnorm_in_the_scan(orc):
         "without the flag, rescaled tokens must change the output"
 
 
-def _loss(orc, q, k, v, b, g, s0, do, dsf):
-    r = orc.scan_fwd(q, k, v, b, g, s0=s0)
+def _loss(orc, q, k, v, b, g, s0, do, dsf, qk_rmsnorm=False):
+    r = orc.scan_fwd(q, k, v, b, g, s0=s0, qk_rmsnorm=qk_rmsnorm)
     return float(np.sum(r["o"] * do) + np.sum(r["s_final"] * dsf))
 
 
@@ -560,9 +560,77 @@ def pin_backward_pure_decay(orc):
     _close(r["dk"], np.zeros_like(k), 0.0, "beta = 0: dk")
 
 
-def _loss_bidir(orc, q, k, v, b, g, s0, do, dsf, L):
-    r = orc.scan_bidir_chunked(q, k, v, b, g, L, s0=s0)
+def _loss_bidir(orc, q, k, v, b, g, s0, do, dsf, L, qk_rmsnorm=False):
+    r = orc.scan_bidir_chunked(q, k, v, b, g, L, s0=s0, qk_rmsnorm=qk_rmsnorm)
     return float(np.sum(r["o"] * do) + np.sum(r["s_final"] * dsf))
+
+
+def _fd_check(grads, args, loss, what, h=1e-6, tol=1e-6):
+    names = {"q": "dq", "k": "dk", "v": "dv", "beta": "dbeta", "gamma": "dgamma", "s0": "ds0"}
+    for name, arr in args.items():
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = loss()
+            arr[idx] = old - h
+            lm = loss()
+            arr[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        got = grads[names[name]]
+        err = np.max(np.abs(got - fd)) / max(1.0, np.max(np.abs(fd)))
+        assert err < tol, f"{what} {names[name]}: finite-difference mismatch {err:.3e}"
+
+
+def _fd_case(rng, B, H, T, S, D):
+    q = rng.standard_normal((B, H, T, S, D))
+    k = rng.standard_normal((B, H, T, S, D))
+    k = np.where(np.abs(k) < 0.1, 0.1 * np.sign(k + 1e-30) + k, k)
+    v = rng.standard_normal((B, H, T, S, D))
+    b = rng.uniform(0.1, 1.0, (B, H, T, S))
+    g = rng.uniform(0.8, 1.0, (B, H, T))
+    s0 = rng.standard_normal((B, H, D, D))
+    do = rng.standard_normal((B, H, T, S, D))
+    dsf = rng.standard_normal((B, H, D, D))
+    return q, k, v, b, g, s0, do, dsf
+
+
+def pin_rms_norm_bwd_finite_differences(orc):
+    """rms_norm_bwd(x, dy) is the gradient of <dy, rms_norm(x)>: central
+    finite differences element by element, including a token of tiny norm
+    (where eps matters)."""
+    rng = np.random.default_rng(35)
+    x = rng.standard_normal((3, 5))
+    x[2] *= 1e-3
+    dy = rng.standard_normal((3, 5))
+    got = orc.rms_norm_bwd(x, dy)
+    h = 1e-7
+    fd = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        old = x[idx]
+        x[idx] = old + h
+        lp = float(np.sum(orc.rms_norm(x) * dy))
+        x[idx] = old - h
+        lm = float(np.sum(orc.rms_norm(x) * dy))
+        x[idx] = old
+        fd[idx] = (lp - lm) / (2 * h)
+    err = np.max(np.abs(got - fd)) / max(1.0, np.max(np.abs(fd)))
+    assert err < 1e-6, f"rms_norm_bwd: finite-difference mismatch {err:.3e}"
+
+
+def pin_backward_rmsnorm_finite_differences(orc):
+    """The causal and the chunk-causal backward with the RMSNorm of q and k:
+    every gradient against central finite differences of the forward oracle
+    with the same flag."""
+    rng = np.random.default_rng(36)
+    q, k, v, b, g, s0, do, dsf = _fd_case(rng, 1, 1, 3, 3, 3)
+    args = {"q": q, "k": k, "v": v, "beta": b, "gamma": g, "s0": s0}
+    grads = orc.scan_fwd_bwd(q, k, v, b, g, do, ds_final=dsf, s0=s0, qk_rmsnorm=True)
+    _fd_check(grads, args, lambda: _loss(orc, q, k, v, b, g, s0, do, dsf, True),
+              "backward with RMSNorm")
+    grads = orc.scan_bidir_bwd(q, k, v, b, g, 2, do, ds_final=dsf, s0=s0, qk_rmsnorm=True)
+    _fd_check(grads, args, lambda: _loss_bidir(orc, q, k, v, b, g, s0, do, dsf, 2, True),
+              "bidirectional backward with RMSNorm")
 
 
 def pin_bidir_backward_finite_differences(orc):
@@ -638,4 +706,6 @@ ALL_PINS = [
     pin_backward_pure_decay,
     pin_bidir_backward_finite_differences,
     pin_bidir_backward_without_readout,
+    pin_rms_norm_bwd_finite_differences,
+    pin_backward_rmsnorm_finite_differences,
 ]

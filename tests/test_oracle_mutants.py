@@ -113,7 +113,8 @@ def _reverse_off_by_one(k, v, beta, gamma, chunk_len, key_scale=None, keys_prepa
 
 def _bwd_variant(kind):
     """scan_fwd_bwd with one planted mistake."""
-    def f(q, k, v, beta, gamma, do, ds_final=None, s0=None, key_scale=None, keys_prepared=False):
+    def f(q, k, v, beta, gamma, do, ds_final=None, s0=None, key_scale=None, keys_prepared=False,
+          qk_rmsnorm=False):
         q, k, v, beta, gamma, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, beta, gamma, do))
         B, H, T, S, D = k.shape
         out = {n: np.zeros_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dbeta", beta),
@@ -157,7 +158,7 @@ def _bwd_variant(kind):
 def _bidir_bwd_variant(kind):
     """scan_bidir_bwd with one planted mistake."""
     def f(q, k, v, beta, gamma, chunk_len, do, ds_final=None, s0=None, key_scale=None,
-          keys_prepared=False):
+          keys_prepared=False, qk_rmsnorm=False):
         q, k, v, beta, gamma, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, beta, gamma, do))
         B, H, T, S, D = k.shape
         fwd = orc.scan_fwd(None, k, v, beta, gamma, s0=s0, key_scale=key_scale,
@@ -213,6 +214,15 @@ def _bidir_bwd_variant(kind):
     return f
 
 
+def _rms_bwd_flipped(x, dy, eps):
+    """rms_norm_bwd with the sign of the projection term flipped."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    D = x.shape[-1]
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return r * dy + r ** 3 * np.sum(x * dy, axis=-1, keepdims=True) * x / D
+
+
 MUTANTS = {
     "U_transposed": ("frame_terms", _frame_terms_variant("U_transposed")),
     "U_no_beta": ("frame_terms", _frame_terms_variant("U_no_beta")),
@@ -251,6 +261,12 @@ MUTANTS = {
     "rms_q_ignored": ("_queries", lambda q, rmsnorm: None if q is None
                       else np.asarray(q, dtype=np.float64)),
     "combine_left_multiply": ("combine", _combine_swapped),
+    "rms_bwd_no_projection": ("rms_norm_bwd", lambda x, dy, eps=orc.RMS_EPS:
+                              np.asarray(dy, dtype=np.float64)
+                              / np.sqrt(np.mean(np.asarray(x, dtype=np.float64) ** 2, axis=-1,
+                                                keepdims=True) + eps)),
+    "rms_bwd_plus_projection": ("rms_norm_bwd", lambda x, dy, eps=orc.RMS_EPS:
+                                _rms_bwd_flipped(x, dy, eps)),
     "bidir_bwd_F_not_reset": ("scan_bidir_bwd", _bidir_bwd_variant("F_not_reset")),
     "bidir_bwd_F_same_frame_M": ("scan_bidir_bwd", _bidir_bwd_variant("F_same_frame_M")),
     "bidir_bwd_dM_no_R_term": ("scan_bidir_bwd", _bidir_bwd_variant("dM_no_R_term")),
