@@ -520,7 +520,6 @@ gdn_status run_bwd(const gdn_desc* desc, int32_t chunk_len, const void* q, const
   Shape sh;
   gdn_status s = check_desc(desc, &sh);
   if (s != GDN_OK) return s;
-  if (sh.qk_norm) return GDN_EUNSUPPORTED;
   const bool bidir = chunk_len > 0;
   if (chunk_len < 0) return GDN_EINVAL;
   const int64_t n_rev = bidir && sh.T > 0 ? ((int64_t)sh.T + chunk_len - 1) / chunk_len : 0;
@@ -570,12 +569,15 @@ gdn_status run_bwd(const gdn_desc* desc, int32_t chunk_len, const void* q, const
     Shape shq = sh;
     shq.prepared = 1;
     shq.c = 1.f;
+    // with the RMSNorm of q, E_t uses the normalised queries (the generic
+    // phase-1 kernel's mode 2: prepared keys normalised, no ReLU)
+    shq.qk_norm = sh.qk_norm ? 2 : 0;
     gdn::TermsOut eout{nullptr, E, DD, 0};
-    if (dq != nullptr && gdn::edq_fused(shq)) {
+    if ((dq != nullptr || sh.qk_norm) && gdn::edq_fused(shq)) {
       // one pass over q and d_o forms E_t and dq = (S_t [+ R_t])^T do together
       // (one workgroup per frame-head, whatever split phase 1 uses)
-      GDN_HIP(gdn::launch_edq(shq, q, d_o, states, bidir ? rev : nullptr, dq, E, st));
-      fused_dq = true;
+      GDN_HIP(gdn::launch_edq(shq, q, d_o, states, bidir ? rev : nullptr, dq, E, sh.qk_norm != 0, st));
+      fused_dq = dq != nullptr;
     } else if (L.n_split == 1) {
       GDN_HIP(gdn::launch_fill_f32(ones, sh.FH() * sh.S, 1.f, st));
       GDN_HIP(gdn::launch_terms(shq, q, d_o, ones, 1, eout, mfma, st));
@@ -644,8 +646,8 @@ gdn_status run_bwd(const gdn_desc* desc, int32_t chunk_len, const void* q, const
   }
   GDN_HIP(gdn::launch_frame_grad(sh, states, s0, G, ginit, terms, mfma, gamma, P, dgamma, rg, st));
   if (dq || dk || dv || dbeta)
-    GDN_HIP(gdn::launch_token_grad(sh, k, v, beta, d_o, states, bidir ? rev : nullptr, G, ginit, P,
-                                   fused_dq ? nullptr : dq, dk, dv, dbeta, st));
+    GDN_HIP(gdn::launch_token_grad(sh, q, k, v, beta, d_o, states, bidir ? rev : nullptr, G, ginit,
+                                   P, fused_dq ? nullptr : dq, dk, dv, dbeta, st));
   return GDN_OK;
 }
 

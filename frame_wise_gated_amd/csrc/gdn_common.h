@@ -115,6 +115,14 @@ __device__ __forceinline__ float sum_lane_xor16(float x) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
   return __int_as_float(p[0]) + __int_as_float(p[1]);
 }
+// Sum over the 16 lanes of a DPP row (rotations by 1, 2, 4, 8).
+__device__ __forceinline__ float sum_row16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  return x;
+}
 // Sum over the 16 lanes of the wave congruent to this one mod 4: DPP row
 // rotations by 4 and 8 sum the four such lanes of each 16-lane row, then the
 // row swaps add the other rows.
@@ -225,8 +233,10 @@ hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const flo
 // dq = S_t^T do (bf16) in one pass over q and d_o (bf16, D = 128 only).
 bool edq_fused(const Shape& sh);
 // states2 (nullable): reverse states summed into the state of dq.
+// norm: q is RMS-normalised for E and dq passes back through the norm; dq may
+// be NULL (E alone).
 hipError_t launch_edq(const Shape& sh, const void* q, const void* d_o, const float* states,
-                      const float* states2, void* dq, float* E, hipStream_t st);
+                      const float* states2, void* dq, float* E, bool norm, hipStream_t st);
 hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_split,
                                   TermsOut out, bool scan_layout, hipStream_t st);
 bool scan_uses_mfma(const Shape& sh);
@@ -250,7 +260,9 @@ hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* 
                              const float* gamma, float* P, float* dgamma, const RevGrad& rg,
                              hipStream_t st);
 // states2 (nullable): reverse states summed into the state of dq.
-hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, const float* beta,
+// q is read only with the RMSNorm of q (sh.qk_norm) for dq.
+hipError_t launch_token_grad(const Shape& sh, const void* q, const void* k, const void* v,
+                             const float* beta,
                              const void* dout, const float* states, const float* states2,
                              const float* gbuf, const float* ginit, const float* P, void* dq,
                              void* dk, void* dv, float* dbeta, hipStream_t st);

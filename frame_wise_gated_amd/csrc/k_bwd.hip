@@ -175,15 +175,18 @@ __global__ void __launch_bounds__(256) frame_grad_kernel(
 
 // Per-token gradients, fp32 vector path (any io type, D <= 128). A workgroup
 // handles 256 / D tokens of one frame-head; thread (token, i) forms entry i
-// of the four products, dbeta is reduced over the token's D threads.
+// of the four products, per-token sums run over the token's D threads.
+// With `norm` (the RMSNorm of q and k, raw keys only for k): the keys enter
+// the products as c ReLU(k r_k), and dq, dk pass back through the norm,
+// dx = r (dy - (y . dy) y / D) with y = x r.
 template <typename TIn, int D>
 __global__ void __launch_bounds__(256) token_grad_generic(
-    const TIn* __restrict__ k, const TIn* __restrict__ v, const float* __restrict__ beta,
-    const TIn* __restrict__ dout, const float* __restrict__ states,
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const float* __restrict__ beta, const TIn* __restrict__ dout, const float* __restrict__ states,
     const float* __restrict__ states2, const float* __restrict__ gbuf,
     const float* __restrict__ ginit, const float* __restrict__ P, TIn* __restrict__ dq,
     TIn* __restrict__ dk, TIn* __restrict__ dv, float* __restrict__ dbeta, int S, int T,
-    int ntile, float c, int prepared) {
+    int ntile, float c, int prepared, int norm) {
   constexpr int TPW = 256 / D;
   constexpr int64_t DD = (int64_t)D * D;
   __shared__ float kh[TPW][D], vs[TPW][D], ds[TPW][D], red[TPW][D];
@@ -203,8 +206,22 @@ __global__ void __launch_bounds__(256) token_grad_generic(
     if constexpr (sizeof(TIn) == 2) ((uint16_t*)p)[idx] = (uint16_t)(pack_bf16x2(x, 0.f) & 0xFFFFu);
     else ((float*)p)[idx] = x;
   };
+  // sum over the D threads of this token (every thread of the block calls it)
+  auto rowsum = [&](float x) -> float {
+    __syncthreads();
+    red[tl][i] = x;
+    __syncthreads();
+    for (int w = D / 2; w > 0; w >>= 1) {
+      if (i < w) red[tl][i] += red[tl][i + w];
+      __syncthreads();
+    }
+    return red[tl][0];
+  };
+  const bool knorm = norm && !prepared;  // prepared keys are used as given
   const float kraw = on ? ld(k, row + i) : 0.f;
-  kh[tl][i] = prepared ? kraw : (kraw > 0.f ? kraw : 0.f) * c;
+  const float rk = knorm ? rms_inv(rowsum(kraw * kraw), D) : 1.f;
+  const float kt = kraw * rk;  // the key before its ReLU
+  kh[tl][i] = prepared ? kraw : (kt > 0.f ? kt : 0.f) * c;
   vs[tl][i] = on ? ld(v, row + i) : 0.f;
   ds[tl][i] = on ? ld(dout, row + i) : 0.f;
   __syncthreads();
@@ -221,29 +238,26 @@ __global__ void __launch_bounds__(256) token_grad_generic(
     y3 = fmaf(Gt[(int64_t)i * D + j], kh[tl][j], y3);
   }
   const float b = on ? beta[f * S + s] : 0.f;
-  red[tl][i] = 0.5f * kh[tl][i] * y1 + vs[tl][i] * y3;
+  const float dbsum = rowsum(0.5f * kh[tl][i] * y1 + vs[tl][i] * y3);
+  // dk: through the ReLU and the key scale, then through the norm
+  const float dkh = b * (y1 + y2);
+  float dkv = prepared ? dkh : (kt > 0.f ? dkh * c : 0.f);
+  if (knorm) dkv = rk * (dkv - rowsum(kt * dkv) * kt / (float)D);
+  // dq: through the norm of the query
+  if (norm && dq) {
+    const float qraw = on ? ld(q, row + i) : 0.f;
+    const float rq = rms_inv(rowsum(qraw * qraw), D);
+    const float qh = qraw * rq;
+    dqv = rq * (dqv - rowsum(qh * dqv) * qh / (float)D);
+  }
   if (on) {
     if (dq) st(dq, row + i, dqv);
-    const float dkh = b * (y1 + y2);
-    if (dk) st(dk, row + i, prepared ? dkh : (kraw > 0.f ? dkh * c : 0.f));
+    if (dk) st(dk, row + i, dkv);
     if (dv) st(dv, row + i, b * y3);
+    if (i == 0 && dbeta != nullptr) dbeta[f * S + s] = dbsum;
   }
-  __syncthreads();
-  for (int w = D / 2; w > 0; w >>= 1) {
-    if (i < w) red[tl][i] += red[tl][i + w];
-    __syncthreads();
-  }
-  if (on && i == 0 && dbeta != nullptr) dbeta[f * S + s] = red[tl][0];
 }
 
-// Sum over the 16 lanes of a DPP row (rotations by 1, 2, 4, 8).
-__device__ __forceinline__ float sum_row16(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
-  return x;
-}
 
 // Weights-stationary MFMA path of the per-token gradients (bf16, D = 128).
 // Wave w keeps rows 32 w .. 32 w + 31 of P_t, G_t^T and G_t as bf16 MFMA
@@ -273,7 +287,11 @@ __device__ __forceinline__ bf16x8_t pack8(float4 a, float4 b) {
                                                  pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w)));
 }
 
-template <bool kPrepared>
+// kNorm (the RMSNorm of the raw keys): the copying waves normalise their own
+// key copies in place (k r, r = 1 / rms(k); the 16 chunks of a token sit in
+// one DPP row) and keep r per token; the row pass then takes dk through the
+// norm, dk = r (dkt - (kt . dkt) kt / D) with kt = k r.
+template <bool kPrepared, bool kNorm>
 __global__ void __launch_bounds__(256, 2)
 token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                         const float* __restrict__ beta, const float* __restrict__ gbuf,
@@ -286,6 +304,7 @@ token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restri
   __shared__ __attribute__((aligned(16))) uint8_t Zs[kWsKv];
   __shared__ __attribute__((aligned(16))) uint8_t Wsb[kWsKv];
   __shared__ __attribute__((aligned(16))) uint8_t Vsb[kWsKv];
+  __shared__ float rks[kNorm ? kWsNst : 1][kWsTok];  // 1 / rms of each token's key
 
   // nb workgroups per frame-head, all on one XCD (consecutive workgroups go
   // to consecutive XCDs); part p takes stages p, p + nb, p + 2 nb, .. so the
@@ -357,8 +376,32 @@ token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restri
 
   for (int j = 0; j < nmine; ++j) {
     const int st = part + j * nb;
-    if (wave < 2) wait_vmcnt_lgkm0<(kWsNst - 2) * kOps>();  // this wave's copies of stage j
-    else wait_vmcnt_lgkm0<63>();                             // lgkmcnt(0)
+    if (wave < 2) {
+      wait_vmcnt_lgkm0<(kWsNst - 2) * kOps>();  // this wave's copies of stage j
+      if (kNorm) {
+        uint8_t* slot_w = ring[j % kWsNst];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int blk = 4 * wave + b;
+          uint4* pk = (uint4*)(slot_w + 1024 * blk + 16 * lane);
+          const uint4 x = *pk;
+          const uint32_t w0[4] = {x.x, x.y, x.z, x.w};
+          float ss = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss = sumsq_bf16x2(w0[e], ss);
+          const float r = rms_inv(sum_row16(ss), D);
+          uint32_t o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[e] = pack_bf16x2(__uint_as_float(w0[e] << 16) * r, __uint_as_float(w0[e] & 0xFFFF0000u) * r);
+          *pk = make_uint4(o[0], o[1], o[2], o[3]);
+          if ((lane & 15) == 0) rks[kNorm ? j % kWsNst : 0][4 * blk + (lane >> 4)] = r;
+        }
+        wait_vmcnt_lgkm0<63>();  // lgkmcnt(0): the normalised keys are written
+      }
+    } else {
+      wait_vmcnt_lgkm0<63>();  // lgkmcnt(0)
+    }
     bare_barrier();  // stage j has landed; stage j - 1's slot and the staging are free
     if (wave < 2) issue(j + kWsNst - 1);
     const uint8_t* slot = ring[j % kWsNst];
@@ -420,7 +463,7 @@ token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restri
         const uint32_t ww[4] = {wc.x, wc.y, wc.z, wc.w};
         const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
         uint32_t out[4];
-        float partial = 0.f;
+        float partial = 0.f, kdot = 0.f, dkt[8], kt[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float k0 = __uint_as_float(kw[q] << 16), k1 = __uint_as_float(kw[q] & 0xFFFF0000u);
@@ -434,9 +477,21 @@ token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restri
             m0 = k0 > 0.f ? c : 0.f; m1 = k1 > 0.f ? c : 0.f;
           }
           partial += h0 * w0 + h1 * w1;
-          out[q] = pack_bf16x2(bt * m0 * z0, bt * m1 * z1);
+          dkt[2 * q] = bt * m0 * z0;
+          dkt[2 * q + 1] = bt * m1 * z1;
+          kt[2 * q] = k0;
+          kt[2 * q + 1] = k1;
+          kdot += k0 * dkt[2 * q] + k1 * dkt[2 * q + 1];
         }
         partial = sum_row16(partial);
+        if (kNorm) {  // through the norm of the key
+          const float proj = sum_row16(kdot) / (float)D;
+          const float rr = rks[kNorm ? j % kWsNst : 0][r];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dkt[e] = rr * (dkt[e] - proj * kt[e]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[q] = pack_bf16x2(dkt[2 * q], dkt[2 * q + 1]);
         const int64_t sr = min(st * kWsTok + r, S - 1);
         if (dkf) *(uint4*)(dkf + sr * D + 8 * ch) = make_uint4(out[0], out[1], out[2], out[3]);
         if (dvf) *(uint4*)(dvf + sr * D + 8 * ch) = *(const uint4*)(Vsb + at);
@@ -653,7 +708,8 @@ hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* 
 
 bool token_grad_uses_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
 
-hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, const float* beta,
+hipError_t launch_token_grad(const Shape& sh, const void* q, const void* k, const void* v,
+                             const float* beta,
                              const void* dout, const float* states, const float* states2,
                              const float* gbuf, const float* ginit, const float* P, void* dq,
                              void* dk, void* dv, float* dbeta, hipStream_t st) {
@@ -661,7 +717,7 @@ hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, cons
   if (token_grad_uses_mfma(sh)) {
     // dq = states^T do: the readout with the state staged transposed (the
     // summed states of the bidirectional scan go through the fused E pass)
-    if (dq && states2) return hipErrorInvalidValue;
+    if (dq && (states2 || sh.qk_norm)) return hipErrorInvalidValue;
     if (dq) {
       hipError_t e = launch_readout(sh, dout, states, nullptr, dq, st, true);
       if (e != hipSuccess) return e;
@@ -673,14 +729,14 @@ hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, cons
     dim3 grid((unsigned)(groups * 8 * nb));
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
-    if (sh.prepared)
-      token_grad_ws_bf16_d128<true><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P, (uint16_t*)dk,
-                                                           (uint16_t*)dv, dbeta, sh.S, sh.T, sh.FH(),
-                                                           nb, sh.c);
-    else
-      token_grad_ws_bf16_d128<false><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P, (uint16_t*)dk,
-                                                            (uint16_t*)dv, dbeta, sh.S, sh.T, sh.FH(),
-                                                            nb, sh.c);
+#define GDN_TOKEN_WS(PR, NM)                                                                    \
+  token_grad_ws_bf16_d128<PR, NM><<<grid, 256, 0, st>>>(kk, vv, beta, gbuf, ginit, P, (uint16_t*)dk, \
+                                                        (uint16_t*)dv, dbeta, sh.S, sh.T, sh.FH(), nb,  \
+                                                        sh.c)
+    if (sh.prepared) GDN_TOKEN_WS(true, false);  // prepared keys are used as given
+    else if (sh.qk_norm) GDN_TOKEN_WS(false, true);
+    else GDN_TOKEN_WS(false, false);
+#undef GDN_TOKEN_WS
     return hipGetLastError();
   }
   const int tpw = 256 / sh.D;
@@ -688,8 +744,8 @@ hipError_t launch_token_grad(const Shape& sh, const void* k, const void* v, cons
   dim3 grid((unsigned)(sh.FH() * ntile));
 #define GDN_TG(TT, DV)                                                                        \
   token_grad_generic<TT, DV><<<grid, 256, 0, st>>>(                                          \
-      (const TT*)k, (const TT*)v, beta, (const TT*)dout, states, states2, gbuf, ginit, P, (TT*)dq, \
-      (TT*)dk, (TT*)dv, dbeta, sh.S, sh.T, ntile, sh.c, sh.prepared)
+      (const TT*)q, (const TT*)k, (const TT*)v, beta, (const TT*)dout, states, states2, gbuf,    \
+      ginit, P, (TT*)dq, (TT*)dk, (TT*)dv, dbeta, sh.S, sh.T, ntile, sh.c, sh.prepared, sh.qk_norm)
   if (sh.io == 1) {
     switch (sh.D) {
       case 16: GDN_TG(uint16_t, 16); break;

@@ -99,16 +99,20 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
                     TermsOut out, const float* __restrict__ sdq, const float* __restrict__ sdq2,
                     uint16_t* __restrict__ dq) {
   constexpr int D = 128;
-  static_assert(!kDq || (kScanLayout && kPrepared && !kNorm && !kAOnly), "dq mode of the E pass");
+  static_assert(!kDq || (kScanLayout && kPrepared && !kAOnly), "dq mode of the E pass");
   // ring slot: k block, v block, then the stage's 32 gates; wbuf[st % 2]
   // holds the second operand bf16(beta . ReLU(k)) of stage st
   // Without v a slot is half as large, and the same LDS holds twice the stages.
-  constexpr int kNs = kDq ? GDN_EDQ_NST : (kAOnly ? 2 * kNst : kNst);
+  constexpr int kNs = kDq ? (kNorm ? GDN_EDQ_NST - 1 : GDN_EDQ_NST) : (kAOnly ? 2 * kNst : kNst);
   constexpr int kGateOff = (kAOnly ? 1 : 2) * kKvBytes;
   constexpr int kSlot = kGateOff + 4 * kTsd;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kNs][kSlot];
   __shared__ __attribute__((aligned(16))) uint8_t wbuf[2][kKvBytes];
   __shared__ uint4 Sl[kDq ? D * 16 : 1];  // kDq: S_t^T in bf16, row i = column i of S_t
+  // kDq with the RMSNorm of q: the stage's normalised queries in the staging
+  // layout of dq (for the norm's backward) and 1 / rms per token
+  __shared__ __attribute__((aligned(16))) uint8_t qstg[kDq && kNorm ? 2 : 1][kDq && kNorm ? kKvBytes : 16];
+  __shared__ float rqs[kDq && kNorm ? 3 : 1][kTsd];
 
   const int64_t fh = blockIdx.x / n_split;
   const int split = blockIdx.x % n_split;
@@ -281,21 +285,57 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
           make_uint2(pack_bf16x2(dacc[4 * jg], dacc[4 * jg + 1]),
                      pack_bf16x2(dacc[4 * jg + 2], dacc[4 * jg + 3]));
     }
+    if (kNorm) {  // this wave's 32 features of the stage's normalised queries
+      const uint8_t* Qs = ring[st % kNs];
+      uint8_t* qd = qstg[kNorm ? (st & 1) : 0];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int i = lane + 64 * m;
+        const int tq = i >> 2, cq = 4 * wave + (i & 3);
+        *(uint4*)(qd + tq * 256 + ((cq ^ (tq & 15)) << 4)) =
+            *(const uint4*)(Qs + 1024 * (tq >> 2) + 64 * cq + 16 * (tq & 3));
+      }
+    }
   };
   // Stores of the staged dq tile of stage st by waves 0-3 (two 16-byte row
   // pieces per thread). Tokens past the end were computed from clamped copies
   // of row S - 1, so they carry exactly row S - 1's values and are written
   // there again.
-  uint16_t* dqf = kDq ? dq + fh * (int64_t)S * D : nullptr;
+  uint16_t* dqf = (kDq && dq) ? dq + fh * (int64_t)S * D : nullptr;
+  // With the RMSNorm of q the staged tile is the gradient dqh for the
+  // normalised query qh = q r, and dq = r (dqh - (qh . dqh) qh / D); the 16
+  // chunks of a row sit in one DPP row of 16 lanes.
   auto store_dq = [&](int st) {
     const uint8_t* stg = wbuf[st & 1];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int idx = tid + 256 * r;
       const int row = idx >> 4, ch = idx & 15;
-      const uint4 x = *(const uint4*)(stg + row * 256 + ((ch ^ (row & 15)) << 4));
+      const int at = row * 256 + ((ch ^ (row & 15)) << 4);
+      uint4 x = *(const uint4*)(stg + at);
+      if (kNorm) {
+        const uint4 qv = *(const uint4*)(qstg[kNorm ? (st & 1) : 0] + at);
+        const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, qw[4] = {qv.x, qv.y, qv.z, qv.w};
+        float dv8[8], qv8[8], dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dv8[2 * e] = __uint_as_float(xw[e] << 16);
+          dv8[2 * e + 1] = __uint_as_float(xw[e] & 0xFFFF0000u);
+          qv8[2 * e] = __uint_as_float(qw[e] << 16);
+          qv8[2 * e + 1] = __uint_as_float(qw[e] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot += qv8[e] * dv8[e];
+        dot = sum_row16(dot) / (float)D;
+        const float rr = rqs[kNorm ? st % 3 : 0][row];
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = pack_bf16x2(rr * (dv8[2 * e] - dot * qv8[2 * e]), rr * (dv8[2 * e + 1] - dot * qv8[2 * e + 1]));
+        x = make_uint4(o[0], o[1], o[2], o[3]);
+      }
       const int sr = min(st * kTsd + row, S - 1);
-      *(uint4*)(dqf + (int64_t)sr * D + 8 * ch) = x;
+      if (dqf) *(uint4*)(dqf + (int64_t)sr * D + 8 * ch) = x;
     }
   };
 
@@ -311,7 +351,33 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   for (int i = 0; i < kNs - 1; ++i) issue(st_begin + i);
   if (kDq) {
     for (int st = st_begin; st < st_end; ++st) {
-      if (wave >= 4) {
+      if (wave >= 4 && kNorm) {
+        wait_vmcnt_lgkm0<(kNs - 2) * kOps>();  // this wave's copies of stage st
+        // RMSNorm of this wave's own query copies, in place: the 16 chunks of
+        // a token sit in the lanes congruent to this one mod 4. Tokens past
+        // the end are zeroed (they add nothing to E_t).
+        uint8_t* slot = ring[st % kNs];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int blk = 2 * (wave - 4) + h;
+          uint4* p = (uint4*)(slot + 1024 * blk + 16 * lane);
+          const uint4 x = *p;
+          const uint32_t w0[4] = {x.x, x.y, x.z, x.w};
+          float ss = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss = sumsq_bf16x2(w0[e], ss);
+          const float r = rms_inv(sum_lanes_mod4(ss), D);
+          const bool past = st * kTsd + 4 * blk + (lane & 3) >= S;
+          uint32_t o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[e] = past ? 0u
+                        : pack_bf16x2(__uint_as_float(w0[e] << 16) * r, __uint_as_float(w0[e] & 0xFFFF0000u) * r);
+          *p = make_uint4(o[0], o[1], o[2], o[3]);
+          if ((lane >> 2) == 0) rqs[kNorm ? st % 3 : 0][4 * blk + (lane & 3)] = r;
+        }
+        wait_vmcnt_lgkm0<63>();
+      } else if (wave >= 4) {
         wait_vmcnt_lgkm0<(kNs - 2) * kOps>();  // this wave's copies of stage st
         if ((st + 1) * kTsd > S) {
           // tokens past the end hold copies of row S - 1 and have no gate
@@ -483,7 +549,9 @@ terms_generic(const TIn* __restrict__ k, const TIn* __restrict__ v, const float*
     __syncthreads();
     if (tid < TSG) {
       float f = c;
-      if (norm && !prepared && s0 + tid < s_end) {
+      // norm == 2: prepared keys normalised without ReLU (queries of the
+      // backward's E pass)
+      if (norm && (!prepared || norm == 2) && s0 + tid < s_end) {
         float ss = 0.f;
         for (int j = 0; j < D; ++j) {
           const float kv = ld<TIn>(kf, (int64_t)(s0 + tid) * D + j);
@@ -502,7 +570,7 @@ terms_generic(const TIn* __restrict__ k, const TIn* __restrict__ v, const float*
       if (tok < s_end) {
         if (m < D) {
           float kv = ld<TIn>(kf, (int64_t)tok * D + m);
-          val = prepared ? kv : (kv > 0.f ? kv : 0.f) * rn[s];
+          val = prepared ? (norm == 2 ? kv * rn[s] : kv) : (kv > 0.f ? kv : 0.f) * rn[s];
         } else {
           val = ld<TIn>(vf, (int64_t)tok * D + (m - D));
         }
@@ -516,7 +584,7 @@ terms_generic(const TIn* __restrict__ k, const TIn* __restrict__ v, const float*
       float val = 0.f;
       if (tok < s_end) {
         float kv = ld<TIn>(kf, (int64_t)tok * D + n);
-        val = bf[tok] * (prepared ? kv : (kv > 0.f ? kv : 0.f) * rn[s]);
+        val = bf[tok] * (prepared ? (norm == 2 ? kv * rn[s] : kv) : (kv > 0.f ? kv : 0.f) * rn[s]);
       }
       Ws[s][n] = val;
     }
@@ -644,8 +712,10 @@ hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const flo
 #define GDN_TERMS_DMA(L, P, N, AO)                                                           \
   terms_dma_bf16_d128<L, P, N, AO, false><<<grid, 512, 0, st>>>(kk, vv, beta, sh.S, n_split, sh.c, \
                                                                 out, nullptr, nullptr, nullptr)
-    if (scan_layout && out.outU == nullptr && !norm) {  // A_t alone (the backward's recompute)
+    if (sh.qk_norm == 2) return hipErrorInvalidValue;  // the generic path's E mode only
+    if (scan_layout && out.outU == nullptr) {  // A_t alone (the backward's recompute)
       if (sh.prepared) GDN_TERMS_DMA(true, true, false, true);
+      else if (norm) GDN_TERMS_DMA(true, false, true, true);
       else GDN_TERMS_DMA(true, false, false, true);
     } else if (scan_layout) {
       if (sh.prepared) GDN_TERMS_DMA(true, true, false, false);
@@ -666,13 +736,18 @@ hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const flo
 bool edq_fused(const Shape& sh) { return terms_use_mfma(sh); }
 
 hipError_t launch_edq(const Shape& sh, const void* q, const void* d_o, const float* states,
-                      const float* states2, void* dq, float* E, hipStream_t st) {
+                      const float* states2, void* dq, float* E, bool norm, hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
   if (!edq_fused(sh)) return hipErrorInvalidValue;
   TermsOut out{nullptr, E, (int64_t)sh.D * sh.D, 0};
-  terms_dma_bf16_d128<true, true, false, false, true><<<dim3((unsigned)sh.FH()), 512, 0, st>>>(
-      (const uint16_t*)q, (const uint16_t*)d_o, nullptr, sh.S, 1, 1.f, out, states, states2,
-      (uint16_t*)dq);
+  if (norm)
+    terms_dma_bf16_d128<true, true, true, false, true><<<dim3((unsigned)sh.FH()), 512, 0, st>>>(
+        (const uint16_t*)q, (const uint16_t*)d_o, nullptr, sh.S, 1, 1.f, out, states, states2,
+        (uint16_t*)dq);
+  else
+    terms_dma_bf16_d128<true, true, false, false, true><<<dim3((unsigned)sh.FH()), 512, 0, st>>>(
+        (const uint16_t*)q, (const uint16_t*)d_o, nullptr, sh.S, 1, 1.f, out, states, states2,
+        (uint16_t*)dq);
   return hipGetLastError();
 }
 

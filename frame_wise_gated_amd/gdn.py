@@ -293,10 +293,10 @@ def gdn_bwd_workspace_bytes(desc: gdn_desc) -> int:
 
 def gdn_scan_bwd(q, k, v, beta, gamma, states, d_o, s0=None, ds_final=None, key_scale=0.0,
                  keys_prepared=False, want=("dq", "dk", "dv", "dbeta", "dgamma", "ds0"),
-                 out=None, ws=None, stream=None):
+                 out=None, ws=None, stream=None, qk_rmsnorm=False):
     """Gradients of the causal frame scan; `states` are the forward's
     per-frame states. Returns a dict with the requested gradients."""
-    d = _desc_from(k, key_scale, keys_prepared)
+    d = _desc_from(k, key_scale, keys_prepared, qk_rmsnorm)
     B, H, T, S, D = k.shape
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (d_o, "d_o")):
         _need(t, n, k.shape, k.dtype)
@@ -333,11 +333,11 @@ def gdn_bidir_bwd_workspace_bytes(desc: gdn_desc, chunk_len: int) -> int:
 def gdn_scan_bidir_chunked_bwd(q, k, v, beta, gamma, chunk_len, states_fwd, states_rev, d_o,
                                s0=None, ds_final=None, key_scale=0.0, keys_prepared=False,
                                want=("dq", "dk", "dv", "dbeta", "dgamma", "ds0"), out=None,
-                               ws=None, stream=None):
+                               ws=None, stream=None, qk_rmsnorm=False):
     """Gradients of the chunk-causal bidirectional scan; `states_fwd` and
     `states_rev` are the forward call's states. Returns a dict with the
     requested gradients."""
-    d = _desc_from(k, key_scale, keys_prepared)
+    d = _desc_from(k, key_scale, keys_prepared, qk_rmsnorm)
     B, H, T, S, D = k.shape
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (d_o, "d_o")):
         _need(t, n, k.shape, k.dtype)

@@ -125,7 +125,7 @@ def test_null_and_chunk_arguments(L):
     bwd = lambda dd, states, nb: L.gdn_scan_bwd(ctypes.byref(dd), fake, fake, fake, fake, fake, None,
                                                 states, fake, None, fake, fake, fake, fake, fake,
                                                 None, fake, nb, None)
-    assert bwd(dn, fake, 1 << 30) == gdn.GDN_EUNSUPPORTED
+    assert bwd(dn, fake, 16) == gdn.GDN_EWORKSPACE  # RMSNorm accepted
     assert bwd(d, None, 1 << 30) == gdn.GDN_EINVAL
     assert bwd(d, fake, 16) == gdn.GDN_EWORKSPACE
     nbw = ctypes.c_size_t(0)
@@ -138,7 +138,7 @@ def test_null_and_chunk_arguments(L):
         fake, fake, fake, None, fake, nb, None)
     assert bbw(d, 0, fake, 1 << 30) == gdn.GDN_EINVAL
     assert bbw(d, 2, None, 1 << 30) == gdn.GDN_EINVAL
-    assert bbw(dn, 2, fake, 1 << 30) == gdn.GDN_EUNSUPPORTED
+    assert bbw(dn, 2, fake, 16) == gdn.GDN_EWORKSPACE  # RMSNorm accepted
     assert bbw(d, 2, fake, 16) == gdn.GDN_EWORKSPACE
     dlong = gdn.make_desc(1, 1, 300, 12, 16, gdn.GDN_F32)
     assert bbw(dlong, 1, fake, 1 << 30) == gdn.GDN_EUNSUPPORTED

@@ -774,6 +774,88 @@ def test_scan_bidir_bwd_layer_full_size():
             assert e <= tol(w), (n, e)
 
 
+RMS_BWD_CASES = {
+    # name: (workload, chunk_len (0: causal), keys_prepared)
+    "f32_D16": (gi.workload(1), 0, False),
+    "f32_D64": (gi.workload(1).with_shape(D=64, S=40, T=4), 0, False),
+    "f32_D16_bidir_L3": (gi.workload(1), 3, False),
+    "bf16_D128": (gi.workload(2).with_shape(H=2, T=5, S=300), 0, False),
+    "bf16_D128_split_S2100": (gi.workload(2).with_shape(T=3, S=2100), 0, False),
+    "bf16_D128_bidir_L2": (gi.workload(2).with_shape(H=2, T=5, S=170), 2, False),
+    "bf16_D128_prepared": (gi.workload(2).with_shape(H=2, T=4, S=170), 0, True),
+    "bf16_D64": (gi.workload(2).with_shape(D=64, T=4, S=130), 0, False),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RMS_BWD_CASES))
+def test_scan_bwd_rmsnorm(name):
+    """Backward with the RMSNorm of q and k (raw keys; prepared keys are used
+    as given) against the float64 oracle, on inputs whose tokens are
+    rescaled so that a missing or wrong norm would show."""
+    w, L, prepared = RMS_BWD_CASES[name]
+    x, d = _gen_rescaled(w)
+    if prepared:
+        kh = orc.prepare_keys(x["k"]).astype(np.float32)
+        bits = gi.f32_to_bf16_bits(kh)
+        kh = gi.bf16_bits_to_f32(bits)
+        d["k"] = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+        x["k"] = kh
+    do, do_d, s0, dsf = _bwd_inputs(w, x, d, True)
+    dev = lambda a: None if a is None else torch.from_numpy(a).to(DEV)
+    say("scan_bwd rmsnorm", name, "forward")
+    if L:
+        fwd = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], L,
+                                         s0=dev(s0), keys_prepared=prepared, want_o=False,
+                                         qk_rmsnorm=True)
+        say("scan_bwd rmsnorm", name, "backward")
+        g = gdn.gdn_scan_bidir_chunked_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], L,
+                                           fwd["states_fwd"], fwd["states_rev"], do_d, s0=dev(s0),
+                                           ds_final=dev(dsf), keys_prepared=prepared,
+                                           qk_rmsnorm=True)
+    else:
+        fwd = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], s0=dev(s0),
+                               keys_prepared=prepared, want_o=False, qk_rmsnorm=True)
+        say("scan_bwd rmsnorm", name, "backward")
+        g = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], do_d,
+                             s0=dev(s0), ds_final=dev(dsf), keys_prepared=prepared,
+                             qk_rmsnorm=True)
+    torch.cuda.synchronize()
+    for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
+        a = head_arrays(x, b, h)
+        kw = dict(ds_final=dsf[b, h][None, None].astype(np.float64),
+                  s0=s0[b, h][None, None].astype(np.float64), keys_prepared=prepared,
+                  qk_rmsnorm=True)
+        dof = do[b, h][None, None].astype(np.float64)
+        if L:
+            ref = orc.scan_bidir_bwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"], L, dof, **kw)
+        else:
+            ref = orc.scan_fwd_bwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"], dof, **kw)
+        for n in ("dq", "dk", "dv", "dbeta", "dgamma", "ds0"):
+            e = rel_fro(host(g[n][b, h]), ref[n][0, 0])
+            say(name, (b, h), n, f"{e:.2e}")
+            assert e <= tol(w), (n, e)
+
+
+def test_scan_bwd_rmsnorm_without_dq():
+    """With the RMSNorm of q, E_t still comes from the fused pass when dq is
+    not wanted; the other gradients are bitwise those of the full call."""
+    w = gi.workload(2).with_shape(H=2, T=4, S=200)
+    x, d = _gen_rescaled(w)
+    do, do_d, s0, dsf = _bwd_inputs(w, x, d, True)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    fwd = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], s0=dev(s0), want_o=False,
+                           qk_rmsnorm=True)
+    say("scan_bwd rmsnorm without dq")
+    full = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], do_d,
+                            s0=dev(s0), ds_final=dev(dsf), qk_rmsnorm=True)
+    part = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], do_d,
+                            s0=dev(s0), ds_final=dev(dsf), qk_rmsnorm=True,
+                            want=("dk", "dv", "dbeta", "dgamma", "ds0"))
+    torch.cuda.synchronize()
+    for n in ("dk", "dv", "dbeta", "dgamma", "ds0"):
+        assert torch.equal(full[n], part[n]), n
+
+
 def test_scan_bwd_no_frames():
     w = gi.workload(1).with_shape(T=0)
     x, d = _gen(w)
