@@ -183,7 +183,10 @@ GDN_API gdn_status gdn_bwd_workspace_bytes(const gdn_desc* desc, size_t* bytes);
  * required), ds_final [B,H,D,D] (NULL = zero). Outputs (each may be NULL):
  * dq, dk, dv [B,H,T,S,D] (io dtype), dbeta [B,H,T,S], dgamma [B,H,T],
  * ds0 [B,H,D,D] (fp32). The adjoint recurrence runs sequentially over the
- * frames. GDN_QK_RMSNORM is not supported here (GDN_EUNSUPPORTED).
+ * frames. With GDN_QK_RMSNORM, E_t and the readout use the normalised
+ * queries and the raw keys are normalised before their ReLU (as in the
+ * forward call); dq and dk then pass back through the norm, dx =
+ * r (dy - (y . dy) y / D) with y = x r, r = 1 / rms(x).
  * Workspace: gdn_bwd_workspace_bytes. */
 GDN_API gdn_status gdn_scan_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
                                 const float* beta, const float* gamma, const float* s0,
@@ -209,7 +212,7 @@ GDN_API gdn_status gdn_bidir_bwd_workspace_bytes(const gdn_desc* desc, int32_t c
  * Inputs: as gdn_scan_bwd plus chunk_len (>= 1, as in the forward call) and
  * the forward's states_fwd and states_rev [B,H,T,D,D] (both required).
  * Outputs as gdn_scan_bwd (each may be NULL). More than 256 chunks:
- * GDN_EUNSUPPORTED. GDN_QK_RMSNORM is not supported here.
+ * GDN_EUNSUPPORTED. GDN_QK_RMSNORM as in gdn_scan_bwd.
  * Workspace: gdn_bidir_bwd_workspace_bytes. */
 GDN_API gdn_status gdn_scan_bidir_chunked_bwd(const gdn_desc* desc, int32_t chunk_len,
                                               const void* q, const void* k, const void* v,
