@@ -269,7 +269,7 @@ def main():
         }
         del A, U
 
-    if not args.no_backward and not norm:
+    if not args.no_backward:
         # backward of the same layer: gradients of <d_o, o> for a random d_o
         # (the chunk-causal backward for the bidirectional workload)
         print("[bench] backward", file=sys.stderr, flush=True)
@@ -284,11 +284,11 @@ def main():
                               device=dev)
             bstep = lambda: gdn.gdn_scan_bidir_chunked_bwd(q, k, v, beta, gamma, w.chunk_len, st_fwd,
                                                            st_rev, d_o, out=grads, ws=bws,
-                                                           stream=stream)
+                                                           stream=stream, qk_rmsnorm=norm)
         else:
             bws = torch.empty(gdn.gdn_bwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
             bstep = lambda: gdn.gdn_scan_bwd(q, k, v, beta, gamma, st_fwd, d_o, out=grads, ws=bws,
-                                             stream=stream)
+                                             stream=stream, qk_rmsnorm=norm)
         for _ in range(2):
             bstep()
         t_bwd = timed(bstep, max(args.steps // 2, 3))
