@@ -47,30 +47,35 @@ def per_frame_head(w):
                 readout_bytes=readout_bytes, step_flop=step_flop, step_bytes=step_bytes)
 
 
-def kernel_names(w):
-    """Names of the phase-1 and readout kernels the library launches for w."""
+def kernel_names(w, norm):
+    """(name, template arguments, source) of the phase-1 and readout kernels
+    that gdn_frame_terms and gdn_readout launch for w, as rocprofv3 names them."""
     if w.io == "bf16" and w.D == 128:
-        return {"terms": ("terms_dma_bf16_d128", "k_terms.hip"),
-                "readout": ("readout_mfma_bf16_d128", "k_readout.hip")}
-    return {"terms": ("terms_generic", "k_terms.hip"), "readout": ("readout_generic", "k_readout.hip")}
+        n = "true" if norm else "false"
+        return {"terms": ("terms_dma_bf16_d128", f"<false, false, {n}, false, false>", "k_terms.hip"),
+                "readout": ("readout_mfma_bf16_d128", f"<{n}, false>", "k_readout.hip")}
+    return {"terms": ("terms_generic", "", "k_terms.hip"),
+            "readout": ("readout_generic", "", "k_readout.hip")}
 
 
-def recorded_traffic(kernel, source, workload):
-    """HBM bytes per launch of `kernel` on `workload` from the committed
-    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled by the
-    plain-copy calibration), or None when there is none or the kernel's
-    source has changed since the counters were taken."""
+def recorded_traffic(kernel, variant, source, workload):
+    """HBM bytes per launch of `kernel` (template arguments `variant`) on
+    `workload` from the committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE, scaled by the plain-copy calibration), or None when there is
+    none, it covers another instance of the kernel, or the kernel's source has
+    changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__hbm_traffic.txt")
     src = os.path.join(ROOT, "frame_wise_gated_amd", "csrc", source)
     if not (os.path.exists(path) and os.path.exists(src)):
         return None
     fields = {}
     for line in open(path):
-        parts = line.split()
-        if len(parts) == 2 and parts[0] in ("source_sha256", "hbm_bytes_per_launch"):
-            fields[parts[0]] = parts[1]
+        key, _, val = line.strip().partition(" ")
+        if key in ("source_sha256", "hbm_bytes_per_launch", "kernel_instance"):
+            fields[key] = val.strip()
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("source_sha256") != sha or "hbm_bytes_per_launch" not in fields:
+    if (fields.get("source_sha256") != sha or "hbm_bytes_per_launch" not in fields
+            or fields.get("kernel_instance") != kernel + variant):
         return None
     return int(fields["hbm_bytes_per_launch"])
 
@@ -253,14 +258,14 @@ def main():
         name = max(phases, key=lambda n: phases[n][0])
         t, nbytes, nflop = phases[name]
         achieved = nbytes / (t / 1e3) / 1e9
-        kname, ksrc = kernel_names(w)[name]
+        kname, kvar, ksrc = kernel_names(w, norm)[name]
         out["roofline"] = {
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": recorded_traffic(kname, ksrc, w.name),
+            "traffic": recorded_traffic(kname, kvar, ksrc, out["config"]["workload"]),
             "kernel": kname,
             "algorithmic_bytes_per_launch": nbytes,
             "ms_per_launch": t,

@@ -32,10 +32,11 @@ def test_per_frame_head_bytes_and_flops():
     assert pf["step_flop"] == 4 * D * D * S + 2 * D * D * S + 2 * D ** 3
 
 
-def _traffic_file(tmp_path, kernel, workload, sha, nbytes):
+def _traffic_file(tmp_path, kernel, variant, workload, sha, nbytes):
     (tmp_path / "profiles").mkdir(exist_ok=True)
     (tmp_path / "profiles" / f"{kernel}__{workload}__hbm_traffic.txt").write_text(
-        f"header\nsource_sha256 {sha}\nhbm_bytes_per_launch {nbytes}\n")
+        f"header\nkernel_instance {kernel}{variant}\nsource_sha256 {sha}\n"
+        f"hbm_bytes_per_launch {nbytes}\n")
 
 
 def test_recorded_traffic_follows_source_hash(tmp_path, monkeypatch):
@@ -43,12 +44,26 @@ def test_recorded_traffic_follows_source_hash(tmp_path, monkeypatch):
     src_dir.mkdir(parents=True)
     (src_dir / "k.hip").write_text("kernel v1\n")
     sha = hashlib.sha256(b"kernel v1\n").hexdigest()
-    _traffic_file(tmp_path, "kern", "wl", sha, 1234)
+    _traffic_file(tmp_path, "kern", "<false, true>", "wl", sha, 1234)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench.recorded_traffic("kern", "k.hip", "wl") == 1234
+    assert bench.recorded_traffic("kern", "<false, true>", "k.hip", "wl") == 1234
+    # another instance of the same kernel, another workload: no figure
+    assert bench.recorded_traffic("kern", "<true, true>", "k.hip", "wl") is None
+    assert bench.recorded_traffic("kern", "<false, true>", "k.hip", "wl_qk_rmsnorm") is None
     (src_dir / "k.hip").write_text("kernel v2\n")      # source changed: counters are stale
-    assert bench.recorded_traffic("kern", "k.hip", "wl") is None
-    assert bench.recorded_traffic("other", "k.hip", "wl") is None
+    assert bench.recorded_traffic("kern", "<false, true>", "k.hip", "wl") is None
+    assert bench.recorded_traffic("other", "<false, true>", "k.hip", "wl") is None
+
+
+def test_kernel_names_match_launched_instances():
+    from frame_wise_gated_amd.inputs import workload
+    w = workload(4)
+    plain, normed = bench.kernel_names(w, False), bench.kernel_names(w, True)
+    assert plain["terms"][:2] == ("terms_dma_bf16_d128", "<false, false, false, false, false>")
+    assert plain["readout"][:2] == ("readout_mfma_bf16_d128", "<false, false>")
+    assert normed["terms"][1] == "<false, false, true, false, false>"
+    assert normed["readout"][1] == "<true, false>"
+    assert bench.kernel_names(workload(1), False)["terms"][0] == "terms_generic"
 
 
 def test_profsum_trace_and_pmc(tmp_path):
