@@ -187,14 +187,15 @@ def main():
     ws = gdn.workspace(desc, w.time_chunks, dev)
     stream = torch.cuda.current_stream()
 
-    def step():
+    def step(ws_=None):
+        ws_ = ws if ws_ is None else ws_
         if w.mode == "bidir":
             gdn.gdn_scan_bidir_chunked(q, k, v, beta, gamma, w.chunk_len, n_time_chunks=w.time_chunks,
                                        states_fwd=st_fwd, states_rev=st_rev, s_final=s_fin, o=o,
-                                       ws=ws, stream=stream, qk_rmsnorm=norm)
+                                       ws=ws_, stream=stream, qk_rmsnorm=norm)
         else:
             gdn.gdn_scan_fwd(q, k, v, beta, gamma, n_time_chunks=w.time_chunks, states=st_fwd,
-                             s_final=s_fin, o=o, ws=ws, stream=stream, qk_rmsnorm=norm)
+                             s_final=s_fin, o=o, ws=ws_, stream=stream, qk_rmsnorm=norm)
 
     def timed(fn, reps):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -287,16 +288,28 @@ def main():
         if w.mode == "bidir":
             bws = torch.empty(gdn.gdn_bidir_bwd_workspace_bytes(desc, w.chunk_len), dtype=torch.uint8,
                               device=dev)
-            bstep = lambda: gdn.gdn_scan_bidir_chunked_bwd(q, k, v, beta, gamma, w.chunk_len, st_fwd,
-                                                           st_rev, d_o, out=grads, ws=bws,
-                                                           stream=stream, qk_rmsnorm=norm)
+            bcall = lambda ws_, reuse: gdn.gdn_scan_bidir_chunked_bwd(
+                q, k, v, beta, gamma, w.chunk_len, st_fwd, st_rev, d_o, out=grads, ws=ws_,
+                stream=stream, qk_rmsnorm=norm, reuse_fwd_terms=reuse)
         else:
             bws = torch.empty(gdn.gdn_bwd_workspace_bytes(desc), dtype=torch.uint8, device=dev)
-            bstep = lambda: gdn.gdn_scan_bwd(q, k, v, beta, gamma, st_fwd, d_o, out=grads, ws=bws,
-                                             stream=stream, qk_rmsnorm=norm)
+            bcall = lambda ws_, reuse: gdn.gdn_scan_bwd(
+                q, k, v, beta, gamma, st_fwd, d_o, out=grads, ws=ws_, stream=stream,
+                qk_rmsnorm=norm, reuse_fwd_terms=reuse)
+        bstep = lambda: bcall(bws, False)
         for _ in range(2):
             bstep()
         t_bwd = timed(bstep, max(args.steps // 2, 3))
+        # the same backward reading A_t from the workspace of its forward call
+        # (GDN_REUSE_FWD_TERMS): one forward call into a workspace sized for
+        # both, then the timed backward calls on it
+        fws = torch.empty(max(ws.numel(), bws.numel()), dtype=torch.uint8, device=dev)
+        step(fws)
+        rstep = lambda: bcall(fws, True)
+        for _ in range(2):
+            rstep()
+        t_bwd_r = timed(rstep, max(args.steps // 2, 3))
+        del fws
         # algorithmic bytes: q, k, v, d_o, beta, gamma and the forward states
         # (both directions for the bidirectional scan) in; dq, dk, dv, dbeta,
         # dgamma out
@@ -308,6 +321,11 @@ def main():
             "layer_frames_per_s": T / (t_bwd / 1e3),
             "algorithmic_bytes": bw_bytes,
             "hbm_frac": bw_bytes / (t_bwd / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "reusing_fwd_terms": {
+                "ms_per_call": t_bwd_r,
+                "layer_frames_per_s": T / (t_bwd_r / 1e3),
+                "hbm_frac": bw_bytes / (t_bwd_r / 1e3) / 1e9 / HBM_PEAK_GBS,
+            },
         }
         del grads, bws, d_o
 

@@ -22,7 +22,8 @@ gdn_status check_desc(const gdn_desc* d, Shape* sh) {
   if (d == nullptr) return GDN_EINVAL;
   if (d->B < 0 || d->H < 0 || d->T < 0 || d->S < 1 || d->D < 1) return GDN_EINVAL;
   if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) return GDN_EINVAL;
-  if ((d->flags & ~(GDN_KEYS_PREPARED | GDN_QK_RMSNORM)) != 0) return GDN_EINVAL;
+  if ((d->flags & ~(GDN_KEYS_PREPARED | GDN_QK_RMSNORM | GDN_REUSE_FWD_TERMS)) != 0)
+    return GDN_EINVAL;
   if (!(std::isfinite(d->key_scale))) return GDN_EINVAL;
   if (d->D != 16 && d->D != 32 && d->D != 64 && d->D != 128) return GDN_EUNSUPPORTED;
   // element counts must stay far from 64-bit overflow
@@ -36,6 +37,7 @@ gdn_status check_desc(const gdn_desc* d, Shape* sh) {
   sh->io = d->io_dtype;
   sh->prepared = (d->flags & GDN_KEYS_PREPARED) ? 1 : 0;
   sh->qk_norm = (d->flags & GDN_QK_RMSNORM) ? 1 : 0;
+  sh->reuse_terms = (d->flags & GDN_REUSE_FWD_TERMS) ? 1 : 0;
   if (sh->prepared) {
     sh->c = 1.0f;
   } else if (d->key_scale > 0.f) {
@@ -76,7 +78,9 @@ Layout layout(const Shape& sh, int P) {
   return L;
 }
 
-// Workspace of the backward pass: phase-1 terms (A), split partials, E_t,
+// Workspace of the backward pass: phase-1 terms (A; the same offset and size
+// as in the forward layout, so a forward call's workspace can hand its terms
+// over), split partials, E_t,
 // the adjoint states G, the per-frame P_t, G_{T-1} per head and a ones gate;
 // for the chunk-causal scan (n_rev chunks) also the reverse-state adjoint F
 // and its value at every chunk start.
@@ -551,8 +555,10 @@ gdn_status run_bwd(const gdn_desc* desc, int32_t chunk_len, const void* q, const
   float* P = at<float>(ws, L.P);
   float* ginit = at<float>(ws, L.ginit);
   float* ones = at<float>(ws, L.ones);
-  // A_t of every frame (the U half is not needed)
-  {
+  // A_t of every frame (the U half is not needed), unless the workspace
+  // still holds the forward call's terms: both layouts put them first, in the
+  // same internal format, and nothing below writes there
+  if (!sh.reuse_terms) {
     gdn::TermsOut direct{terms, nullptr, 2 * DD, 0};
     if (L.n_split == 1) {
       GDN_HIP(gdn::launch_terms(sh, k, v, beta, 1, direct, mfma, st));

@@ -158,6 +158,7 @@ struct Shape {
   float c;         // key scale applied to ReLU(k) (1 for prepared keys)
   int prepared;    // keys already hold K_hat: no ReLU
   int qk_norm;     // RMS-normalise q (and k unless prepared) per token over D
+  int reuse_terms; // backward: the workspace already holds the forward's terms
   int64_t BH() const { return (int64_t)B * H; }
   int64_t FH() const { return (int64_t)B * H * T; }
 };

@@ -21,7 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "gdn.h")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = range(5)
 GDN_F32, GDN_BF16 = 0, 1
-GDN_KEYS_RAW, GDN_KEYS_PREPARED, GDN_QK_RMSNORM = 0, 1, 2
+GDN_KEYS_RAW, GDN_KEYS_PREPARED, GDN_QK_RMSNORM, GDN_REUSE_FWD_TERMS = 0, 1, 2, 4
 GDN_MAX_TIME_CHUNKS = 256
 
 
@@ -118,13 +118,14 @@ def _stream(stream) -> int | None:
 
 
 def make_desc(B, H, T, S, D, io_dtype, key_scale=0.0, keys_prepared=False,
-              qk_rmsnorm=False) -> gdn_desc:
+              qk_rmsnorm=False, reuse_fwd_terms=False) -> gdn_desc:
     flags = (GDN_KEYS_PREPARED if keys_prepared else GDN_KEYS_RAW) | \
-        (GDN_QK_RMSNORM if qk_rmsnorm else 0)
+        (GDN_QK_RMSNORM if qk_rmsnorm else 0) | (GDN_REUSE_FWD_TERMS if reuse_fwd_terms else 0)
     return gdn_desc(B, H, T, S, D, io_dtype, float(key_scale), flags)
 
 
-def _desc_from(k: torch.Tensor, key_scale, keys_prepared, qk_rmsnorm=False) -> gdn_desc:
+def _desc_from(k: torch.Tensor, key_scale, keys_prepared, qk_rmsnorm=False,
+               reuse_fwd_terms=False) -> gdn_desc:
     if k.dim() != 5:
         raise ValueError("k must be [B, H, T, S, D]")
     if k.dtype == torch.float32:
@@ -134,7 +135,7 @@ def _desc_from(k: torch.Tensor, key_scale, keys_prepared, qk_rmsnorm=False) -> g
     else:
         raise ValueError(f"unsupported io dtype {k.dtype}")
     B, H, T, S, D = k.shape
-    return make_desc(B, H, T, S, D, io, key_scale, keys_prepared, qk_rmsnorm)
+    return make_desc(B, H, T, S, D, io, key_scale, keys_prepared, qk_rmsnorm, reuse_fwd_terms)
 
 
 def _need(t: torch.Tensor | None, name: str, shape, dtype) -> None:
@@ -293,10 +294,14 @@ def gdn_bwd_workspace_bytes(desc: gdn_desc) -> int:
 
 def gdn_scan_bwd(q, k, v, beta, gamma, states, d_o, s0=None, ds_final=None, key_scale=0.0,
                  keys_prepared=False, want=("dq", "dk", "dv", "dbeta", "dgamma", "ds0"),
-                 out=None, ws=None, stream=None, qk_rmsnorm=False):
+                 out=None, ws=None, stream=None, qk_rmsnorm=False, reuse_fwd_terms=False):
     """Gradients of the causal frame scan; `states` are the forward's
-    per-frame states. Returns a dict with the requested gradients."""
-    d = _desc_from(k, key_scale, keys_prepared, qk_rmsnorm)
+    per-frame states. Returns a dict with the requested gradients.
+    reuse_fwd_terms: `ws` is the workspace the forward call used (sized for
+    both calls, untouched since), and A_t is read from it (GDN_REUSE_FWD_TERMS)."""
+    if reuse_fwd_terms and ws is None:
+        raise ValueError("reuse_fwd_terms needs the forward call's workspace as ws")
+    d = _desc_from(k, key_scale, keys_prepared, qk_rmsnorm, reuse_fwd_terms)
     B, H, T, S, D = k.shape
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (d_o, "d_o")):
         _need(t, n, k.shape, k.dtype)
@@ -333,11 +338,13 @@ def gdn_bidir_bwd_workspace_bytes(desc: gdn_desc, chunk_len: int) -> int:
 def gdn_scan_bidir_chunked_bwd(q, k, v, beta, gamma, chunk_len, states_fwd, states_rev, d_o,
                                s0=None, ds_final=None, key_scale=0.0, keys_prepared=False,
                                want=("dq", "dk", "dv", "dbeta", "dgamma", "ds0"), out=None,
-                               ws=None, stream=None, qk_rmsnorm=False):
+                               ws=None, stream=None, qk_rmsnorm=False, reuse_fwd_terms=False):
     """Gradients of the chunk-causal bidirectional scan; `states_fwd` and
     `states_rev` are the forward call's states. Returns a dict with the
-    requested gradients."""
-    d = _desc_from(k, key_scale, keys_prepared, qk_rmsnorm)
+    requested gradients. reuse_fwd_terms as in gdn_scan_bwd."""
+    if reuse_fwd_terms and ws is None:
+        raise ValueError("reuse_fwd_terms needs the forward call's workspace as ws")
+    d = _desc_from(k, key_scale, keys_prepared, qk_rmsnorm, reuse_fwd_terms)
     B, H, T, S, D = k.shape
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (d_o, "d_o")):
         _need(t, n, k.shape, k.dtype)

@@ -77,6 +77,18 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  * the pages give no axis, epsilon or weight, so these are this library's
  * reading. Fused into the kernels' load paths (no extra HBM pass). */
 #define GDN_QK_RMSNORM 2u
+/* Backward calls only (forward calls ignore it): the workspace passed to the
+ * backward already holds the phase-1 terms of the forward call that produced
+ * its states, and A_t is read from there instead of being recomputed (one
+ * pass over k and beta less). That forward call (gdn_scan_fwd,
+ * gdn_scan_bidir_chunked or gdn_step) must have used this same workspace
+ * buffer, the same k and beta, and a descriptor that differs from the
+ * backward's in this bit alone, and nothing may have written to the buffer
+ * since. Size it for both calls: the larger of gdn_workspace_bytes(desc, P)
+ * and the backward's own query. The phase-1 terms occupy the same leading
+ * bytes in both layouts. If the buffer does not hold those terms, the
+ * gradients are wrong (every access still stays inside the workspace). */
+#define GDN_REUSE_FWD_TERMS 4u
 
 #define GDN_MAX_TIME_CHUNKS 256
 
@@ -84,7 +96,8 @@ typedef struct {
   int32_t B, H, T, S, D;  /* batch, heads, frames, tokens per frame, head dim (Dk = Dv) */
   int32_t io_dtype;       /* gdn_dtype of q, k, v, o, k_hat */
   float key_scale;        /* <= 0 selects 1/sqrt(D*S) */
-  uint32_t flags;         /* GDN_KEYS_RAW or GDN_KEYS_PREPARED, optionally | GDN_QK_RMSNORM */
+  uint32_t flags;         /* GDN_KEYS_RAW or GDN_KEYS_PREPARED, optionally | GDN_QK_RMSNORM,
+                           * | GDN_REUSE_FWD_TERMS (backward calls) */
 } gdn_desc;
 
 /* Human-readable name of a status code (static string; never NULL). */
@@ -187,7 +200,8 @@ GDN_API gdn_status gdn_bwd_workspace_bytes(const gdn_desc* desc, size_t* bytes);
  * queries and the raw keys are normalised before their ReLU (as in the
  * forward call); dq and dk then pass back through the norm, dx =
  * r (dy - (y . dy) y / D) with y = x r, r = 1 / rms(x).
- * Workspace: gdn_bwd_workspace_bytes. */
+ * Workspace: gdn_bwd_workspace_bytes; with GDN_REUSE_FWD_TERMS, the forward
+ * call's workspace (see that flag). */
 GDN_API gdn_status gdn_scan_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
                                 const float* beta, const float* gamma, const float* s0,
                                 const float* states, const void* d_o, const float* ds_final,
@@ -213,7 +227,8 @@ GDN_API gdn_status gdn_bidir_bwd_workspace_bytes(const gdn_desc* desc, int32_t c
  * the forward's states_fwd and states_rev [B,H,T,D,D] (both required).
  * Outputs as gdn_scan_bwd (each may be NULL). More than 256 chunks:
  * GDN_EUNSUPPORTED. GDN_QK_RMSNORM as in gdn_scan_bwd.
- * Workspace: gdn_bidir_bwd_workspace_bytes. */
+ * Workspace: gdn_bidir_bwd_workspace_bytes; with GDN_REUSE_FWD_TERMS, the
+ * forward call's workspace (see that flag). */
 GDN_API gdn_status gdn_scan_bidir_chunked_bwd(const gdn_desc* desc, int32_t chunk_len,
                                               const void* q, const void* k, const void* v,
                                               const float* beta, const float* gamma,

@@ -63,14 +63,27 @@ def test_workspace_sizes():
     assert _ws(gdn.make_desc(1, 1, 0, 12, 16, gdn.GDN_F32)) < 4096
 
 
+def test_reuse_flag_changes_no_workspace_size():
+    """GDN_REUSE_FWD_TERMS only tells a backward call where A_t already is:
+    every workspace query answers the same with or without it."""
+    d = gdn.make_desc(1, 2, 5, 300, 128, gdn.GDN_BF16)
+    r = gdn.make_desc(1, 2, 5, 300, 128, gdn.GDN_BF16, reuse_fwd_terms=True)
+    assert r.flags == d.flags | gdn.GDN_REUSE_FWD_TERMS
+    for P in (1, 3):
+        assert gdn.gdn_workspace_bytes(r, P) == gdn.gdn_workspace_bytes(d, P)
+    assert gdn.gdn_bwd_workspace_bytes(r) == gdn.gdn_bwd_workspace_bytes(d)
+    assert gdn.gdn_bidir_bwd_workspace_bytes(r, 2) == gdn.gdn_bidir_bwd_workspace_bytes(d, 2)
+
+
 @pytest.mark.parametrize("mutate,status", [
     (dict(D=48), gdn.GDN_EUNSUPPORTED),
     (dict(D=256), gdn.GDN_EUNSUPPORTED),
     (dict(S=0), gdn.GDN_EINVAL),
     (dict(T=-1), gdn.GDN_EINVAL),
     (dict(io_dtype=7), gdn.GDN_EINVAL),
-    (dict(flags=4), gdn.GDN_EINVAL),
+    (dict(flags=8), gdn.GDN_EINVAL),
     (dict(flags=3), gdn.GDN_OK),
+    (dict(flags=7), gdn.GDN_OK),
     (dict(key_scale=float("nan")), gdn.GDN_EINVAL),
 ])
 def test_bad_descriptor(mutate, status):

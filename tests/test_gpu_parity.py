@@ -856,6 +856,82 @@ def test_scan_bwd_rmsnorm_without_dq():
         assert torch.equal(full[n], part[n]), n
 
 
+REUSE_CASES = {
+    # name: (workload, chunk_len (0: causal, -1: one gdn_step block), P, rmsnorm, keys_prepared)
+    "bf16_D128_P3": (gi.workload(2).with_shape(H=2, T=6, S=300), 0, 3, False, False),
+    "bf16_D128_split_S2100": (gi.workload(2).with_shape(T=3, S=2100), 0, 1, False, False),
+    "bf16_D128_bidir_L2_norm": (gi.workload(2).with_shape(H=2, T=5, S=170), 2, 2, True, False),
+    "bf16_D128_step_prepared": (gi.workload(2).with_shape(H=2, T=3, S=170), -1, 1, False, True),
+    "bf16_D64_norm": (gi.workload(2).with_shape(D=64, T=4, S=130), 0, 2, True, False),
+    "f32_D16_bidir_L3": (gi.workload(1), 3, 1, False, False),
+}
+
+
+@pytest.mark.parametrize("name", sorted(REUSE_CASES))
+def test_scan_bwd_reuses_forward_terms(name):
+    """GDN_REUSE_FWD_TERMS: a backward call on the workspace of its forward
+    call reads A_t from there instead of recomputing it. Both passes form
+    every entry of A_t from the same operands in the same order, so all
+    gradients are bitwise those of the recomputing call; a second backward on
+    the same workspace shows that the first left the terms in place."""
+    w, L, P, norm, prepared = REUSE_CASES[name]
+    x, d = (_gen_rescaled if norm else _gen)(w)
+    if prepared:
+        kh = orc.prepare_keys(x["k"]).astype(np.float32)
+        bits = gi.f32_to_bf16_bits(kh)
+        d["k"] = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+    do, do_d, s0, dsf = _bwd_inputs(w, x, d, True)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    desc = gdn._desc_from(d["k"], 0.0, prepared, norm)
+    chunk = w.T if L < 0 else L
+    bwd_bytes = (gdn.gdn_bidir_bwd_workspace_bytes(desc, chunk) if L
+                 else gdn.gdn_bwd_workspace_bytes(desc))
+    ws = torch.empty(max(gdn.gdn_workspace_bytes(desc, P), bwd_bytes), dtype=torch.uint8,
+                     device=DEV)
+    say("reuse terms", name, "forward")
+    kw = dict(keys_prepared=prepared, qk_rmsnorm=norm)
+    if L < 0:
+        fwd = gdn.gdn_step(d["q"], d["k"], d["v"], d["beta"], d["gamma"], carry_in=dev(s0),
+                           want_o=False, want_states=True, ws=ws, **kw)
+    elif L:
+        fwd = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], L,
+                                         s0=dev(s0), n_time_chunks=P, want_o=False, ws=ws, **kw)
+    else:
+        fwd = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], s0=dev(s0),
+                               n_time_chunks=P, want_o=False, ws=ws, **kw)
+
+    def bwd(reuse):
+        args = (d["q"], d["k"], d["v"], d["beta"], d["gamma"])
+        extra = dict(s0=dev(s0), ds_final=dev(dsf), reuse_fwd_terms=reuse,
+                     ws=ws if reuse else None, **kw)
+        if L:
+            return gdn.gdn_scan_bidir_chunked_bwd(*args, chunk, fwd["states_fwd"],
+                                                  fwd["states_rev"], do_d, **extra)
+        return gdn.gdn_scan_bwd(*args, fwd["states"], do_d, **extra)
+
+    say("reuse terms", name, "backward, reusing")
+    g1 = bwd(True)
+    torch.cuda.synchronize()
+    g1 = {n: t.clone() for n, t in g1.items()}
+    say("reuse terms", name, "backward, reusing again")
+    g2 = bwd(True)
+    say("reuse terms", name, "backward, recomputing")
+    ref = bwd(False)
+    torch.cuda.synchronize()
+    for n in ("dq", "dk", "dv", "dbeta", "dgamma", "ds0"):
+        assert torch.equal(g1[n], ref[n]), n
+        assert torch.equal(g2[n], ref[n]), n
+
+
+def test_scan_bwd_reuse_needs_workspace():
+    w = gi.workload(2).with_shape(T=2, S=64)
+    x, d = _gen(w)
+    with pytest.raises(ValueError):
+        gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"],
+                         torch.zeros((1, 1, 2, 128, 128), device=DEV), d["q"],
+                         reuse_fwd_terms=True)
+
+
 def test_scan_bwd_no_frames():
     w = gi.workload(1).with_shape(T=0)
     x, d = _gen(w)
