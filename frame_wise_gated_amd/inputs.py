@@ -68,7 +68,7 @@ WORKLOADS = {
     4: Workload(4, "layer_720p_60s_H16_T121_cp8", 1, 16, 121, 3600, 128, "bf16", "uniform", 0.98,
                 "fwd", time_chunks=8),
     5: Workload(5, "layer_720p_60s_H16_T121_bidir10", 1, 16, 121, 3600, 128, "bf16", "beta05",
-                0.999, "bidir", chunk_len=10),
+                0.999, "bidir", time_chunks=8, chunk_len=10),
 }
 
 

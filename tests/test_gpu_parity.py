@@ -299,14 +299,18 @@ def test_named_workload_full_size(idx, heads):
         errs = {g: rel_fro(host(res[g][b, h]), ref[r][0, 0]) for g, r in pairs}
         say(w.name, (b, h), {k: f"{v:.2e}" for k, v in errs.items()})
         assert max(errs.values()) <= tol(w), errs
-    if idx == 4:
+    if w.time_chunks > 1:
         # composite route versus the sequential scan on every head (same terms)
         say("sequential vs composite", w.name)
-        seq = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], n_time_chunks=1)
+        key = "states_fwd" if w.mode == "bidir" else "states"
+        seq = _run_workload(w.with_shape(time_chunks=1), d)
         torch.cuda.synchronize()
         for h in range(w.H):
-            e = rel_fro(host(res["states"][0, h]), host(seq["states"][0, h]))
+            e = rel_fro(host(res[key][0, h]), host(seq[key][0, h]))
+            say(w.name, "composite vs sequential", h, f"{e:.2e}")
             assert e <= 1e-4, (h, e)
+            if w.mode == "bidir":
+                assert torch.equal(res["states_rev"][0, h], seq["states_rev"][0, h])
 
 
 # ------------------------------------------------------------ graph capture
