@@ -174,72 +174,70 @@ void uniform_offsets(int* offs, int T, int P) {
   for (int p = 0; p <= P; ++p) offs[p] = (int)(((int64_t)p * T) / P);
 }
 
-// Forward scan (sequential or composite) from the terms buffer into x.fwd
-// (per-frame states, nullable) and x.s_final (nullable).
-gdn_status run_forward(const Shape& sh, int P, const Slice& x, hipStream_t st) {
+// Parameters of the scan launches over the terms buffer.
+// Sequential forward scan into x.fwd (nullable) and x.s_final (nullable).
+gdn::ScanParams seq_params(const Shape& sh, const Slice& x) {
   const int64_t DD = (int64_t)sh.D * sh.D;
-  if (P <= 1) {
-    gdn::ScanParams p;
-    memset(&p, 0, sizeof(p));
-    p.terms = x.terms;
-    p.gamma = x.gamma;
-    p.T = sh.T;
-    p.nchunk = 1;
-    p.mode = gdn::SCAN_FORWARD;
-    p.init = x.s0;
-    p.init_bh_stride = DD;
-    p.init_c_stride = 0;
-    p.states = x.fwd;
-    p.finA = x.s_final;
-    p.fin_bh_stride = DD;
-    p.fin_last_only = 1;
-    p.offsets[0] = 0;
-    p.offsets[1] = sh.T;
-    GDN_HIP(gdn::launch_scan(sh, p, st));
-    return GDN_OK;
-  }
-  {
-    gdn::ScanParams p;
-    memset(&p, 0, sizeof(p));
-    p.terms = x.terms;
-    p.gamma = x.gamma;
-    p.T = sh.T;
-    p.nchunk = P;
-    p.mode = gdn::SCAN_COMPOSE;
-    p.finA = x.compC;
-    p.finB = x.compH;
-    p.fin_bh_stride = (int64_t)P * DD;
-    p.fin_c_stride = DD;
-    uniform_offsets(p.offsets, sh.T, P);
-    GDN_HIP(gdn::launch_scan(sh, p, st));
-  }
-  {
-    gdn::CombineParams cp{x.compC, x.compH, x.s0, x.start, P};
-    GDN_HIP(gdn::launch_combine(sh, cp, st));
-  }
-  {
-    gdn::ScanParams p;
-    memset(&p, 0, sizeof(p));
-    p.terms = x.terms;
-    p.gamma = x.gamma;
-    p.T = sh.T;
-    p.nchunk = P;
-    p.mode = gdn::SCAN_FORWARD;
-    p.init = x.start;
-    p.init_bh_stride = (int64_t)P * DD;
-    p.init_c_stride = DD;
-    p.states = x.fwd;
-    p.finA = x.s_final;
-    p.fin_bh_stride = DD;
-    p.fin_last_only = 1;
-    uniform_offsets(p.offsets, sh.T, P);
-    GDN_HIP(gdn::launch_scan(sh, p, st));
-  }
-  return GDN_OK;
+  gdn::ScanParams p;
+  memset(&p, 0, sizeof(p));
+  p.terms = x.terms;
+  p.gamma = x.gamma;
+  p.T = sh.T;
+  p.nchunk = 1;
+  p.mode = gdn::SCAN_FORWARD;
+  p.init = x.s0;
+  p.init_bh_stride = DD;
+  p.init_c_stride = 0;
+  p.states = x.fwd;
+  p.finA = x.s_final;
+  p.fin_bh_stride = DD;
+  p.fin_last_only = 1;
+  p.offsets[0] = 0;
+  p.offsets[1] = sh.T;
+  return p;
+}
+
+// Composites (C_p, H_p) of P time chunks into x.compC, x.compH.
+gdn::ScanParams compose_params(const Shape& sh, int P, const Slice& x) {
+  const int64_t DD = (int64_t)sh.D * sh.D;
+  gdn::ScanParams p;
+  memset(&p, 0, sizeof(p));
+  p.terms = x.terms;
+  p.gamma = x.gamma;
+  p.T = sh.T;
+  p.nchunk = P;
+  p.mode = gdn::SCAN_COMPOSE;
+  p.finA = x.compC;
+  p.finB = x.compH;
+  p.fin_bh_stride = (int64_t)P * DD;
+  p.fin_c_stride = DD;
+  uniform_offsets(p.offsets, sh.T, P);
+  return p;
+}
+
+// Every chunk replayed from its start state x.start into x.fwd / x.s_final.
+gdn::ScanParams replay_params(const Shape& sh, int P, const Slice& x) {
+  const int64_t DD = (int64_t)sh.D * sh.D;
+  gdn::ScanParams p;
+  memset(&p, 0, sizeof(p));
+  p.terms = x.terms;
+  p.gamma = x.gamma;
+  p.T = sh.T;
+  p.nchunk = P;
+  p.mode = gdn::SCAN_FORWARD;
+  p.init = x.start;
+  p.init_bh_stride = (int64_t)P * DD;
+  p.init_c_stride = DD;
+  p.states = x.fwd;
+  p.finA = x.s_final;
+  p.fin_bh_stride = DD;
+  p.fin_last_only = 1;
+  uniform_offsets(p.offsets, sh.T, P);
+  return p;
 }
 
 // Reverse scan restarted at every chunk_len-frame boundary into x.rev.
-gdn_status run_reverse(const Shape& sh, int chunk_len, const Slice& x, hipStream_t st) {
+gdn::ScanParams reverse_params(const Shape& sh, int chunk_len, const Slice& x) {
   const int64_t n_rev = ((int64_t)sh.T + chunk_len - 1) / chunk_len;
   gdn::ScanParams p;
   memset(&p, 0, sizeof(p));
@@ -253,19 +251,33 @@ gdn_status run_reverse(const Shape& sh, int chunk_len, const Slice& x, hipStream
     int64_t off = (int64_t)c * chunk_len;
     p.offsets[c] = (int)(off < sh.T ? off : sh.T);
   }
-  GDN_HIP(gdn::launch_scan(sh, p, st));
-  return GDN_OK;
+  return p;
 }
 
 // Everything after phase 1 except the readout: forward scan (when per-frame
-// forward states or the final state are wanted) and the chunk-reset reverse
-// scan (chunk_len > 0, when reverse states are wanted).
+// forward states or the final state are wanted; sequential for P <= 1, else
+// compose, combine and replay) and the chunk-reset reverse scan (chunk_len >
+// 0, when reverse states are wanted). The reverse scan needs only the terms,
+// so on the MFMA path it shares a launch with the first forward one, whose
+// grid leaves much of the chip idle (the compose's second round of
+// workgroups, or the handful of row blocks of a sequential scan).
 gdn_status run_scans(const Shape& sh, int P, int chunk_len, const Slice& x, hipStream_t st) {
-  gdn_status s;
-  if (x.fwd || x.s_final)
-    if ((s = run_forward(sh, P, x, st)) != GDN_OK) return s;
-  if (chunk_len > 0 && x.rev)
-    if ((s = run_reverse(sh, chunk_len, x, st)) != GDN_OK) return s;
+  const bool fwd = x.fwd || x.s_final;
+  const bool rev = chunk_len > 0 && x.rev;
+  const bool pair = fwd && rev && gdn::scan_pairs(sh);
+  if (fwd) {
+    const gdn::ScanParams first = P <= 1 ? seq_params(sh, x) : compose_params(sh, P, x);
+    if (pair)
+      GDN_HIP(gdn::launch_scan_pair(sh, first, reverse_params(sh, chunk_len, x), st));
+    else
+      GDN_HIP(gdn::launch_scan(sh, first, st));
+    if (P > 1) {
+      gdn::CombineParams cp{x.compC, x.compH, x.s0, x.start, P};
+      GDN_HIP(gdn::launch_combine(sh, cp, st));
+      GDN_HIP(gdn::launch_scan(sh, replay_params(sh, P, x), st));
+    }
+  }
+  if (rev && !pair) GDN_HIP(gdn::launch_scan(sh, reverse_params(sh, chunk_len, x), st));
   return GDN_OK;
 }
 

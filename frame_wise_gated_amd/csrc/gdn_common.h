@@ -242,6 +242,11 @@ hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_s
                                   TermsOut out, bool scan_layout, hipStream_t st);
 bool scan_uses_mfma(const Shape& sh);
 hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st);
+// Two independent scans over the same terms in one launch (MFMA path only:
+// scan_pairs(sh) must hold, else hipErrorInvalidValue and nothing launched).
+bool scan_pairs(const Shape& sh);
+hipError_t launch_scan_pair(const Shape& sh, const ScanParams& a, const ScanParams& b,
+                            hipStream_t st);
 hipError_t launch_combine(const Shape& sh, const CombineParams& p, hipStream_t st);
 // transpose_state (bf16, D = 128 only): o = states^T q, for the backward pass.
 hipError_t launch_readout(const Shape& sh, const void* q, const float* st_a, const float* st_b,

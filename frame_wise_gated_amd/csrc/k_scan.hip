@@ -109,8 +109,10 @@ __global__ void __launch_bounds__(256) scan_rows_kernel(ScanParams p) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
       const int i = ig + RG * r;
-      float xn = g * (Xs[cur][i][n] - acc[r]);
-      if (u_on) xn += Ut[(int64_t)(srow0 + i) * D + n];
+      // one rounding of g (X - XA) + U (an explicit fma, so that the result
+      // does not depend on how the compiler contracts the expression)
+      const float dx = Xs[cur][i][n] - acc[r];
+      const float xn = u_on ? fmaf(g, dx, Ut[(int64_t)(srow0 + i) * D + n]) : g * dx;
       Xs[cur ^ 1][i][n] = xn;
       if (p.states != nullptr) p.states[f * DD + (int64_t)(srow0 + i) * D + n] = xn;
     }
@@ -334,8 +336,9 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_d128(CombineParams p) {
 // frame loop is unrolled by kF); loads past the last frame re-read it, so
 // the outstanding-load bookkeeping is identical in every step. Wave w owns
 // output columns [32w, 32w + 32) as two 16-column MFMA tiles.
+// One workgroup's job; `blk` is its block index within the launch of p.
 template <int MT, int kF>
-__global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
+__device__ __forceinline__ void scan_block(const ScanParams& p, int64_t blk) {
   constexpr int D = 128;
   constexpr int R = 16 * MT;
   constexpr int LDB = D + 8;  // bf16 row stride 272 B: 8 lanes reading 16 B at one column are conflict-free
@@ -347,7 +350,7 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
   const int nrb = rows_total / R;
   int64_t job;
   int rb;
-  xcd_job(blockIdx.x, nrb, &job, &rb);
+  xcd_job(blk, nrb, &job, &rb);
   if (job >= p.njobs) return;
   const int c = (int)(job % p.nchunk);
   const int64_t bh = job / p.nchunk;
@@ -495,7 +498,8 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
           const int m = 16 * mt + l16;
           f32x4_t xn;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) xn[r] = gm * (xr[mt][nt][r] - acc[mt][nt][r]) + umr[j] * u[j][mt][nt][r];
+          for (int r = 0; r < 4; ++r)  // one rounding: umr is 0 or 1, so umr u is exact
+            xn[r] = __builtin_fmaf(gm, xr[mt][nt][r] - acc[mt][nt][r], umr[j] * u[j][mt][nt][r]);
           if (active) xr[mt][nt] = xn;
           put_split(cur ^ 1, m, ncol(nt), xr[mt][nt]);
         }
@@ -524,9 +528,44 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p) {
       *(f32x4_t*)(fin + (int64_t)(srow0 + 16 * mt + l16) * D + ncol(nt)) = xr[mt][nt];
 }
 
+// Blocks [0, split) run the jobs of p0 and blocks [split, grid) those of p1:
+// two independent scans over the same terms can share one launch (split is a
+// multiple of the XCD count, so both keep their XCD mapping). Each branch
+// reads its own kernel argument (a runtime choice between the two would copy
+// them to scratch memory).
+template <int MT, int kF>
+__global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p0, ScanParams p1,
+                                                      int64_t split) {
+  if ((int64_t)blockIdx.x < split)
+    scan_block<MT, kF>(p0, (int64_t)blockIdx.x);
+  else
+    scan_block<MT, kF>(p1, (int64_t)blockIdx.x - split);
+}
+
 }  // namespace
 
 bool scan_uses_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
+
+bool scan_pairs(const Shape& sh) {
+  return scan_uses_mfma(sh) && GDN_SCAN_MT == GDN_SCAN_MT_COMPOSE && GDN_SCAN_F == GDN_SCAN_F_COMPOSE;
+}
+
+hipError_t launch_scan_pair(const Shape& sh, const ScanParams& a, const ScanParams& b,
+                            hipStream_t st) {
+  if (!scan_pairs(sh)) return hipErrorInvalidValue;
+  ScanParams qa = a, qb = b;
+  qa.njobs = sh.BH() * a.nchunk;
+  qb.njobs = sh.BH() * b.nchunk;
+  constexpr int R = 16 * GDN_SCAN_MT;
+  auto blocks = [&](const ScanParams& q) -> int64_t {
+    const int rows = q.mode == SCAN_COMPOSE ? 2 * sh.D : sh.D;
+    return q.njobs ? xcd_grid(q.njobs, rows / R) : 0;
+  };
+  const int64_t na = blocks(qa), nb = blocks(qb);
+  if (na + nb == 0) return hipSuccess;
+  scan_mfma_d128<GDN_SCAN_MT, GDN_SCAN_F><<<dim3((unsigned)(na + nb)), 256, 0, st>>>(qa, qb, na);
+  return hipGetLastError();
+}
 
 hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st) {
   const int64_t rows_total = (p.mode == SCAN_COMPOSE) ? 2 * sh.D : sh.D;
@@ -534,14 +573,15 @@ hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st) {
   q.njobs = sh.BH() * p.nchunk;
   if (q.njobs == 0) return hipSuccess;
   if (scan_uses_mfma(sh)) {
+    const int64_t none = INT64_MAX;  // every block runs q
     if (p.mode == SCAN_COMPOSE) {
       constexpr int MT = GDN_SCAN_MT_COMPOSE;
       const int64_t blocks = xcd_grid(q.njobs, (int)(rows_total / (16 * MT)));
-      scan_mfma_d128<MT, GDN_SCAN_F_COMPOSE><<<dim3((unsigned)blocks), 256, 0, st>>>(q);
+      scan_mfma_d128<MT, GDN_SCAN_F_COMPOSE><<<dim3((unsigned)blocks), 256, 0, st>>>(q, q, none);
     } else {
       constexpr int MT = GDN_SCAN_MT;
       const int64_t blocks = xcd_grid(q.njobs, (int)(rows_total / (16 * MT)));
-      scan_mfma_d128<MT, GDN_SCAN_F><<<dim3((unsigned)blocks), 256, 0, st>>>(q);
+      scan_mfma_d128<MT, GDN_SCAN_F><<<dim3((unsigned)blocks), 256, 0, st>>>(q, q, none);
     }
     return hipGetLastError();
   }

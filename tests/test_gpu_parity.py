@@ -250,6 +250,31 @@ def test_deterministic():
         assert torch.equal(r1[n], r2[n]), n
 
 
+@pytest.mark.parametrize("P", [1, 3])
+def test_bidir_scans_sharing_a_launch_match_separate_scans(P):
+    """The chunk-causal call runs its reverse scan in the same launch as the
+    first forward one (the sequential scan, or the compose). Sharing the
+    launch changes no arithmetic: the forward states equal gdn_scan_fwd's and
+    the reverse states those of a call that wants only them (which runs the
+    reverse scan alone), bit for bit."""
+    w = gi.workload(5).with_shape(H=3, T=13, S=256)
+    x, d = _gen(w)
+    say("bidir with shared launch, P =", P)
+    both = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], 4,
+                                      n_time_chunks=P)
+    fwd = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], n_time_chunks=P,
+                           want_o=False)
+    rev_only = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], 4,
+                                          n_time_chunks=P, want_o=False, want_s_final=False,
+                                          want_states=False,
+                                          states_rev=torch.empty_like(both["states_rev"]))
+    assert rev_only["states_fwd"] is None
+    torch.cuda.synchronize()
+    assert torch.equal(both["states_fwd"], fwd["states"])
+    assert torch.equal(both["s_final"], fwd["s_final"])
+    assert torch.equal(both["states_rev"], rev_only["states_rev"])
+
+
 # ---------------------------------------------- full-size named workloads
 def _full(idx, heads, seed=0):
     w = gi.workload(idx)
