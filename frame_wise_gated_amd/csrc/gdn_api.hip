@@ -258,17 +258,18 @@ gdn::ScanParams reverse_params(const Shape& sh, int chunk_len, const Slice& x) {
 // forward states or the final state are wanted; sequential for P <= 1, else
 // compose, combine and replay) and the chunk-reset reverse scan (chunk_len >
 // 0, when reverse states are wanted). The reverse scan needs only the terms,
-// so on the MFMA path it shares a launch with the first forward one, whose
-// grid leaves much of the chip idle (the compose's second round of
-// workgroups, or the handful of row blocks of a sequential scan).
+// so on the MFMA path it shares a launch with the first forward one when
+// both run with the same row block (the compose of several chunks and the
+// reverse scan do; a sequential scan of a few heads takes smaller blocks).
 gdn_status run_scans(const Shape& sh, int P, int chunk_len, const Slice& x, hipStream_t st) {
   const bool fwd = x.fwd || x.s_final;
   const bool rev = chunk_len > 0 && x.rev;
-  const bool pair = fwd && rev && gdn::scan_pairs(sh);
+  const gdn::ScanParams first = P <= 1 ? seq_params(sh, x) : compose_params(sh, P, x);
+  const gdn::ScanParams second = rev ? reverse_params(sh, chunk_len, x) : first;
+  const bool pair = fwd && rev && gdn::scan_pairs(sh, first, second);
   if (fwd) {
-    const gdn::ScanParams first = P <= 1 ? seq_params(sh, x) : compose_params(sh, P, x);
     if (pair)
-      GDN_HIP(gdn::launch_scan_pair(sh, first, reverse_params(sh, chunk_len, x), st));
+      GDN_HIP(gdn::launch_scan_pair(sh, first, second, st));
     else
       GDN_HIP(gdn::launch_scan(sh, first, st));
     if (P > 1) {
@@ -277,7 +278,7 @@ gdn_status run_scans(const Shape& sh, int P, int chunk_len, const Slice& x, hipS
       GDN_HIP(gdn::launch_scan(sh, replay_params(sh, P, x), st));
     }
   }
-  if (rev && !pair) GDN_HIP(gdn::launch_scan(sh, reverse_params(sh, chunk_len, x), st));
+  if (rev && !pair) GDN_HIP(gdn::launch_scan(sh, second, st));
   return GDN_OK;
 }
 

@@ -18,19 +18,22 @@
 // while the row block stays in LDS.
 #include "gdn_common.h"
 
-// Build-time tuning knobs of the MFMA scan: row block in 16-row MFMA tiles,
-// and frames of A_t / U_t prefetched in registers.
+// Build-time tuning knobs of the MFMA scan: the row block in 16-row MFMA
+// tiles of launches that fill the chip, that of launches which would have
+// fewer workgroups than CUs at that size (the sequential scans of a few
+// heads), and the frames of A_t / U_t prefetched in registers. Measured on
+// MI355X for the 60 s 720p layer: the sequential 121-frame scan of 16 heads
+// took 159 us with 16-row blocks against 223-236 us with 32-row blocks, while
+// the compose and the replay of 8 chunks took 101 and 83 us with 16-row
+// blocks against 81 and 67 us with 32-row blocks.
 #ifndef GDN_SCAN_MT
 #define GDN_SCAN_MT 2
 #endif
-#ifndef GDN_SCAN_MT_COMPOSE
-#define GDN_SCAN_MT_COMPOSE GDN_SCAN_MT
+#ifndef GDN_SCAN_MT_SMALL
+#define GDN_SCAN_MT_SMALL 1
 #endif
 #ifndef GDN_SCAN_F
 #define GDN_SCAN_F 2
-#endif
-#ifndef GDN_SCAN_F_COMPOSE
-#define GDN_SCAN_F_COMPOSE GDN_SCAN_F
 #endif
 // bf16 D = 128: the combine on MFMA (1) or on fp32 vector FMAs (0)
 #ifndef GDN_COMBINE_MFMA
@@ -546,45 +549,62 @@ __global__ void __launch_bounds__(256) scan_mfma_d128(ScanParams p0, ScanParams 
 
 bool scan_uses_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
 
-bool scan_pairs(const Shape& sh) {
-  return scan_uses_mfma(sh) && GDN_SCAN_MT == GDN_SCAN_MT_COMPOSE && GDN_SCAN_F == GDN_SCAN_F_COMPOSE;
+namespace {
+
+constexpr int kCUs = 256;
+
+// Workgroups of one MFMA scan launch with MT-tile row blocks (0 without jobs).
+int64_t mfma_blocks(const Shape& sh, const ScanParams& q, int MT) {
+  const int rows = q.mode == SCAN_COMPOSE ? 2 * sh.D : sh.D;
+  return q.njobs ? xcd_grid(q.njobs, rows / (16 * MT)) : 0;
+}
+
+// Row block of a launch: the small one when the large one leaves CUs idle.
+int mfma_mt(const Shape& sh, const ScanParams& q) {
+  return mfma_blocks(sh, q, GDN_SCAN_MT) < kCUs ? GDN_SCAN_MT_SMALL : GDN_SCAN_MT;
+}
+
+ScanParams with_jobs(const Shape& sh, const ScanParams& p) {
+  ScanParams q = p;
+  q.njobs = sh.BH() * p.nchunk;
+  return q;
+}
+
+// One launch running the jobs of a and then those of b (b may be null).
+template <int MT>
+hipError_t launch_mfma(const Shape& sh, const ScanParams& a, const ScanParams* b, hipStream_t st) {
+  const int64_t na = mfma_blocks(sh, a, MT);
+  const int64_t nb = b ? mfma_blocks(sh, *b, MT) : 0;
+  if (na + nb == 0) return hipSuccess;
+  scan_mfma_d128<MT, GDN_SCAN_F><<<dim3((unsigned)(na + nb)), 256, 0, st>>>(
+      a, b ? *b : a, b ? na : INT64_MAX);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma(const Shape& sh, const ScanParams& a, const ScanParams* b, int mt,
+                       hipStream_t st) {
+  return mt == GDN_SCAN_MT ? launch_mfma<GDN_SCAN_MT>(sh, a, b, st)
+                           : launch_mfma<GDN_SCAN_MT_SMALL>(sh, a, b, st);
+}
+
+}  // namespace
+
+bool scan_pairs(const Shape& sh, const ScanParams& a, const ScanParams& b) {
+  return scan_uses_mfma(sh) && mfma_mt(sh, with_jobs(sh, a)) == mfma_mt(sh, with_jobs(sh, b));
 }
 
 hipError_t launch_scan_pair(const Shape& sh, const ScanParams& a, const ScanParams& b,
                             hipStream_t st) {
-  if (!scan_pairs(sh)) return hipErrorInvalidValue;
-  ScanParams qa = a, qb = b;
-  qa.njobs = sh.BH() * a.nchunk;
-  qb.njobs = sh.BH() * b.nchunk;
-  constexpr int R = 16 * GDN_SCAN_MT;
-  auto blocks = [&](const ScanParams& q) -> int64_t {
-    const int rows = q.mode == SCAN_COMPOSE ? 2 * sh.D : sh.D;
-    return q.njobs ? xcd_grid(q.njobs, rows / R) : 0;
-  };
-  const int64_t na = blocks(qa), nb = blocks(qb);
-  if (na + nb == 0) return hipSuccess;
-  scan_mfma_d128<GDN_SCAN_MT, GDN_SCAN_F><<<dim3((unsigned)(na + nb)), 256, 0, st>>>(qa, qb, na);
-  return hipGetLastError();
+  if (!scan_pairs(sh, a, b)) return hipErrorInvalidValue;
+  const ScanParams qa = with_jobs(sh, a), qb = with_jobs(sh, b);
+  return launch_mfma(sh, qa, &qb, mfma_mt(sh, qa), st);
 }
 
 hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st) {
   const int64_t rows_total = (p.mode == SCAN_COMPOSE) ? 2 * sh.D : sh.D;
-  ScanParams q = p;
-  q.njobs = sh.BH() * p.nchunk;
+  const ScanParams q = with_jobs(sh, p);
   if (q.njobs == 0) return hipSuccess;
-  if (scan_uses_mfma(sh)) {
-    const int64_t none = INT64_MAX;  // every block runs q
-    if (p.mode == SCAN_COMPOSE) {
-      constexpr int MT = GDN_SCAN_MT_COMPOSE;
-      const int64_t blocks = xcd_grid(q.njobs, (int)(rows_total / (16 * MT)));
-      scan_mfma_d128<MT, GDN_SCAN_F_COMPOSE><<<dim3((unsigned)blocks), 256, 0, st>>>(q, q, none);
-    } else {
-      constexpr int MT = GDN_SCAN_MT;
-      const int64_t blocks = xcd_grid(q.njobs, (int)(rows_total / (16 * MT)));
-      scan_mfma_d128<MT, GDN_SCAN_F><<<dim3((unsigned)blocks), 256, 0, st>>>(q, q, none);
-    }
-    return hipGetLastError();
-  }
+  if (scan_uses_mfma(sh)) return launch_mfma(sh, q, nullptr, mfma_mt(sh, q), st);
   dim3 grid((unsigned)xcd_grid(q.njobs, (int)(rows_total / kR)));
   switch (sh.D) {
     case 16: scan_rows_kernel<16><<<grid, 256, 0, st>>>(q); break;
