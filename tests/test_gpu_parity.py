@@ -275,6 +275,72 @@ def test_bidir_scans_sharing_a_launch_match_separate_scans(P):
     assert torch.equal(both["states_rev"], rev_only["states_rev"])
 
 
+# ------------------------------------------------------------ limits
+def test_largest_chunk_counts():
+    """The largest chunk counts the library takes, on one 720p-width head
+    (D = 128, bf16) with 256 frames of 40 tokens: 256 composite time chunks of
+    one frame each, a reverse scan restarted after every frame (256 chunks),
+    explicit composites of 256 chunks, and the backward with 256 reverse
+    chunks."""
+    w = gi.workload(2).with_shape(T=256, S=40)
+    x, d = _gen(w)
+    say("256 time chunks")
+    r256 = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], n_time_chunks=256)
+    seq = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], n_time_chunks=1)
+    torch.cuda.synchronize()
+    _check_fwd(w, x, r256, None, [(0, 0)], P=256, what="P = 256")
+    assert rel_fro(host(r256["states"]), host(seq["states"])) <= 1e-4
+    say("reverse scan restarted after every frame")
+    bid = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], 1,
+                                     n_time_chunks=256)
+    _, U = gdn.gdn_frame_terms(d["k"], d["v"], d["beta"])
+    torch.cuda.synchronize()
+    assert torch.equal(bid["states_rev"], U)  # one frame from a zero state: R_t = U_t
+    assert torch.equal(bid["states_fwd"], r256["states"])
+    say("composites of 256 chunks")
+    comp = gdn.gdn_compose(d["k"], d["v"], d["beta"], d["gamma"], list(range(257)))
+    torch.cuda.synchronize()
+    # chunk p is frame p alone: H_p = U_p, and s_start[p + 1] is the state after frame p
+    assert torch.equal(comp["Hc"], U)
+    assert rel_fro(host(comp["s_start"][0, 0, 1:]), host(seq["states"][0, 0, :-1])) <= 1e-4
+    say("backward with 256 reverse chunks")
+    do, do_d, s0, dsf = _bwd_inputs(w, x, d, True)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    fb = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], 1,
+                                    s0=dev(s0), n_time_chunks=256, want_o=False)
+    g = gdn.gdn_scan_bidir_chunked_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], 1,
+                                       fb["states_fwd"], fb["states_rev"], do_d, s0=dev(s0),
+                                       ds_final=dev(dsf))
+    torch.cuda.synchronize()
+    a = head_arrays(x, 0, 0)
+    ref = orc.scan_bidir_bwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"], 1,
+                             do[0, 0][None, None].astype(np.float64),
+                             ds_final=dsf[0, 0][None, None].astype(np.float64),
+                             s0=s0[0, 0][None, None].astype(np.float64))
+    for n in ("dq", "dk", "dv", "dbeta", "dgamma", "ds0"):
+        e = rel_fro(host(g[n][0, 0]), ref[n][0, 0])
+        say("256 reverse chunks", n, f"{e:.2e}")
+        assert e <= tol(w), (n, e)
+
+
+def test_long_frame():
+    """A frame of 40,000 tokens (11 times a 720p frame; 1250 token tiles of
+    phase 1, ragged against the readout's tiles): frame terms, states and
+    outputs of a 2-frame scan against the oracle."""
+    w = gi.workload(2).with_shape(T=2, S=40000)
+    x, d = _gen(w)
+    say("S = 40000")
+    res = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"])
+    A, U = gdn.gdn_frame_terms(d["k"], d["v"], d["beta"])
+    torch.cuda.synchronize()
+    kh = orc.prepare_keys(x["k"][0, 0])
+    for t in range(w.T):
+        Ar, Ur = orc.frame_terms(kh[t], x["v"][0, 0, t], x["beta"][0, 0, t])
+        assert rel_fro(host(A[0, 0, t]), Ar) <= tol(w)
+        assert rel_fro(host(U[0, 0, t]), Ur) <= tol(w)
+    _check_fwd(w, x, res, None, [(0, 0)], what="S = 40000")
+
+
 # ---------------------------------------------- full-size named workloads
 def _full(idx, heads, seed=0):
     w = gi.workload(idx)
