@@ -505,10 +505,13 @@ token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restri
 // MFMA path of the per-frame gradients (D = 128): dM = S_prev^T G on fp32
 // MFMA (v_mfma_f32_32x32x2_f32: exact fp32 products), wave w owns rows
 // 32w .. 32w + 31 of dM as four 32 x 32 tiles. The A operand of lane l is
-// S_prev[i][32w + l % 32] with i = 2 ks + l / 32, the B operand
-// G[i][32 nb + l % 32]; both are conflict-free row reads of the staged
-// matrices.
-__global__ void __launch_bounds__(256, 1)
+// S_prev[i][32w + l % 32] with i = 2 ks + l / 32: the wave's 64 such values
+// per lane are loaded straight into registers (coalesced 128-byte row
+// pieces). The B operand G[i][32 nb + l % 32] is shared by the four waves and
+// read from LDS. One padded D x D buffer then holds G_t (the chunk-causal
+// scan's F_t next) and finally dM for its transposed read: 68 KB of LDS, two
+// workgroups per CU, so that one's loads overlap the other's products.
+__global__ void __launch_bounds__(256, 2)
 frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__ s0,
                      float* __restrict__ gbuf, float* __restrict__ ginit,
                      const float* __restrict__ terms, int a_granule_bf16,
@@ -517,8 +520,7 @@ frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__
   constexpr int D = 128;
   constexpr int LDT = D + 4;  // padded row for the transposed read of dM
   constexpr int64_t DD = (int64_t)D * D;
-  __shared__ float Ss[D][LDT];
-  __shared__ float Gs[D][D];
+  __shared__ float Ws[D][LDT];
   __shared__ float red[4];
   const int64_t f = blockIdx.x;
   const int64_t bh = f / T;
@@ -544,24 +546,25 @@ frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__
         ag[nb][jg] = *(const uint2*)((const uint16_t*)At +
                                      (int64_t)a_granule(32 * nb + l32, 4 * wave + jg) * 8 + 4 * hk);
   }
-  // S_prev and G_t into LDS: all 32 loads of a thread are issued before the
-  // first LDS write, so the staging costs one memory round trip
+  // this lane's A operands (S_prev, or zero) in registers and G_t into LDS:
+  // every load of a thread is issued before its first LDS write, so the
+  // staging costs one memory round trip
+  constexpr int kPer = D * D / 4 / 256;
+  float sa[D / 2];
+  auto load_a_operands = [&](const float* X) {
+    const float* col = X ? X + 32 * wave + l32 : nullptr;
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ++ks) sa[ks] = col ? col[(int64_t)(2 * ks + hk) * D] : 0.f;
+  };
   {
-    constexpr int kPer = D * D / 4 / 256;
-    float4 sv[kPer], gv[kPer];
+    float4 gv[kPer];
+    load_a_operands(Sp);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) gv[u] = *(const float4*)(Gt + 4 * (int64_t)(tid + 256 * u));
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int e = tid + 256 * u;
-      const int r = e / (D / 4), c4 = 4 * (e % (D / 4));
-      sv[u] = Sp ? *(const float4*)(Sp + (int64_t)r * D + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
-      gv[u] = *(const float4*)(Gt + (int64_t)r * D + c4);
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = tid + 256 * u;
-      const int r = e / (D / 4), c4 = 4 * (e % (D / 4));
-      Ss[r][c4] = sv[u].x; Ss[r][c4 + 1] = sv[u].y; Ss[r][c4 + 2] = sv[u].z; Ss[r][c4 + 3] = sv[u].w;
-      *(float4*)&Gs[r][c4] = gv[u];
+      *(float4*)&Ws[e / (D / 4)][4 * (e % (D / 4))] = gv[u];
     }
   }
   __syncthreads();
@@ -570,14 +573,13 @@ frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[nb][j] = 0.f;
-  auto product = [&]() {  // acc += Ss^T Gs
-#pragma unroll 4
+  auto product = [&]() {  // acc += X^T Ws, X^T's operands in sa
+#pragma unroll
     for (int ks = 0; ks < D / 2; ++ks) {
       const int i = 2 * ks + hk;
-      const float a = Ss[i][32 * wave + l32];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Gs[i][32 * nb + l32], acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[ks], Ws[i][32 * nb + l32], acc[nb], 0, 0, 0);
     }
   };
   product();
@@ -586,24 +588,25 @@ frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__
     bool more;
     const float* Ft = rev_adjoint(rg, f, bh, t, T, DD, &more);
     const float* Rn = rg.rev + (f + 1) * DD;
-    constexpr int kPer = D * D / 4 / 256;
-    float4 fv[kPer], rv[kPer];
+    load_a_operands(more ? Rn : nullptr);
+    __syncthreads();  // every wave is done with G_t in Ws
+    // F_t in two halves (registers are short here: the accumulators, the A_t
+    // entries and the new A operands are live)
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = tid + 256 * u;
-      fv[u] = *(const float4*)(Ft + 4 * (int64_t)e);
-      rv[u] = more ? *(const float4*)(Rn + 4 * (int64_t)e) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    __syncthreads();  // every wave is done with Ss and Gs
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      float4 fv[kPer / 2];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = tid + 256 * u;
-      const int r = e / (D / 4), c4 = 4 * (e % (D / 4));
-      const float4 g4 = *(const float4*)&Gs[r][c4];
-      *(float4*)(Gt + 4 * (int64_t)e) =
-          make_float4(g4.x + fv[u].x, g4.y + fv[u].y, g4.z + fv[u].z, g4.w + fv[u].w);
-      *(float4*)&Gs[r][c4] = fv[u];
-      Ss[r][c4] = rv[u].x; Ss[r][c4 + 1] = rv[u].y; Ss[r][c4 + 2] = rv[u].z; Ss[r][c4 + 3] = rv[u].w;
+      for (int u = 0; u < kPer / 2; ++u)
+        fv[u] = *(const float4*)(Ft + 4 * (int64_t)(tid + 256 * (u + hlf * kPer / 2)));
+#pragma unroll
+      for (int u = 0; u < kPer / 2; ++u) {
+        const int e = tid + 256 * (u + hlf * kPer / 2);
+        float* w = &Ws[e / (D / 4)][4 * (e % (D / 4))];
+        const float4 g4 = *(const float4*)w;
+        *(float4*)(Gt + 4 * (int64_t)e) =
+            make_float4(g4.x + fv[u].x, g4.y + fv[u].y, g4.z + fv[u].z, g4.w + fv[u].w);
+        *(float4*)w = fv[u];
+      }
     }
     __syncthreads();
     if (more) product();
@@ -623,14 +626,14 @@ frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__
     }
   part = sum_lane_xor32(sum_lane_xor16(sum_row16(part)));
   if (lane == 0) red[wave] = part;
-  __syncthreads();  // every wave is done reading Ss
+  __syncthreads();  // every wave is done reading Ws
   const float g = gamma[f];
   if (tid == 0 && dgamma != nullptr) dgamma[f] = red[0] + red[1] + red[2] + red[3];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      Ss[32 * wave + 8 * (j >> 2) + 4 * hk + (j & 3)][32 * nb + l32] = acc[nb][j];
+      Ws[32 * wave + 8 * (j >> 2) + 4 * hk + (j & 3)][32 * nb + l32] = acc[nb][j];
   __syncthreads();
   float* Pf = P + f * DD;
 #pragma unroll
@@ -638,7 +641,7 @@ frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int a = 32 * wave + 8 * (j >> 2) + 4 * hk + (j & 3), b = 32 * nb + l32;
-      Pf[(int64_t)a * D + b] = -g * (acc[nb][j] + Ss[b][a]);
+      Pf[(int64_t)a * D + b] = -g * (acc[nb][j] + Ws[b][a]);
     }
 }
 
