@@ -72,7 +72,7 @@ def recorded_traffic(kernel, variant, source, workload):
     for line in open(path):
         key, _, val = line.strip().partition(" ")
         if key in ("source_sha256", "hbm_bytes_per_launch", "kernel_instance"):
-            fields[key] = val.strip()
+            fields.setdefault(key, val.strip())  # the first occurrence is the field
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     if (fields.get("source_sha256") != sha or "hbm_bytes_per_launch" not in fields
             or fields.get("kernel_instance") != kernel + variant):

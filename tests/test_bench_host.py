@@ -36,7 +36,9 @@ def _traffic_file(tmp_path, kernel, variant, workload, sha, nbytes):
     (tmp_path / "profiles").mkdir(exist_ok=True)
     (tmp_path / "profiles" / f"{kernel}__{workload}__hbm_traffic.txt").write_text(
         f"header\nkernel_instance {kernel}{variant}\nsource_sha256 {sha}\n"
-        f"hbm_bytes_per_launch {nbytes}\n")
+        f"hbm_bytes_per_launch {nbytes}\n"
+        f"(notes: a later line may start with a field name;\n"
+        f"kernel_instance is what the first such line says)\n")
 
 
 def test_recorded_traffic_follows_source_hash(tmp_path, monkeypatch):
