@@ -139,8 +139,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the scan shards "
-              f"over heads and time chunks, but multi-GPU runs are not part of this build)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the scan would "
+              f"shard over heads and time chunks, but no multi-GPU path is implemented)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -60,7 +60,7 @@ extern "C" {
 typedef enum {
   GDN_OK = 0,
   GDN_EINVAL = 1,        /* NULL required pointer, bad size, bad dtype, bad chunking */
-  GDN_EUNSUPPORTED = 2,  /* valid request this build does not implement (e.g. D) */
+  GDN_EUNSUPPORTED = 2,  /* valid request the library does not implement (e.g. D) */
   GDN_EWORKSPACE = 3,    /* ws_bytes smaller than gdn_workspace_bytes() asks for */
   GDN_EHIP = 4           /* a HIP launch failed */
 } gdn_status;
