@@ -264,14 +264,15 @@ __global__ void __launch_bounds__(256) token_grad_generic(
 // "A" fragments in registers (96 VGPRs) for the whole frame, and the frame's
 // tokens stream through a ring of 32-token LDS stages filled by direct
 // global -> LDS copies, so no register holds a prefetch and k is read once for
-// both the MFMA operand and the row pass. Per stage every wave forms its 32
-// rows of Y1 = P relu(k), Y2 = G^T v and Y3 = G relu(k) for the 32 tokens and
-// drops Z = c Y1 + Y2, W = c Y1 / 2 + Y2 and beta c Y3 into LDS (bf16, token
-// rows); then a row pass forms dk = beta c [k > 0] Z (prepared keys:
-// beta Z), dbeta = k_hat . W and dv = beta c Y3 and writes whole 16-byte row
-// chunks. Waves 0-1 issue every copy (their vmcnt counts copies only, so the
-// explicit waits are exact) and waves 2-3 run the row pass and issue every
-// store. Two workgroups fit a CU (74 KB of LDS each).
+// both the MFMA operand and the gradients. Per stage every wave forms its 32
+// rows of Y1 = P relu(k), Y2 = G^T v and Y3 = G relu(k) for the 32 tokens and,
+// still in fp32 registers, with Z = c Y1 + Y2 and W = c Y1 / 2 + Y2, its
+// features of dk = beta c [k > 0] Z (prepared keys: beta Z) and dv = beta c Y3
+// and its part of dbeta = k_hat . W; it drops dk and dv into LDS (bf16, token
+// rows) and one partial dbeta per token. A store pass then writes whole
+// 16-byte row chunks. Waves 0-1 issue every copy (their vmcnt counts copies
+// only, so the explicit waits are exact) and waves 2-3 issue every store. Two
+// workgroups fit a CU (66 KB of LDS each).
 constexpr int kWsTok = 32;                       // tokens per stage
 constexpr int kWsNst = 3;                        // ring stages
 constexpr int kWsKv = kWsTok * 256;              // one stage of k (or v): 32 rows x 256 B
@@ -289,8 +290,9 @@ __device__ __forceinline__ bf16x8_t pack8(float4 a, float4 b) {
 
 // kNorm (the RMSNorm of the raw keys): the copying waves normalise their own
 // key copies in place (k r, r = 1 / rms(k); the 16 chunks of a token sit in
-// one DPP row) and keep r per token; the row pass then takes dk through the
-// norm, dk = r (dkt - (kt . dkt) kt / D) with kt = k r.
+// one DPP row) and keep r per token; the waves form dkt, the gradient for
+// kt = k r, and their parts of kt . dkt, and the store pass takes dk through
+// the norm, dk = r (dkt - (kt . dkt) kt / D).
 template <bool kPrepared, bool kNorm>
 __global__ void __launch_bounds__(256, 2)
 token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -301,9 +303,10 @@ token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restri
   constexpr int D = 128;
   constexpr int64_t DD = (int64_t)D * D;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWsNst][kWsSlot];
-  __shared__ __attribute__((aligned(16))) uint8_t Zs[kWsKv];
-  __shared__ __attribute__((aligned(16))) uint8_t Wsb[kWsKv];
-  __shared__ __attribute__((aligned(16))) uint8_t Vsb[kWsKv];
+  __shared__ __attribute__((aligned(16))) uint8_t Zs[kWsKv];   // dk (kNorm: dkt) of the stage
+  __shared__ __attribute__((aligned(16))) uint8_t Vsb[kWsKv];  // dv of the stage
+  __shared__ float dbp[4][kWsTok];                              // per-wave parts of dbeta
+  __shared__ float dkp[kNorm ? 4 : 1][kWsTok];                  // per-wave parts of kt . dkt
   __shared__ float rks[kNorm ? kWsNst : 1][kWsTok];  // 1 / rms of each token's key
 
   // nb workgroups per frame-head, all on one XCD (consecutive workgroups go
@@ -425,77 +428,78 @@ token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restri
       y2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gta[kk], __builtin_bit_cast(bf16x8_t, vb), y2, 0, 0, 0);
       y3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[kk], kv8, y3, 0, 0, 0);
     }
-    // lane (h, l32): token l32, features 32 w + 8 jg + 4 h + 0..3
-    const float bc = gates[l32] * ck;
+    // lane (h, l32): token l32, features 32 w + 8 jg + 4 h + 0..3, and the
+    // key's same four features (kNorm: normalised) at the same place of its row
+    const float bt = gates[l32];
+    const float bc = bt * ck;
+    float pb = 0.f, pk = 0.f;  // this lane's parts of dbeta and (kNorm) kt . dkt
 #pragma unroll
     for (int jg = 0; jg < 4; ++jg) {
-      float z[4], w4[4], d[4];
+      const int at = ws_at(l32, 4 * wave + jg) + 8 * h;
+      const uint2 kq = *(const uint2*)(slot + at);
+      const float kv[4] = {__uint_as_float(kq.x << 16), __uint_as_float(kq.x & 0xFFFF0000u),
+                           __uint_as_float(kq.y << 16), __uint_as_float(kq.y & 0xFFFF0000u)};
+      float dk4[4], d[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float a1 = y1[4 * jg + r] * ck, a2 = y2[4 * jg + r];
-        z[r] = a1 + a2;
-        w4[r] = 0.5f * a1 + a2;
+        const float z = a1 + a2, wv = 0.5f * a1 + a2;
+        float kh, m;
+        if (kPrepared) {
+          kh = kv[r];
+          m = 1.f;
+        } else {
+          kh = (kv[r] > 0.f ? kv[r] : 0.f) * c;
+          m = kv[r] > 0.f ? c : 0.f;
+        }
+        pb += kh * wv;
+        dk4[r] = bt * m * z;
+        if (kNorm) pk += kv[r] * dk4[r];
         d[r] = bc * y3[4 * jg + r];
       }
-      const int at = ws_at(l32, 4 * wave + jg) + 8 * h;
-      *(uint2*)(Zs + at) = make_uint2(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]));
-      *(uint2*)(Wsb + at) = make_uint2(pack_bf16x2(w4[0], w4[1]), pack_bf16x2(w4[2], w4[3]));
+      *(uint2*)(Zs + at) = make_uint2(pack_bf16x2(dk4[0], dk4[1]), pack_bf16x2(dk4[2], dk4[3]));
       *(uint2*)(Vsb + at) = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+    }
+    // lanes l32 and l32 + 32 hold different features of one token
+    pb = sum_lane_xor32(pb);
+    if (kNorm) pk = sum_lane_xor32(pk);
+    if (h == 0) {
+      dbp[wave][l32] = pb;
+      if (kNorm) dkp[kNorm ? wave : 0][l32] = pk;
     }
     wait_vmcnt_lgkm0<63>();  // lgkmcnt(0): the staged tiles are written
     bare_barrier();
     if (wave >= 2) {
-      // row pass: thread u handles chunk u % 16 of rows u / 16 + 8 m; the 16
-      // chunks of a row sit in one DPP row of 16 lanes. Rows past the end
-      // were computed from copies of row S - 1, hold its values and are
-      // written there again.
+      // store pass: thread u handles chunk u % 16 of rows u / 16 + 8 m. Rows
+      // past the end were computed from copies of row S - 1, hold its values
+      // and are written there again.
       const int u = tid - 128;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int i = u + 128 * m;
         const int r = i >> 4, ch = i & 15;
         const int at = ws_at(r, ch);
-        const uint4 zc = *(const uint4*)(Zs + at);
-        const uint4 wc = *(const uint4*)(Wsb + at);
-        const uint4 kc = *(const uint4*)(slot + at);
-        const float bt = gates[r];
-        const uint32_t zw[4] = {zc.x, zc.y, zc.z, zc.w};
-        const uint32_t ww[4] = {wc.x, wc.y, wc.z, wc.w};
-        const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
-        uint32_t out[4];
-        float partial = 0.f, kdot = 0.f, dkt[8], kt[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float k0 = __uint_as_float(kw[q] << 16), k1 = __uint_as_float(kw[q] & 0xFFFF0000u);
-          const float z0 = __uint_as_float(zw[q] << 16), z1 = __uint_as_float(zw[q] & 0xFFFF0000u);
-          const float w0 = __uint_as_float(ww[q] << 16), w1 = __uint_as_float(ww[q] & 0xFFFF0000u);
-          float h0, h1, m0, m1;
-          if (kPrepared) {
-            h0 = k0; h1 = k1; m0 = m1 = 1.f;
-          } else {
-            h0 = (k0 > 0.f ? k0 : 0.f) * c; h1 = (k1 > 0.f ? k1 : 0.f) * c;
-            m0 = k0 > 0.f ? c : 0.f; m1 = k1 > 0.f ? c : 0.f;
-          }
-          partial += h0 * w0 + h1 * w1;
-          dkt[2 * q] = bt * m0 * z0;
-          dkt[2 * q + 1] = bt * m1 * z1;
-          kt[2 * q] = k0;
-          kt[2 * q + 1] = k1;
-          kdot += k0 * dkt[2 * q] + k1 * dkt[2 * q + 1];
-        }
-        partial = sum_row16(partial);
+        uint4 dkc = *(const uint4*)(Zs + at);
         if (kNorm) {  // through the norm of the key
-          const float proj = sum_row16(kdot) / (float)D;
+          const uint4 kc = *(const uint4*)(slot + at);
+          const float proj =
+              (dkp[0][r] + dkp[kNorm ? 1 : 0][r] + dkp[kNorm ? 2 : 0][r] + dkp[kNorm ? 3 : 0][r]) / (float)D;
           const float rr = rks[kNorm ? j % kWsNst : 0][r];
+          const uint32_t dw[4] = {dkc.x, dkc.y, dkc.z, dkc.w};
+          const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
+          uint32_t out[4];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) dkt[e] = rr * (dkt[e] - proj * kt[e]);
+          for (int q = 0; q < 4; ++q) {
+            const float d0 = __uint_as_float(dw[q] << 16), d1 = __uint_as_float(dw[q] & 0xFFFF0000u);
+            const float k0 = __uint_as_float(kw[q] << 16), k1 = __uint_as_float(kw[q] & 0xFFFF0000u);
+            out[q] = pack_bf16x2(rr * (d0 - proj * k0), rr * (d1 - proj * k1));
+          }
+          dkc = make_uint4(out[0], out[1], out[2], out[3]);
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) out[q] = pack_bf16x2(dkt[2 * q], dkt[2 * q + 1]);
         const int64_t sr = min(st * kWsTok + r, S - 1);
-        if (dkf) *(uint4*)(dkf + sr * D + 8 * ch) = make_uint4(out[0], out[1], out[2], out[3]);
+        if (dkf) *(uint4*)(dkf + sr * D + 8 * ch) = dkc;
         if (dvf) *(uint4*)(dvf + sr * D + 8 * ch) = *(const uint4*)(Vsb + at);
-        if (dbf && ch == 0) dbf[sr] = partial;
+        if (dbf && ch == 0) dbf[sr] = dbp[0][r] + dbp[1][r] + dbp[2][r] + dbp[3][r];
       }
     }
   }
