@@ -18,6 +18,22 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p % 16) == 0; }
 
+// Every launch must hold fewer than 2^32 work-items (the limit of a dispatch).
+// Conservative bounds of the grids a call on sh can launch, `chunks` being its
+// largest count of time chunks or reverse-scan chunks: the per-frame-head
+// kernels (phase 1 with up to 4 splits of 512 threads, the readout, the
+// backward's passes) at most 4096 work-items per frame-head; the fp32 and
+// small-D kernels at most S D + 4096 per frame-head; the scans and the
+// combine at most 32 blocks of 256 threads per (head, chunk) job.
+bool grids_fit(const gdn::Shape& sh, int64_t chunks) {
+  const long double limit = (long double)gdn::kGridLimit;
+  const long double fh = (long double)sh.FH();
+  if (fh * 4096.0L > limit) return false;
+  if (!(sh.io == 1 && sh.D == 128) && fh * ((long double)sh.S * sh.D + 4096.0L) > limit) return false;
+  const long double jobs = (long double)sh.BH() * (long double)(chunks > 1 ? chunks : 1);
+  return (jobs + 8.0L) * 32.0L * 256.0L <= limit;
+}
+
 gdn_status check_desc(const gdn_desc* d, Shape* sh) {
   if (d == nullptr) return GDN_EINVAL;
   if (d->B < 0 || d->H < 0 || d->T < 0 || d->S < 1 || d->D < 1) return GDN_EINVAL;
@@ -38,6 +54,7 @@ gdn_status check_desc(const gdn_desc* d, Shape* sh) {
   sh->prepared = (d->flags & GDN_KEYS_PREPARED) ? 1 : 0;
   sh->qk_norm = (d->flags & GDN_QK_RMSNORM) ? 1 : 0;
   sh->reuse_terms = (d->flags & GDN_REUSE_FWD_TERMS) ? 1 : 0;
+  if (!grids_fit(*sh, 1)) return GDN_EUNSUPPORTED;
   if (sh->prepared) {
     sh->c = 1.0f;
   } else if (d->key_scale > 0.f) {
@@ -333,6 +350,7 @@ gdn_status gdn_workspace_bytes(const gdn_desc* desc, int32_t n_time_chunks, size
   Shape sh;
   gdn_status s = check_desc(desc, &sh);
   if (s != GDN_OK) return s;
+  if (!grids_fit(sh, n_time_chunks)) return GDN_EUNSUPPORTED;
   if (bytes == nullptr || n_time_chunks < 1 || n_time_chunks > GDN_MAX_TIME_CHUNKS)
     return GDN_EINVAL;
   *bytes = layout(sh, n_time_chunks).total;
@@ -383,6 +401,7 @@ gdn_status gdn_scan_fwd(const gdn_desc* desc, const void* q, const void* k, cons
   if (s != GDN_OK) return s;
   if (n_time_chunks < 1 || n_time_chunks > GDN_MAX_TIME_CHUNKS) return GDN_EINVAL;
   if (sh.T > 0 && n_time_chunks > sh.T) return GDN_EINVAL;
+  if (!grids_fit(sh, n_time_chunks)) return GDN_EUNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(s0) || !aligned16(states) ||
       !aligned16(s_final) || !aligned16(o))
     return GDN_EINVAL;
@@ -419,6 +438,7 @@ gdn_status gdn_scan_bidir_chunked(const gdn_desc* desc, const void* q, const voi
   if (sh.T > 0 && n_time_chunks > sh.T) return GDN_EINVAL;
   const int64_t n_rev = sh.T > 0 ? ((int64_t)sh.T + chunk_len - 1) / chunk_len : 0;
   if (n_rev > gdn::kMaxChunks) return GDN_EUNSUPPORTED;
+  if (!grids_fit(sh, n_rev > n_time_chunks ? n_rev : n_time_chunks)) return GDN_EUNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(s0) ||
       !aligned16(states_fwd) || !aligned16(states_rev) || !aligned16(s_final) || !aligned16(o))
     return GDN_EINVAL;
@@ -462,6 +482,7 @@ gdn_status gdn_compose(const gdn_desc* desc, const void* k, const void* v, const
   gdn_status s = check_desc(desc, &sh);
   if (s != GDN_OK) return s;
   if (P < 1 || P > GDN_MAX_TIME_CHUNKS || chunk_offsets == nullptr) return GDN_EINVAL;
+  if (!grids_fit(sh, P)) return GDN_EUNSUPPORTED;
   if (chunk_offsets[0] != 0 || chunk_offsets[P] != sh.T) return GDN_EINVAL;
   for (int p = 0; p < P; ++p)
     if (chunk_offsets[p + 1] < chunk_offsets[p]) return GDN_EINVAL;
@@ -519,6 +540,7 @@ gdn_status gdn_bidir_bwd_workspace_bytes(const gdn_desc* desc, int32_t chunk_len
   if (bytes == nullptr || chunk_len < 1) return GDN_EINVAL;
   const int64_t n_rev = sh.T > 0 ? ((int64_t)sh.T + chunk_len - 1) / chunk_len : 0;
   if (n_rev > gdn::kMaxChunks) return GDN_EUNSUPPORTED;
+  if (!grids_fit(sh, n_rev)) return GDN_EUNSUPPORTED;
   *bytes = bwd_layout(sh, n_rev).total;
   return GDN_OK;
 }
@@ -541,6 +563,7 @@ gdn_status run_bwd(const gdn_desc* desc, int32_t chunk_len, const void* q, const
   if (chunk_len < 0) return GDN_EINVAL;
   const int64_t n_rev = bidir && sh.T > 0 ? ((int64_t)sh.T + chunk_len - 1) / chunk_len : 0;
   if (n_rev > gdn::kMaxChunks) return GDN_EUNSUPPORTED;
+  if (!grids_fit(sh, n_rev)) return GDN_EUNSUPPORTED;
   for (const void* p : {q, k, v, (const void*)s0, (const void*)states, (const void*)rev, d_o,
                         (const void*)ds_final, (const void*)dq, (const void*)dk, (const void*)dv,
                         (const void*)ds0})

@@ -75,6 +75,12 @@ __device__ __forceinline__ void lds_barrier() {
 // A_t) map linear id -> (job, member) so that a job's members share one XCD.
 constexpr int kNumXcd = 8;
 
+// Work-items one dispatch can hold (its grid size is a 32-bit count).
+constexpr int64_t kGridLimit = 0xFFFFFFFFLL;
+inline bool grid_fits(int64_t blocks, int threads) {
+  return blocks >= 0 && blocks <= kGridLimit / threads;
+}
+
 __host__ __device__ inline int64_t xcd_grid(int64_t njobs, int per) {
   return (njobs + kNumXcd - 1) / kNumXcd * kNumXcd * per;
 }

@@ -683,6 +683,7 @@ hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* 
   if (rg.rev != nullptr && (rg.L < 1 || rg.fbuf == nullptr || rg.finit == nullptr ||
                             (int64_t)rg.nchunk * rg.L < sh.T))
     return hipErrorInvalidValue;
+  if (!grid_fits(sh.FH(), 256)) return hipErrorInvalidValue;
   dim3 grid((unsigned)sh.FH());
   const int ag = a_granule_bf16 ? 1 : 0;
   if (sh.D == 128) {
@@ -733,6 +734,7 @@ hipError_t launch_token_grad(const Shape& sh, const void* q, const void* k, cons
     // GDN_TG_NB workgroups per frame-head on one XCD; two fit a CU
     const int nb = GDN_TG_NB;
     const int64_t groups = (sh.FH() + 7) / 8;
+    if (!grid_fits(groups * 8 * nb, 256)) return hipErrorInvalidValue;
     dim3 grid((unsigned)(groups * 8 * nb));
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
@@ -748,6 +750,7 @@ hipError_t launch_token_grad(const Shape& sh, const void* q, const void* k, cons
   }
   const int tpw = 256 / sh.D;
   const int ntile = (sh.S + tpw - 1) / tpw;
+  if (!grid_fits(sh.FH() * ntile, 256)) return hipErrorInvalidValue;
   dim3 grid((unsigned)(sh.FH() * ntile));
 #define GDN_TG(TT, DV)                                                                        \
   token_grad_generic<TT, DV><<<grid, 256, 0, st>>>(                                          \

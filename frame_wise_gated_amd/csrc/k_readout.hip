@@ -250,6 +250,7 @@ hipError_t launch_readout_generic(const Shape& sh, const void* q, const float* s
                                   void* o, hipStream_t st) {
   const int TT = 2048 / sh.D;
   const int ntile = (sh.S + TT - 1) / TT;
+  if (!grid_fits(sh.FH() * ntile, 256)) return hipErrorInvalidValue;
   dim3 grid((unsigned)(sh.FH() * ntile));
   const TIn* qq = (const TIn*)q;
   TIn* oo = (TIn*)o;
@@ -274,6 +275,7 @@ hipError_t launch_readout(const Shape& sh, const void* q, const float* sa, const
     int nb = (ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
     if (nb > kBlocksPerFrameHead) nb = kBlocksPerFrameHead;
     const int64_t groups = (sh.FH() + kXcd - 1) / kXcd;
+    if (!grid_fits(groups * kXcd * nb, 256)) return hipErrorInvalidValue;
     dim3 grid((unsigned)(groups * kXcd * nb));
     if (transpose_state)
       readout_mfma_bf16_d128<false, true><<<grid, 256, 0, st>>>((const uint16_t*)q, sa, nullptr,

@@ -576,6 +576,7 @@ hipError_t launch_mfma(const Shape& sh, const ScanParams& a, const ScanParams* b
   const int64_t na = mfma_blocks(sh, a, MT);
   const int64_t nb = b ? mfma_blocks(sh, *b, MT) : 0;
   if (na + nb == 0) return hipSuccess;
+  if (!grid_fits(na + nb, 256)) return hipErrorInvalidValue;
   scan_mfma_d128<MT, GDN_SCAN_F><<<dim3((unsigned)(na + nb)), 256, 0, st>>>(
       a, b ? *b : a, b ? na : INT64_MAX);
   return hipGetLastError();
@@ -605,6 +606,7 @@ hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st) {
   const ScanParams q = with_jobs(sh, p);
   if (q.njobs == 0) return hipSuccess;
   if (scan_uses_mfma(sh)) return launch_mfma(sh, q, nullptr, mfma_mt(sh, q), st);
+  if (!grid_fits(xcd_grid(q.njobs, (int)(rows_total / kR)), 256)) return hipErrorInvalidValue;
   dim3 grid((unsigned)xcd_grid(q.njobs, (int)(rows_total / kR)));
   switch (sh.D) {
     case 16: scan_rows_kernel<16><<<grid, 256, 0, st>>>(q); break;
@@ -628,9 +630,11 @@ hipError_t launch_combine(const Shape& sh, const CombineParams& p, hipStream_t s
   CombineParams q = p;
   q.BH = sh.BH();
   if (GDN_COMBINE_MFMA && scan_uses_mfma(sh)) {
+    if (!grid_fits(xcd_grid(q.BH, 4), 256)) return hipErrorInvalidValue;
     combine_mfma_d128<<<dim3((unsigned)xcd_grid(q.BH, 4)), 256, 0, st>>>(q);
     return hipGetLastError();
   }
+  if (!grid_fits(xcd_grid(q.BH, sh.D / rows), 256)) return hipErrorInvalidValue;
   dim3 grid((unsigned)xcd_grid(q.BH, sh.D / rows));
   switch (sh.D) {
     case 16: combine_rows_kernel<16><<<grid, 256, 0, st>>>(q); break;

@@ -662,6 +662,7 @@ reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, in
 template <typename TIn>
 hipError_t launch_generic(const Shape& sh, const void* k, const void* v, const float* beta,
                           int n_split, TermsOut out, hipStream_t st) {
+  if (!grid_fits(sh.FH() * n_split, 256)) return hipErrorInvalidValue;
   dim3 grid((unsigned)(sh.FH() * n_split));
   const TIn* kk = (const TIn*)k;
   const TIn* vv = (const TIn*)v;
@@ -705,6 +706,7 @@ hipError_t launch_terms(const Shape& sh, const void* k, const void* v, const flo
                         int n_split, TermsOut out, bool scan_layout, hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
   if (terms_use_mfma(sh)) {
+    if (!grid_fits(sh.FH() * n_split, 512)) return hipErrorInvalidValue;
     dim3 grid((unsigned)(sh.FH() * n_split));
     const uint16_t* kk = (const uint16_t*)k;
     const uint16_t* vv = (const uint16_t*)v;
@@ -738,7 +740,7 @@ bool edq_fused(const Shape& sh) { return terms_use_mfma(sh); }
 hipError_t launch_edq(const Shape& sh, const void* q, const void* d_o, const float* states,
                       const float* states2, void* dq, float* E, bool norm, hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
-  if (!edq_fused(sh)) return hipErrorInvalidValue;
+  if (!edq_fused(sh) || !grid_fits(sh.FH(), 512)) return hipErrorInvalidValue;
   TermsOut out{nullptr, E, (int64_t)sh.D * sh.D, 0};
   if (norm)
     terms_dma_bf16_d128<true, true, true, false, true><<<dim3((unsigned)sh.FH()), 512, 0, st>>>(

@@ -39,7 +39,12 @@
  *     results (no atomics, fixed reduction orders).
  *   - Supported shapes: B, H, T >= 0, S >= 1. D = 128 with bf16 runs the MFMA
  *     path; D in {16, 32, 64} (bf16 or fp32) and D = 128 with fp32 run the
- *     fp32 vector path. Other D give GDN_EUNSUPPORTED.
+ *     fp32 vector path. Other D give GDN_EUNSUPPORTED. Every kernel launch
+ *     must stay below 2^32 work-items, which bounds a call to about
+ *     B*H*T < 2^20 frame-heads (and B*H*T*S*D < 2^32 on the fp32 vector path)
+ *     and B*H times the number of time or reverse chunks below 2^19; larger
+ *     calls give GDN_EUNSUPPORTED before anything is enqueued (split them
+ *     over batch, heads or calls).
  */
 #ifndef GDN_H_
 #define GDN_H_

@@ -63,6 +63,31 @@ def test_workspace_sizes():
     assert _ws(gdn.make_desc(1, 1, 0, 12, 16, gdn.GDN_F32)) < 4096
 
 
+def test_shapes_whose_grids_exceed_a_dispatch_are_unsupported():
+    """A dispatch holds fewer than 2^32 work-items; shapes that would need a
+    larger grid are refused on the host (GDN_EUNSUPPORTED), before anything is
+    enqueued, instead of launching a truncated grid."""
+    n = ctypes.c_size_t(0)
+    ws = lambda d, P=1: gdn.lib().gdn_workspace_bytes(ctypes.byref(d), P, ctypes.byref(n))
+    # fp32 path: token-parallel kernels need about S * D work-items per frame-head
+    assert ws(gdn.make_desc(1, 1, 20000, 3600, 128, gdn.GDN_F32)) == gdn.GDN_EUNSUPPORTED
+    assert ws(gdn.make_desc(1, 1, 2000, 3600, 128, gdn.GDN_F32)) == gdn.GDN_OK
+    # MFMA path: per-frame-head kernels, up to 4096 work-items each
+    assert ws(gdn.make_desc(1, 1, 1000000, 16, 128, gdn.GDN_BF16)) == gdn.GDN_OK
+    assert ws(gdn.make_desc(1, 2, 1000000, 16, 128, gdn.GDN_BF16)) == gdn.GDN_EUNSUPPORTED
+    # scans: up to 32 blocks per (head, chunk) job, so the time-chunk count counts
+    d = gdn.make_desc(1, 8000, 100, 16, 128, gdn.GDN_BF16)
+    assert ws(d, 1) == gdn.GDN_OK
+    assert ws(d, 100) == gdn.GDN_EUNSUPPORTED
+    bb = ctypes.c_size_t(0)
+    assert gdn.lib().gdn_bidir_bwd_workspace_bytes(ctypes.byref(d), 1, ctypes.byref(bb)) == \
+        gdn.GDN_EUNSUPPORTED
+    # and the entry points refuse them the same way, with nothing to enqueue
+    fake = ctypes.c_void_p(256)
+    assert gdn.lib().gdn_scan_fwd(ctypes.byref(d), fake, fake, fake, fake, fake, None, fake, None,
+                                  None, 100, fake, 1 << 40, None) == gdn.GDN_EUNSUPPORTED
+
+
 def test_reuse_flag_changes_no_workspace_size():
     """GDN_REUSE_FWD_TERMS only tells a backward call where A_t already is:
     every workspace query answers the same with or without it."""
