@@ -91,6 +91,13 @@ __device__ __forceinline__ uint4 tr_frag(const uint8_t* base, int lb, int k0, in
 #ifndef GDN_EDQ_NST
 #define GDN_EDQ_NST 6
 #endif
+// Ring stages of the A-only mode (k alone: half-size slots). On MI355X the
+// 60 s 720p layer's recompute took 371-374 us with 4 stages, 376-378 us with
+// 6, 379 us with 7 and 453-460 us with 8 (one workgroup per CU); 4 stages at
+// three workgroups per CU spilled registers and took 825 us.
+#ifndef GDN_AONLY_NST
+#define GDN_AONLY_NST 4
+#endif
 template <bool kScanLayout, bool kPrepared, bool kNorm, bool kAOnly, bool kDq>
 __global__ void __launch_bounds__(512)
 __attribute__((amdgpu_waves_per_eu(kDq ? 2 : GDN_TERMS_WAVES_PER_EU, kDq ? 2 : GDN_TERMS_WAVES_PER_EU)))
@@ -103,7 +110,7 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   // ring slot: k block, v block, then the stage's 32 gates; wbuf[st % 2]
   // holds the second operand bf16(beta . ReLU(k)) of stage st
   // Without v a slot is half as large, and the same LDS holds twice the stages.
-  constexpr int kNs = kDq ? (kNorm ? GDN_EDQ_NST - 1 : GDN_EDQ_NST) : (kAOnly ? 2 * kNst : kNst);
+  constexpr int kNs = kDq ? (kNorm ? GDN_EDQ_NST - 1 : GDN_EDQ_NST) : (kAOnly ? GDN_AONLY_NST : kNst);
   constexpr int kGateOff = (kAOnly ? 1 : 2) * kKvBytes;
   constexpr int kSlot = kGateOff + 4 * kTsd;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kNs][kSlot];
