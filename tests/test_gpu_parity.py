@@ -15,7 +15,7 @@ from frame_wise_gated_amd import gdn
 from frame_wise_gated_amd import inputs as gi
 from oracle import gdn_oracle as orc
 
-from gpu_helpers import DEV, head_arrays, host, rel_fro, say, tol, upload
+from gpu_helpers import DEV, bits_to_dev, head_arrays, host, rel_fro, say, tol, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -1025,6 +1025,51 @@ def test_scan_bwd_reuse_needs_workspace():
         gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"],
                          torch.zeros((1, 1, 2, 128, 128), device=DEV), d["q"],
                          reuse_fwd_terms=True)
+
+
+def test_rmsnorm_layer_60s_forward_and_backward():
+    """The 60 s 720p layer (T = 121, S = 3600, 16 heads) with the RMSNorm of q
+    and k, in the benchmark's launch configuration (8 time chunks; the
+    backward reading A_t from the forward's workspace), on tokens whose q and
+    k are rescaled per token by factors in [0.2, 5] (a missing norm would be
+    far off): states, outputs and every gradient of two sampled heads against
+    the oracle."""
+    w = gi.workload(4)
+    heads = [(0, 4), (0, 11)]
+    say("generate", w.name)
+    x = gi.batch_inputs(w, 0, keep_f32=False)
+    for h in range(w.H):  # per-token rescaling, per head to bound host memory
+        rng = np.random.default_rng([77, 4, h])
+        for n in ("q", "k"):
+            bits = x[n + "_bits"][0, h]
+            fac = rng.uniform(0.2, 5.0, bits.shape[:-1] + (1,)).astype(np.float32)
+            bits[...] = gi.f32_to_bf16_bits(gi.bf16_bits_to_f32(bits) * fac)
+    d = upload(x, w)
+    rng = np.random.default_rng([88, 12])
+    do_bits = gi.f32_to_bf16_bits(rng.standard_normal((w.B, w.H, w.T, w.S, w.D)).astype(np.float32))
+    do_d = bits_to_dev(do_bits)
+    desc = gdn._desc_from(d["k"], 0.0, False, True)
+    ws = torch.empty(max(gdn.gdn_workspace_bytes(desc, w.time_chunks), gdn.gdn_bwd_workspace_bytes(desc)),
+                     dtype=torch.uint8, device=DEV)
+    say("forward + backward with the RMSNorm", w.name)
+    fwd = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], n_time_chunks=w.time_chunks,
+                           ws=ws, qk_rmsnorm=True)
+    g = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], do_d, ws=ws,
+                         qk_rmsnorm=True, reuse_fwd_terms=True)
+    torch.cuda.synchronize()
+    for (b, h) in heads:
+        a = {n: gi.bf16_bits_to_f32(x[n + "_bits"][b, h]).astype(np.float64)[None, None]
+             for n in ("q", "k", "v")}
+        for n in ("beta", "gamma"):
+            a[n] = np.asarray(x[n][b, h], dtype=np.float64)[None, None]
+        ref = orc.scan_fwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"], qk_rmsnorm=True)
+        errs = {n: rel_fro(host(fwd[n][b, h]), ref[n][0, 0]) for n in ("states", "o", "s_final")}
+        dof = gi.bf16_bits_to_f32(do_bits[b, h]).astype(np.float64)[None, None]
+        gref = orc.scan_fwd_bwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"], dof, qk_rmsnorm=True)
+        errs.update({n: rel_fro(host(g[n][b, h]), gref[n][0, 0])
+                     for n in ("dq", "dk", "dv", "dbeta", "dgamma", "ds0")})
+        say(w.name, "rmsnorm", (b, h), {n: f"{e:.2e}" for n, e in errs.items()})
+        assert max(errs.values()) <= tol(w), errs
 
 
 def test_scan_bwd_no_frames():
