@@ -53,7 +53,7 @@ def kernel_names(w, norm):
     if w.io == "bf16" and w.D == 128:
         n = "true" if norm else "false"
         return {"terms": ("terms_dma_bf16_d128", f"<false, false, {n}, false, false>", "k_terms.hip"),
-                "readout": ("readout_mfma_bf16_d128", f"<{n}, false>", "k_readout.hip")}
+                "readout": ("readout_mfma_bf16_d128", f"<{n}>", "k_readout.hip")}
     return {"terms": ("terms_generic", "", "k_terms.hip"),
             "readout": ("readout_generic", "", "k_readout.hip")}
 

@@ -255,9 +255,8 @@ bool scan_pairs(const Shape& sh, const ScanParams& a, const ScanParams& b);
 hipError_t launch_scan_pair(const Shape& sh, const ScanParams& a, const ScanParams& b,
                             hipStream_t st);
 hipError_t launch_combine(const Shape& sh, const CombineParams& p, hipStream_t st);
-// transpose_state (bf16, D = 128 only): o = states^T q, for the backward pass.
 hipError_t launch_readout(const Shape& sh, const void* q, const float* st_a, const float* st_b,
-                          void* o, hipStream_t st, bool transpose_state = false);
+                          void* o, hipStream_t st);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st);
 hipError_t launch_zero_f32(float* dst, int64_t n, hipStream_t st);
 hipError_t launch_fill_f32(float* dst, int64_t n, float value, hipStream_t st);

@@ -723,13 +723,8 @@ hipError_t launch_token_grad(const Shape& sh, const void* q, const void* k, cons
                              void* dk, void* dv, float* dbeta, hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
   if (token_grad_uses_mfma(sh)) {
-    // dq = states^T do: the readout with the state staged transposed (the
-    // summed states of the bidirectional scan go through the fused E pass)
-    if (dq && (states2 || sh.qk_norm)) return hipErrorInvalidValue;
-    if (dq) {
-      hipError_t e = launch_readout(sh, dout, states, nullptr, dq, st, true);
-      if (e != hipSuccess) return e;
-    }
+    // on this path dq comes from the fused E_t pass over q and d_o
+    if (dq) return hipErrorInvalidValue;
     if (!dk && !dv && !dbeta) return hipSuccess;
     // GDN_TG_NB workgroups per frame-head on one XCD; two fit a CU
     const int nb = GDN_TG_NB;

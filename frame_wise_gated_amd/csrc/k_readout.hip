@@ -42,7 +42,7 @@ __device__ __forceinline__ uint4 ld_q(const uint16_t* q, int s, int S, int j) {
 // consecutive rows read at the same logical chunk hit eight distinct bank groups.
 __device__ __forceinline__ int rswz(int row, int chunk) { return chunk ^ (row & 7); }
 
-template <bool kNorm, bool kTransposeState>
+template <bool kNorm>
 __global__ void __launch_bounds__(256, 2)
 readout_mfma_bf16_d128(const uint16_t* __restrict__ q, const float* __restrict__ sa,
                        const float* __restrict__ sb, uint16_t* __restrict__ o, int S, int64_t FH,
@@ -63,38 +63,23 @@ readout_mfma_bf16_d128(const uint16_t* __restrict__ q, const float* __restrict__
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // Stage the (summed) state once per workgroup: fp32 -> bf16, coalesced
-  // (kTransposeState: row i of the staged matrix is column i of the state,
-  // gathered with strided reads; the backward pass uses it for dq = S^T do).
-  if (kTransposeState) {
-    const float* s1 = sa + fh * D * D;
-    for (int c = tid; c < D * 16; c += 256) {
-      const int i = c >> 4;
-      const int ch = c & 15;
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = s1[(int64_t)(8 * ch + e) * D + i];
-      Sl[i * 16 + rswz(i, ch)] = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                            pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+  // Stage the (summed) state once per workgroup: fp32 -> bf16, coalesced.
+  const float* s1 = sa + fh * D * D;
+  const float* s2 = sb ? sb + fh * D * D : nullptr;
+  for (int c = tid; c < D * 16; c += 256) {
+    const int i = c >> 4;
+    const int ch = c & 15;
+    const int64_t off = (int64_t)i * D + 8 * ch;
+    float4 x0 = *(const float4*)(s1 + off);
+    float4 x1 = *(const float4*)(s1 + off + 4);
+    if (s2) {
+      float4 y0 = *(const float4*)(s2 + off);
+      float4 y1 = *(const float4*)(s2 + off + 4);
+      x0.x += y0.x; x0.y += y0.y; x0.z += y0.z; x0.w += y0.w;
+      x1.x += y1.x; x1.y += y1.y; x1.z += y1.z; x1.w += y1.w;
     }
-  } else {
-    const float* s1 = sa + fh * D * D;
-    const float* s2 = sb ? sb + fh * D * D : nullptr;
-    for (int c = tid; c < D * 16; c += 256) {
-      const int i = c >> 4;
-      const int ch = c & 15;
-      const int64_t off = (int64_t)i * D + 8 * ch;
-      float4 x0 = *(const float4*)(s1 + off);
-      float4 x1 = *(const float4*)(s1 + off + 4);
-      if (s2) {
-        float4 y0 = *(const float4*)(s2 + off);
-        float4 y1 = *(const float4*)(s2 + off + 4);
-        x0.x += y0.x; x0.y += y0.y; x0.z += y0.z; x0.w += y0.w;
-        x1.x += y1.x; x1.y += y1.y; x1.z += y1.z; x1.w += y1.w;
-      }
-      Sl[i * 16 + rswz(i, ch)] = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
-                                            pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
-    }
+    Sl[i * 16 + rswz(i, ch)] = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
+                                          pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
   }
   __syncthreads();
 
@@ -267,8 +252,7 @@ hipError_t launch_readout_generic(const Shape& sh, const void* q, const float* s
 }  // namespace
 
 hipError_t launch_readout(const Shape& sh, const void* q, const float* sa, const float* sb, void* o,
-                          hipStream_t st, bool transpose_state) {
-  if (transpose_state && !(sh.io == 1 && sh.D == 128)) return hipErrorInvalidValue;
+                          hipStream_t st) {
   if (sh.FH() == 0) return hipSuccess;
   if (sh.io == 1 && sh.D == 128) {
     const int ntiles = (sh.S + kTokPerWave - 1) / kTokPerWave;
@@ -277,15 +261,12 @@ hipError_t launch_readout(const Shape& sh, const void* q, const float* sa, const
     const int64_t groups = (sh.FH() + kXcd - 1) / kXcd;
     if (!grid_fits(groups * kXcd * nb, 256)) return hipErrorInvalidValue;
     dim3 grid((unsigned)(groups * kXcd * nb));
-    if (transpose_state)
-      readout_mfma_bf16_d128<false, true><<<grid, 256, 0, st>>>((const uint16_t*)q, sa, nullptr,
-                                                                (uint16_t*)o, sh.S, sh.FH(), nb);
-    else if (sh.qk_norm)
-      readout_mfma_bf16_d128<true, false><<<grid, 256, 0, st>>>((const uint16_t*)q, sa, sb,
-                                                                (uint16_t*)o, sh.S, sh.FH(), nb);
+    if (sh.qk_norm)
+      readout_mfma_bf16_d128<true><<<grid, 256, 0, st>>>((const uint16_t*)q, sa, sb, (uint16_t*)o,
+                                                         sh.S, sh.FH(), nb);
     else
-      readout_mfma_bf16_d128<false, false><<<grid, 256, 0, st>>>((const uint16_t*)q, sa, sb,
-                                                                 (uint16_t*)o, sh.S, sh.FH(), nb);
+      readout_mfma_bf16_d128<false><<<grid, 256, 0, st>>>((const uint16_t*)q, sa, sb, (uint16_t*)o,
+                                                          sh.S, sh.FH(), nb);
     return hipGetLastError();
   }
   if (sh.io == 1) return launch_readout_generic<uint16_t>(sh, q, sa, sb, o, st);
