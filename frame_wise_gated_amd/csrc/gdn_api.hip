@@ -275,15 +275,14 @@ gdn::ScanParams reverse_params(const Shape& sh, int chunk_len, const Slice& x) {
 // forward states or the final state are wanted; sequential for P <= 1, else
 // compose, combine and replay) and the chunk-reset reverse scan (chunk_len >
 // 0, when reverse states are wanted). The reverse scan needs only the terms,
-// so on the MFMA path it shares a launch with the first forward one when
-// both run with the same row block (the compose of several chunks and the
-// reverse scan do; a sequential scan of a few heads takes smaller blocks).
+// so on the MFMA path it shares a launch with the first forward one (the
+// compose of several chunks, or a sequential scan that leaves most CUs idle).
 gdn_status run_scans(const Shape& sh, int P, int chunk_len, const Slice& x, hipStream_t st) {
   const bool fwd = x.fwd || x.s_final;
   const bool rev = chunk_len > 0 && x.rev;
   const gdn::ScanParams first = P <= 1 ? seq_params(sh, x) : compose_params(sh, P, x);
   const gdn::ScanParams second = rev ? reverse_params(sh, chunk_len, x) : first;
-  const bool pair = fwd && rev && gdn::scan_pairs(sh, first, second);
+  const bool pair = fwd && rev && gdn::scan_pairs(sh);
   if (fwd) {
     if (pair)
       GDN_HIP(gdn::launch_scan_pair(sh, first, second, st));
@@ -634,57 +633,63 @@ gdn_status run_bwd(const gdn_desc* desc, int32_t chunk_len, const void* q, const
   // adjoint recurrence: frames T-1 .. 0 from G_{T-1}, adding E_{f-1} after
   // frame f's transition, so the state after frame f is G_{f-1} (stored in
   // slot f) and after frame 0 it is dL/dS0
-  {
-    gdn::ScanParams p;
-    memset(&p, 0, sizeof(p));
-    p.terms = terms;
-    p.gamma = gamma;
-    p.T = sh.T;
-    p.nchunk = 1;
-    p.mode = gdn::SCAN_REVERSE;
-    p.usrc = E;
-    p.ushift = -1;
-    p.init = ginit;
-    p.init_bh_stride = DD;
-    p.states = G;
-    p.finA = ds0;
-    p.fin_bh_stride = DD;
-    p.fin_last_only = 1;
-    p.offsets[0] = 0;
-    p.offsets[1] = sh.T;
-    GDN_HIP(gdn::launch_scan(sh, p, st));
-  }
+  gdn::ScanParams pg;
+  memset(&pg, 0, sizeof(pg));
+  pg.terms = terms;
+  pg.gamma = gamma;
+  pg.T = sh.T;
+  pg.nchunk = 1;
+  pg.mode = gdn::SCAN_REVERSE;
+  pg.usrc = E;
+  pg.ushift = -1;
+  pg.init = ginit;
+  pg.init_bh_stride = DD;
+  pg.states = G;
+  pg.finA = ds0;
+  pg.fin_bh_stride = DD;
+  pg.fin_last_only = 1;
+  pg.offsets[0] = 0;
+  pg.offsets[1] = sh.T;
   gdn::RevGrad rg;
   if (bidir) {
     // adjoint of the reverse states, forward inside every chunk [a, e):
     // F_a = E_a and F_{t+1} = F_t M_t + E_{t+1}. The scan starts each chunk
     // from E_a, steps frames a .. e-1 adding E_{f+1} after frame f's
     // transition and stores F_{f+1} in slot f (the last step of a chunk
-    // leaves a value nobody reads).
+    // leaves a value nobody reads). Both adjoints need only E_t and the
+    // terms: on the MFMA path they share one launch, the short chunks
+    // running beside the long sequential chain of G.
     float* F = at<float>(ws, L.F);
     float* finit = at<float>(ws, L.finit);
     GDN_HIP(gdn::launch_chunk_init(sh, E, chunk_len, (int)n_rev, finit, mfma, st));
-    gdn::ScanParams p;
-    memset(&p, 0, sizeof(p));
-    p.terms = terms;
-    p.gamma = gamma;
-    p.T = sh.T;
-    p.nchunk = (int)n_rev;
-    p.mode = gdn::SCAN_FORWARD;
-    p.usrc = E;
-    p.ushift = 1;
-    p.init = finit;
-    p.init_bh_stride = n_rev * DD;
-    p.init_c_stride = DD;
-    p.states = F;
+    gdn::ScanParams pf;
+    memset(&pf, 0, sizeof(pf));
+    pf.terms = terms;
+    pf.gamma = gamma;
+    pf.T = sh.T;
+    pf.nchunk = (int)n_rev;
+    pf.mode = gdn::SCAN_FORWARD;
+    pf.usrc = E;
+    pf.ushift = 1;
+    pf.init = finit;
+    pf.init_bh_stride = n_rev * DD;
+    pf.init_c_stride = DD;
+    pf.states = F;
     for (int c = 0; c <= (int)n_rev; ++c)
-      p.offsets[c] = (int)std::min<int64_t>((int64_t)c * chunk_len, sh.T);
-    GDN_HIP(gdn::launch_scan(sh, p, st));
+      pf.offsets[c] = (int)std::min<int64_t>((int64_t)c * chunk_len, sh.T);
+    if (gdn::scan_pairs(sh)) {
+      GDN_HIP(gdn::launch_scan_pair(sh, pg, pf, st));
+    } else {
+      GDN_HIP(gdn::launch_scan(sh, pg, st));
+      GDN_HIP(gdn::launch_scan(sh, pf, st));
+    }
     rg.rev = rev;
     rg.fbuf = F;
     rg.finit = finit;
     rg.L = chunk_len;
     rg.nchunk = (int)n_rev;
+  } else {
+    GDN_HIP(gdn::launch_scan(sh, pg, st));
   }
   GDN_HIP(gdn::launch_frame_grad(sh, states, s0, G, ginit, terms, mfma, gamma, P, dgamma, rg, st));
   if (dq || dk || dv || dbeta)

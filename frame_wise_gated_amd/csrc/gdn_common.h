@@ -248,10 +248,9 @@ hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_s
                                   TermsOut out, bool scan_layout, hipStream_t st);
 bool scan_uses_mfma(const Shape& sh);
 hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st);
-// Two independent scans over the same terms in one launch (MFMA path, and
-// both must pick the same row block: scan_pairs must hold, else
-// hipErrorInvalidValue and nothing launched).
-bool scan_pairs(const Shape& sh, const ScanParams& a, const ScanParams& b);
+// Two independent scans over the same terms in one launch (MFMA path only:
+// scan_pairs must hold, else hipErrorInvalidValue and nothing launched).
+bool scan_pairs(const Shape& sh);
 hipError_t launch_scan_pair(const Shape& sh, const ScanParams& a, const ScanParams& b,
                             hipStream_t st);
 hipError_t launch_combine(const Shape& sh, const CombineParams& p, hipStream_t st);

@@ -590,15 +590,17 @@ hipError_t launch_mfma(const Shape& sh, const ScanParams& a, const ScanParams* b
 
 }  // namespace
 
-bool scan_pairs(const Shape& sh, const ScanParams& a, const ScanParams& b) {
-  return scan_uses_mfma(sh) && mfma_mt(sh, with_jobs(sh, a)) == mfma_mt(sh, with_jobs(sh, b));
-}
+bool scan_pairs(const Shape& sh) { return scan_uses_mfma(sh); }
 
+// Both job lists take the smaller of their two row blocks: a short scan that
+// shares the launch of a long chain of few blocks (a sequential scan) fills
+// the CUs that chain leaves idle.
 hipError_t launch_scan_pair(const Shape& sh, const ScanParams& a, const ScanParams& b,
                             hipStream_t st) {
-  if (!scan_pairs(sh, a, b)) return hipErrorInvalidValue;
+  if (!scan_pairs(sh)) return hipErrorInvalidValue;
   const ScanParams qa = with_jobs(sh, a), qb = with_jobs(sh, b);
-  return launch_mfma(sh, qa, &qb, mfma_mt(sh, qa), st);
+  const int mta = mfma_mt(sh, qa), mtb = mfma_mt(sh, qb);
+  return launch_mfma(sh, qa, &qb, mta < mtb ? mta : mtb, st);
 }
 
 hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st) {
