@@ -1,7 +1,8 @@
-// Backward pass of the causal frame scan: the per-frame and per-token
-// gradient kernels. The adjoint recurrence itself runs on the scan kernels
-// (k_scan.hip, REVERSE mode with a shifted U source); phase 1 supplies A_t and
-// E_t = dO_t^T Q_t.
+// Backward pass of the causal and the chunk-causal frame scan: the per-frame
+// and per-token gradient kernels. The adjoint recurrences themselves run on
+// the scan kernels (k_scan.hip: REVERSE mode with a shifted U source for G,
+// and per chunk FORWARD for the reverse states' adjoint F); phase 1 supplies
+// A_t and E_t = dO_t^T Q_t.
 //
 // Forward rule (blog.hotdry.top SANA-WM post, section "混合线性注意力"):
 // S_t = S_{t-1} M_t + U_t, M_t = gamma_t (I - A_t), o = S_t q. With

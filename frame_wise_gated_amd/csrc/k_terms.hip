@@ -21,11 +21,10 @@ namespace gdn {
 
 namespace {
 
-// MFMA path. Phase 1 is bound by the HBM reads of k and v, and the bytes in
-// flight per CU decide how close it gets: with the loads staged through
-// registers (two workgroups per CU, about 64 KB outstanding) the stream
-// reaches about 5 TB/s, while the same access pattern with more in flight
-// reaches about 7 TB/s. Here the loads bypass registers: global_load_lds_dwordx4
+// MFMA path. Phase 1 is bound by the HBM reads of k and v. With the loads
+// staged through registers (two workgroups per CU, about 64 KB outstanding)
+// the stream reached about 5 TB/s, while a plain read stream with more in
+// flight reaches about 7 TB/s. Here the loads bypass registers: global_load_lds_dwordx4
 // copies 16 bytes per lane straight into a ring of kNst LDS stages (32 tokens
 // of k and v each), so kNst - 1 stages stay in flight while one is consumed.
 // MFMA fragments (eight consecutive tokens of one feature) are read with
