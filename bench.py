@@ -132,6 +132,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phases", action="store_true", help="skip the per-phase timing loops")
+    ap.add_argument("--no-streaming", action="store_true",
+                    help="skip the streaming leg (the layer stepped in blocks of frames)")
+    ap.add_argument("--stream-block", type=int, default=3,
+                    help="latent frames per streaming block (default 3)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward pass")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -274,6 +278,40 @@ def main():
             "mfma_frac": nflop / (t / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
         }
         del A, U
+
+    if not args.no_streaming:
+        # streaming: the same layer stepped through blocks of a few latent
+        # frames with gdn_step (bidirectional inside a block, the forward state
+        # carried in place from block to block), as a chunk-causal model runs
+        # it; the inputs are cut into contiguous per-block tensors beforehand
+        print("[bench] streaming", file=sys.stderr, flush=True)
+        L = max(1, min(args.stream_block, T))
+        cuts = [(a, min(a + L, T)) for a in range(0, T, L)]
+        blk = [{n: t[:, :, a:b].contiguous() for n, t in (("q", q), ("k", k), ("v", v),
+                                                          ("beta", beta), ("gamma", gamma))}
+               for a, b in cuts]
+        blk_o = [torch.empty_like(b["q"]) for b in blk]
+        carry = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+        bws_s = gdn.workspace(gdn.make_desc(B, H, L, S, D, gdn.GDN_BF16 if bf else gdn.GDN_F32,
+                                            qk_rmsnorm=norm), 1, dev)
+
+        def stream_pass():
+            cin = None  # the first block starts from the zero state
+            for b, ob in zip(blk, blk_o):
+                gdn.gdn_step(b["q"], b["k"], b["v"], b["beta"], b["gamma"], carry_in=cin,
+                             carry_out=carry, o=ob, ws=bws_s, stream=stream, qk_rmsnorm=norm)
+                cin = carry
+
+        stream_pass()
+        t_stream = timed(stream_pass, max(args.steps // 4, 3))
+        out["streaming"] = {
+            "block_frames": L,
+            "blocks": len(cuts),
+            "ms_per_layer": t_stream,
+            "ms_per_block": t_stream / len(cuts),
+            "layer_frames_per_s": T / (t_stream / 1e3),
+        }
+        del blk, blk_o, carry, bws_s
 
     if not args.no_backward:
         # backward of the same layer: gradients of <d_o, o> for a random d_o

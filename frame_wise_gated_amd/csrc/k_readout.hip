@@ -32,6 +32,7 @@ constexpr int kWavesPerBlock = 4;
 #define GDN_READOUT_NB 4
 #endif
 constexpr int kBlocksPerFrameHead = GDN_READOUT_NB;
+constexpr int kMaxBlocksPerFrameHead = 16;
 constexpr int kXcd = 8;
 
 __device__ __forceinline__ uint4 ld_q(const uint16_t* q, int s, int S, int j) {
@@ -256,8 +257,12 @@ hipError_t launch_readout(const Shape& sh, const void* q, const float* sa, const
   if (sh.FH() == 0) return hipSuccess;
   if (sh.io == 1 && sh.D == 128) {
     const int ntiles = (sh.S + kTokPerWave - 1) / kTokPerWave;
+    // calls with few frame-heads (a streaming block) take more workgroups per
+    // frame-head, aiming at about two per CU
+    int64_t want = (512 + sh.FH() - 1) / sh.FH();
+    want = want < kBlocksPerFrameHead ? kBlocksPerFrameHead : (want > kMaxBlocksPerFrameHead ? kMaxBlocksPerFrameHead : want);
     int nb = (ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (nb > kBlocksPerFrameHead) nb = kBlocksPerFrameHead;
+    if (nb > want) nb = (int)want;
     const int64_t groups = (sh.FH() + kXcd - 1) / kXcd;
     if (!grid_fits(groups * kXcd * nb, 256)) return hipErrorInvalidValue;
     dim3 grid((unsigned)(groups * kXcd * nb));

@@ -631,18 +631,25 @@ reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, in
     const int64_t e = (i % per) * 4;
     const float* base = partial + (f * n_split) * 2 * D * D;
     if (scan_layout && e < (int64_t)D * D) {
-      // group = (column nn, rows mm..mm+3)
+      // group = (column nn, rows mm..mm+3) of A_t, read as row nn, columns
+      // mm..mm+3: A_t is symmetric, and the two differ only in which operand
+      // carried the bf16 rounding of beta . ReLU(k); the row is one
+      // coalesced 16-byte load per split
       const int64_t nn = e / D;
       const int64_t mm = e % D;
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int p = 0; p < n_split; ++p)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] += base[(int64_t)p * 2 * D * D + (mm + q) * D + nn];
+      float4 v = *(const float4*)(base + nn * D + mm);
+      for (int p = 1; p < n_split; ++p) {
+        const float4 t = *(const float4*)(base + (int64_t)p * 2 * D * D + nn * D + mm);
+        v.x += t.x;
+        v.y += t.y;
+        v.z += t.z;
+        v.w += t.w;
+      }
       if (out.outA == nullptr) continue;
       uint16_t* At = (uint16_t*)(out.outA + f * out.fstride);
       // scan_layout is only requested for D = 128 (granule layout)
       const int64_t at = (int64_t)a_granule((int)nn, (int)(mm >> 3)) * 8 + (mm & 7);
-      *(uint2*)(At + at) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      *(uint2*)(At + at) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
       continue;
     }
     const float4* src = (const float4*)(base + e);
