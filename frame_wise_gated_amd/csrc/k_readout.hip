@@ -258,8 +258,9 @@ hipError_t launch_readout(const Shape& sh, const void* q, const float* sa, const
   if (sh.io == 1 && sh.D == 128) {
     const int ntiles = (sh.S + kTokPerWave - 1) / kTokPerWave;
     // calls with few frame-heads (a streaming block) take more workgroups per
-    // frame-head, aiming at about two per CU
-    int64_t want = (512 + sh.FH() - 1) / sh.FH();
+    // frame-head, up to two per CU in one round (512: more would start a
+    // second round of workgroups)
+    int64_t want = 512 / sh.FH();
     want = want < kBlocksPerFrameHead ? kBlocksPerFrameHead : (want > kMaxBlocksPerFrameHead ? kMaxBlocksPerFrameHead : want);
     int nb = (ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
     if (nb > want) nb = (int)want;

@@ -711,6 +711,8 @@ int terms_split(const Shape& sh) {
   if (fh <= 0) return 1;
   const int64_t want = (512 + fh - 1) / fh;  // about two workgroups per CU on 256 CUs
   int64_t cap = sh.S / 512;                   // keep at least 512 tokens per split
+  // at most 4 splits: with 7 (48 frame-heads of 3600 tokens, a 3-frame
+  // streaming block of the 16-head layer) the block took 74.7 us against 71
   cap = std::min<int64_t>(std::max<int64_t>(cap, 1), 4);
   return (int)std::max<int64_t>(1, std::min(want, cap));
 }
