@@ -8,6 +8,13 @@
         per-kernel mean counter value per dispatch (KiB for FETCH_SIZE and
         WRITE_SIZE) from DIR/*counter_collection.csv, also multiplied by F
         and shown in MB.
+    python -m frame_wise_gated_amd.profsum mfma DIR [--simds N] [--clock-ghz F]
+        per-kernel MFMA utilisation from a counter run that collected
+        SQ_INSTS_MFMA and SQ_VALU_MFMA_BUSY_CYCLES: the busy cycles summed over
+        all SIMDs, divided by SIMDs x clock x the dispatch's duration (its start
+        and end timestamps in the same CSV). The defaults are MI355X's 1024
+        SIMDs (256 CUs x 4) at its 2.4 GHz peak engine clock, the clock of the
+        published dense MFMA peak.
 
 Kernels are keyed by name and grid size, so launches of one kernel with
 different shapes stay apart.
@@ -84,14 +91,45 @@ def pmc(d: str, scale: float) -> list[str]:
     return out
 
 
+def mfma(d: str, simds: int, clock_ghz: float) -> list[str]:
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "*counter_collection.csv")))))
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in rows:
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        agg[key][r["Counter_Name"]].append((float(r["Counter_Value"]), dur))
+    out = [f"{'kernel':54s} {'grid':>9s} {'calls':>5s} {'mean_us':>9s} {'mfma_insts':>11s} "
+           f"{'busy/inst':>9s} {'mfma_util':>9s}"]
+    for (name, grid), ctr in sorted(agg.items()):
+        busy, insts = ctr.get("SQ_VALU_MFMA_BUSY_CYCLES"), ctr.get("SQ_INSTS_MFMA")
+        if not busy or not insts:
+            continue
+        n = len(busy)
+        b = sum(x for x, _ in busy) / n
+        t = sum(x for _, x in busy) / n
+        m = sum(x for x, _ in insts) / len(insts)
+        if m == 0 or t <= 0:
+            continue
+        out.append(f"{name:54s} {grid:9d} {n:5d} {t * 1e6:9.1f} {m:11.0f} {b / m:9.1f} "
+                   f"{b / (simds * clock_ghz * 1e9 * t):9.3f}")
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("kind", choices=("trace", "pmc"))
+    ap.add_argument("kind", choices=("trace", "pmc", "mfma"))
     ap.add_argument("dir")
     ap.add_argument("--skip", type=int, default=0)
     ap.add_argument("--scale", type=float, default=1.0)
+    ap.add_argument("--simds", type=int, default=1024)
+    ap.add_argument("--clock-ghz", type=float, default=2.4)
     a = ap.parse_args(argv)
-    lines = trace(a.dir, a.skip) if a.kind == "trace" else pmc(a.dir, a.scale)
+    if a.kind == "trace":
+        lines = trace(a.dir, a.skip)
+    elif a.kind == "pmc":
+        lines = pmc(a.dir, a.scale)
+    else:
+        lines = mfma(a.dir, a.simds, a.clock_ghz)
     print("\n".join(lines))
     return 0
 

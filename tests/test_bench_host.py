@@ -85,3 +85,18 @@ def test_profsum_trace_and_pmc(tmp_path):
     row = [l for l in lines if l.startswith("readout_mfma_bf16_d128")][0].split()
     assert float(row[4]) == pytest.approx(200.0)
     assert float(row[5]) == pytest.approx(200 * 1024 * 2 / 1e6, rel=1e-3)
+
+
+def test_profsum_mfma_utilisation(tmp_path):
+    # 1000 MFMA instructions of 32 busy cycles each over 10 us on 4 SIMDs at
+    # 1 GHz: 32000 busy cycles of 40000 available
+    (tmp_path / "run_counter_collection.csv").write_text(
+        "Kernel_Name,Grid_Size,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n"
+        "readout_mfma_bf16_d128<false>(x),64,SQ_INSTS_MFMA,1000,0,10000\n"
+        "readout_mfma_bf16_d128<false>(x),64,SQ_VALU_MFMA_BUSY_CYCLES,32000,0,10000\n"
+        "grad_init_kernel(x),64,SQ_INSTS_MFMA,0,0,1000\n"
+        "grad_init_kernel(x),64,SQ_VALU_MFMA_BUSY_CYCLES,0,0,1000\n")
+    lines = profsum.mfma(str(tmp_path), simds=4, clock_ghz=1.0)
+    assert not any(l.startswith("grad_init_kernel") for l in lines)
+    row = [l for l in lines if l.startswith("readout_mfma_bf16_d128<false>")][0].split()
+    assert row[-5:] == ["1", "10.0", "1000", "32.0", "0.800"]
