@@ -339,26 +339,20 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_d128(CombineParams p) {
 // frame loop is unrolled by kF); loads past the last frame re-read it, so
 // the outstanding-load bookkeeping is identical in every step. Wave w owns
 // output columns [32w, 32w + 32) as two 16-column MFMA tiles.
-// One workgroup's job; `blk` is its block index within the launch of p.
-template <int MT, int kF>
-__device__ __forceinline__ void scan_block(const ScanParams& p, int64_t blk) {
+// Rows of one workgroup's job: row block rb of job `job`. kC: the composite C
+// rows of a COMPOSE job (start I, no U term), which load no U entries.
+constexpr int kScanLdb = 128 + 8;  // bf16 row stride 272 B: 8 lanes reading 16 B at one column are conflict-free
+template <int MT, int kF, bool kC>
+__device__ __forceinline__ void scan_rows(const ScanParams& p, int64_t job, int rb,
+                                          uint16_t (*Xh)[16 * MT][kScanLdb],
+                                          uint16_t (*Xl)[16 * MT][kScanLdb]) {
   constexpr int D = 128;
   constexpr int R = 16 * MT;
-  constexpr int LDB = D + 8;  // bf16 row stride 272 B: 8 lanes reading 16 B at one column are conflict-free
   constexpr int64_t DD = (int64_t)D * D;
-  __shared__ __attribute__((aligned(16))) uint16_t Xh[2][R][LDB];
-  __shared__ __attribute__((aligned(16))) uint16_t Xl[2][R][LDB];
-
-  const int rows_total = (p.mode == SCAN_COMPOSE) ? 2 * D : D;
-  const int nrb = rows_total / R;
-  int64_t job;
-  int rb;
-  xcd_job(blk, nrb, &job, &rb);
-  if (job >= p.njobs) return;
   const int c = (int)(job % p.nchunk);
   const int64_t bh = job / p.nchunk;
   const int row0 = rb * R;
-  const bool c_rows = (p.mode == SCAN_COMPOSE) && row0 < D;
+  constexpr bool c_rows = kC;
   const float umul = c_rows ? 0.f : 1.f;
   const int srow0 = row0 % D;
 
@@ -427,12 +421,16 @@ __device__ __forceinline__ void scan_block(const ScanParams& p, int64_t blk) {
       for (int ks = 0; ks < 4; ++ks)  // a_granule(n0 + 16nt + l16, 4ks + g)
         af[j][nt][ks] = At[((2 * wave + nt) * 4 + ks) * 64 + lane];
   };
-  // Composite C rows have no U term (umul = 0): their U loads re-read granules
-  // of the frame's A block, which the workgroup fetches anyway (cache hits,
-  // finite values), so that every workgroup issues the same load sequence.
+  // Composite C rows have no U term: they load only gamma (their load
+  // sequence differs from the other rows', so they are a separate
+  // instantiation with exact waits of its own).
   auto load_u = [&](int j, int step) {
-    const f32x4_t* Ug = (const f32x4_t*)(terms_of(step) + (c_rows ? 0 : DD));
     umr[j] = umul;
+    if (kC) {
+      gmr[j] = p.gamma[bh * p.T + frame_of(step)];
+      return;
+    }
+    const f32x4_t* Ug = (const f32x4_t*)(terms_of(step) + DD);
     if (p.usrc != nullptr && !c_rows) {
       // U of frame f from the shifted source slot (zero outside [0, T))
       const int fs = frame_of(step) + p.ushift;
@@ -502,7 +500,7 @@ __device__ __forceinline__ void scan_block(const ScanParams& p, int64_t blk) {
           f32x4_t xn;
 #pragma unroll
           for (int r = 0; r < 4; ++r)  // one rounding: umr is 0 or 1, so umr u is exact
-            xn[r] = __builtin_fmaf(gm, xr[mt][nt][r] - acc[mt][nt][r], umr[j] * u[j][mt][nt][r]);
+            xn[r] = __builtin_fmaf(gm, xr[mt][nt][r] - acc[mt][nt][r], kC ? 0.f : umr[j] * u[j][mt][nt][r]);
           if (active) xr[mt][nt] = xn;
           put_split(cur ^ 1, m, ncol(nt), xr[mt][nt]);
         }
@@ -529,6 +527,25 @@ __device__ __forceinline__ void scan_block(const ScanParams& p, int64_t blk) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
       *(f32x4_t*)(fin + (int64_t)(srow0 + 16 * mt + l16) * D + ncol(nt)) = xr[mt][nt];
+}
+
+// One workgroup's job; `blk` is its block index within the launch of p. The
+// split state copy lives here, once per kernel, for both row kinds.
+template <int MT, int kF>
+__device__ __forceinline__ void scan_block(const ScanParams& p, int64_t blk) {
+  constexpr int D = 128;
+  constexpr int R = 16 * MT;
+  __shared__ __attribute__((aligned(16))) uint16_t Xh[2][R][kScanLdb];
+  __shared__ __attribute__((aligned(16))) uint16_t Xl[2][R][kScanLdb];
+  const int rows_total = (p.mode == SCAN_COMPOSE) ? 2 * D : D;
+  int64_t job;
+  int rb;
+  xcd_job(blk, rows_total / R, &job, &rb);
+  if (job >= p.njobs) return;
+  if (p.mode == SCAN_COMPOSE && rb * R < D)
+    scan_rows<MT, kF, true>(p, job, rb, Xh, Xl);
+  else
+    scan_rows<MT, kF, false>(p, job, rb, Xh, Xl);
 }
 
 // Blocks [0, split) run the jobs of p0 and blocks [split, grid) those of p1:
