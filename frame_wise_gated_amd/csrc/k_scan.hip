@@ -35,6 +35,18 @@
 #ifndef GDN_SCAN_F
 #define GDN_SCAN_F 2
 #endif
+// A compose launch of its own (not sharing a launch with a reverse scan) that
+// fills the chip takes 64-row blocks with a one-frame ring (168 registers,
+// two workgroups per CU): each workgroup reads A_t once for twice the rows.
+// 60 s 720p layer, 8 chunks: 64-66 us against 73-75 us with 32-row blocks
+// and a two-frame ring; the replay stays faster with 32-row blocks (63 us
+// against 64-65 us).
+#ifndef GDN_COMPOSE_MT
+#define GDN_COMPOSE_MT 4
+#endif
+#ifndef GDN_COMPOSE_F
+#define GDN_COMPOSE_F 1
+#endif
 // bf16 D = 128: the combine on MFMA (1) or on fp32 vector FMAs (0)
 #ifndef GDN_COMBINE_MFMA
 #define GDN_COMBINE_MFMA 1
@@ -588,13 +600,13 @@ ScanParams with_jobs(const Shape& sh, const ScanParams& p) {
 }
 
 // One launch running the jobs of a and then those of b (b may be null).
-template <int MT>
+template <int MT, int kF = GDN_SCAN_F>
 hipError_t launch_mfma(const Shape& sh, const ScanParams& a, const ScanParams* b, hipStream_t st) {
   const int64_t na = mfma_blocks(sh, a, MT);
   const int64_t nb = b ? mfma_blocks(sh, *b, MT) : 0;
   if (na + nb == 0) return hipSuccess;
   if (!grid_fits(na + nb, 256)) return hipErrorInvalidValue;
-  scan_mfma_d128<MT, GDN_SCAN_F><<<dim3((unsigned)(na + nb)), 256, 0, st>>>(
+  scan_mfma_d128<MT, kF><<<dim3((unsigned)(na + nb)), 256, 0, st>>>(
       a, b ? *b : a, b ? na : INT64_MAX);
   return hipGetLastError();
 }
@@ -624,7 +636,11 @@ hipError_t launch_scan(const Shape& sh, const ScanParams& p, hipStream_t st) {
   const int64_t rows_total = (p.mode == SCAN_COMPOSE) ? 2 * sh.D : sh.D;
   const ScanParams q = with_jobs(sh, p);
   if (q.njobs == 0) return hipSuccess;
-  if (scan_uses_mfma(sh)) return launch_mfma(sh, q, nullptr, mfma_mt(sh, q), st);
+  if (scan_uses_mfma(sh)) {
+    if (q.mode == SCAN_COMPOSE && mfma_blocks(sh, q, GDN_COMPOSE_MT) >= kCUs)
+      return launch_mfma<GDN_COMPOSE_MT, GDN_COMPOSE_F>(sh, q, nullptr, st);
+    return launch_mfma(sh, q, nullptr, mfma_mt(sh, q), st);
+  }
   if (!grid_fits(xcd_grid(q.njobs, (int)(rows_total / kR)), 256)) return hipErrorInvalidValue;
   dim3 grid((unsigned)xcd_grid(q.njobs, (int)(rows_total / kR)));
   switch (sh.D) {

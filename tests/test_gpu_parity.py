@@ -111,6 +111,8 @@ SCAN_CASES = {
     "tiny_f32_B2H3": (gi.workload(1).with_shape(B=2, H=3), 3, True),
     "bf16_D128_seq": (gi.workload(2).with_shape(H=2, T=6, S=700), 1, False),
     "bf16_D128_cp3_s0": (gi.workload(2).with_shape(H=2, T=6, S=700), 3, True),
+    # 64 (head, chunk) jobs: a compose launch that fills the chip, with 64-row blocks
+    "bf16_D128_H16_cp4_s0": (gi.workload(2).with_shape(H=16, T=9, S=100), 4, True),
     "bf16_D64_seq": (gi.workload(2).with_shape(D=64, T=4, S=130), 1, True),
     "f32_D128_cp2": (gi.workload(1).with_shape(D=128, T=4, S=200), 2, True),
 }
