@@ -196,6 +196,8 @@ def test_scan_bidir(name):
     ("tiny_f32_empty_chunk", gi.workload(1), [0, 3, 3, 8]),
     ("tiny_f32_one_chunk", gi.workload(1), [0, 8]),
     ("bf16_D128", gi.workload(4).with_shape(H=2, T=7, S=500), [0, 2, 5, 7]),
+    # 64 (head, chunk) jobs: the compose launch with 64-row blocks, one chunk empty
+    ("bf16_D128_H16_empty_chunk", gi.workload(4).with_shape(H=16, T=7, S=60), [0, 2, 2, 5, 7]),
 ])
 def test_compose(name, w, offs):
     x, d = _gen(w)
