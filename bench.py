@@ -277,7 +277,14 @@ def main():
             "mfma_tflops": nflop / (t / 1e3) / 1e12,
             "mfma_frac": nflop / (t / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
         }
-        del A, U
+        # a plain device copy of q (the readout's input) on the same stream, as
+        # the mixed read + write stream this box sustains next to the readout
+        qc = torch.empty_like(q)
+        t_copy = timed(lambda: qc.copy_(q), reps)
+        copy_gbs = 2 * q.numel() * q.element_size() / (t_copy / 1e3) / 1e9
+        out["roofline"]["copy_reference_GBps"] = copy_gbs
+        out["roofline"]["achieved_over_copy"] = achieved / copy_gbs
+        del A, U, qc
 
     if not args.no_streaming:
         # streaming: the same layer stepped through blocks of a few latent
