@@ -507,14 +507,19 @@ token_grad_ws_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restri
   wait_vmcnt_lgkm0<0>();  // no copy may still be landing in LDS when the workgroup retires
 }
 
-// MFMA path of the per-frame gradients (D = 128): dM = S_prev^T G on fp32
-// MFMA (v_mfma_f32_32x32x2_f32: exact fp32 products), wave w owns rows
-// 32w .. 32w + 31 of dM as four 32 x 32 tiles. The A operand of lane l is
-// S_prev[i][32w + l % 32] with i = 2 ks + l / 32: the wave's 64 such values
+// MFMA path of the per-frame gradients (D = 128): dM = S_prev^T G on bf16
+// MFMA with both operands split into hi/lo bf16 pairs (Sh Gh + Sl Gh + Sh Gl,
+// fp32 accumulation; |X - Xh - Xl| <= 2^-17 |X|), about 16 significant bits
+// per product as in the scan's own steps, while P_t leaves for the token
+// kernel rounded to bf16. Wave w owns rows 32w .. 32w + 31 of dM as four
+// 32 x 32 tiles. The first operand of lane l is S_prev[i][32w + l % 32] for
+// the eight i = 16 ks + 8 (l / 32) + 0..7 of step ks: the wave's 64 values
 // per lane are loaded straight into registers (coalesced 128-byte row
-// pieces). The B operand G[i][32 nb + l % 32] is shared by the four waves and
-// read from LDS. One padded D x D buffer then holds G_t (the chunk-causal
-// scan's F_t next) and finally dM for its transposed read: 68 KB of LDS, two
+// pieces) and split there. The second operand, G[i][32 nb + l % 32] for the
+// same i, is shared by the four waves: G_t sits in LDS transposed as a hi/lo
+// pair (row b holds column b, 16-byte chunk c = rows 8c .. 8c + 7 at position
+// c ^ (b % 16)), one 16-byte read per fragment. The same 66 KB then hold the
+// chunk-causal scan's F_t, and finally dM for its transposed read: two
 // workgroups per CU, so that one's loads overlap the other's products.
 __global__ void __launch_bounds__(256, 2)
 frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__ s0,
@@ -525,7 +530,10 @@ frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__
   constexpr int D = 128;
   constexpr int LDT = D + 4;  // padded row for the transposed read of dM
   constexpr int64_t DD = (int64_t)D * D;
-  __shared__ float Ws[D][LDT];
+  __shared__ __attribute__((aligned(16))) float Ws[D][LDT];
+  static_assert(sizeof(Ws) >= 2 * D * 16 * sizeof(uint4), "the hi/lo operand pair fits the dM buffer");
+  uint4* const Bh = (uint4*)&Ws[0][0];  // second operand, hi
+  uint4* const Bl = Bh + D * 16;        // second operand, lo
   __shared__ float red[4];
   const int64_t f = blockIdx.x;
   const int64_t bh = f / T;
@@ -551,40 +559,64 @@ frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__
         ag[nb][jg] = *(const uint2*)((const uint16_t*)At +
                                      (int64_t)a_granule(32 * nb + l32, 4 * wave + jg) * 8 + 4 * hk);
   }
-  // this lane's A operands (S_prev, or zero) in registers and G_t into LDS:
-  // every load of a thread is issued before its first LDS write, so the
-  // staging costs one memory round trip
-  constexpr int kPer = D * D / 4 / 256;
-  float sa[D / 2];
+  auto split8 = [](const float* x, uint4* hi, uint4* lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      h[q] = pack_bf16x2(x[2 * q], x[2 * q + 1]);
+      l[q] = pack_bf16x2(x[2 * q] - bf16_to_f32(h[q] & 0xFFFFu), x[2 * q + 1] - bf16_to_f32(h[q] >> 16));
+    }
+    *hi = make_uint4(h[0], h[1], h[2], h[3]);
+    *lo = make_uint4(l[0], l[1], l[2], l[3]);
+  };
+  // this lane's first operands (S_prev, or zero), split in registers
+  uint4 sh[D / 16], sl[D / 16];
   auto load_a_operands = [&](const float* X) {
     const float* col = X ? X + 32 * wave + l32 : nullptr;
 #pragma unroll
-    for (int ks = 0; ks < D / 2; ++ks) sa[ks] = col ? col[(int64_t)(2 * ks + hk) * D] : 0.f;
-  };
-  {
-    float4 gv[kPer];
-    load_a_operands(Sp);
+    for (int ks = 0; ks < D / 16; ++ks) {
+      float x[8];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) gv[u] = *(const float4*)(Gt + 4 * (int64_t)(tid + 256 * u));
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = tid + 256 * u;
-      *(float4*)&Ws[e / (D / 4)][4 * (e % (D / 4))] = gv[u];
+      for (int e = 0; e < 8; ++e) x[e] = col ? col[(int64_t)(16 * ks + 8 * hk + e) * D] : 0.f;
+      split8(x, &sh[ks], &sl[ks]);
     }
-  }
+  };
+  // X (row-major D x D fp32) into LDS as the transposed hi/lo pair: thread t
+  // takes column t % 128 and the chunks 8 (t / 128) .. + 7 (rows 64 (t / 128) ..)
+  auto stage_b = [&](const float* X) {
+    const int bc = tid & 127, c0 = 8 * (tid >> 7);
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const int c = c0 + cc;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = X[(int64_t)(8 * c + e) * D + bc];
+      split8(x, &Bh[bc * 16 + (c ^ (bc & 15))], &Bl[bc * 16 + (c ^ (bc & 15))]);
+    }
+  };
+  load_a_operands(Sp);
+  stage_b(Gt);
   __syncthreads();
   f32x16_t acc[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[nb][j] = 0.f;
-  auto product = [&]() {  // acc += X^T Ws, X^T's operands in sa
+  auto product = [&]() {  // acc += X^T B, X^T's operands in sh / sl, B in LDS
 #pragma unroll
-    for (int ks = 0; ks < D / 2; ++ks) {
-      const int i = 2 * ks + hk;
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int c = 2 * ks + hk;
+      const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, sh[ks]);
+      const bf16x8_t al = __builtin_bit_cast(bf16x8_t, sl[ks]);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[ks], Ws[i][32 * nb + l32], acc[nb], 0, 0, 0);
+      for (int nb = 0; nb < 4; ++nb) {
+        const int bcol = 32 * nb + l32;
+        const bf16x8_t bhv = __builtin_bit_cast(bf16x8_t, Bh[bcol * 16 + (c ^ (bcol & 15))]);
+        const bf16x8_t blv = __builtin_bit_cast(bf16x8_t, Bl[bcol * 16 + (c ^ (bcol & 15))]);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bhv, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bhv, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, blv, acc[nb], 0, 0, 0);
+      }
     }
   };
   product();
@@ -593,28 +625,21 @@ frame_grad_mfma_d128(const float* __restrict__ states, const float* __restrict__
     bool more;
     const float* Ft = rev_adjoint(rg, f, bh, t, T, DD, &more);
     const float* Rn = rg.rev + (f + 1) * DD;
-    load_a_operands(more ? Rn : nullptr);
-    __syncthreads();  // every wave is done with G_t in Ws
-    // F_t in two halves (registers are short here: the accumulators, the A_t
-    // entries and the new A operands are live)
+    __syncthreads();  // every wave is done with G_t's operands, and every thread has read G_t
+    constexpr int kPer = D * D / 4 / 256;
 #pragma unroll
-    for (int hlf = 0; hlf < 2; ++hlf) {
-      float4 fv[kPer / 2];
-#pragma unroll
-      for (int u = 0; u < kPer / 2; ++u)
-        fv[u] = *(const float4*)(Ft + 4 * (int64_t)(tid + 256 * (u + hlf * kPer / 2)));
-#pragma unroll
-      for (int u = 0; u < kPer / 2; ++u) {
-        const int e = tid + 256 * (u + hlf * kPer / 2);
-        float* w = &Ws[e / (D / 4)][4 * (e % (D / 4))];
-        const float4 g4 = *(const float4*)w;
-        *(float4*)(Gt + 4 * (int64_t)e) =
-            make_float4(g4.x + fv[u].x, g4.y + fv[u].y, g4.z + fv[u].z, g4.w + fv[u].w);
-        *(float4*)w = fv[u];
-      }
+    for (int u = 0; u < kPer; ++u) {
+      const int64_t e = 4 * (int64_t)(tid + 256 * u);
+      const float4 g4 = *(const float4*)(Gt + e);
+      const float4 f4 = *(const float4*)(Ft + e);
+      *(float4*)(Gt + e) = make_float4(g4.x + f4.x, g4.y + f4.y, g4.z + f4.z, g4.w + f4.w);
     }
-    __syncthreads();
-    if (more) product();
+    if (more) {
+      load_a_operands(Rn);
+      stage_b(Ft);
+      __syncthreads();
+      product();
+    }
   }
   // acc[nb][j] = dM[a][b], a = 32 wave + 8 (j / 4) + 4 hk + j % 4, b = 32 nb + l32
   float part = 0.f;
