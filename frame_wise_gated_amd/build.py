@@ -1,7 +1,8 @@
-"""Build libgdn.so (the HIP/gfx950 C-ABI library) in-tree with hipcc.
+"""Build libgdn.so (the HIP/gfx950 C-ABI library) in-tree with hipcc, and
+libhbm_probe.so (the plain HBM streams the benchmark's calibration mode times).
 
 Usage: python -m frame_wise_gated_amd.build   (or call build()).
-Every call recompiles; the shared object lands next to this file.
+Every call recompiles; the shared objects land next to this file.
 """
 
 from __future__ import annotations
@@ -18,6 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libgdn.so")
 SOURCES = ["gdn_api.hip", "k_misc.hip", "k_terms.hip", "k_scan.hip", "k_readout.hip", "k_bwd.hip"]
+PROBE_OUT = os.path.join(HERE, "libhbm_probe.so")
+PROBE_SOURCES = ["hbm_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -48,20 +51,26 @@ def _compile(src: str, obj_dir: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    obj_dir = os.path.join(HERE, "_build")
-    os.makedirs(obj_dir, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, obj_dir), SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs: list[str], out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, obj_dir), srcs))
+    _link(objs[:len(SOURCES)], OUT)
+    _link(objs[len(SOURCES):], PROBE_OUT)
     shutil.rmtree(obj_dir, ignore_errors=True)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {PROBE_OUT}")
     return OUT
 
 

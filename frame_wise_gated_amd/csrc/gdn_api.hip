@@ -141,6 +141,20 @@ T* at(void* ws, size_t off) {
     if ((x) != hipSuccess) return GDN_EHIP;        \
   } while (0)
 
+// The calling thread's phase trace (gdn_trace_set), or NULL.
+thread_local gdn_trace* t_trace = nullptr;
+
+// Records the next event of the thread's trace on `st`, tagged with `phase`.
+hipError_t mark(int phase, hipStream_t st) {
+  gdn_trace* t = t_trace;
+  if (t == nullptr || t->count < 0 || t->count >= t->capacity) return hipSuccess;
+  const hipError_t e = hipEventRecord((hipEvent_t)t->events[t->count], st);
+  if (e != hipSuccess) return e;
+  t->phases[t->count++] = phase;
+  return hipSuccess;
+}
+#define GDN_MARK(phase, st) GDN_HIP(mark(phase, st))
+
 // Device pointers of one call.
 struct Slice {
   const char* q;
@@ -179,10 +193,13 @@ gdn_status run_terms(const Shape& sh, int n_split, const Slice& x, hipStream_t s
   const bool scan_layout = gdn::scan_uses_mfma(sh);
   if (n_split == 1) {
     GDN_HIP(gdn::launch_terms(sh, x.k, x.v, x.beta, 1, direct, scan_layout, st));
+    GDN_MARK(GDN_PHASE_TERMS, st);
   } else {
     gdn::TermsOut po{x.partial, x.partial + DD, (int64_t)n_split * 2 * DD, 2 * DD};
     GDN_HIP(gdn::launch_terms(sh, x.k, x.v, x.beta, n_split, po, false, st));
+    GDN_MARK(GDN_PHASE_TERMS, st);
     GDN_HIP(gdn::launch_reduce_partials(sh, x.partial, n_split, direct, scan_layout, st));
+    GDN_MARK(GDN_PHASE_TERMS_REDUCE, st);
   }
   return GDN_OK;
 }
@@ -288,18 +305,27 @@ gdn_status run_scans(const Shape& sh, int P, int chunk_len, const Slice& x, hipS
       GDN_HIP(gdn::launch_scan_pair(sh, first, second, st));
     else
       GDN_HIP(gdn::launch_scan(sh, first, st));
+    GDN_MARK(GDN_PHASE_SCAN, st);
     if (P > 1) {
       gdn::CombineParams cp{x.compC, x.compH, x.s0, x.start, P};
       GDN_HIP(gdn::launch_combine(sh, cp, st));
+      GDN_MARK(GDN_PHASE_COMBINE, st);
       GDN_HIP(gdn::launch_scan(sh, replay_params(sh, P, x), st));
+      GDN_MARK(GDN_PHASE_REPLAY, st);
     }
   }
-  if (rev && !pair) GDN_HIP(gdn::launch_scan(sh, second, st));
+  if (rev && !pair) {
+    GDN_HIP(gdn::launch_scan(sh, second, st));
+    GDN_MARK(GDN_PHASE_REVERSE, st);
+  }
   return GDN_OK;
 }
 
 gdn_status run_readout(const Shape& sh, const Slice& x, hipStream_t st) {
-  if (x.o) GDN_HIP(gdn::launch_readout(sh, x.q, x.fwd, x.rev, x.o, st));
+  if (x.o) {
+    GDN_HIP(gdn::launch_readout(sh, x.q, x.fwd, x.rev, x.o, st));
+    GDN_MARK(GDN_PHASE_READOUT, st);
+  }
   return GDN_OK;
 }
 
@@ -307,6 +333,7 @@ gdn_status run_readout(const Shape& sh, const Slice& x, hipStream_t st) {
 gdn_status run_path(const Shape& sh, int n_split, int P, int chunk_len, const Slice& x,
                     hipStream_t st) {
   gdn_status s;
+  GDN_MARK(GDN_PHASE_CALL_BEGIN, st);
   if ((s = run_terms(sh, n_split, x, st)) != GDN_OK) return s;
   if ((s = run_scans(sh, P, chunk_len, x, st)) != GDN_OK) return s;
   return run_readout(sh, x, st);
@@ -315,11 +342,13 @@ gdn_status run_path(const Shape& sh, int n_split, int P, int chunk_len, const Sl
 // No frames: the final state is the initial state.
 gdn_status run_empty(const Shape& sh, const float* s0, float* s_final, hipStream_t st) {
   if (s_final == nullptr) return GDN_OK;
+  GDN_MARK(GDN_PHASE_CALL_BEGIN, st);
   const int64_t n = sh.BH() * sh.D * sh.D;
   if (s0)
     GDN_HIP(gdn::launch_copy_f32(s0, s_final, n, st));
   else
     GDN_HIP(gdn::launch_zero_f32(s_final, n, st));
+  GDN_MARK(GDN_PHASE_OTHER, st);
   return GDN_OK;
 }
 
@@ -345,6 +374,14 @@ const char* gdn_status_str(int32_t s) {
   }
 }
 
+gdn_status gdn_trace_set(gdn_trace* trace) {
+  if (trace != nullptr &&
+      (trace->events == nullptr || trace->phases == nullptr || trace->capacity < 0 || trace->count < 0))
+    return GDN_EINVAL;
+  t_trace = trace;
+  return GDN_OK;
+}
+
 gdn_status gdn_workspace_bytes(const gdn_desc* desc, int32_t n_time_chunks, size_t* bytes) {
   Shape sh;
   gdn_status s = check_desc(desc, &sh);
@@ -363,7 +400,9 @@ gdn_status gdn_prepare(const gdn_desc* desc, const void* k, void* k_hat, void* s
   if (sh.prepared) return GDN_EINVAL;
   if (sh.FH() == 0) return GDN_OK;
   if (k == nullptr || k_hat == nullptr || !aligned16(k) || !aligned16(k_hat)) return GDN_EINVAL;
+  GDN_MARK(GDN_PHASE_CALL_BEGIN, (hipStream_t)stream);
   GDN_HIP(gdn::launch_prepare(sh, k, k_hat, (hipStream_t)stream));
+  GDN_MARK(GDN_PHASE_OTHER, (hipStream_t)stream);
   return GDN_OK;
 }
 
@@ -380,13 +419,17 @@ gdn_status gdn_frame_terms(const gdn_desc* desc, const void* k, const void* v, c
   hipStream_t st = (hipStream_t)stream;
   const int64_t DD = (int64_t)sh.D * sh.D;
   gdn::TermsOut direct{A, U, DD, 0};
+  GDN_MARK(GDN_PHASE_CALL_BEGIN, st);
   if (L.n_split == 1) {
     GDN_HIP(gdn::launch_terms(sh, k, v, beta, 1, direct, false, st));
+    GDN_MARK(GDN_PHASE_TERMS, st);
   } else {
     float* part = at<float>(ws, L.partial);
     gdn::TermsOut po{part, part + DD, (int64_t)L.n_split * 2 * DD, 2 * DD};
     GDN_HIP(gdn::launch_terms(sh, k, v, beta, L.n_split, po, false, st));
+    GDN_MARK(GDN_PHASE_TERMS, st);
     GDN_HIP(gdn::launch_reduce_partials(sh, part, L.n_split, direct, false, st));
+    GDN_MARK(GDN_PHASE_TERMS_REDUCE, st);
   }
   return GDN_OK;
 }
@@ -496,6 +539,7 @@ gdn_status gdn_compose(const gdn_desc* desc, const void* k, const void* v, const
   const int64_t DD = (int64_t)sh.D * sh.D;
   float* Cb = C ? C : at<float>(ws, L.compC);
   float* Hb = Hc ? Hc : at<float>(ws, L.compH);
+  GDN_MARK(GDN_PHASE_CALL_BEGIN, st);
   if (sh.T > 0) {
     Slice x = work_slice(L, ws);
     x.k = (const char*)k;
@@ -516,9 +560,11 @@ gdn_status gdn_compose(const gdn_desc* desc, const void* k, const void* v, const
   p.fin_c_stride = DD;
   for (int c = 0; c <= P; ++c) p.offsets[c] = chunk_offsets[c];
   GDN_HIP(gdn::launch_scan(sh, p, st));
+  GDN_MARK(GDN_PHASE_SCAN, st);
   if (s_start) {
     gdn::CombineParams cp{Cb, Hb, s0, s_start, P};
     GDN_HIP(gdn::launch_combine(sh, cp, st));
+    GDN_MARK(GDN_PHASE_COMBINE, st);
   }
   return GDN_OK;
 }
@@ -573,8 +619,10 @@ gdn_status run_bwd(const gdn_desc* desc, int32_t chunk_len, const void* q, const
   if (sh.T == 0) {
     // no frames: L depends on s0 only through S_{-1} = s0 = S_{T-1}
     if (ds0 == nullptr) return GDN_OK;
+    GDN_MARK(GDN_PHASE_CALL_BEGIN, st);
     if (ds_final) GDN_HIP(gdn::launch_copy_f32(ds_final, ds0, sh.BH() * DD, st));
     else GDN_HIP(gdn::launch_zero_f32(ds0, sh.BH() * DD, st));
+    GDN_MARK(GDN_PHASE_OTHER, st);
     return GDN_OK;
   }
   if (!q || !k || !v || !beta || !gamma || !states || !d_o) return GDN_EINVAL;
@@ -590,6 +638,7 @@ gdn_status run_bwd(const gdn_desc* desc, int32_t chunk_len, const void* q, const
   float* P = at<float>(ws, L.P);
   float* ginit = at<float>(ws, L.ginit);
   float* ones = at<float>(ws, L.ones);
+  GDN_MARK(GDN_PHASE_CALL_BEGIN, st);
   // A_t of every frame (the U half is not needed), unless the workspace
   // still holds the forward call's terms: both layouts put them first, in the
   // same internal format, and nothing below writes there
@@ -602,6 +651,7 @@ gdn_status run_bwd(const gdn_desc* desc, int32_t chunk_len, const void* q, const
       GDN_HIP(gdn::launch_terms(sh, k, v, beta, L.n_split, po, false, st));
       GDN_HIP(gdn::launch_reduce_partials(sh, part, L.n_split, direct, mfma, st));
     }
+    GDN_MARK(GDN_PHASE_BWD_TERMS, st);
   }
   // E_t = d_o_t^T q_t: the phase-1 contraction with q as prepared keys, d_o
   // as values and unit gates (the U half of its output)
@@ -628,6 +678,7 @@ gdn_status run_bwd(const gdn_desc* desc, int32_t chunk_len, const void* q, const
       GDN_HIP(gdn::launch_terms(shq, q, d_o, ones, L.n_split, po, false, st));
       GDN_HIP(gdn::launch_reduce_partials(shq, part, L.n_split, eout, mfma, st));
     }
+    GDN_MARK(GDN_PHASE_BWD_EDQ, st);
   }
   GDN_HIP(gdn::launch_grad_init(sh, E, ds_final, ginit, mfma, st));
   // adjoint recurrence: frames T-1 .. 0 from G_{T-1}, adding E_{f-1} after
@@ -662,6 +713,7 @@ gdn_status run_bwd(const gdn_desc* desc, int32_t chunk_len, const void* q, const
     float* F = at<float>(ws, L.F);
     float* finit = at<float>(ws, L.finit);
     GDN_HIP(gdn::launch_chunk_init(sh, E, chunk_len, (int)n_rev, finit, mfma, st));
+    GDN_MARK(GDN_PHASE_BWD_INIT, st);
     gdn::ScanParams pf;
     memset(&pf, 0, sizeof(pf));
     pf.terms = terms;
@@ -683,18 +735,24 @@ gdn_status run_bwd(const gdn_desc* desc, int32_t chunk_len, const void* q, const
       GDN_HIP(gdn::launch_scan(sh, pg, st));
       GDN_HIP(gdn::launch_scan(sh, pf, st));
     }
+    GDN_MARK(GDN_PHASE_BWD_ADJOINT, st);
     rg.rev = rev;
     rg.fbuf = F;
     rg.finit = finit;
     rg.L = chunk_len;
     rg.nchunk = (int)n_rev;
   } else {
+    GDN_MARK(GDN_PHASE_BWD_INIT, st);
     GDN_HIP(gdn::launch_scan(sh, pg, st));
+    GDN_MARK(GDN_PHASE_BWD_ADJOINT, st);
   }
   GDN_HIP(gdn::launch_frame_grad(sh, states, s0, G, ginit, terms, mfma, gamma, P, dgamma, rg, st));
-  if (dq || dk || dv || dbeta)
+  GDN_MARK(GDN_PHASE_BWD_FRAME, st);
+  if (dq || dk || dv || dbeta) {
     GDN_HIP(gdn::launch_token_grad(sh, q, k, v, beta, d_o, states, bidir ? rev : nullptr, G, ginit,
                                    P, fused_dq ? nullptr : dq, dk, dv, dbeta, st));
+    GDN_MARK(GDN_PHASE_BWD_TOKEN, st);
+  }
   return GDN_OK;
 }
 
@@ -732,7 +790,9 @@ gdn_status gdn_readout(const gdn_desc* desc, const void* q, const float* states,
   if (!q || !states || !o) return GDN_EINVAL;
   if (!aligned16(q) || !aligned16(states) || !aligned16(states_add) || !aligned16(o))
     return GDN_EINVAL;
+  GDN_MARK(GDN_PHASE_CALL_BEGIN, (hipStream_t)stream);
   GDN_HIP(gdn::launch_readout(sh, q, states, states_add, o, (hipStream_t)stream));
+  GDN_MARK(GDN_PHASE_READOUT, (hipStream_t)stream);
   return GDN_OK;
 }
 

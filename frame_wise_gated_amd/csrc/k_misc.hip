@@ -10,6 +10,20 @@ namespace gdn {
 
 namespace {
 
+// x * c for x >= 0, c > 0, rounded to odd in fp32: the product rounded to
+// nearest, then, when it is inexact (the fma residual is nonzero), the
+// truncated value with its last bit set. A later round-to-nearest-even to bf16
+// (8 significant bits, far fewer than 24 - 2) then rounds the exact product
+// once, as if it were converted directly (Boldo and Melquiond, "When double
+// rounding is odd", 2005).
+__device__ __forceinline__ float mul_round_odd(float x, float c) {
+  const float p = x * c;
+  const float e = __builtin_fmaf(x, c, -p);
+  uint32_t b = __float_as_uint(p);
+  if (e != 0.f) b = (e < 0.f ? b - 1u : b) | 1u;
+  return __uint_as_float(b);
+}
+
 __global__ void __launch_bounds__(256) prepare_bf16_kernel(const uint4* __restrict__ k,
                                                            uint4* __restrict__ out, int64_t n8,
                                                            float c) {
@@ -22,7 +36,8 @@ __global__ void __launch_bounds__(256) prepare_bf16_kernel(const uint4* __restri
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       uint32_t z = relu_bf16x2(w[p]);
-      r[p] = pack_bf16x2(bf16_to_f32(z & 0xFFFFu) * c, bf16_to_f32(z >> 16) * c);
+      r[p] = pack_bf16x2(mul_round_odd(bf16_to_f32(z & 0xFFFFu), c),
+                         mul_round_odd(bf16_to_f32(z >> 16), c));
     }
     out[i] = make_uint4(r[0], r[1], r[2], r[3]);
   }

@@ -304,9 +304,11 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
     }
   };
   // Stores of the staged dq tile of stage st by waves 0-3 (two 16-byte row
-  // pieces per thread). Tokens past the end were computed from clamped copies
-  // of row S - 1, so they carry exactly row S - 1's values and are written
-  // there again.
+  // pieces per thread). Rows past the frame's end are not stored: with the
+  // RMSNorm their staged queries are zero (they were silenced for E_t), so
+  // the norm's backward would give them a value that is not row S - 1's.
+  // Waves 0-3 issue no loads in the stage loop, so the exec-masked store
+  // holds back no prefetch.
   uint16_t* dqf = (kDq && dq) ? dq + fh * (int64_t)S * D : nullptr;
   // With the RMSNorm of q the staged tile is the gradient dqh for the
   // normalised query qh = q r, and dq = r (dqh - (qh . dqh) qh / D); the 16
@@ -340,8 +342,8 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
           o[e] = pack_bf16x2(rr * (dv8[2 * e] - dot * qv8[2 * e]), rr * (dv8[2 * e + 1] - dot * qv8[2 * e + 1]));
         x = make_uint4(o[0], o[1], o[2], o[3]);
       }
-      const int sr = min(st * kTsd + row, S - 1);
-      if (dqf) *(uint4*)(dqf + (int64_t)sr * D + 8 * ch) = x;
+      const int sr = st * kTsd + row;
+      if (dqf && sr < S) *(uint4*)(dqf + (int64_t)sr * D + 8 * ch) = x;
     }
   };
 

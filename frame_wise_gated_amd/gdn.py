@@ -44,6 +44,20 @@ class gdn_desc(ctypes.Structure):
     ]
 
 
+class gdn_trace(ctypes.Structure):
+    _fields_ = [
+        ("events", ctypes.POINTER(ctypes.c_void_p)),
+        ("phases", ctypes.POINTER(ctypes.c_int32)),
+        ("capacity", ctypes.c_int32),
+        ("count", ctypes.c_int32),
+    ]
+
+
+# gdn_phase ids (include/gdn.h) -> names
+PHASES = {0: "call_begin", 1: "terms", 2: "terms_reduce", 3: "scan", 4: "combine", 5: "replay",
+          6: "reverse", 7: "readout", 8: "bwd_terms", 9: "bwd_edq", 10: "bwd_init",
+          11: "bwd_adjoint", 12: "bwd_frame", 13: "bwd_token", 14: "other"}
+
 _lib = None
 _vp = ctypes.c_void_p
 _st = ctypes.c_int32
@@ -94,6 +108,8 @@ def lib() -> ctypes.CDLL:
                                              + [_vp, ctypes.c_size_t, _vp])
     L.gdn_readout.restype = _st
     L.gdn_readout.argtypes = [P(gdn_desc), _vp, _vp, _vp, _vp, _vp]
+    L.gdn_trace_set.restype = _st
+    L.gdn_trace_set.argtypes = [P(gdn_trace)]
     _lib = L
     return L
 
@@ -384,3 +400,99 @@ def gdn_readout(q, states, states_add=None, o=None, qk_rmsnorm=False, stream=Non
     _check(lib().gdn_readout(ctypes.byref(d), _ptr(q), _ptr(states), _ptr(states_add), _ptr(o),
                              _stream(stream)), "gdn_readout")
     return o
+
+
+_hip = None
+HIP_EVENT_RELEASE_TO_DEVICE = 0x40000000  # hipEventReleaseToDevice
+
+
+def _hip_runtime() -> ctypes.CDLL:
+    """The HIP runtime already loaded by torch (same soname as libgdn needs),
+    for creating and reading the trace events."""
+    global _hip
+    if _hip is None:
+        torch.cuda.init()
+        h = ctypes.CDLL("libamdhip64.so.7")
+        h.hipEventCreateWithFlags.restype = ctypes.c_int
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        h.hipEventElapsedTime.restype = ctypes.c_int
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        h.hipEventDestroy.restype = ctypes.c_int
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _hip = h
+    return _hip
+
+
+class PhaseTrace:
+    """Per-phase device times of the library calls made on this thread.
+
+    Inside ``with PhaseTrace(capacity) as tr:`` every call records HIP events
+    on its stream at its start and after each launch group (gdn_trace_set).
+    After a synchronisation, ``tr.calls()`` returns one dict per call:
+    ``{"total": ms, <phase name>: ms, ...}``, the device time from the call's
+    first event to its last and of each phase. The events are created here
+    with a device-scope release (hipEventReleaseToDevice): recording them
+    writes nothing back to the host, so they barely disturb the timed work."""
+
+    def __init__(self, capacity: int, flags: int = HIP_EVENT_RELEASE_TO_DEVICE):
+        h = _hip_runtime()
+        self._ev = (ctypes.c_void_p * capacity)()
+        for i in range(capacity):
+            e = ctypes.c_void_p()
+            if h.hipEventCreateWithFlags(ctypes.byref(e), flags) != 0:
+                self.close()
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self._ev[i] = e.value
+        self._ph = (ctypes.c_int32 * capacity)()
+        self._t = gdn_trace(self._ev, self._ph, capacity, 0)
+
+    def close(self) -> None:
+        if _hip is not None and getattr(self, "_ev", None) is not None:
+            for e in self._ev:
+                if e:
+                    _hip.hipEventDestroy(e)
+            self._ev = None
+
+    def __del__(self):
+        self.close()
+
+    def reset(self) -> None:
+        self._t.count = 0
+
+    def __enter__(self):
+        _check(lib().gdn_trace_set(ctypes.byref(self._t)), "gdn_trace_set")
+        return self
+
+    def __exit__(self, *exc):
+        lib().gdn_trace_set(None)
+        return False
+
+    @property
+    def count(self) -> int:
+        return int(self._t.count)
+
+    def full(self) -> bool:
+        return self._t.count >= self._t.capacity
+
+    def _ms(self, i: int, j: int) -> float:
+        out = ctypes.c_float(0.0)
+        if _hip.hipEventElapsedTime(ctypes.byref(out), self._ev[i], self._ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed (events not complete?)")
+        return float(out.value)
+
+    def calls(self) -> list[dict]:
+        out, cur, first = [], None, None
+        for i in range(self._t.count):
+            ph = PHASES.get(int(self._ph[i]), "other")
+            if ph == "call_begin":
+                if cur is not None:
+                    cur["total"] = self._ms(first, i - 1)
+                    out.append(cur)
+                cur, first = {}, i
+            elif cur is not None:
+                cur[ph] = cur.get(ph, 0.0) + self._ms(i - 1, i)
+        if cur is not None:
+            cur["total"] = self._ms(first, self._t.count - 1)
+            out.append(cur)
+        return out

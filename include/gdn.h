@@ -24,8 +24,9 @@
  *
  * Conventions for every entry point:
  *   - Ownership: the caller owns every buffer, the workspace included. The
- *     library allocates and frees no device memory and keeps no global state;
- *     calls are re-entrant.
+ *     library allocates and frees no device memory and keeps no global state
+ *     (apart from the opt-in per-thread phase trace, gdn_trace_set); calls are
+ *     re-entrant.
  *   - Streams: `stream` is a hipStream_t (NULL = the default stream). Work is
  *     only enqueued on it; no call synchronises.
  *   - Errors: arguments are checked on the host before anything is enqueued.
@@ -252,6 +253,50 @@ GDN_API gdn_status gdn_scan_bidir_chunked_bwd(const gdn_desc* desc, int32_t chun
  * states, states_add: [B,H,T,D,D] fp32. */
 GDN_API gdn_status gdn_readout(const gdn_desc* desc, const void* q, const float* states,
                                const float* states_add, void* o, void* stream);
+
+/* Phase timing (tracing). A caller that wants per-phase device times sets a
+ * trace on its host thread; from then on every call made on that thread
+ * records, on the call's own stream, one caller-created hipEvent_t when it
+ * starts enqueueing (phase GDN_PHASE_CALL_BEGIN) and one after each launch
+ * group, tagged with the phase that group ran, so that the elapsed time
+ * between events[i-1] and events[i] is the device time of phases[i]. The
+ * events must have been created with timing enabled; the library only
+ * records them. When `capacity` events have been recorded, further marks are
+ * dropped (the call itself is unaffected). A call that fails its argument
+ * checks records nothing. gdn_trace_set(NULL) stops tracing on the thread.
+ * This per-thread pointer is the only state the library keeps; the trace
+ * struct and its arrays belong to the caller and must outlive the traced
+ * calls. A call inside HIP graph capture records its events into the graph
+ * like any other work (do not trace such calls). */
+typedef enum {
+  GDN_PHASE_CALL_BEGIN = 0,   /* a call started enqueueing */
+  GDN_PHASE_TERMS = 1,        /* phase 1: A_t and U_t of every frame */
+  GDN_PHASE_TERMS_REDUCE = 2, /* sum of phase 1's split partials (calls with few frame-heads) */
+  GDN_PHASE_SCAN = 3,         /* first scan launch: the sequential scan or the composites
+                               * (with the reverse chunk scan when they share the launch) */
+  GDN_PHASE_COMBINE = 4,      /* chunk start states from the composites */
+  GDN_PHASE_REPLAY = 5,       /* every time chunk replayed from its start state */
+  GDN_PHASE_REVERSE = 6,      /* the reverse chunk scan in a launch of its own */
+  GDN_PHASE_READOUT = 7,      /* o = (S_t [+ R_t]) q */
+  GDN_PHASE_BWD_TERMS = 8,    /* backward: A_t recomputed */
+  GDN_PHASE_BWD_EDQ = 9,      /* backward: E_t = d_o^T q (and dq in the same pass) */
+  GDN_PHASE_BWD_INIT = 10,    /* backward: adjoint start values */
+  GDN_PHASE_BWD_ADJOINT = 11, /* backward: adjoint recurrences */
+  GDN_PHASE_BWD_FRAME = 12,   /* backward: per-frame gradients dM_t, dgamma, P_t */
+  GDN_PHASE_BWD_TOKEN = 13,   /* backward: per-token gradients dk, dv, dbeta (dq) */
+  GDN_PHASE_OTHER = 14        /* copies and fills */
+} gdn_phase;
+
+typedef struct {
+  void** events;      /* capacity hipEvent_t handles, created by the caller */
+  int32_t* phases;    /* capacity entries, written: phases[i] = gdn_phase of events[i] */
+  int32_t capacity;
+  int32_t count;      /* events recorded so far (the caller may reset it to 0) */
+} gdn_trace;
+
+/* Sets (or with NULL clears) the trace of the calling host thread. Returns
+ * GDN_EINVAL for a trace with NULL arrays or a negative capacity or count. */
+GDN_API gdn_status gdn_trace_set(gdn_trace* trace);
 
 #ifdef __cplusplus
 }

@@ -59,3 +59,38 @@ def rel_fro(got, ref) -> float:
 
 def host(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
+
+
+def rne_bf16_bits(x) -> np.ndarray:
+    """bf16 bit patterns of float64 values rounded ONCE to nearest even (8
+    significant bits); finite values in the normal range of bf16."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                      # x = m 2^e, 0.5 <= |m| < 1
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)  # np.rint rounds half to even
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def frame_errs(got, ref) -> np.ndarray:
+    """Relative Frobenius error of every frame: arrays [T, ...] (one head)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    T = ref.shape[0]
+    g = got.reshape(T, -1)
+    r = ref.reshape(T, -1)
+    den = np.linalg.norm(r, axis=1)
+    num = np.linalg.norm(g - r, axis=1)
+    return num / np.where(den > 0, den, 1.0)
+
+
+def token_errs(got, ref, floor: float = 1e-3) -> np.ndarray:
+    """Relative error of every token vector (last axis), arrays [T, S, D]:
+    |g_s - r_s| / max(|r_s|, floor * rms_s'|r_s'|) with the rms over the
+    frame's tokens, so that a token whose reference is (near) zero is measured
+    against the frame's typical token norm."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rn = np.linalg.norm(ref, axis=-1)
+    typ = np.sqrt(np.mean(rn * rn, axis=-1, keepdims=True))
+    den = np.maximum(rn, floor * typ)
+    num = np.linalg.norm(got - ref, axis=-1)
+    return num / np.where(den > 0, den, 1.0)

@@ -23,7 +23,8 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"gdn_status_str", "gdn_workspace_bytes", "gdn_prepare", "gdn_frame_terms",
                           "gdn_scan_fwd", "gdn_scan_bidir_chunked", "gdn_compose", "gdn_readout",
                           "gdn_step", "gdn_scan_bwd", "gdn_bwd_workspace_bytes",
-                          "gdn_scan_bidir_chunked_bwd", "gdn_bidir_bwd_workspace_bytes"}
+                          "gdn_scan_bidir_chunked_bwd", "gdn_bidir_bwd_workspace_bytes",
+                          "gdn_trace_set"}
     out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -196,3 +197,26 @@ def test_null_and_chunk_arguments(L):
     d0 = gdn.make_desc(0, 4, 4, 12, 16, gdn.GDN_F32)
     assert L.gdn_scan_fwd(ctypes.byref(d0), None, None, None, None, None, None, None, None, None, 1,
                           None, 0, None) == gdn.GDN_OK
+
+
+def test_trace_set_validates_and_clears(L):
+    """gdn_trace_set refuses a trace with NULL arrays or negative sizes and
+    accepts NULL (tracing off); with a trace set, a call that fails its
+    argument checks records nothing."""
+    ev = (ctypes.c_void_p * 4)()
+    ph = (ctypes.c_int32 * 4)()
+    assert L.gdn_trace_set(ctypes.byref(gdn.gdn_trace(None, ph, 4, 0))) == gdn.GDN_EINVAL
+    assert L.gdn_trace_set(ctypes.byref(gdn.gdn_trace(ev, None, 4, 0))) == gdn.GDN_EINVAL
+    assert L.gdn_trace_set(ctypes.byref(gdn.gdn_trace(ev, ph, -1, 0))) == gdn.GDN_EINVAL
+    t = gdn.gdn_trace(ev, ph, 4, 0)
+    assert L.gdn_trace_set(ctypes.byref(t)) == gdn.GDN_OK
+    try:
+        d = gdn.make_desc(1, 1, 2, 12, 16, gdn.GDN_F32)
+        # NULL k with an output wanted (a host address that is never touched):
+        # refused before anything is enqueued
+        st = L.gdn_scan_fwd(ctypes.byref(d), None, None, None, None, None, None,
+                            ctypes.c_void_p(0x1000), None, None, 1, None, 0, None)
+        assert st == gdn.GDN_EINVAL
+        assert t.count == 0
+    finally:
+        assert L.gdn_trace_set(None) == gdn.GDN_OK

@@ -26,7 +26,9 @@ def test_per_frame_head_bytes_and_flops():
     w = gi.workload(4)
     pf = bench.per_frame_head(w)
     S, D = 3600, 128
-    assert pf["terms_bytes"] == 2 * S * D * 2 + 4 * S + 2 * D * D * 4
+    # phase 1 as the step runs it: bf16 A_t and fp32 U_t in the scan's layout
+    assert pf["terms_bytes"] == 2 * S * D * 2 + 4 * S + D * D * (2 + 4)
+    assert pf["step_bytes"] == 3766340
     assert pf["readout_bytes"] == 2 * S * D * 2 + 4 * D * D
     assert pf["terms_flop"] == 4 * D * D * S
     assert pf["step_flop"] == 4 * D * D * S + 2 * D * D * S + 2 * D ** 3
@@ -61,9 +63,9 @@ def test_kernel_names_match_launched_instances():
     from frame_wise_gated_amd.inputs import workload
     w = workload(4)
     plain, normed = bench.kernel_names(w, False), bench.kernel_names(w, True)
-    assert plain["terms"][:2] == ("terms_dma_bf16_d128", "<false, false, false, false, false>")
+    assert plain["terms"][:2] == ("terms_dma_bf16_d128", "<true, false, false, false, false>")
     assert plain["readout"][:2] == ("readout_mfma_bf16_d128", "<false>")
-    assert normed["terms"][1] == "<false, false, true, false, false>"
+    assert normed["terms"][1] == "<true, false, true, false, false>"
     assert normed["readout"][1] == "<true>"
     assert bench.kernel_names(workload(1), False)["terms"][0] == "terms_generic"
 
@@ -100,3 +102,21 @@ def test_profsum_mfma_utilisation(tmp_path):
     assert not any(l.startswith("grad_init_kernel") for l in lines)
     row = [l for l in lines if l.startswith("readout_mfma_bf16_d128<false>")][0].split()
     assert row[-5:] == ["1", "10.0", "1000", "32.0", "0.800"]
+
+
+def test_summarize_calls_median_min_and_phases():
+    calls = [{"total": 3.0, "terms": 1.0, "readout": 1.5},
+             {"total": 1.0, "terms": 0.4, "readout": 0.5, "scan": 0.1},
+             {"total": 2.0, "terms": 0.7, "readout": 1.0}]
+    s = bench.summarize_calls(calls)
+    assert s["mean"] == pytest.approx(2.0) and s["median"] == 2.0 and s["min"] == 1.0
+    assert s["phase_median"]["terms"] == 0.7 and s["phase_median"]["readout"] == 1.0
+    # a phase missing from a call counts as zero time in that call
+    assert s["phase_median"]["scan"] == 0.0
+    assert s["phase_mean"]["scan"] == pytest.approx(0.1 / 3)
+
+
+def test_pages_context_is_labelled_not_comparable():
+    assert bench.PAGES_CONTEXT["comparable"] is False
+    assert "34 s" in bench.PAGES_CONTEXT["whole_model_60s_720p"]
+    assert "1.5-2x" in bench.PAGES_CONTEXT["fused_kernel_speedup"]
