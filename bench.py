@@ -9,11 +9,15 @@ workload: H = 16 heads, D = 128, S = 3600 tokens (80 x 45 latent grid of a
 720p frame), T = 121 latent frames (a 60 s clip), causal scan split into 8
 time chunks combined by affine composites.
 
-Prints ONE JSON line (rank 0, N = 1). The timed steps run with the library's
-phase trace on (gdn_trace_set): HIP events recorded on the library's stream
-at the start of each call and after each launch group give per-step times
-(mean, median, min) and the device time of every phase of the step itself;
-the dominant kernel's time gives the ``roofline`` object. Sub-objects: the
+Prints ONE JSON line (rank 0, N = 1). ``value`` and ``ms_per_step`` come from
+exactly K steps between two events with nothing else enqueued. The same K
+steps are then run twice more: with an event between consecutive steps (the
+per-step median and min), and with the library's phase trace on
+(gdn_trace_set: HIP events recorded on the library's stream at the start of
+each call and after each launch group), which gives the device time of every
+phase of the step itself; the dominant kernel's time gives the ``roofline``
+object. (The trace's events cost a few microseconds each, which is why the
+headline figure comes from the untraced steps.) Sub-objects: the
 other named workloads (``configs``), a cache-resident phase-1 leg
 (``warm``), the streaming step, the backward, and the float64 oracle timed
 on the host cores on a bounded sample (``cpu_baseline``).
@@ -333,6 +337,20 @@ def main():
         calls = tr.calls()
         return ms, summarize_calls(calls)
 
+    def per_step(fn, reps):
+        """reps calls of fn with one event between consecutive calls (and one
+        before the first, one after the last): the device time of every call,
+        as (median, min) in ms."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(reps):
+            fn()
+            ev[i + 1].record(stream)
+        ev[-1].synchronize()
+        t = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+        return statistics.median(t), min(t)
+
     w = gi.workload(args.workload)
     log("generating", w.name)
     d = load(w)
@@ -342,14 +360,18 @@ def main():
     log("warmup", args.warmup)
     for _ in range(args.warmup):
         step()
+    # the timed region: exactly K steps between two events, nothing else
+    # enqueued in between
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ms, summ = timed(step, args.steps)
+    ms, _ = timed(step, args.steps, traced=False)
     wall = (time.perf_counter() - wall0) / args.steps * 1e3
-    log(f"{args.steps} steps: {ms:.3f} ms/step (events), {wall:.3f} ms/step (wall), "
-        f"median {summ['median']:.3f}, min {summ['min']:.3f}")
-    ms_untraced, _ = timed(step, args.steps, traced=False)
-    log(f"{args.steps} untraced steps: {ms_untraced:.3f} ms/step")
+    log(f"{args.steps} steps: {ms:.3f} ms/step (events), {wall:.3f} ms/step (wall)")
+    # the same K steps with an event between consecutive steps (per-step
+    # median and min), then with the phase trace on (per-phase device times)
+    med, mn = per_step(step, args.steps)
+    ms_traced, summ = timed(step, args.steps)
+    log(f"per step: median {med:.3f}, min {mn:.3f}; phase-traced steps: {ms_traced:.3f} ms/step")
 
     pf = per_frame_head(w)
     fh = B * H * T
@@ -370,9 +392,9 @@ def main():
                    "S": S, "D": D,
                    "scan": w.mode, "time_chunks": w.time_chunks, "chunk_len": w.chunk_len,
                    "parallelism": "single GPU"},
-        "ms_step_median": summ["median"],
-        "ms_step_min": summ["min"],
-        "ms_per_step_untraced": ms_untraced,
+        "ms_step_median": med,
+        "ms_step_min": mn,
+        "ms_per_step_phase_traced": ms_traced,
     }
     eff_tf = pf["step_flop"] * fh / (ms / 1e3) / 1e12
     out["effective_tflops"] = eff_tf
@@ -449,7 +471,8 @@ def main():
 
         stream_pass()
         reps = max(args.steps // 4, 3)
-        t_stream, ss = timed(stream_pass, reps, events_per_call=24 * len(cuts))
+        t_stream, _ = timed(stream_pass, reps, traced=False)
+        _, ss = timed(stream_pass, reps, events_per_call=24 * len(cuts))
         full_blocks = [c for c in range(len(cuts)) if cuts[c][1] - cuts[c][0] == L]
         out["streaming"] = {
             "block_frames": L,
@@ -489,7 +512,8 @@ def main():
         bstep = lambda: bcall(bws, False)
         for _ in range(2):
             bstep()
-        t_bwd, bs = timed(bstep, max(args.steps // 2, 3))
+        t_bwd, _ = timed(bstep, max(args.steps // 2, 3), traced=False)
+        _, bs = timed(bstep, max(args.steps // 2, 3))
         # the same backward reading A_t from the workspace of its forward call
         # (GDN_REUSE_FWD_TERMS): one forward call into a workspace sized for
         # both, then the timed backward calls on it
@@ -498,7 +522,8 @@ def main():
         rstep = lambda: bcall(fws, True)
         for _ in range(2):
             rstep()
-        t_bwd_r, rs = timed(rstep, max(args.steps // 2, 3))
+        t_bwd_r, _ = timed(rstep, max(args.steps // 2, 3), traced=False)
+        _, rs = timed(rstep, max(args.steps // 2, 3))
         del fws
         # algorithmic bytes: q, k, v, d_o, beta, gamma and the forward states
         # (both directions for the bidirectional scan) in; dq, dk, dv, dbeta,
@@ -569,11 +594,13 @@ def main():
             sc = step_fn(wc, dc)
             for _ in range(3):
                 sc()
-            msc, sm = timed(sc, args.steps)
+            msc, _ = timed(sc, args.steps, traced=False)
+            medc, mnc = per_step(sc, args.steps)
+            _, sm = timed(sc, args.steps)
             pc = per_frame_head(wc)
             fhc = wc.B * wc.H * wc.T
             out["configs"][wc.name] = {
-                "ms_per_step": msc, "ms_step_median": sm["median"], "ms_step_min": sm["min"],
+                "ms_per_step": msc, "ms_step_median": medc, "ms_step_min": mnc,
                 "layer_frames_per_s": wc.T / (msc / 1e3),
                 "hbm_frac_step": pc["step_bytes"] * fhc / (msc / 1e3) / 1e9 / HBM_PEAK_GBS,
                 "effective_tflops": pc["step_flop"] * fhc / (msc / 1e3) / 1e12,
