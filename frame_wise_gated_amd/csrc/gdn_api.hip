@@ -4,9 +4,15 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "gdn.h"
 #include "gdn_common.h"
+
+// Device scratch of gdn_step_noalloc (one copy per GPU). Host code never uses
+// this name as an address: it holds a host-side stand-in; the device address
+// comes from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -514,6 +520,55 @@ gdn_status gdn_step(const gdn_desc* desc, const void* q, const void* k, const vo
   const int32_t chunk_len = desc->T > 0 ? desc->T : 1;
   return gdn_scan_bidir_chunked(desc, q, k, v, beta, gamma, carry_in, chunk_len, states_fwd,
                                 states_rev, carry_out, o, 1, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device of `st`, which must be the
+// current device; looked up on the device's first call and kept.
+gdn_status scratch_address(hipStream_t st, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return GDN_EHIP;
+  int dev = cur;
+  if (st != nullptr) {
+    hipDevice_t d = -1;
+    if (hipStreamGetDevice(st, &d) != hipSuccess) return GDN_EINVAL;
+    dev = d;
+  }
+  if (dev != cur) return GDN_EINVAL;
+  if (dev < 0 || dev >= kMaxDevices) return GDN_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return GDN_EHIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_step_noalloc(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                            const float* beta, const float* gamma, const float* carry_in,
+                            float* carry_out, void* o, float* states_fwd, float* states_rev,
+                            void* stream) {
+  Shape sh;
+  gdn_status s = check_desc(desc, &sh);
+  if (s != GDN_OK) return s;
+  if (layout(sh, 1).total > GDN_NOALLOC_SCRATCH_BYTES) return GDN_EWORKSPACE;
+  void* ws = nullptr;
+  if ((s = scratch_address((hipStream_t)stream, &ws)) != GDN_OK) return s;
+  return gdn_step(desc, q, k, v, beta, gamma, carry_in, carry_out, o, states_fwd, states_rev, ws,
+                  GDN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 gdn_status gdn_compose(const gdn_desc* desc, const void* k, const void* v, const float* beta,

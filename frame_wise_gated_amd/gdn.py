@@ -23,6 +23,7 @@ GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = range(5)
 GDN_F32, GDN_BF16 = 0, 1
 GDN_KEYS_RAW, GDN_KEYS_PREPARED, GDN_QK_RMSNORM, GDN_REUSE_FWD_TERMS = 0, 1, 2, 4
 GDN_MAX_TIME_CHUNKS = 256
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class GdnError(RuntimeError):
@@ -94,6 +95,8 @@ def lib() -> ctypes.CDLL:
     L.gdn_step.restype = _st
     L.gdn_step.argtypes = [P(gdn_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            ctypes.c_size_t, _vp]
+    L.gdn_step_noalloc.restype = _st
+    L.gdn_step_noalloc.argtypes = [P(gdn_desc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.gdn_compose.restype = _st
     L.gdn_compose.argtypes = [P(gdn_desc), _vp, _vp, _vp, _vp, P(ctypes.c_int32), ctypes.c_int32,
                               _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -278,6 +281,32 @@ def gdn_step(q, k, v, beta, gamma, carry_in=None, carry_out=None, key_scale=0.0,
     _check(lib().gdn_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gamma),
                           _ptr(carry_in), _ptr(carry_out), _ptr(o), _ptr(states_fwd),
                           _ptr(states_rev), _ptr(ws), nb, _stream(stream)), "gdn_step")
+    return {"carry_out": carry_out, "o": o, "states_fwd": states_fwd, "states_rev": states_rev}
+
+
+def gdn_step_noalloc(q, k, v, beta, gamma, carry_in=None, carry_out=None, key_scale=0.0,
+                     keys_prepared=False, want_o=True, want_states=False, o=None, states_fwd=None,
+                     states_rev=None, stream=None, qk_rmsnorm=False):
+    """gdn_step on the library's static device scratch instead of a workspace
+    (gdn_step_noalloc): the library allocates nothing. Outputs that are not
+    given are allocated here by torch, so a caller that must not allocate
+    passes every wanted output."""
+    d = _desc_from(k, key_scale, keys_prepared, qk_rmsnorm)
+    B, H, T, S, D = k.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _need(t, n, k.shape, k.dtype)
+    _need(beta, "beta", (B, H, T, S), torch.float32)
+    _need(gamma, "gamma", (B, H, T), torch.float32)
+    _need(carry_in, "carry_in", (B, H, D, D), torch.float32)
+    _need(carry_out, "carry_out", (B, H, D, D), torch.float32)
+    carry_out = _out(carry_out, True, (B, H, D, D), torch.float32, k.device)
+    o = _out(o, want_o, k.shape, k.dtype, k.device)
+    states_fwd = _out(states_fwd, want_states, (B, H, T, D, D), torch.float32, k.device)
+    states_rev = _out(states_rev, want_states, (B, H, T, D, D), torch.float32, k.device)
+    _check(lib().gdn_step_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                  _ptr(gamma), _ptr(carry_in), _ptr(carry_out), _ptr(o),
+                                  _ptr(states_fwd), _ptr(states_rev), _stream(stream)),
+           "gdn_step_noalloc")
     return {"carry_out": carry_out, "o": o, "states_fwd": states_fwd, "states_rev": states_rev}
 
 

@@ -172,6 +172,29 @@ GDN_API gdn_status gdn_step(const gdn_desc* desc, const void* q, const void* k, 
                             float* carry_out, void* o, float* states_fwd, float* states_rev,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* Size of the device scratch array that gdn_step_noalloc uses in place of a
+ * workspace: one copy per GPU the library runs on, held until the process
+ * ends. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* gdn_step without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, results and errors as gdn_step
+ * (bitwise the same outputs), but the workspace is the library's own static
+ * device array of GDN_NOALLOC_SCRATCH_BYTES: shapes whose
+ * gdn_workspace_bytes(desc, 1) exceeds it give GDN_EWORKSPACE before anything
+ * is enqueued (a 720p block of 16 heads, S = 3600, fits up to 4 frames).
+ * The call allocates nothing; the array's device address is looked up once
+ * per device, on that device's first call. `stream` must belong to the
+ * current device (else GDN_EINVAL). Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (other host threads, or streams that
+ * are not ordered with each other) race and give wrong results; calls
+ * ordered on one stream are safe. */
+GDN_API gdn_status gdn_step_noalloc(const gdn_desc* desc, const void* q, const void* k,
+                                    const void* v, const float* beta, const float* gamma,
+                                    const float* carry_in, float* carry_out, void* o,
+                                    float* states_fwd, float* states_rev, void* stream);
+
 /* Affine composites of explicit time chunks (blog.hotdry.top SANA-WM post,
  * section "显存分片: Context-Parallel 的工程实现"): for chunk p = [a_p, a_{p+1}),
  * C_p = M_{a_p} ... M_{a_{p+1}-1} (ordered product) and H_p = the chunk scanned

@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol(L):
                           "gdn_scan_fwd", "gdn_scan_bidir_chunked", "gdn_compose", "gdn_readout",
                           "gdn_step", "gdn_scan_bwd", "gdn_bwd_workspace_bytes",
                           "gdn_scan_bidir_chunked_bwd", "gdn_bidir_bwd_workspace_bytes",
-                          "gdn_trace_set"}
+                          "gdn_trace_set", "gdn_step_noalloc"}
     out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -220,3 +220,23 @@ def test_trace_set_validates_and_clears(L):
         assert t.count == 0
     finally:
         assert L.gdn_trace_set(None) == gdn.GDN_OK
+
+
+def test_step_noalloc_refuses_shapes_beyond_its_scratch(L):
+    """gdn_step_noalloc works in a fixed device array; a block whose workspace
+    would not fit is refused with GDN_EWORKSPACE on the host, before any HIP
+    call (the pointers below are never touched)."""
+    big = gdn.make_desc(1, 16, 8, 3600, 128, gdn.GDN_BF16)
+    assert gdn.gdn_workspace_bytes(big, 1) > gdn.GDN_NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(0x1000)
+    st = L.gdn_step_noalloc(ctypes.byref(big), fake, fake, fake, fake, fake, None, fake, fake,
+                            None, None, None)
+    assert st == gdn.GDN_EWORKSPACE
+    # the 720p streaming block (16 heads, 3 and 4 frames) fits
+    for T in (3, 4):
+        d = gdn.make_desc(1, 16, T, 3600, 128, gdn.GDN_BF16)
+        assert gdn.gdn_workspace_bytes(d, 1) <= gdn.GDN_NOALLOC_SCRATCH_BYTES
+    # a bad descriptor is still EINVAL
+    bad = gdn.make_desc(1, 1, 1, 0, 128, gdn.GDN_BF16)
+    assert L.gdn_step_noalloc(ctypes.byref(bad), fake, fake, fake, fake, fake, None, fake, fake,
+                              None, None, None) == gdn.GDN_EINVAL
