@@ -38,9 +38,16 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, obj_dir: str) -> str:
+# Host-only sanitizers for the C-ABI layer (argument checks, workspace layout,
+# launch sequencing): each -fsanitize applies to the host pass alone, the
+# device code is built as usual.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, obj_dir: str, extra=()) -> str:
     obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -51,9 +58,9 @@ def _compile(src: str, obj_dir: str) -> str:
     return obj
 
 
-def _link(objs: list[str], out: str) -> None:
+def _link(objs: list[str], out: str, extra=()) -> None:
     tmp = out + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
@@ -72,6 +79,32 @@ def build(verbose: bool = True) -> str:
     if verbose:
         print(f"built {OUT} and {PROBE_OUT}")
     return OUT
+
+
+def build_sanitized(out_dir: str) -> str:
+    """libgdn.so with its C-ABI layer (gdn_api.hip) built under host-only
+    AddressSanitizer and UndefinedBehaviorSanitizer, into out_dir. Load it
+    into a process that preloads the ASan runtime (sanitizer_runtime())."""
+    obj_dir = os.path.join(out_dir, "obj")
+    os.makedirs(obj_dir, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, obj_dir, SANITIZE_HOST if s == "gdn_api.hip" else ()),
+                           SOURCES))
+    out = os.path.join(out_dir, "libgdn.so")
+    # the sanitizer entry points stay undefined in the library and resolve
+    # against the preloaded runtime
+    _link(objs, out)
+    return out
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang ASan runtime that a sanitized libgdn.so needs preloaded."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                       text=True, check=True)
+    return r.stdout.strip()
 
 
 if __name__ == "__main__":

@@ -710,8 +710,14 @@ bool terms_use_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
 
 int terms_split(const Shape& sh) {
   const int64_t fh = sh.FH();
-  if (fh <= 0) return 1;
-  const int64_t want = (512 + fh - 1) / fh;  // about two workgroups per CU on 256 CUs
+  // A workgroup streams a frame-head at the rate of its CU's pipeline, so a
+  // call with at least half as many frame-heads as CUs runs them whole: on
+  // MI355X the 16-head 5 s layer (176 frame-heads) took 94 us unsplit against
+  // 98 and 115 us (reduction included) with 2 and 3 splits. Fewer frame-heads
+  // are split to about one workgroup per CU (the split partials cost a
+  // reduction launch and their traffic).
+  if (fh <= 0 || fh >= 128) return 1;
+  const int64_t want = (256 + fh - 1) / fh;
   int64_t cap = sh.S / 512;                   // keep at least 512 tokens per split
   // at most 4 splits: with 7 (48 frame-heads of 3600 tokens, a 3-frame
   // streaming block of the 16-head layer) the block took 74.7 us against 71

@@ -183,7 +183,7 @@ GDN_API gdn_status gdn_step(const gdn_desc* desc, const void* q, const void* k, 
  * (bitwise the same outputs), but the workspace is the library's own static
  * device array of GDN_NOALLOC_SCRATCH_BYTES: shapes whose
  * gdn_workspace_bytes(desc, 1) exceeds it give GDN_EWORKSPACE before anything
- * is enqueued (a 720p block of 16 heads, S = 3600, fits up to 4 frames).
+ * is enqueued (16 heads at S = 3600, D = 128, bf16: blocks of up to 6 frames fit).
  * The call allocates nothing; the array's device address is looked up once
  * per device, on that device's first call. `stream` must belong to the
  * current device (else GDN_EINVAL). Every call on one GPU shares that GPU's

@@ -89,7 +89,7 @@ def test_step_noalloc_in_place_carry_chain():
 
 
 def test_step_noalloc_refuses_oversized_block():
-    w = gi.workload(5).with_shape(H=16, T=8, S=3600)
+    w = gi.workload(5).with_shape(H=16, T=32, S=3600)
     z = torch.zeros((1, 1, 1, 1, 1), device=DEV)
     desc = gdn.make_desc(w.B, w.H, w.T, w.S, w.D, gdn.GDN_BF16)
     import ctypes
