@@ -341,8 +341,13 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_d128(CombineParams p) {
 // four consecutive columns n of one state row m, so its U_t entries, its
 // per-frame state store and its share of the split bf16 copy in LDS are
 // single 16- or 8-byte accesses. Each lane keeps its fp32 state entries in
-// registers for the whole scan; LDS holds only the split copy that the MFMA
-// reads (double-buffered, one barrier per frame).
+// registers for the whole scan; LDS holds the split copy that the MFMA reads
+// (double-buffered, one barrier per frame) and, for row blocks of up to 32
+// rows, a copy of the new fp32 rows that the per-frame state store reads back
+// after the barrier: a lane's own entries cover only 64 bytes of each
+// 128-byte line, and stores of whole 512-byte rows (two per wave
+// instruction) took the sequential 121-frame scan of 16 heads from 152 to
+// 132 us and the replay of 8 chunks from 66 to 61 us.
 //
 // The per-frame step is short (64 MFMAs per wave for MT = 4) next to the
 // latency of a global load, so the A_t fragments and U_t entries of the next
@@ -354,10 +359,12 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_d128(CombineParams p) {
 // Rows of one workgroup's job: row block rb of job `job`. kC: the composite C
 // rows of a COMPOSE job (start I, no U term), which load no U entries.
 constexpr int kScanLdb = 128 + 8;  // bf16 row stride 272 B: 8 lanes reading 16 B at one column are conflict-free
+constexpr int kSstLd = 128 + 4;   // fp32 row stride 528 B: the 16 rows of a lane group start 4 banks apart
 template <int MT, int kF, bool kC>
 __device__ __forceinline__ void scan_rows(const ScanParams& p, int64_t job, int rb,
                                           uint16_t (*Xh)[16 * MT][kScanLdb],
-                                          uint16_t (*Xl)[16 * MT][kScanLdb]) {
+                                          uint16_t (*Xl)[16 * MT][kScanLdb],
+                                          float (*Sst)[MT <= 2 ? 16 * MT : 1][kSstLd]) {
   constexpr int D = 128;
   constexpr int R = 16 * MT;
   constexpr int64_t DD = (int64_t)D * D;
@@ -516,7 +523,19 @@ __device__ __forceinline__ void scan_rows(const ScanParams& p, int64_t job, int 
           if (active) xr[mt][nt] = xn;
           put_split(cur ^ 1, m, ncol(nt), xr[mt][nt]);
         }
-      if (active && p.states != nullptr) {
+      // per-frame state: staged rows (stored whole after the barrier), or
+      // each lane's own entries for the 64-row blocks
+      constexpr bool kStage = MT <= 2;
+      const int sb = step & 1;
+      if (kStage) {
+        if (p.states != nullptr) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+              *(f32x4_t*)&Sst[sb][16 * mt + l16][ncol(nt)] = xr[mt][nt];
+        }
+      } else if (active && p.states != nullptr) {
         float* st = p.states + f * DD + (int64_t)srow0 * D;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -527,6 +546,18 @@ __device__ __forceinline__ void scan_rows(const ScanParams& p, int64_t job, int 
       load_u(j, step + kF);
       cur ^= 1;
       lds_barrier();  // a plain __syncthreads() would also wait for the prefetched frames
+      // wave w stores rows 4 MT w .. 4 MT w + 4 MT - 1, two whole rows per
+      // instruction. Sst[sb] is written again two frames later, after the
+      // next barrier, which this wave reaches only once these reads are done.
+      if (kStage && active && p.states != nullptr) {
+        float* st = p.states + f * DD + (int64_t)srow0 * D;
+#pragma unroll
+        for (int i = 0; i < 2 * MT; ++i) {
+          const int row = wave * (4 * MT) + 2 * i + (lane >> 5);
+          const f32x4_t x = *(const f32x4_t*)&Sst[sb][row][4 * (lane & 31)];
+          *(f32x4_t*)(st + row * D + 4 * (lane & 31)) = x;
+        }
+      }
     }
   }
 
@@ -549,15 +580,16 @@ __device__ __forceinline__ void scan_block(const ScanParams& p, int64_t blk) {
   constexpr int R = 16 * MT;
   __shared__ __attribute__((aligned(16))) uint16_t Xh[2][R][kScanLdb];
   __shared__ __attribute__((aligned(16))) uint16_t Xl[2][R][kScanLdb];
+  __shared__ __attribute__((aligned(16))) float Sst[MT <= 2 ? 2 : 1][MT <= 2 ? R : 1][kSstLd];
   const int rows_total = (p.mode == SCAN_COMPOSE) ? 2 * D : D;
   int64_t job;
   int rb;
   xcd_job(blk, rows_total / R, &job, &rb);
   if (job >= p.njobs) return;
   if (p.mode == SCAN_COMPOSE && rb * R < D)
-    scan_rows<MT, kF, true>(p, job, rb, Xh, Xl);
+    scan_rows<MT, kF, true>(p, job, rb, Xh, Xl, Sst);
   else
-    scan_rows<MT, kF, false>(p, job, rb, Xh, Xl);
+    scan_rows<MT, kF, false>(p, job, rb, Xh, Xl, Sst);
 }
 
 // Blocks [0, split) run the jobs of p0 and blocks [split, grid) those of p1:
