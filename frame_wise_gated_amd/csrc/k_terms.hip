@@ -617,10 +617,43 @@ terms_generic(const TIn* __restrict__ k, const TIn* __restrict__ v, const float*
   }
 }
 
+// p[0] + p[stride] + ... + p[(n - 1) stride] as four-float groups, added in
+// index order. With the split count known at compile time (kN > 0) every
+// load is issued before the first addition, so a thread waits for one round
+// trip rather than one per split.
+template <int kN>
+__device__ __forceinline__ float4 sum_splits(const float* p, int n, int64_t stride) {
+  if (kN > 0) {
+    float4 t[kN > 0 ? kN : 1];
+#pragma unroll
+    for (int b = 0; b < kN; ++b) t[b] = *(const float4*)(p + (int64_t)b * stride);
+    float4 acc = t[0];
+#pragma unroll
+    for (int b = 1; b < kN; ++b) {
+      acc.x += t[b].x;
+      acc.y += t[b].y;
+      acc.z += t[b].z;
+      acc.w += t[b].w;
+    }
+    return acc;
+  }
+  float4 acc = *(const float4*)p;
+  for (int b = 1; b < n; ++b) {
+    const float4 t = *(const float4*)(p + (int64_t)b * stride);
+    acc.x += t.x;
+    acc.y += t.y;
+    acc.z += t.z;
+    acc.w += t.w;
+  }
+  return acc;
+}
+
 // Sum of the token-range partials in a fixed order (deterministic). With
 // scan_layout, the A half is written as bf16 in the scan's granule layout (as
 // the MFMA epilogue does): each thread then sums four consecutive m of one
 // column.
+// kN: the split count when it is a compile-time constant (0: n_split).
+template <int kN>
 __global__ void __launch_bounds__(256)
 reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, int64_t FH,
                        TermsOut out, int scan_layout) {
@@ -639,14 +672,7 @@ reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, in
       // coalesced 16-byte load per split
       const int64_t nn = e / D;
       const int64_t mm = e % D;
-      float4 v = *(const float4*)(base + nn * D + mm);
-      for (int p = 1; p < n_split; ++p) {
-        const float4 t = *(const float4*)(base + (int64_t)p * 2 * D * D + nn * D + mm);
-        v.x += t.x;
-        v.y += t.y;
-        v.z += t.z;
-        v.w += t.w;
-      }
+      const float4 v = sum_splits<kN>(base + nn * D + mm, n_split, (int64_t)2 * D * D);
       if (out.outA == nullptr) continue;
       uint16_t* At = (uint16_t*)(out.outA + f * out.fstride);
       // scan_layout is only requested for D = 128 (granule layout)
@@ -654,15 +680,7 @@ reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, in
       *(uint2*)(At + at) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
       continue;
     }
-    const float4* src = (const float4*)(base + e);
-    float4 s = src[0];
-    for (int p = 1; p < n_split; ++p) {
-      float4 t = src[(int64_t)p * 2 * D * D / 4];
-      s.x += t.x;
-      s.y += t.y;
-      s.z += t.z;
-      s.w += t.w;
-    }
+    const float4 s = sum_splits<kN>(base + e, n_split, (int64_t)2 * D * D);
     const int64_t row = e / D;
     const int64_t col = e % D;
     float* dst = row < D ? out.outA : out.outU;
@@ -708,6 +726,9 @@ hipError_t launch_generic(const Shape& sh, const void* k, const void* v, const f
 
 bool terms_use_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
 
+#ifndef GDN_TERMS_SPLIT_MAX
+#define GDN_TERMS_SPLIT_MAX 5
+#endif
 int terms_split(const Shape& sh) {
   const int64_t fh = sh.FH();
   // A workgroup streams a frame-head at the rate of its CU's pipeline, so a
@@ -719,9 +740,12 @@ int terms_split(const Shape& sh) {
   if (fh <= 0 || fh >= 128) return 1;
   const int64_t want = (256 + fh - 1) / fh;
   int64_t cap = sh.S / 512;                   // keep at least 512 tokens per split
-  // at most 4 splits: with 7 (48 frame-heads of 3600 tokens, a 3-frame
-  // streaming block of the 16-head layer) the block took 74.7 us against 71
-  cap = std::min<int64_t>(std::max<int64_t>(cap, 1), 4);
+  // at most GDN_TERMS_SPLIT_MAX splits: a 3-frame streaming block of the
+  // 16-head layer (48 frame-heads of 3600 tokens) took 74.7 us with 7 splits
+  // against 71 us with 4; 5 splits (240 workgroups, one round) cut its
+  // phase 1 and reduction from 38.7 to 37.4 us, while 6 (288 workgroups)
+  // took 45.6 us
+  cap = std::min<int64_t>(std::max<int64_t>(cap, 1), GDN_TERMS_SPLIT_MAX);
   return (int)std::max<int64_t>(1, std::min(want, cap));
 }
 
@@ -781,8 +805,13 @@ hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_s
   const int64_t n = sh.FH() * 2 * sh.D * sh.D / 4;
   if (n == 0) return hipSuccess;
   int64_t g = std::min<int64_t>((n + 255) / 256, 8192);
-  reduce_partials_kernel<<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out,
-                                                      scan_layout ? 1 : 0);
+  const int sl = scan_layout ? 1 : 0;
+  switch (n_split) {
+    case 2: reduce_partials_kernel<2><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out, sl); break;
+    case 3: reduce_partials_kernel<3><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out, sl); break;
+    case 4: reduce_partials_kernel<4><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out, sl); break;
+    default: reduce_partials_kernel<0><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out, sl); break;
+  }
   return hipGetLastError();
 }
 
