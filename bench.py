@@ -188,14 +188,18 @@ def calibrate_hbm(dev, reps=10):
 
     out = {"bytes": nbytes, "reps": reps,
            "kernels": "libhbm_probe.so (16-byte accesses, grid-stride, 8 loads in flight per "
-                      "thread; plain or non-temporal)", "GBps": {}, "best_config": {}, "sweep": {}}
+                      "thread, plain or non-temporal; read_span: one contiguous span per "
+                      "workgroup, 32 KB steps, non-temporal register loads; read_span_lds: the "
+                      "same spans as global -> LDS copies into a two-step ring)",
+           "GBps": {}, "best_config": {}, "sweep": {}}
     for kind, name, moved in ((0, "read_only", nbytes), (1, "write_only", nbytes),
-                              (2, "copy", 2 * nbytes)):
+                              (2, "copy", 2 * nbytes), (3, "read_span", nbytes),
+                              (4, "read_span_lds", nbytes)):
         best, cfg = 0.0, None
-        for nt in (0, 1):
+        for nt in ((0, 1) if kind <= 2 else (1,)):
             for blocks in (1024, 2048, 4096, 8192, 16384, 32768):
                 s_ = src.data_ptr() if kind != 1 else None
-                d_ = sink.data_ptr() if kind == 0 else dst.data_ptr()
+                d_ = sink.data_ptr() if kind in (0, 3, 4) else dst.data_ptr()
 
                 def fn(kind=kind, s_=s_, d_=d_, blocks=blocks, nt=nt):
                     rc = probe.hbm_probe(kind, s_, d_, nbytes, blocks, nt, sp)

@@ -8,9 +8,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdn_dma.h"
+
 namespace {
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+using gdn::dma16;
+using gdn::u32x4_t;
+using gdn::wait_vmcnt_lgkm0;
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
@@ -70,21 +74,63 @@ __global__ void __launch_bounds__(kThreads) probe_copy(const u32x4_t* __restrict
   for (; i < n; i += stride) st<kNt>(ld<kNt>(src + i), dst + i);
 }
 
+// Read-only over contiguous spans: block b reads bytes [b span, (b + 1) span)
+// in 32 KB steps (each wave 8 KB of consecutive 1 KB pieces per step), the
+// way a phase kernel streams one frame-head's tokens. kLds: the loads are
+// global -> LDS copies (global_load_lds_dwordx4, non-temporal, into a
+// two-step LDS ring, one step in flight while the next is issued), as in the
+// phase-1 ring; otherwise 16-byte register loads folded into an XOR.
+template <bool kLds>
+__global__ void __launch_bounds__(kThreads) probe_read_span(const u32x4_t* __restrict__ src,
+                                                             int64_t span16,
+                                                             uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kLds ? 2 : 1][kLds ? 32768 : 16];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const u32x4_t* base = src + (int64_t)blockIdx.x * span16;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  int step = 0;
+  for (int64_t i0 = 0; i0 < span16; i0 += 2048, ++step) {  // 2048 x 16 B = 32 KB per step
+    const u32x4_t* w = base + i0 + 512 * wave + lane;      // this wave's 8 KB
+    if (kLds) {
+      uint8_t* slot = &ring[kLds ? (step & 1) : 0][8192 * wave];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dma16(w + 64 * u, slot + 1024 * u);
+      wait_vmcnt_lgkm0<8>();  // the previous step's copies have landed
+    } else {
+      u32x4_t x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = __builtin_nontemporal_load(w + 64 * u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc ^= x[u];
+    }
+  }
+  wait_vmcnt_lgkm0<0>();
+  const uint32_t r = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (r == 0x9E3779B9u) sink[0] = r;
+}
+
 template <bool kNt>
 void launch(int kind, const void* src, void* dst, int64_t n, int blocks, hipStream_t s) {
   if (kind == 0)
     probe_read<kNt><<<blocks, kThreads, 0, s>>>((const u32x4_t*)src, n, (uint32_t*)dst);
   else if (kind == 1)
     probe_write<kNt><<<blocks, kThreads, 0, s>>>((u32x4_t*)dst, n, 0x01234567u);
-  else
+  else if (kind == 2)
     probe_copy<kNt><<<blocks, kThreads, 0, s>>>((const u32x4_t*)src, (u32x4_t*)dst, n);
+  else if (kind == 3)
+    probe_read_span<false><<<blocks, kThreads, 0, s>>>((const u32x4_t*)src, n / blocks, (uint32_t*)dst);
+  else
+    probe_read_span<true><<<blocks, kThreads, 0, s>>>((const u32x4_t*)src, n / blocks, (uint32_t*)dst);
 }
 
 }  // namespace
 
 // kind 0: read `bytes` of src (dst: one writable uint32, the sink); 1: write
-// `bytes` of dst; 2: copy `bytes` from src to dst. nontemporal != 0 selects
-// non-temporal loads and stores. bytes must be a multiple of 16 and the
+// `bytes` of dst; 2: copy `bytes` from src to dst; 3: read `bytes` of src as
+// one contiguous span per workgroup (dst: the sink); 4: the same spans
+// through global -> LDS copies. nontemporal != 0 selects non-temporal loads
+// and stores (kinds 0-2; kinds 3 and 4 always load non-temporally). bytes
+// must be a multiple of 16 (of 32 KB x blocks for kinds 3 and 4) and the
 // pointers 16-byte aligned; blocks = workgroups of 256 threads (<= 0: 2048).
 // Returns 0 on success, 1 for bad arguments, 2 when the launch failed.
 extern "C" __attribute__((visibility("default"))) int hbm_probe(int kind, const void* src,
@@ -92,8 +138,9 @@ extern "C" __attribute__((visibility("default"))) int hbm_probe(int kind, const 
                                                                  int blocks, int nontemporal,
                                                                  void* stream) {
   if (bytes % 16 != 0 || ((uintptr_t)src % 16) != 0 || ((uintptr_t)dst % 16) != 0) return 1;
-  if (kind < 0 || kind > 2 || dst == nullptr || (kind != 1 && src == nullptr)) return 1;
+  if (kind < 0 || kind > 4 || dst == nullptr || (kind != 1 && src == nullptr)) return 1;
   if (blocks <= 0) blocks = 2048;
+  if (kind >= 3 && bytes % ((size_t)blocks * 32768) != 0) return 1;
   const int64_t n = (int64_t)(bytes / 16);
   if (nontemporal)
     launch<true>(kind, src, dst, n, blocks, (hipStream_t)stream);
