@@ -190,13 +190,14 @@ def calibrate_hbm(dev, reps=10):
            "kernels": "libhbm_probe.so (16-byte accesses, grid-stride, 8 loads in flight per "
                       "thread, plain or non-temporal; read_span: one contiguous span per "
                       "workgroup, 32 KB steps, non-temporal register loads; read_span_lds: the "
-                      "same spans as global -> LDS copies into a two-step ring)",
+                      "same spans as global -> LDS copies into a two-step ring; copy_span: "
+                      "one contiguous span copied per workgroup, plain or non-temporal stores)",
            "GBps": {}, "best_config": {}, "sweep": {}}
     for kind, name, moved in ((0, "read_only", nbytes), (1, "write_only", nbytes),
                               (2, "copy", 2 * nbytes), (3, "read_span", nbytes),
-                              (4, "read_span_lds", nbytes)):
+                              (4, "read_span_lds", nbytes), (5, "copy_span", 2 * nbytes)):
         best, cfg = 0.0, None
-        for nt in ((0, 1) if kind <= 2 else (1,)):
+        for nt in ((0, 1) if kind in (0, 1, 2, 5) else (1,)):
             for blocks in (1024, 2048, 4096, 8192, 16384, 32768):
                 s_ = src.data_ptr() if kind != 1 else None
                 d_ = sink.data_ptr() if kind in (0, 3, 4) else dst.data_ptr()

@@ -109,6 +109,26 @@ __global__ void __launch_bounds__(kThreads) probe_read_span(const u32x4_t* __res
   if (r == 0x9E3779B9u) sink[0] = r;
 }
 
+// Copy over contiguous spans: block b copies bytes [b span, (b + 1) span) of
+// src to the same place in dst in 32 KB steps, eight 16-byte loads in flight
+// per thread (the readout's pattern: one frame-head's q tiles in, o tiles
+// out); non-temporal loads, stores plain or non-temporal.
+template <bool kNt>
+__global__ void __launch_bounds__(kThreads) probe_copy_span(const u32x4_t* __restrict__ src,
+                                                             u32x4_t* __restrict__ dst,
+                                                             int64_t span16) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t b0 = (int64_t)blockIdx.x * span16;
+  for (int64_t i0 = 0; i0 < span16; i0 += 2048) {
+    const int64_t w = b0 + i0 + 512 * wave + lane;
+    u32x4_t x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = __builtin_nontemporal_load(src + w + 64 * u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) st<kNt>(x[u], dst + w + 64 * u);
+  }
+}
+
 template <bool kNt>
 void launch(int kind, const void* src, void* dst, int64_t n, int blocks, hipStream_t s) {
   if (kind == 0)
@@ -119,8 +139,10 @@ void launch(int kind, const void* src, void* dst, int64_t n, int blocks, hipStre
     probe_copy<kNt><<<blocks, kThreads, 0, s>>>((const u32x4_t*)src, (u32x4_t*)dst, n);
   else if (kind == 3)
     probe_read_span<false><<<blocks, kThreads, 0, s>>>((const u32x4_t*)src, n / blocks, (uint32_t*)dst);
-  else
+  else if (kind == 4)
     probe_read_span<true><<<blocks, kThreads, 0, s>>>((const u32x4_t*)src, n / blocks, (uint32_t*)dst);
+  else
+    probe_copy_span<kNt><<<blocks, kThreads, 0, s>>>((const u32x4_t*)src, (u32x4_t*)dst, n / blocks);
 }
 
 }  // namespace
@@ -128,9 +150,10 @@ void launch(int kind, const void* src, void* dst, int64_t n, int blocks, hipStre
 // kind 0: read `bytes` of src (dst: one writable uint32, the sink); 1: write
 // `bytes` of dst; 2: copy `bytes` from src to dst; 3: read `bytes` of src as
 // one contiguous span per workgroup (dst: the sink); 4: the same spans
-// through global -> LDS copies. nontemporal != 0 selects non-temporal loads
-// and stores (kinds 0-2; kinds 3 and 4 always load non-temporally). bytes
-// must be a multiple of 16 (of 32 KB x blocks for kinds 3 and 4) and the
+// through global -> LDS copies; 5: copy `bytes` as one contiguous span per
+// workgroup. nontemporal != 0 selects non-temporal loads and stores (kinds
+// 0-2; kinds 3-5 always load non-temporally, kind 5 stores as selected).
+// bytes must be a multiple of 16 (of 32 KB x blocks for kinds 3-5) and the
 // pointers 16-byte aligned; blocks = workgroups of 256 threads (<= 0: 2048).
 // Returns 0 on success, 1 for bad arguments, 2 when the launch failed.
 extern "C" __attribute__((visibility("default"))) int hbm_probe(int kind, const void* src,
@@ -138,7 +161,7 @@ extern "C" __attribute__((visibility("default"))) int hbm_probe(int kind, const 
                                                                  int blocks, int nontemporal,
                                                                  void* stream) {
   if (bytes % 16 != 0 || ((uintptr_t)src % 16) != 0 || ((uintptr_t)dst % 16) != 0) return 1;
-  if (kind < 0 || kind > 4 || dst == nullptr || (kind != 1 && src == nullptr)) return 1;
+  if (kind < 0 || kind > 5 || dst == nullptr || (kind != 1 && src == nullptr)) return 1;
   if (blocks <= 0) blocks = 2048;
   if (kind >= 3 && bytes % ((size_t)blocks * 32768) != 0) return 1;
   const int64_t n = (int64_t)(bytes / 16);

@@ -692,6 +692,47 @@ reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, in
   }
 }
 
+// The same sum written in the scan's granule layout (D = 128), one 16-byte
+// granule per thread in granule order, so that every wave's stores are 1 KB
+// of consecutive bytes: per frame-head the 2048 granules of bf16(A) (8 rows m
+// of column n, read as row n, columns m.. by the symmetry of A_t, two 16-byte
+// loads per split), then the 4096 granules of U (4 columns of row m). The
+// additions run in split order, as in reduce_partials_kernel.
+template <int kN>
+__global__ void __launch_bounds__(256)
+reduce_partials_granules(const float* __restrict__ partial, int n_split, int64_t FH, TermsOut out) {
+  constexpr int D = 128;
+  constexpr int64_t DD = (int64_t)D * D;
+  constexpr int kAG = D * D / 8, kUG = D * D / 4;  // granules of A (bf16) and of U (fp32)
+  const int64_t n = FH * (kAG + kUG);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t f = i / (kAG + kUG);
+    const int g = (int)(i % (kAG + kUG));
+    const float* base = partial + (f * n_split) * 2 * DD;
+    if (g < kAG) {
+      const int blk = g >> 6, r = g & 63;
+      const int nn = (blk >> 2) * 16 + (r & 15);  // inverse of a_granule
+      const int kc = (blk & 3) * 4 + (r >> 4);
+      const float* src = base + (int64_t)nn * D + 8 * kc;
+      const float4 lo = sum_splits<kN>(src, n_split, 2 * DD);
+      const float4 hi = sum_splits<kN>(src + 4, n_split, 2 * DD);
+      if (out.outA == nullptr) continue;
+      uint4* At = (uint4*)(out.outA + f * out.fstride);
+      At[g] = make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
+                         pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
+    } else {
+      const int gu = g - kAG;
+      const int blk = gu >> 6, r = gu & 63;
+      const int m = (blk >> 3) * 16 + (r & 15);  // inverse of u_granule
+      const int nc = (blk & 7) * 4 + (r >> 4);
+      const float4 v = sum_splits<kN>(base + DD + (int64_t)m * D + 4 * nc, n_split, 2 * DD);
+      if (out.outU == nullptr) continue;
+      ((float4*)(out.outU + f * out.fstride))[gu] = v;
+    }
+  }
+}
+
 template <typename TIn>
 hipError_t launch_generic(const Shape& sh, const void* k, const void* v, const float* beta,
                           int n_split, TermsOut out, hipStream_t st) {
@@ -805,11 +846,25 @@ hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_s
   const int64_t n = sh.FH() * 2 * sh.D * sh.D / 4;
   if (n == 0) return hipSuccess;
   int64_t g = std::min<int64_t>((n + 255) / 256, 8192);
-  const int sl = scan_layout ? 1 : 0;
+  if (scan_layout) {
+    // scan_layout is only requested for D = 128
+    const int64_t ng = sh.FH() * (sh.D * sh.D / 8 + sh.D * sh.D / 4);
+    const int64_t gg = std::min<int64_t>((ng + 255) / 256, 8192);
+    switch (n_split) {
+      case 2: reduce_partials_granules<2><<<(unsigned)gg, 256, 0, st>>>(partial, n_split, sh.FH(), out); break;
+      case 3: reduce_partials_granules<3><<<(unsigned)gg, 256, 0, st>>>(partial, n_split, sh.FH(), out); break;
+      case 4: reduce_partials_granules<4><<<(unsigned)gg, 256, 0, st>>>(partial, n_split, sh.FH(), out); break;
+      case 5: reduce_partials_granules<5><<<(unsigned)gg, 256, 0, st>>>(partial, n_split, sh.FH(), out); break;
+      default: reduce_partials_granules<0><<<(unsigned)gg, 256, 0, st>>>(partial, n_split, sh.FH(), out); break;
+    }
+    return hipGetLastError();
+  }
+  const int sl = 0;
   switch (n_split) {
     case 2: reduce_partials_kernel<2><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out, sl); break;
     case 3: reduce_partials_kernel<3><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out, sl); break;
     case 4: reduce_partials_kernel<4><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out, sl); break;
+    case 5: reduce_partials_kernel<5><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out, sl); break;
     default: reduce_partials_kernel<0><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out, sl); break;
   }
   return hipGetLastError();
