@@ -69,7 +69,11 @@ def test_prepare(io):
 # ------------------------------------------------------------- frame terms
 TERMS_CASES = {
     "bf16_D128_ragged_S1000": gi.workload(2).with_shape(H=2, T=3, S=1000),
-    "bf16_D128_split4_S3600": gi.workload(2).with_shape(T=2),
+    # calls with few frame-heads split each frame's tokens over up to five
+    # workgroups, at most one per 512 tokens: 5, 3 and 2 splits (ragged tails)
+    "bf16_D128_split5_S3600": gi.workload(2).with_shape(T=2),
+    "bf16_D128_split3_S1700": gi.workload(2).with_shape(T=2, S=1700),
+    "bf16_D128_split2_S1100": gi.workload(2).with_shape(T=2, S=1100),
     "bf16_D128_S5": gi.workload(2).with_shape(T=2, S=5),
     "bf16_D128_S1": gi.workload(2).with_shape(T=1, S=1),
     "f32_D16": gi.workload(1),
@@ -125,6 +129,11 @@ SCAN_CASES = {
     "bf16_D128_H16_cp4_s0": (gi.workload(2).with_shape(H=16, T=9, S=100), 4, True),
     "bf16_D64_seq": (gi.workload(2).with_shape(D=64, T=4, S=130), 1, True),
     "f32_D128_cp2": (gi.workload(1).with_shape(D=128, T=4, S=200), 2, True),
+    # split phase 1 reduced straight into the scan's granule layout: 5, 3 and
+    # 2 token splits per frame
+    "bf16_D128_split5_S2600": (gi.workload(2).with_shape(T=2, S=2600), 1, False),
+    "bf16_D128_split3_S1700_cp2": (gi.workload(2).with_shape(T=4, S=1700), 2, True),
+    "bf16_D128_split2_S1100": (gi.workload(2).with_shape(H=2, T=3, S=1100), 1, True),
 }
 
 
