@@ -27,7 +27,7 @@ bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p % 16) == 0;
 // Every launch must hold fewer than 2^32 work-items (the limit of a dispatch).
 // Conservative bounds of the grids a call on sh can launch, `chunks` being its
 // largest count of time chunks or reverse-scan chunks: the per-frame-head
-// kernels (phase 1 with up to 4 splits of 512 threads, the readout, the
+// kernels (phase 1 with up to 5 splits of 512 threads, the readout, the
 // backward's passes) at most 4096 work-items per frame-head; the fp32 and
 // small-D kernels at most S D + 4096 per frame-head; the scans and the
 // combine at most 32 blocks of 256 threads per (head, chunk) job.

@@ -648,15 +648,13 @@ __device__ __forceinline__ float4 sum_splits(const float* p, int n, int64_t stri
   return acc;
 }
 
-// Sum of the token-range partials in a fixed order (deterministic). With
-// scan_layout, the A half is written as bf16 in the scan's granule layout (as
-// the MFMA epilogue does): each thread then sums four consecutive m of one
-// column.
+// Sum of the token-range partials in a fixed order (deterministic), as fp32
+// row-major A_t and U_t (the scan's granule layout: reduce_partials_granules).
 // kN: the split count when it is a compile-time constant (0: n_split).
 template <int kN>
 __global__ void __launch_bounds__(256)
 reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, int64_t FH,
-                       TermsOut out, int scan_layout) {
+                       TermsOut out) {
   const int64_t per = (int64_t)2 * D * D / 4;  // four-element groups per frame-head
   const int64_t n = FH * per;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -665,30 +663,12 @@ reduce_partials_kernel(const float* __restrict__ partial, int n_split, int D, in
     const int64_t f = i / per;
     const int64_t e = (i % per) * 4;
     const float* base = partial + (f * n_split) * 2 * D * D;
-    if (scan_layout && e < (int64_t)D * D) {
-      // group = (column nn, rows mm..mm+3) of A_t, read as row nn, columns
-      // mm..mm+3: A_t is symmetric, and the two differ only in which operand
-      // carried the bf16 rounding of beta . ReLU(k); the row is one
-      // coalesced 16-byte load per split
-      const int64_t nn = e / D;
-      const int64_t mm = e % D;
-      const float4 v = sum_splits<kN>(base + nn * D + mm, n_split, (int64_t)2 * D * D);
-      if (out.outA == nullptr) continue;
-      uint16_t* At = (uint16_t*)(out.outA + f * out.fstride);
-      // scan_layout is only requested for D = 128 (granule layout)
-      const int64_t at = (int64_t)a_granule((int)nn, (int)(mm >> 3)) * 8 + (mm & 7);
-      *(uint2*)(At + at) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-      continue;
-    }
     const float4 s = sum_splits<kN>(base + e, n_split, (int64_t)2 * D * D);
     const int64_t row = e / D;
     const int64_t col = e % D;
     float* dst = row < D ? out.outA : out.outU;
     if (dst == nullptr) continue;
-    if (scan_layout && row >= D)
-      *(float4*)(dst + f * out.fstride + (int64_t)u_granule((int)(row - D), (int)(col >> 2)) * 4) = s;
-    else
-      *(float4*)(dst + f * out.fstride + (row % D) * D + col) = s;
+    *(float4*)(dst + f * out.fstride + (row % D) * D + col) = s;
   }
 }
 
@@ -847,7 +827,7 @@ hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_s
   if (n == 0) return hipSuccess;
   int64_t g = std::min<int64_t>((n + 255) / 256, 8192);
   if (scan_layout) {
-    // scan_layout is only requested for D = 128
+    if (sh.D != 128) return hipErrorInvalidValue;  // the granule layout is D = 128's
     const int64_t ng = sh.FH() * (sh.D * sh.D / 8 + sh.D * sh.D / 4);
     const int64_t gg = std::min<int64_t>((ng + 255) / 256, 8192);
     switch (n_split) {
@@ -859,13 +839,12 @@ hipError_t launch_reduce_partials(const Shape& sh, const float* partial, int n_s
     }
     return hipGetLastError();
   }
-  const int sl = 0;
   switch (n_split) {
-    case 2: reduce_partials_kernel<2><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out, sl); break;
-    case 3: reduce_partials_kernel<3><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out, sl); break;
-    case 4: reduce_partials_kernel<4><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out, sl); break;
-    case 5: reduce_partials_kernel<5><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out, sl); break;
-    default: reduce_partials_kernel<0><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out, sl); break;
+    case 2: reduce_partials_kernel<2><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out); break;
+    case 3: reduce_partials_kernel<3><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out); break;
+    case 4: reduce_partials_kernel<4><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out); break;
+    case 5: reduce_partials_kernel<5><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out); break;
+    default: reduce_partials_kernel<0><<<(unsigned)g, 256, 0, st>>>(partial, n_split, sh.D, sh.FH(), out); break;
   }
   return hipGetLastError();
 }
