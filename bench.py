@@ -364,11 +364,12 @@ def main():
     step = step_fn(w, d)
     pf = per_frame_head(w)
     fh = B * H * T
-    # The streaming leg runs before the forward step's warm-up and timed
-    # steps: on a device that has just been idle, the first ~30 ms of steps
-    # run about 3 % slower than the rest (20 steps after a 5-step warm-up:
-    # 1.539 against 1.489-1.493 ms/step for the next 20-step blocks), and the
-    # headline is meant as the steady rate of back-to-back steps.
+    # Order: the streaming leg, the forward step's per-step pass and its
+    # phase-traced pass (K steps each), then the W warm-up steps and the K
+    # timed steps of the headline. The first ~40 ms of back-to-back forward
+    # steps run 2-3 % slower than the rest (20 steps after a 5-step warm-up:
+    # 1.539 ms/step, every later block of 20 1.489-1.493), and the headline
+    # is meant as the steady rate of back-to-back steps, so it comes last.
     streaming_out = None
     if not args.no_streaming:
         # streaming: the same layer stepped through blocks of a few latent
@@ -393,7 +394,7 @@ def main():
                 cin = carry
 
         stream_pass()
-        reps = max(args.steps // 4, 3)
+        reps = max(args.steps // 2, 10)
         t_stream, _ = timed(stream_pass, reps, traced=False)
         _, ss = timed(stream_pass, reps, events_per_call=24 * len(cuts))
         full_blocks = [c for c in range(len(cuts)) if cuts[c][1] - cuts[c][0] == L]
@@ -409,6 +410,15 @@ def main():
         }
         del blk, blk_o, carry, bws_s, full_blocks
 
+    # K steps with an event between consecutive steps (the first steps of the
+    # call on this device), K steps with the phase trace on (per-phase device
+    # times), K steps with per-step events again (per-step median and min)
+    log("per-step and phase-traced passes")
+    med_first, _ = per_step(step, args.steps)
+    ms_traced, summ = timed(step, args.steps)
+    med, mn = per_step(step, args.steps)
+    log(f"per step: median {med:.3f} (first pass {med_first:.3f}), min {mn:.3f}; "
+        f"phase-traced steps: {ms_traced:.3f} ms/step")
     log("warmup", args.warmup)
     for _ in range(args.warmup):
         step()
@@ -419,11 +429,6 @@ def main():
     ms, _ = timed(step, args.steps, traced=False)
     wall = (time.perf_counter() - wall0) / args.steps * 1e3
     log(f"{args.steps} steps: {ms:.3f} ms/step (events), {wall:.3f} ms/step (wall)")
-    # the same K steps with an event between consecutive steps (per-step
-    # median and min), then with the phase trace on (per-phase device times)
-    med, mn = per_step(step, args.steps)
-    ms_traced, summ = timed(step, args.steps)
-    log(f"per step: median {med:.3f}, min {mn:.3f}; phase-traced steps: {ms_traced:.3f} ms/step")
 
     out = {
         "metric": "GDN layer latent frames/s (H=16,D=128,S=3600) + % of bf16 MFMA peak",
@@ -444,6 +449,7 @@ def main():
                    "parallelism": "single GPU"},
         "ms_step_median": med,
         "ms_step_min": mn,
+        "ms_step_median_first_pass": med_first,
         "ms_per_step_phase_traced": ms_traced,
     }
     eff_tf = pf["step_flop"] * fh / (ms / 1e3) / 1e12
@@ -491,6 +497,8 @@ def main():
     # a plain device copy of q (the readout's input) on the same stream: the
     # mixed read + write stream this box sustains next to the readout
     qc = torch.empty_like(d["q"])
+    for _ in range(3):  # a fresh allocation: its first copies run slower
+        qc.copy_(d["q"])
     t_copy, _ = timed(lambda: qc.copy_(d["q"]), max(args.steps // 2, 5), traced=False)
     copy_gbs = 2 * d["q"].numel() * d["q"].element_size() / (t_copy / 1e3) / 1e9
     out["roofline"]["copy_reference_GBps"] = copy_gbs
@@ -598,8 +606,9 @@ def main():
         del dw, sf, wsw
 
     if not args.no_configs:
-        # the other named workloads, each timed the same way (warm-up, then
-        # traced steps), as sub-objects of the one line
+        # the other named workloads as sub-objects of the one line, each timed
+        # in the headline's order (per-step and traced passes, then the
+        # warm-up and the timed steps)
         del d, step
         torch.cuda.empty_cache()
         out["configs"] = {}
@@ -610,15 +619,17 @@ def main():
             log("config", wc.name)
             dc = load(wc)
             sc = step_fn(wc, dc)
-            for _ in range(3):
+            medc_first, _ = per_step(sc, args.steps)
+            _, sm = timed(sc, args.steps)
+            medc, mnc = per_step(sc, args.steps)
+            for _ in range(args.warmup):
                 sc()
             msc, _ = timed(sc, args.steps, traced=False)
-            medc, mnc = per_step(sc, args.steps)
-            _, sm = timed(sc, args.steps)
             pc = per_frame_head(wc)
             fhc = wc.B * wc.H * wc.T
             out["configs"][wc.name] = {
                 "ms_per_step": msc, "ms_step_median": medc, "ms_step_min": mnc,
+                "ms_step_median_first_pass": medc_first,
                 "layer_frames_per_s": wc.T / (msc / 1e3),
                 "hbm_frac_step": pc["step_bytes"] * fhc / (msc / 1e3) / 1e9 / HBM_PEAK_GBS,
                 "effective_tflops": pc["step_flop"] * fhc / (msc / 1e3) / 1e12,
