@@ -580,6 +580,39 @@ def test_streaming_step_chain_equals_chunk_causal_scan():
         assert e <= tol(w), (n, e)
 
 
+def test_streaming_step_full_size():
+    """gdn_step as the benchmark streams the 60 s 720p layer (16 heads,
+    S = 3600, 3-frame blocks; each block's phase 1 split over its tokens),
+    chained over the first 4 blocks with the forward state carried in place:
+    every head's outputs, forward and reverse states (per frame and per token)
+    and the carry against the oracle's chunk-causal scan with chunk_len = 3."""
+    L = 3
+    w = gi.workload(4).with_shape(T=4 * L, time_chunks=1)
+    x, d = _gen(w, seed=3)
+    carry = torch.zeros((w.B, w.H, w.D, w.D), dtype=torch.float32, device=DEV)
+    outs, fwd, rev = [], [], []
+    for a in range(0, w.T, L):
+        say("streaming full size: block", a, a + L)
+        blk = {n: d[n][:, :, a:a + L].contiguous() for n in ("q", "k", "v", "beta", "gamma")}
+        r = gdn.gdn_step(blk["q"], blk["k"], blk["v"], blk["beta"], blk["gamma"], carry_in=carry,
+                         carry_out=carry, want_states=True)
+        outs.append(r["o"])
+        fwd.append(r["states_fwd"])
+        rev.append(r["states_rev"])
+    torch.cuda.synchronize()
+    got = {"o": torch.cat(outs, dim=2), "states_fwd": torch.cat(fwd, dim=2),
+           "states_rev": torch.cat(rev, dim=2)}
+    for h in range(w.H):
+        a = head_arrays(x, 0, h)
+        ref = orc.scan_bidir_chunked(a["q"], a["k"], a["v"], a["beta"], a["gamma"], L)
+        errs = {n: float(frame_errs(host(got[n][0, h]), ref[n][0, 0]).max())
+                for n in ("o", "states_fwd", "states_rev")}
+        errs["o token"] = float(token_errs(host(got["o"][0, h]), ref["o"][0, 0]).max())
+        errs["carry"] = rel_fro(host(carry[0, h]), ref["s_final"][0, 0])
+        say("streaming full size, head", h, {k: f"{v:.2e}" for k, v in errs.items()})
+        assert max(errs.values()) <= tol(w), (h, errs)
+
+
 # ------------------------------------------------------ fused q/k RMSNorm
 def _gen_rescaled(w, seed=0):
     """Seeded inputs whose q and k tokens are rescaled by factors in
