@@ -1072,6 +1072,9 @@ REUSE_CASES = {
     "bf16_D128_split_S2100": (gi.workload(2).with_shape(T=3, S=2100), 0, 1, False, False),
     "bf16_D128_bidir_L2_norm": (gi.workload(2).with_shape(H=2, T=5, S=170), 2, 2, True, False),
     "bf16_D128_step_prepared": (gi.workload(2).with_shape(H=2, T=3, S=170), -1, 1, False, True),
+    # 90 tokens: the last 32-token stage of the recompute holds 26 tokens
+    "bf16_D128_S90": (gi.workload(2).with_shape(H=2, T=3, S=90), 0, 1, False, False),
+    "bf16_D128_S90_norm": (gi.workload(2).with_shape(H=2, T=3, S=90), 0, 2, True, False),
     "bf16_D64_norm": (gi.workload(2).with_shape(D=64, T=4, S=130), 0, 2, True, False),
     "f32_D16_bidir_L3": (gi.workload(1), 3, 1, False, False),
 }
