@@ -281,6 +281,71 @@ def test_deterministic():
         assert torch.equal(r1[n], r2[n]), n
 
 
+DEGENERATE_KINDS = ("beta_zero", "gates_off_on_odd_frames", "gamma_zero", "keys_nonpositive",
+                    "beta_binary")
+
+
+def _degenerate(x, w, kind):
+    """One of the method's degenerate regimes, made in place from seeded inputs
+    (float copies and, for bf16, the bit patterns the device gets)."""
+    if kind == "beta_zero":                  # no writes: S_t = gamma_t S_{t-1}
+        x["beta"][:] = 0.0
+    elif kind == "gates_off_on_odd_frames":  # frames 1, 3, ... write nothing
+        x["beta"][:, :, 1::2] = 0.0
+    elif kind == "gamma_zero":               # no memory: S_t = U_t (R_t = U_t)
+        x["gamma"][:] = 0.0
+    elif kind == "keys_nonpositive":         # ReLU zeroes every key: A_t = U_t = 0
+        x["k"][:] = -np.abs(x["k"])
+        if w.io == "bf16":
+            x["k_bits"] |= np.uint16(0x8000)
+    elif kind == "beta_binary":              # every token written fully or not at all
+        rng = np.random.default_rng([77, w.S])
+        x["beta"][:] = (rng.random(x["beta"].shape) < 0.5).astype(np.float32)
+    else:
+        raise ValueError(kind)
+
+
+@pytest.mark.parametrize("wname", ["bf16_D128", "f32_D16"])
+@pytest.mark.parametrize("kind", DEGENERATE_KINDS)
+def test_degenerate_inputs(kind, wname):
+    """The degenerate regimes of the recurrence (P1 "混合线性注意力": M_t =
+    gamma_t (I - A_t), U_t = V beta K_hat^T) on the MFMA path and on the fp32
+    vector path: forward states and outputs (3 time chunks, with s0) and the
+    chunk-causal scan (chunks of 2 frames) against the oracle at the usual bar;
+    where the arithmetic makes them exact, A_t = U_t = 0 (no gate or no
+    positive key) and S_t = R_t = U_t (gamma = 0), bit for bit."""
+    w = (gi.workload(2).with_shape(H=2, T=6, S=300) if wname == "bf16_D128"
+         else gi.workload(1).with_shape(T=6))
+    x = gi.batch_inputs(w, 0)
+    _degenerate(x, w, kind)
+    d = upload(x, w)
+    s0 = _s0(w)
+    s0d = torch.from_numpy(s0).to(DEV)
+    say("degenerate", kind, wname, "terms")
+    A, U = gdn.gdn_frame_terms(d["k"], d["v"], d["beta"])
+    say("degenerate", kind, wname, "forward, 3 time chunks")
+    res = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], s0=s0d, n_time_chunks=3)
+    say("degenerate", kind, wname, "chunk-causal, chunks of 2")
+    bid = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], 2, s0=s0d,
+                                     n_time_chunks=2)
+    torch.cuda.synchronize()
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    _check_fwd(w, x, res, s0, heads, 3, f"degenerate {kind} {wname}")
+    for (b, h) in heads:
+        a = head_arrays(x, b, h)
+        ref = orc.scan_bidir_chunked(a["q"], a["k"], a["v"], a["beta"], a["gamma"], 2,
+                                     s0=s0[b, h][None, None].astype(np.float64))
+        for n in ("states_fwd", "states_rev", "o"):
+            assert frame_errs(host(bid[n][b, h]), ref[n][0, 0]).max() <= tol(w), n
+    zero_frames = {"beta_zero": range(w.T), "keys_nonpositive": range(w.T),
+                   "gates_off_on_odd_frames": range(1, w.T, 2)}.get(kind, ())
+    for t in zero_frames:
+        assert not A[:, :, t].any() and not U[:, :, t].any(), t
+    if kind == "gamma_zero":
+        assert torch.equal(res["states"], U)
+        assert torch.equal(bid["states_fwd"], U) and torch.equal(bid["states_rev"], U)
+
+
 @pytest.mark.parametrize("P", [1, 3])
 def test_bidir_scans_sharing_a_launch_match_separate_scans(P):
     """The chunk-causal call runs its reverse scan in the same launch as the
