@@ -1001,6 +1001,52 @@ def test_scan_bidir_bwd(name):
         _check_grads(w, g, ref, b, h, (name,))
 
 
+@pytest.mark.parametrize("wname", ["bf16_D128", "f32_D16"])
+@pytest.mark.parametrize("kind", DEGENERATE_KINDS)
+def test_degenerate_inputs_backward(kind, wname):
+    """Gradients of both scans (causal; chunk-causal in chunks of 2 frames) in
+    the recurrence's degenerate regimes against the oracle's, every head;
+    and the gradients the arithmetic makes exactly zero: dk and dv where the
+    gate is 0 (dk = beta c [k > 0] Z, dv = beta c Y), dk, dv and dbeta when
+    ReLU zeroes every key, ds0 = G_0 M_0 when gamma = 0."""
+    w = (gi.workload(2).with_shape(H=2, T=6, S=300) if wname == "bf16_D128"
+         else gi.workload(1).with_shape(T=6))
+    x = gi.batch_inputs(w, 0)
+    _degenerate(x, w, kind)
+    d = upload(x, w)
+    do, do_d, s0, dsf = _bwd_inputs(w, x, d, True)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    say("degenerate backward", kind, wname, "causal")
+    fwd = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], s0=dev(s0), want_o=False)
+    g = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], do_d,
+                         s0=dev(s0), ds_final=dev(dsf))
+    say("degenerate backward", kind, wname, "chunk-causal")
+    fb = gdn.gdn_scan_bidir_chunked(d["q"], d["k"], d["v"], d["beta"], d["gamma"], 2, s0=dev(s0),
+                                    want_o=False)
+    gb = gdn.gdn_scan_bidir_chunked_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], 2,
+                                        fb["states_fwd"], fb["states_rev"], do_d, s0=dev(s0),
+                                        ds_final=dev(dsf))
+    torch.cuda.synchronize()
+    for (b, h) in [(b, h) for b in range(w.B) for h in range(w.H)]:
+        a = head_arrays(x, b, h)
+        args = (a["q"], a["k"], a["v"], a["beta"], a["gamma"])
+        kw = dict(ds_final=dsf[b, h][None, None].astype(np.float64),
+                  s0=s0[b, h][None, None].astype(np.float64))
+        dob = do[b, h][None, None].astype(np.float64)
+        _check_grads(w, g, orc.scan_fwd_bwd(*args, dob, **kw), b, h, (kind, wname, "causal"))
+        _check_grads(w, gb, orc.scan_bidir_bwd(*args, 2, dob, **kw), b, h,
+                     (kind, wname, "chunk-causal"))
+    gate_off = {"beta_zero": slice(None), "gates_off_on_odd_frames": slice(1, None, 2)}.get(kind)
+    for grads in (g, gb):
+        if gate_off is not None:
+            assert not grads["dk"][:, :, gate_off].any() and not grads["dv"][:, :, gate_off].any()
+        if kind == "keys_nonpositive":
+            for n in ("dk", "dv", "dbeta"):
+                assert not grads[n].any(), n
+        if kind == "gamma_zero":
+            assert not grads["ds0"].any()
+
+
 def test_scan_bidir_bwd_layer_full_size():
     """Backward of the chunk-causal 16-head 720p layer (T = 11, S = 3600,
     chunks of 3 frames) at full size in the MFMA configuration, sampled heads."""
