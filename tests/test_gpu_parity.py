@@ -1157,6 +1157,52 @@ def test_scan_bwd_rmsnorm_last_token_dq(S):
     assert te.max() <= tol(w), te.max()
 
 
+@pytest.mark.parametrize("wname", ["bf16_D128", "f32_D16"])
+def test_rmsnorm_zero_tokens(wname):
+    """Tokens whose q and k are exactly zero under GDN_QK_RMSNORM. The norm's
+    epsilon keeps 1 / rms finite, so such a key adds nothing to A_t and U_t,
+    such a query gives an output of exactly zero, and every gradient stays
+    finite (the norm's backward scales the incoming gradient by 1 / sqrt(eps)
+    there). Forward with 2 time chunks and backward against the oracle."""
+    w = (gi.workload(2).with_shape(H=2, T=4, S=300) if wname == "bf16_D128"
+         else gi.workload(1).with_shape(T=4))
+    x = gi.batch_inputs(w, 0)
+    zero = np.zeros(w.S, dtype=bool)
+    zero[::5] = True
+    for n in ("q", "k"):
+        x[n][:, :, :, zero] = 0.0
+        if w.io == "bf16":
+            x[n + "_bits"][:, :, :, zero] = 0
+    d = upload(x, w)
+    do, do_d, s0, dsf = _bwd_inputs(w, x, d, True)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    say("rmsnorm zero tokens", wname, "forward")
+    fwd = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], s0=dev(s0),
+                           n_time_chunks=2, qk_rmsnorm=True)
+    say("rmsnorm zero tokens", wname, "backward")
+    g = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], do_d,
+                         s0=dev(s0), ds_final=dev(dsf), qk_rmsnorm=True)
+    torch.cuda.synchronize()
+    assert not fwd["o"][:, :, :, torch.from_numpy(zero).to(DEV)].any()
+    for n in ("dq", "dk", "dv", "dbeta", "dgamma", "ds0"):
+        assert torch.isfinite(g[n].float()).all(), n
+    for (b, h) in [(b, h) for b in range(w.B) for h in range(w.H)]:
+        a = head_arrays(x, b, h)
+        args = (a["q"], a["k"], a["v"], a["beta"], a["gamma"])
+        s0h = s0[b, h][None, None].astype(np.float64)
+        ref = orc.scan_fwd(*args, s0=s0h, qk_rmsnorm=True)
+        for n in ("states", "o"):
+            got = host(fwd[n][b, h])
+            e = frame_errs(got, ref[n][0, 0]).max()
+            if n == "o":
+                e = max(e, token_errs(got, ref[n][0, 0]).max())
+            assert e <= tol(w), (n, e)
+        refg = orc.scan_fwd_bwd(*args, do[b, h][None, None].astype(np.float64),
+                                ds_final=dsf[b, h][None, None].astype(np.float64), s0=s0h,
+                                qk_rmsnorm=True)
+        _check_grads(w, g, refg, b, h, ("rmsnorm zero tokens", wname))
+
+
 def test_scan_bwd_rmsnorm_without_dq():
     """With the RMSNorm of q, E_t still comes from the fused pass when dq is
     not wanted; the other gradients are bitwise those of the full call."""
