@@ -434,15 +434,17 @@ def test_long_frame():
     _check_fwd(w, x, res, None, [(0, 0)], what="S = 40000")
 
 
-def test_offsets_beyond_32_bits():
+@pytest.mark.parametrize("mode", ["causal", "chunk_causal"])
+def test_offsets_beyond_32_bits(mode):
     """Three 60 s 720p layers in one call (B = 3, H = 16, T = 121, S = 3600,
     bf16; 2.68e9 elements per token tensor): the last batch's heads start
     beyond 2^31 elements and 2^32 bytes, where an offset held in 32 bits
     anywhere in a kernel would wrap. Forward in the benchmark's launch
-    configuration (8 time chunks) and the backward; states, outputs and every
-    gradient of the first and the last head against the oracle. The two heads
-    carry the workload's seeded inputs, the others seeded device draws."""
-    w = gi.workload(4).with_shape(B=3)
+    configuration (8 time chunks; chunk-causal: chunks of 10 frames) and the
+    backward; states, outputs and every gradient of the first and the last
+    head against the oracle. The two heads carry the workload's seeded
+    inputs, the others seeded device draws."""
+    w = gi.workload(4 if mode == "causal" else 5).with_shape(B=3)
     heads = [(0, 0), (w.B - 1, w.H - 1)]
     shp = (w.B, w.H, w.T, w.S, w.D)
     per_head = w.T * w.S * w.D
@@ -465,22 +467,34 @@ def test_offsets_beyond_32_bits():
         for n in ("beta", "gamma"):
             d[n][b, h] = torch.from_numpy(xh[n]).to(DEV)
         xs[(b, h)] = xh
+    L = w.chunk_len
+    args = (d["q"], d["k"], d["v"], d["beta"], d["gamma"])
     say("forward", w.name, "B = 3")
-    fwd = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], n_time_chunks=w.time_chunks)
-    say("backward", w.name, "B = 3")
-    g = gdn.gdn_scan_bwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], fwd["states"], d["do"])
+    if L:
+        fwd = gdn.gdn_scan_bidir_chunked(*args, L, n_time_chunks=w.time_chunks)
+        say("backward", w.name, "B = 3")
+        g = gdn.gdn_scan_bidir_chunked_bwd(*args, L, fwd["states_fwd"], fwd["states_rev"], d["do"])
+        names = ("states_fwd", "states_rev", "o")
+    else:
+        fwd = gdn.gdn_scan_fwd(*args, n_time_chunks=w.time_chunks)
+        say("backward", w.name, "B = 3")
+        g = gdn.gdn_scan_bwd(*args, fwd["states"], d["do"])
+        names = ("states", "o")
     torch.cuda.synchronize()
     for (b, h) in heads:
         xh = xs[(b, h)]
-        a = {n: np.asarray(xh[n], dtype=np.float64)[None, None]
-             for n in ("q", "k", "v", "beta", "gamma")}
-        ref = orc.scan_fwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"])
+        a = [np.asarray(xh[n], dtype=np.float64)[None, None] for n in ("q", "k", "v", "beta", "gamma")]
+        dob = host(d["do"][b, h])[None, None]
+        if L:
+            ref = orc.scan_bidir_chunked(*a, L)
+            gref = orc.scan_bidir_bwd(*a, L, dob)
+        else:
+            ref = orc.scan_fwd(*a)
+            gref = orc.scan_fwd_bwd(*a, dob)
         errs = {n + " frame": float(frame_errs(host(fwd[n][b, h]), ref[n][0, 0]).max())
-                for n in ("states", "o")}
+                for n in names}
         errs["o token"] = float(token_errs(host(fwd["o"][b, h]), ref["o"][0, 0]).max())
         errs["s_final"] = rel_fro(host(fwd["s_final"][b, h]), ref["s_final"][0, 0])
-        gref = orc.scan_fwd_bwd(a["q"], a["k"], a["v"], a["beta"], a["gamma"],
-                                host(d["do"][b, h])[None, None])
         errs.update(_grad_errs(g, gref, b, h))
         say(w.name, "B = 3", (b, h), {n: f"{e:.2e}" for n, e in errs.items()})
         assert max(errs.values()) <= tol(w), ((b, h), errs)
