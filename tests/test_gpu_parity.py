@@ -7,6 +7,8 @@ several tiles plus ragged tails; the five named workloads run at full size in
 the launch configuration the benchmark times, checked on sampled heads.
 """
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -500,6 +502,98 @@ def test_offsets_beyond_32_bits(mode):
         assert max(errs.values()) <= tol(w), ((b, h), errs)
     del d, fwd, g
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------- readout alone, trace
+READOUT_CASES = {
+    # name: (workload, with a second state, RMSNorm of q)
+    "bf16_D128_ragged_S1000": (gi.workload(2).with_shape(H=2, T=3, S=1000), False, False),
+    "bf16_D128_two_states": (gi.workload(2).with_shape(H=2, T=3, S=1000), True, False),
+    "bf16_D128_two_states_norm": (gi.workload(2).with_shape(H=2, T=3, S=1000), True, True),
+    # two frame-heads: up to 16 workgroups per frame-head, ragged against their tiles
+    "bf16_D128_two_frame_heads_S300": (gi.workload(2).with_shape(T=2, S=300), False, False),
+    "bf16_D64_norm": (gi.workload(2).with_shape(D=64, T=2, S=130), False, True),
+    "f32_D16_two_states": (gi.workload(1), True, False),
+}
+
+
+@pytest.mark.parametrize("name", sorted(READOUT_CASES))
+def test_readout_alone(name):
+    """gdn_readout (phase 3 alone) on given fp32 states against the oracle's
+    readout o = (S_t [+ R_t]) q (with q RMS-normalised when flagged), per frame
+    and per token; and bitwise the output gdn_scan_fwd forms from the same
+    states."""
+    w, two, norm = READOUT_CASES[name]
+    x, d = _gen(w)
+    rng = np.random.default_rng([66, w.S])
+    shp = (w.B, w.H, w.T, w.D, w.D)
+    st = (0.05 * rng.standard_normal(shp)).astype(np.float32)
+    st2 = (0.05 * rng.standard_normal(shp)).astype(np.float32) if two else None
+    dev = lambda a: None if a is None else torch.from_numpy(a).to(DEV)
+    say("readout", name)
+    o = gdn.gdn_readout(d["q"], dev(st), dev(st2), qk_rmsnorm=norm)
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        for h in range(w.H):
+            qh = np.asarray(x["q"][b, h], dtype=np.float64)
+            qn = orc.rms_norm(qh) if norm else qh
+            ssum = st[b, h].astype(np.float64) + (0.0 if st2 is None else st2[b, h].astype(np.float64))
+            ref = np.stack([orc.readout(ssum[t], qn[t]) for t in range(w.T)])
+            got = host(o[b, h])
+            e = max(frame_errs(got, ref).max(), token_errs(got, ref).max())
+            say(name, (b, h), f"{e:.2e}")
+            assert e <= tol(w), ((b, h), e)
+    say("readout", name, "against the scan's own readout")
+    res = gdn.gdn_scan_fwd(d["q"], d["k"], d["v"], d["beta"], d["gamma"], qk_rmsnorm=norm)
+    o2 = gdn.gdn_readout(d["q"], res["states"], qk_rmsnorm=norm)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, res["o"])
+
+
+def test_phase_trace():
+    """gdn_trace_set on the GPU: a traced forward call with composites records a
+    call-begin event and one event per launch group (phase 1, composites,
+    combine, replay, readout), each with a positive device time, summing to the
+    call's total; a call that fails its argument checks records nothing; a full
+    trace drops further marks and the call's results are unchanged; after the
+    trace is cleared nothing is recorded."""
+    w = gi.workload(2).with_shape(H=2, T=6, S=700)
+    x, d = _gen(w)
+    args = (d["q"], d["k"], d["v"], d["beta"], d["gamma"])
+    say("trace: untraced reference call")
+    ref = gdn.gdn_scan_fwd(*args, n_time_chunks=3)
+    tr = gdn.PhaseTrace(64)
+    with tr:
+        say("trace: traced call")
+        res = gdn.gdn_scan_fwd(*args, n_time_chunks=3)
+        torch.cuda.synchronize()
+        n = tr.count
+        bad = gdn.make_desc(1, 2, 6, 700, 0, gdn.GDN_BF16)  # D = 0: rejected before any launch
+        assert gdn.lib().gdn_readout(ctypes.byref(bad), d["q"].data_ptr(), res["states"].data_ptr(),
+                                     None, res["o"].data_ptr(), None) == gdn.GDN_EINVAL
+        assert tr.count == n
+    calls = tr.calls()
+    assert len(calls) == 1, calls
+    c = calls[0]
+    assert set(c) == {"terms", "scan", "combine", "replay", "readout", "total"}, c
+    assert min(c.values()) > 0.0, c
+    parts = sum(v for k, v in c.items() if k != "total")
+    assert abs(parts - c["total"]) <= 1e-3 * c["total"] + 1e-3, c
+    for k in ("states", "s_final", "o"):
+        assert torch.equal(res[k], ref[k]), k
+    say("trace: a full trace")
+    small = gdn.PhaseTrace(3)
+    with small:
+        res3 = gdn.gdn_scan_fwd(*args, n_time_chunks=3)
+        torch.cuda.synchronize()
+    assert small.count == 3 and small.full()
+    assert torch.equal(res3["o"], ref["o"])
+    say("trace: cleared")
+    gdn.gdn_scan_fwd(*args, n_time_chunks=3)
+    torch.cuda.synchronize()
+    assert tr.count == n and small.count == 3
+    tr.close()
+    small.close()
 
 
 # ---------------------------------------------- full-size named workloads
