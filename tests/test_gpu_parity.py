@@ -553,9 +553,10 @@ def test_readout_alone(name):
 def test_phase_trace():
     """gdn_trace_set on the GPU: a traced forward call with composites records a
     call-begin event and one event per launch group (phase 1, composites,
-    combine, replay, readout), whose device times add up to the call's total; a call that fails its argument checks records nothing; a full
-    trace drops further marks and the call's results are unchanged; after the
-    trace is cleared nothing is recorded."""
+    combine, replay, readout), whose device times add up to the call's total;
+    a call that fails its argument checks records nothing; a full trace drops
+    further marks and the call's results are unchanged; after the trace is
+    cleared nothing is recorded."""
     w = gi.workload(2).with_shape(H=2, T=6, S=700)
     x, d = _gen(w)
     args = (d["q"], d["k"], d["v"], d["beta"], d["gamma"])
