@@ -1209,6 +1209,46 @@ def test_degenerate_inputs_backward(kind, wname):
             assert not grads["ds0"].any()
 
 
+@pytest.mark.parametrize("wname", ["bf16_D128", "f32_D16"])
+def test_explicit_key_scale(wname):
+    """A key scale given by the caller instead of 1/sqrt(D S) (phase 1 applies
+    c^2 to A_t and c to U_t; the backward carries c into dk and dbeta):
+    forward (2 time chunks) and chunk-causal scans and both backward passes
+    against the oracle with the same scale, every head. The scale is chosen
+    larger than the default but with tr(A_t) < 1, so that the recurrence stays
+    contractive."""
+    w = (gi.workload(2).with_shape(H=2, T=5, S=300) if wname == "bf16_D128"
+         else gi.workload(1).with_shape(T=5))
+    c = 1.6 / np.sqrt(w.D * w.S)
+    c32 = float(np.float32(c))  # what the descriptor carries
+    x, d = _gen(w)
+    do, do_d, s0, dsf = _bwd_inputs(w, x, d, True)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    args = (d["q"], d["k"], d["v"], d["beta"], d["gamma"])
+    say("explicit key scale", wname)
+    fwd = gdn.gdn_scan_fwd(*args, s0=dev(s0), n_time_chunks=2, key_scale=c32)
+    g = gdn.gdn_scan_bwd(*args, fwd["states"], do_d, s0=dev(s0), ds_final=dev(dsf), key_scale=c32)
+    bid = gdn.gdn_scan_bidir_chunked(*args, 2, s0=dev(s0), key_scale=c32)
+    gb = gdn.gdn_scan_bidir_chunked_bwd(*args, 2, bid["states_fwd"], bid["states_rev"], do_d,
+                                        s0=dev(s0), ds_final=dev(dsf), key_scale=c32)
+    torch.cuda.synchronize()
+    for (b, h) in [(b, h) for b in range(w.B) for h in range(w.H)]:
+        a = [np.asarray(x[n][b, h], dtype=np.float64)[None, None] for n in ("q", "k", "v", "beta", "gamma")]
+        kw = dict(s0=s0[b, h][None, None].astype(np.float64), key_scale=c32)
+        dob = do[b, h][None, None].astype(np.float64)
+        dsb = dsf[b, h][None, None].astype(np.float64)
+        ref = orc.scan_fwd(*a, **kw)
+        refb = orc.scan_bidir_chunked(*a, 2, **kw)
+        for n in ("states", "o"):
+            assert frame_errs(host(fwd[n][b, h]), ref[n][0, 0]).max() <= tol(w), n
+        for n in ("states_fwd", "states_rev", "o"):
+            assert frame_errs(host(bid[n][b, h]), refb[n][0, 0]).max() <= tol(w), n
+        _check_grads(w, g, orc.scan_fwd_bwd(*a, dob, ds_final=dsb, **kw), b, h,
+                     ("key scale", wname, "causal"))
+        _check_grads(w, gb, orc.scan_bidir_bwd(*a, 2, dob, ds_final=dsb, **kw), b, h,
+                     ("key scale", wname, "chunk-causal"))
+
+
 def test_scan_bidir_bwd_layer_full_size():
     """Backward of the chunk-causal 16-head 720p layer (T = 11, S = 3600,
     chunks of 3 frames) at full size in the MFMA configuration, sampled heads."""
