@@ -158,11 +158,17 @@ def _desc_from(k: torch.Tensor, key_scale, keys_prepared, qk_rmsnorm=False,
 
 
 def _need(t: torch.Tensor | None, name: str, shape, dtype) -> None:
+    """Every tensor handed to the library is contiguous, of the expected shape
+    and dtype, and lives on the current GPU (its address goes to the kernels
+    as is: a host tensor or one on another device would fault there)."""
     if t is None:
         return
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
         raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)}, got "
                          f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
+    if not t.is_cuda or t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name}: expected a tensor on the current GPU "
+                         f"(cuda:{torch.cuda.current_device() if t.is_cuda else '?'}), got {t.device}")
 
 
 def _out(given, want: bool, shape, dtype, device):

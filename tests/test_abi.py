@@ -240,3 +240,17 @@ def test_step_noalloc_refuses_shapes_beyond_its_scratch(L):
     bad = gdn.make_desc(1, 1, 1, 0, 128, gdn.GDN_BF16)
     assert L.gdn_step_noalloc(ctypes.byref(bad), fake, fake, fake, fake, fake, None, fake, fake,
                               None, None, None) == gdn.GDN_EINVAL
+
+
+def test_binding_refuses_host_tensors():
+    """The binding passes tensor addresses to the kernels as they are, so it
+    refuses tensors that are not on the current GPU before calling the
+    library (a host address would fault the device)."""
+    import torch
+    B, H, T, S, D = 1, 1, 2, 12, 16
+    q = torch.zeros((B, H, T, S, D))
+    st = torch.zeros((B, H, T, D, D))
+    with pytest.raises(ValueError, match="current GPU"):
+        gdn.gdn_readout(q, st, o=torch.zeros_like(q))
+    with pytest.raises(ValueError, match="current GPU"):
+        gdn.gdn_prepare(q, k_hat=torch.zeros_like(q))
