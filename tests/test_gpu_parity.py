@@ -134,6 +134,9 @@ SCAN_CASES = {
     # split phase 1 reduced straight into the scan's granule layout: 5, 3 and
     # 2 token splits per frame
     "bf16_D128_split5_S2600": (gi.workload(2).with_shape(T=2, S=2600), 1, False),
+    # frames shorter than one stage of phase 1 and one tile of the readout
+    "bf16_D128_S5_cp2_s0": (gi.workload(2).with_shape(H=2, T=4, S=5), 2, True),
+    "bf16_D128_S1_s0": (gi.workload(2).with_shape(T=3, S=1), 1, True),
     "bf16_D128_split3_S1700_cp2": (gi.workload(2).with_shape(T=4, S=1700), 2, True),
     "bf16_D128_split2_S1100": (gi.workload(2).with_shape(H=2, T=3, S=1100), 1, True),
 }
@@ -977,6 +980,11 @@ BWD_CASES = {
     "bf16_D64": (gi.workload(2).with_shape(D=64, T=5, S=130), True, False),
     "f32_D128_prepared": (gi.workload(1).with_shape(D=128, S=40, T=4), True, True),
     "bf16_D128_prepared": (gi.workload(2).with_shape(H=2, T=4, S=170), True, True),
+    # frames shorter than one 32-token stage (every row past the end is a
+    # clamped copy of the last one), a single frame, a single token
+    "bf16_D128_S5": (gi.workload(2).with_shape(H=2, T=3, S=5), True, False),
+    "bf16_D128_T1_S33": (gi.workload(2).with_shape(H=2, T=1, S=33), True, False),
+    "bf16_D128_S1": (gi.workload(2).with_shape(T=2, S=1), True, False),
 }
 
 
@@ -1125,6 +1133,8 @@ BIDIR_BWD_CASES = {
     "bf16_D128_L2_split_S2100": (gi.workload(2).with_shape(T=3, S=2100), 2, True, False),
     "bf16_D64_L2": (gi.workload(2).with_shape(D=64, T=5, S=130), 2, True, False),
     "bf16_D128_L3_prepared": (gi.workload(2).with_shape(H=2, T=5, S=170), 3, True, True),
+    "bf16_D128_L2_S5": (gi.workload(2).with_shape(H=2, T=3, S=5), 2, True, False),
+    "bf16_D128_L1_S1": (gi.workload(2).with_shape(T=2, S=1), 1, True, False),
 }
 
 
