@@ -125,6 +125,9 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   const int stages = (S + kTsd - 1) / kTsd;
   const int st_begin = (int)(((int64_t)split * stages) / n_split);
   const int st_end = (int)(((int64_t)(split + 1) * stages) / n_split);
+  // last token the copies may touch: the ring's prefetch past this
+  // workgroup's range re-reads it instead of the next range's tokens
+  const int tok_last = max(min(st_end * kTsd, S) - 1, 0);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -155,8 +158,9 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
   // k and of v (one 1 KB instruction each; k only when kAOnly) and their 4
   // gates. Lane L of a
   // copy instruction fills LDS slot L of its block: chunk L/4 of token
-  // 4w + L%4. Tokens past the end are clamped to the last token (valid
-  // memory); their gate is zeroed by the transform pass.
+  // 4w + L%4. Tokens past the end of the range are clamped to its last
+  // token (valid memory); past the frame's end their gate is zeroed by the
+  // transform pass, and stages past the range are never consumed.
   const int dtok = 4 * wave + (lane & 3);            // token within the stage
   const int dchunk = lane >> 2;
   constexpr int kOps = kDq ? 4 : (kAOnly ? 2 : 3);  // copy instructions per (copying) wave and stage
@@ -175,7 +179,7 @@ terms_dma_bf16_d128(const uint16_t* __restrict__ k, const uint16_t* __restrict__
       }
       return;
     }
-    const int t = min(st * kTsd + dtok, S - 1);
+    const int t = min(st * kTsd + dtok, tok_last);
     const int64_t off = (int64_t)t * D + 8 * dchunk;
     dma16(kf + off, slot + 1024 * wave);
     if (!kAOnly) dma16(vf + off, slot + kKvBytes + 1024 * wave);
