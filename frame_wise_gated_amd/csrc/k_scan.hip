@@ -357,10 +357,16 @@ __global__ void __launch_bounds__(256, 1) combine_mfma_d128(CombineParams p) {
 // the outstanding-load bookkeeping is identical in every step. Wave w owns
 // output columns [32w, 32w + 32) as two 16-column MFMA tiles.
 // Rows of one workgroup's job: row block rb of job `job`. kC: the composite C
-// rows of a COMPOSE job (start I, no U term), which load no U entries.
+// rows of a COMPOSE job (start I, no U term), which load no U entries. kMix
+// (COMPOSE, MT even): tiles [0, MT/2) hold C rows and tiles [MT/2, MT) the H
+// rows of the same indices, so that every workgroup of a job reads A_t and
+// the same amount of U_t per frame: the workgroups of a job then step
+// together and share each A_t through L2. With whole C and whole H row
+// blocks the C blocks ran ahead and the H blocks, which set the compose's
+// time, fetched A_t again from HBM (the compose read 1.2 times its bytes).
 constexpr int kScanLdb = 128 + 8;  // bf16 row stride 272 B: 8 lanes reading 16 B at one column are conflict-free
 constexpr int kSstLd = 128 + 4;   // fp32 row stride 528 B: the 16 rows of a lane group start 4 banks apart
-template <int MT, int kF, bool kC>
+template <int MT, int kF, bool kC, bool kMix = false>
 __device__ __forceinline__ void scan_rows(const ScanParams& p, int64_t job, int rb,
                                           uint16_t (*Xh)[16 * MT][kScanLdb],
                                           uint16_t (*Xl)[16 * MT][kScanLdb],
@@ -371,9 +377,13 @@ __device__ __forceinline__ void scan_rows(const ScanParams& p, int64_t job, int 
   const int c = (int)(job % p.nchunk);
   const int64_t bh = job / p.nchunk;
   const int row0 = rb * R;
+  static_assert(!kMix || (!kC && MT % 2 == 0), "mixed C/H row blocks");
   constexpr bool c_rows = kC;
   const float umul = c_rows ? 0.f : 1.f;
-  const int srow0 = row0 % D;
+  const int srow0 = kMix ? rb * (R / 2) : row0 % D;
+  // tile mt: C rows or not, and its first row inside its D x D matrix
+  auto is_c = [&](int mt) { return kC || (kMix && mt < MT / 2); };
+  auto trow = [&](int mt) { return srow0 + 16 * (kMix ? mt % (MT / 2) : mt); };
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -404,10 +414,10 @@ __device__ __forceinline__ void scan_rows(const ScanParams& p, int64_t job, int 
       f32x4_t x0 = {0.f, 0.f, 0.f, 0.f};
       if (p.mode == SCAN_COMPOSE) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x0[r] = (c_rows && srow0 + m == n + r) ? 1.f : 0.f;
+        for (int r = 0; r < 4; ++r) x0[r] = (is_c(mt) && trow(mt) + l16 == n + r) ? 1.f : 0.f;
       } else if (p.init != nullptr) {
         x0 = *(const f32x4_t*)(p.init + bh * p.init_bh_stride + (int64_t)c * p.init_c_stride +
-                              (int64_t)(srow0 + m) * D + n);
+                              (int64_t)(trow(mt) + l16) * D + n);
       }
       xr[mt][nt] = x0;
       put_split(0, m, n, x0);
@@ -460,8 +470,8 @@ __device__ __forceinline__ void scan_rows(const ScanParams& p, int64_t job, int 
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)  // u_granule(srow0 + 16mt + l16, ncol(nt) / 4)
-        u[j][mt][nt] = Ug[((srow0 / 16 + mt) * 8 + 2 * wave + nt) * 64 + lane];
+      for (int nt = 0; nt < 2; ++nt)  // u_granule(trow(mt) + l16, ncol(nt) / 4)
+        if (!is_c(mt)) u[j][mt][nt] = Ug[((trow(mt) / 16) * 8 + 2 * wave + nt) * 64 + lane];
     gmr[j] = p.gamma[bh * p.T + frame_of(step)];
   };
   if (nsteps > 0) {
@@ -519,7 +529,7 @@ __device__ __forceinline__ void scan_rows(const ScanParams& p, int64_t job, int 
           f32x4_t xn;
 #pragma unroll
           for (int r = 0; r < 4; ++r)  // one rounding: umr is 0 or 1, so umr u is exact
-            xn[r] = __builtin_fmaf(gm, xr[mt][nt][r] - acc[mt][nt][r], kC ? 0.f : umr[j] * u[j][mt][nt][r]);
+            xn[r] = __builtin_fmaf(gm, xr[mt][nt][r] - acc[mt][nt][r], is_c(mt) ? 0.f : umr[j] * u[j][mt][nt][r]);
           if (active) xr[mt][nt] = xn;
           put_split(cur ^ 1, m, ncol(nt), xr[mt][nt]);
         }
@@ -562,14 +572,15 @@ __device__ __forceinline__ void scan_rows(const ScanParams& p, int64_t job, int 
   }
 
   if (p.fin_last_only && c != p.nchunk - 1) return;
-  float* fin = (p.mode == SCAN_COMPOSE && !c_rows) ? p.finB : p.finA;
-  if (fin == nullptr) return;
-  fin += bh * p.fin_bh_stride + (p.fin_last_only ? 0 : (int64_t)c * p.fin_c_stride);
+  const int64_t fin_off = bh * p.fin_bh_stride + (p.fin_last_only ? 0 : (int64_t)c * p.fin_c_stride);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt) {
+    float* fin = (p.mode == SCAN_COMPOSE && !is_c(mt)) ? p.finB : p.finA;
+    if (fin == nullptr) continue;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
-      *(f32x4_t*)(fin + (int64_t)(srow0 + 16 * mt + l16) * D + ncol(nt)) = xr[mt][nt];
+      *(f32x4_t*)(fin + fin_off + (int64_t)(trow(mt) + l16) * D + ncol(nt)) = xr[mt][nt];
+  }
 }
 
 // One workgroup's job; `blk` is its block index within the launch of p. The
@@ -586,6 +597,12 @@ __device__ __forceinline__ void scan_block(const ScanParams& p, int64_t blk) {
   int rb;
   xcd_job(blk, rows_total / R, &job, &rb);
   if (job >= p.njobs) return;
+  if constexpr (MT % 2 == 0) {
+    if (p.mode == SCAN_COMPOSE) {
+      scan_rows<MT, kF, false, true>(p, job, rb, Xh, Xl, Sst);
+      return;
+    }
+  }
   if (p.mode == SCAN_COMPOSE && rb * R < D)
     scan_rows<MT, kF, true>(p, job, rb, Xh, Xl, Sst);
   else
