@@ -21,43 +21,82 @@ namespace gdn {
 
 namespace {
 
+// Granule g of a D = 128 matrix in the scan's layout holds row m, columns
+// 4 nc .. 4 nc + 3 (the inverse of u_granule). The granule-layout kernels
+// below walk the granules in order, one per thread: their granule-side loads
+// are contiguous, and the four lanes that share a row's 16-row group write (or
+// read) its row-major side as one 64-byte piece. In row-major order instead,
+// every 16-byte granule read fetched a 64-byte sector (4x the bytes).
+__device__ __forceinline__ void granule_rc(int g, int* m, int* nc) {
+  const int blk = g >> 6, r = g & 63;
+  *m = (blk >> 3) * 16 + (r & 15);
+  *nc = (blk & 7) * 4 + (r >> 4);
+}
+
 // G_{T-1} = E_{T-1} + dS_final for every head (row-major output). E is in the
-// scan's granule layout when `granule`, fp32 row-major otherwise.
+// scan's granule layout when `granule` (D = 128), fp32 row-major otherwise.
 __global__ void __launch_bounds__(256) grad_init_kernel(const float* __restrict__ E,
                                                         const float* __restrict__ ds_final,
                                                         float* __restrict__ ginit, int T, int D,
                                                         int64_t BH, int granule) {
   const int64_t DD = (int64_t)D * D;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  if (granule) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < BH * (DD / 4); i += stride) {
+      const int64_t bh = i / (DD / 4);
+      const int g = (int)(i % (DD / 4));
+      int m, nc;
+      granule_rc(g, &m, &nc);
+      float4 x = ((const float4*)(E + (bh * T + (T - 1)) * DD))[g];
+      const int64_t o = bh * DD + (int64_t)m * D + 4 * nc;
+      const float4 d = ds_final ? *(const float4*)(ds_final + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+      x.x += d.x;
+      x.y += d.y;
+      x.z += d.z;
+      x.w += d.w;
+      *(float4*)(ginit + o) = x;
+    }
+    return;
+  }
   const int64_t n_all = BH * DD;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_all;
-       i += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_all; i += stride) {
     const int64_t bh = i / DD;
     const int e = (int)(i % DD);
-    const int m = e / D, n = e % D;
     const float* Et = E + (bh * T + (T - 1)) * DD;
-    const float ev = granule ? Et[(int64_t)u_granule(m, n >> 2) * 4 + (n & 3)] : Et[e];
-    ginit[i] = ev + (ds_final ? ds_final[i] : 0.f);
+    ginit[i] = Et[e] + (ds_final ? ds_final[i] : 0.f);
   }
 }
 
 // F at the first frame of every chunk of the bidirectional backward:
 // finit[bh][c] = E_{c L} (row-major output; E in the scan's granule layout
-// when `granule`).
+// when `granule`, D = 128).
 __global__ void __launch_bounds__(256) chunk_init_kernel(const float* __restrict__ E,
                                                          float* __restrict__ finit, int T, int D,
                                                          int L, int nchunk, int64_t BH,
                                                          int granule) {
   const int64_t DD = (int64_t)D * D;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  if (granule) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < BH * nchunk * (DD / 4);
+         i += stride) {
+      const int64_t bc = i / (DD / 4);
+      const int64_t bh = bc / nchunk;
+      const int c = (int)(bc % nchunk);
+      const int g = (int)(i % (DD / 4));
+      int m, nc;
+      granule_rc(g, &m, &nc);
+      const float4 x = ((const float4*)(E + (bh * T + (int64_t)c * L) * DD))[g];
+      *(float4*)(finit + bc * DD + (int64_t)m * D + 4 * nc) = x;
+    }
+    return;
+  }
   const int64_t n_all = BH * nchunk * DD;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_all;
-       i += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_all; i += stride) {
     const int64_t bc = i / DD;
     const int64_t bh = bc / nchunk;
     const int c = (int)(bc % nchunk);
     const int e = (int)(i % DD);
-    const int m = e / D, n = e % D;
-    const float* Ea = E + (bh * T + (int64_t)c * L) * DD;
-    finit[i] = granule ? Ea[(int64_t)u_granule(m, n >> 2) * 4 + (n & 3)] : Ea[e];
+    finit[i] = E[(bh * T + (int64_t)c * L) * DD + e];
   }
 }
 
@@ -686,8 +725,9 @@ hipError_t launch_grad_init(const Shape& sh, const float* E, const float* ds_fin
                             bool granule, hipStream_t st) {
   const int64_t n = sh.BH() * sh.D * sh.D;
   if (n == 0) return hipSuccess;
-  grad_init_kernel<<<grid_cap(n), 256, 0, st>>>(E, ds_final, ginit, sh.T, sh.D, sh.BH(),
-                                                granule ? 1 : 0);
+  if (granule && sh.D != 128) return hipErrorInvalidValue;  // the granule layout is D = 128's
+  grad_init_kernel<<<grid_cap(granule ? n / 4 : n), 256, 0, st>>>(E, ds_final, ginit, sh.T, sh.D,
+                                                                  sh.BH(), granule ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -696,8 +736,9 @@ hipError_t launch_chunk_init(const Shape& sh, const float* E, int L, int nchunk,
   const int64_t n = sh.BH() * nchunk * sh.D * sh.D;
   if (n == 0) return hipSuccess;
   if (L < 1 || (int64_t)(nchunk - 1) * L >= sh.T) return hipErrorInvalidValue;
-  chunk_init_kernel<<<grid_cap(n), 256, 0, st>>>(E, finit, sh.T, sh.D, L, nchunk, sh.BH(),
-                                                 granule ? 1 : 0);
+  if (granule && sh.D != 128) return hipErrorInvalidValue;  // the granule layout is D = 128's
+  chunk_init_kernel<<<grid_cap(granule ? n / 4 : n), 256, 0, st>>>(E, finit, sh.T, sh.D, L, nchunk,
+                                                                   sh.BH(), granule ? 1 : 0);
   return hipGetLastError();
 }
 
