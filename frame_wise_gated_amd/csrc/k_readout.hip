@@ -25,13 +25,18 @@ constexpr int kTokPerWave = 32;
 constexpr int kWavesPerBlock = 4;
 // Workgroups per frame-head (their tiles interleave). HBM serves a mixed
 // read/write stream faster when the concurrently active workgroups touch a
-// narrower address window: on MI355X, 4 per frame-head ran the 60 s layer's
-// readout in 722 us against 735 us with 2; 8 and 16 lost more to staging the
-// state once per workgroup than they gained.
+// narrower address window, which more workgroups per frame-head give, while
+// every workgroup stages the state once. On MI355X, the 60 s 720p layer's
+// readout (one state) took 706 / 678-686 / 674-678 / 693-698 / 703-710 us
+// with 4 / 8 / 10 / 12 / 16 workgroups per frame-head, and its chunk-causal
+// readout (two states staged) 734 / 723 / 732 / 755-759 us with 4 / 8 / 10 / 12;
+// the 16-head 5 s layer's 81 us with 4 and 71-72 us with 8 to 16.
 #ifndef GDN_READOUT_NB
-#define GDN_READOUT_NB 4
+#define GDN_READOUT_NB 10
 #endif
-constexpr int kBlocksPerFrameHead = GDN_READOUT_NB;
+#ifndef GDN_READOUT_NB2
+#define GDN_READOUT_NB2 8
+#endif
 constexpr int kMaxBlocksPerFrameHead = 16;
 constexpr int kXcd = 8;
 
@@ -286,8 +291,9 @@ hipError_t launch_readout(const Shape& sh, const void* q, const float* sa, const
     // calls with few frame-heads (a streaming block) take more workgroups per
     // frame-head, up to two per CU in one round (512: more would start a
     // second round of workgroups)
+    const int64_t base = sb ? GDN_READOUT_NB2 : GDN_READOUT_NB;
     int64_t want = 512 / sh.FH();
-    want = want < kBlocksPerFrameHead ? kBlocksPerFrameHead : (want > kMaxBlocksPerFrameHead ? kMaxBlocksPerFrameHead : want);
+    want = want < base ? base : (want > kMaxBlocksPerFrameHead ? kMaxBlocksPerFrameHead : want);
     int nb = (ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
     if (nb > want) nb = (int)want;
     const int64_t groups = (sh.FH() + kXcd - 1) / kXcd;
