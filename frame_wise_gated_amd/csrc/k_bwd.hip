@@ -775,10 +775,11 @@ hipError_t launch_frame_grad(const Shape& sh, const float* states, const float* 
 
 // Workgroups per frame-head of the token-gradient kernel. More than one
 // narrows the window of active addresses but reloads the P and G fragments
-// per workgroup; on MI355X 1 ran fastest (1.73 ms against 1.75 ms with 2 and
-// 1.79 ms with 4 on the 60 s layer).
+// per workgroup. On MI355X, 60 s 720p layer: 1524-1551 / 1535-1537 /
+// 1502-1505 / 1516 us with 1 / 2 / 3 / 4 (an earlier version of the kernel,
+// at 1.73 ms, had run fastest with 1).
 #ifndef GDN_TG_NB
-#define GDN_TG_NB 1
+#define GDN_TG_NB 3
 #endif
 
 bool token_grad_uses_mfma(const Shape& sh) { return sh.io == 1 && sh.D == 128; }
