@@ -26,6 +26,7 @@ on the host cores on a bounded sample (``cpu_baseline``).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -80,6 +81,39 @@ def kernel_names(w, norm):
                 "readout": ("readout_mfma_bf16_d128", f"<{n}>", "k_readout.hip")}
     return {"terms": ("terms_generic", "", "k_terms.hip"),
             "readout": ("readout_generic", "", "k_readout.hip")}
+
+
+class Roctx:
+    """Named host-side ranges around the benchmark's legs, one open at a time,
+    for `rocprofv3 --marker-trace` (roctx, which ROCm ships with its profiler
+    SDK); every call is a no-op when no roctx library can be loaded."""
+
+    def __init__(self):
+        self._lib = None
+        self._open = False
+        for name in ("librocprofiler-sdk-roctx.so.1", "libroctx64.so.4"):
+            try:
+                lib = ctypes.CDLL(name)
+            except OSError:
+                continue
+            lib.roctxRangePushA.argtypes = [ctypes.c_char_p]
+            lib.roctxRangePushA.restype = ctypes.c_int
+            lib.roctxRangePop.argtypes = []
+            lib.roctxRangePop.restype = ctypes.c_int
+            self._lib = lib
+            break
+
+    def begin(self, name: str) -> None:
+        """Close the open range (if any) and open one called `name`."""
+        self.end()
+        if self._lib is not None:
+            self._lib.roctxRangePushA(name.encode())
+            self._open = True
+
+    def end(self) -> None:
+        if self._open:
+            self._lib.roctxRangePop()
+            self._open = False
 
 
 def recorded_traffic(kernel, variant, source, workload):
@@ -273,8 +307,15 @@ def main():
     stream = torch.cuda.current_stream()
     norm = bool(args.qk_rmsnorm)
 
-    def log(*a):
+    ranges = Roctx()
+
+    def log(*a, leg=False):
+        """Progress on stderr; leg=True also starts a roctx range of that name
+        (the legs run one after another, so each range ends where the next
+        begins)."""
         print("[bench]", *a, file=sys.stderr, flush=True)
+        if leg:
+            ranges.begin(" ".join(str(x) for x in a))
 
     def load(w):
         """Seeded inputs of workload w on the device, with output buffers."""
@@ -357,7 +398,7 @@ def main():
         return statistics.median(t), min(t)
 
     w = gi.workload(args.workload)
-    log("generating", w.name)
+    log("generating", w.name, leg=True)
     d = load(w)
     B, H, T, S, D = w.B, w.H, w.T, w.S, w.D
     bf = w.io == "bf16"
@@ -376,7 +417,7 @@ def main():
         # frames with gdn_step (bidirectional inside a block, the forward state
         # carried in place from block to block), as a chunk-causal model runs
         # it; the inputs are cut into contiguous per-block tensors beforehand
-        log("streaming")
+        log("streaming", leg=True)
         L = max(1, min(args.stream_block, T))
         cuts = [(a, min(a + L, T)) for a in range(0, T, L)]
         blk = [{n: d[n][:, :, a:b].contiguous() for n in ("q", "k", "v", "beta", "gamma")}
@@ -413,15 +454,16 @@ def main():
     # K steps with an event between consecutive steps (the first steps of the
     # call on this device), K steps with the phase trace on (per-phase device
     # times), K steps with per-step events again (per-step median and min)
-    log("per-step and phase-traced passes")
+    log("per-step and phase-traced passes", leg=True)
     med_first, _ = per_step(step, args.steps)
     ms_traced, summ = timed(step, args.steps)
     med, mn = per_step(step, args.steps)
     log(f"per step: median {med:.3f} (first pass {med_first:.3f}), min {mn:.3f}; "
         f"phase-traced steps: {ms_traced:.3f} ms/step")
-    log("warmup", args.warmup)
+    log("warmup", args.warmup, leg=True)
     for _ in range(args.warmup):
         step()
+    log("timed steps", args.steps, leg=True)
     # the timed region: exactly K steps between two events, nothing else
     # enqueued in between
     torch.cuda.synchronize()
@@ -511,7 +553,7 @@ def main():
     if not args.no_backward:
         # backward of the same layer: gradients of <d_o, o> for a random d_o
         # (the chunk-causal backward for the bidirectional workload)
-        log("backward")
+        log("backward", leg=True)
         gen = torch.Generator(device=dev).manual_seed(args.seed + 1)
         q = d["q"]
         d_o = torch.randn(q.shape, device=dev, dtype=torch.float32, generator=gen).to(q.dtype)
@@ -576,7 +618,7 @@ def main():
         # frame-heads of 448 tokens (16 heads x 32 frames, the first 448
         # tokens of each), k + v = 117 MB. The phase-1 time comes from the
         # same trace events as in the step.
-        log("warm phase-1 leg")
+        log("warm phase-1 leg", leg=True)
         TW, SW = 32, 448
         ww = w.with_shape(T=TW, S=SW, time_chunks=1, chunk_len=0, mode="fwd")
         dw = {n: d[n][:, :, :TW, :SW].contiguous() for n in ("q", "k", "v", "beta")}
@@ -616,7 +658,7 @@ def main():
             if idx == args.workload:
                 continue
             wc = gi.workload(idx)
-            log("config", wc.name)
+            log("config", wc.name, leg=True)
             dc = load(wc)
             sc = step_fn(wc, dc)
             medc_first, _ = per_step(sc, args.steps)
@@ -641,8 +683,9 @@ def main():
             torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline and not norm:
-        log("cpu baseline (float64 oracle)")
+        log("cpu baseline (float64 oracle)", leg=True)
         out["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds)
+    ranges.end()
     print(json.dumps(out), flush=True)
 
 

@@ -15,6 +15,11 @@
         and end timestamps in the same CSV). The defaults are MI355X's 1024
         SIMDs (256 CUs x 4) at its 2.4 GHz peak engine clock, the clock of the
         published dense MFMA peak.
+    python -m frame_wise_gated_amd.profsum markers DIR
+        the roctx ranges of a run traced with --marker-trace and --kernel-trace
+        (bench.py opens one per leg), in order: each range's host duration,
+        the kernel dispatches that started inside it and their summed device
+        time (ms).
 
 Kernels are keyed by name and grid size, so launches of one kernel with
 different shapes stay apart.
@@ -115,9 +120,22 @@ def mfma(d: str, simds: int, clock_ghz: float) -> list[str]:
     return out
 
 
+def markers(d: str) -> list[str]:
+    ranges = list(csv.DictReader(open(_one(os.path.join(d, "*marker_api_trace.csv")))))
+    kt = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+                for r in csv.DictReader(open(_one(os.path.join(d, "*kernel_trace.csv")))))
+    out = [f"{'range':48s} {'host_ms':>10s} {'kernels':>8s} {'kernel_ms':>10s}"]
+    for r in sorted(ranges, key=lambda r: int(r["Start_Timestamp"])):
+        a, b = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        inside = [(s, e) for s, e in kt if a <= s < b]
+        out.append(f"{r['Function'][:48]:48s} {(b - a) / 1e6:10.3f} {len(inside):8d} "
+                   f"{sum(e - s for s, e in inside) / 1e6:10.3f}")
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("kind", choices=("trace", "pmc", "mfma"))
+    ap.add_argument("kind", choices=("trace", "pmc", "mfma", "markers"))
     ap.add_argument("dir")
     ap.add_argument("--skip", type=int, default=0)
     ap.add_argument("--scale", type=float, default=1.0)
@@ -128,6 +146,8 @@ def main(argv=None) -> int:
         lines = trace(a.dir, a.skip)
     elif a.kind == "pmc":
         lines = pmc(a.dir, a.scale)
+    elif a.kind == "markers":
+        lines = markers(a.dir)
     else:
         lines = mfma(a.dir, a.simds, a.clock_ghz)
     print("\n".join(lines))
