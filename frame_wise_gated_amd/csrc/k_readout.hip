@@ -27,12 +27,13 @@ constexpr int kWavesPerBlock = 4;
 // read/write stream faster when the concurrently active workgroups touch a
 // narrower address window, which more workgroups per frame-head give, while
 // every workgroup stages the state once. On MI355X, the 60 s 720p layer's
-// readout (one state) took 706 / 678-686 / 674-678 / 693-698 / 703-710 us
-// with 4 / 8 / 10 / 12 / 16 workgroups per frame-head, and its chunk-causal
-// readout (two states staged) 734 / 723 / 732 / 755-759 us with 4 / 8 / 10 / 12;
-// the 16-head 5 s layer's 81 us with 4 and 71-72 us with 8 to 16.
+// readout (one state) took 706 / 678-686 / 671-675 / 674-684 / 682-684 /
+// 693-698 / 703-710 us with 4 / 8 / 9 / 10 / 11 / 12 / 16 workgroups per
+// frame-head, and its chunk-causal readout (two states staged) 734 / 723 /
+// 732 / 755-759 us with 4 / 8 / 10 / 12; the 16-head 5 s layer's 81 us with 4
+// and 70-72 us with 8 to 16.
 #ifndef GDN_READOUT_NB
-#define GDN_READOUT_NB 10
+#define GDN_READOUT_NB 9
 #endif
 #ifndef GDN_READOUT_NB2
 #define GDN_READOUT_NB2 8
